@@ -1,0 +1,408 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+* the byte sizes the pages print (FreeToken PR #196, bank sizing audit);
+* hand-computed blocks derived from the public GGUF block layout;
+* exhaustive / library checks of the fp16 and bf16 codecs;
+* an independent Python packer (tests/gguf_pack.py) for round trips;
+* brute-force integer dots and a float64 dequantize-then-GEMM identity;
+* q8_1 invariants, tie cases and an independent numpy q8_1 re-implementation.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import gguf_pack as gp
+from gguf_block_quantized_q8_amd import inputs
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+TYPES = [oracle.Q8_0, oracle.Q4_K, oracle.Q6_K]
+
+
+# ---------------------------------------------------------------- sizes
+
+def test_page_bank_sizes():
+    g = json.load(open(os.path.join(GOLD, "page_bank_sizes.json")))
+    gu, dn = g["gate_up"], g["down"]
+    assert oracle.row_bytes(oracle.Q4_K, gu["K"]) * gu["rows"] == gu["bytes_per_expert"]
+    assert oracle.row_bytes(oracle.Q6_K, dn["K"]) * dn["rows"] == dn["bytes_per_expert"]
+    assert g["experts"] * (gu["bytes_per_expert"] + dn["bytes_per_expert"]) == g["bytes_per_layer"]
+    assert g["moe_layers"] * g["bytes_per_layer"] == g["bytes_all_layers"]
+
+
+def test_geometry():
+    assert [oracle.block_len(t) for t in TYPES] == [32, 256, 256]
+    assert [oracle.block_bytes(t) for t in TYPES] == [34, 144, 210]
+    assert [oracle.group_len(t) for t in TYPES] == [32, 32, 16]
+    assert oracle.row_bytes(oracle.Q4_K, 300) == 0
+    assert oracle.row_bytes(oracle.Q8_0, 48) == 0
+    assert oracle.row_bytes(99, 256) == 0
+
+
+# ---------------------------------------------------------------- codecs
+
+def test_fp16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.fp16_to_fp32(int(b)) for b in bits], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_bf16_decode_exhaustive():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    got = np.array([oracle.bf16_to_fp32(int(b)) for b in bits], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_fp32_to_bf16_rne_vs_torch():
+    r = np.random.Generator(np.random.PCG64(7))
+    vals = np.concatenate([
+        r.standard_normal(20000).astype(np.float32) * 10.0 ** r.integers(-30, 30, 20000),
+        # exact ties between two bf16 neighbours: low 16 bits == 0x8000
+        (r.integers(0, 2**31, 4000, dtype=np.uint32) & 0xFFFF0000 | 0x8000).view(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, -3.3895314e38, 1e-40, -1e-42], np.float32),
+    ]).astype(np.float32)
+    vals = vals[np.isfinite(vals) | np.isinf(vals)]
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.fp32_to_bf16_array(vals)
+    assert np.array_equal(got, ref)
+    assert np.isnan(oracle.bf16_to_fp32(oracle.fp32_to_bf16(float("nan"))))
+
+
+# ---------------------------------------------------------------- q8_1
+
+def _q8(x):
+    blk = oracle.quantize_block_q8_1(np.asarray(x, dtype=np.float32))
+    d, s, qs = gp.parse_q8_1(blk)
+    return float(d[0]), float(s[0]), qs
+
+
+def test_q8_1_all_zero():
+    d, s, qs = _q8(np.zeros(32))
+    assert d == 0.0 and s == 0.0 and not qs.any()
+
+
+def test_q8_1_ties_round_half_away():
+    x = np.zeros(32, np.float32)
+    x[:7] = [127, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5]
+    d, s, qs = _q8(x)
+    assert d == 1.0
+    assert list(qs[:7]) == [127, 1, 2, 3, -1, -2, -3]      # half-to-even would give 0, 2, 2
+    assert not qs[7:].any()
+    assert s == 127.0
+
+
+def test_q8_1_small_values():
+    x = np.full(32, 0.001, np.float32)
+    x[0] = 1.0
+    d, s, qs = _q8(x)
+    assert d == np.float32(1.0) / np.float32(127.0)
+    assert qs[0] == 127 and not qs[1:].any()
+    assert s == np.float32(d) * np.float32(127.0)
+
+
+def _q8_1_numpy(x):
+    """Independent numpy q8_1: fp32 division, half-away rounding done in fp64."""
+    x = np.asarray(x, dtype=np.float32).reshape(-1, 32)
+    amax = np.abs(x).max(axis=1)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = (x / d[:, None]).astype(np.float32).astype(np.float64)
+    q = np.sign(v) * np.floor(np.abs(v) + 0.5)
+    q[amax == 0] = 0
+    q = q.astype(np.int64)
+    d[amax == 0] = 0
+    s = (d * q.sum(axis=1).astype(np.float32)).astype(np.float32)
+    return d, s, q
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_q8_1_matches_independent_numpy(seed):
+    r = np.random.Generator(np.random.PCG64(seed))
+    x = (r.standard_normal((64, 256)) * 10.0 ** r.uniform(-3, 3, (64, 1))).astype(np.float32)
+    x[3, 32:64] = 0.0                      # an all-zero block
+    x[5, :32] = np.float32(2.5) * r.integers(-50, 50, 32)    # many exact halves
+    q8 = oracle.quantize_q8_1(x)
+    d, s, qs = gp.parse_q8_1(q8.ravel())
+    dr, sr, qr = _q8_1_numpy(x)
+    assert np.array_equal(d.view(np.uint32), dr.view(np.uint32))
+    assert np.array_equal(qs.astype(np.int64), qr.ravel())
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+
+
+def test_q8_1_invariants_and_bf16_input():
+    x32 = inputs.gen_act(16, 512, 11, "f32")
+    xb = inputs.gen_act(16, 512, 11, "bf16")
+    for x in (x32, xb):
+        q8 = oracle.quantize_q8_1(x)
+        d, s, qs = gp.parse_q8_1(q8.ravel())
+        q = qs.reshape(-1, 32).astype(np.int64)
+        assert np.abs(q).max() <= 127
+        assert (np.abs(q).max(axis=1) == 127).all()          # amax > 0 in every block
+        xf = x if x.dtype == np.float32 else torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float().numpy()
+        err = np.abs(xf.reshape(-1, 32).astype(np.float64) - d[:, None].astype(np.float64) * q)
+        # q = round(fl(x/d)) with |fl(x/d) - x/d| <= 127 * 2^-24: |x - d q| <= d (1/2 + 127 * 2^-24)
+        assert (err <= d[:, None].astype(np.float64) * (0.5 + 128 * 2.0 ** -24)).all()
+        assert np.array_equal(s, (d * q.sum(axis=1).astype(np.float32)).astype(np.float32))
+
+
+# ---------------------------------------------------------------- hand-computed blocks
+
+def test_q8_0_hand_block():
+    blk = gp.pack_q8_0(0x3800, np.arange(32) - 16)      # d = 0.5, q_i = i - 16
+    w = oracle.dequantize(oracle.Q8_0, blk, 1, 32)[0]
+    assert np.array_equal(w, (np.arange(32) - 16) / 2.0)
+    x = np.full((1, 32), 127.0, np.float32)             # -> d8 = 1, qa = 127, s = 4064
+    q8 = oracle.quantize_q8_1(x)
+    d, s, qs = gp.parse_q8_1(q8.ravel())
+    assert d[0] == 1.0 and s[0] == 4064.0 and (qs == 127).all()
+    assert oracle.block_dots(oracle.Q8_0, blk, 1, 32, q8, 1)[0, 0, 0] == -2032
+    assert oracle.mul_mat(oracle.Q8_0, blk, 1, 32, x)[0, 0] == -1016.0
+
+
+def _q4k_weights(blk):
+    return oracle.dequantize(oracle.Q4_K, blk, 1, 256)[0].reshape(8, 32)
+
+
+def test_q4_K_hand_block_low_bits():
+    raw = np.zeros(144, np.uint8)
+    raw[0:2] = [0x00, 0x3C]                             # d = 1.0
+    raw[2:4] = [0x00, 0x38]                             # dmin = 0.5
+    raw[4:16] = [1, 2, 3, 4, 5, 6, 7, 8, 0x21, 0x43, 0x65, 0x87]
+    raw[16:] = 0x21
+    q, sc, mn, d = oracle.unpack_block(oracle.Q4_K, raw)
+    assert list(sc) == [1, 2, 3, 4, 1, 3, 5, 7]
+    assert list(mn) == [5, 6, 7, 8, 2, 4, 6, 8]
+    assert list(d) == [1.0, 0.5]
+    w = _q4k_weights(raw)
+    for j, v in enumerate([-1.5, 1.0, -0.5, 4.0, 0.0, 4.0, 2.0, 10.0]):
+        assert (w[j] == v).all(), j
+
+
+def test_q4_K_hand_block_high_bits():
+    raw = np.zeros(144, np.uint8)
+    raw[0:2] = [0x00, 0x3C]
+    raw[2:4] = [0x00, 0x3C]
+    raw[4:8] = 0xC1
+    raw[8:12] = 0x82
+    raw[12:16] = 0x00
+    raw[16:] = 0xF0
+    q, sc, mn, d = oracle.unpack_block(oracle.Q4_K, raw)
+    assert list(sc) == [1, 1, 1, 1, 48, 48, 48, 48]
+    assert list(mn) == [2, 2, 2, 2, 32, 32, 32, 32]
+    w = _q4k_weights(raw)
+    for j, v in enumerate([-2, 13, -2, 13, -32, 688, -32, 688]):
+        assert (w[j] == v).all(), j
+
+
+def test_q4_K_hand_block_byte_order():
+    raw = np.zeros(144, np.uint8)
+    raw[0:2] = [0x00, 0x3C]
+    raw[4:16] = [1, 1, 1, 1, 0, 0, 0, 0, 1, 1, 1, 1]
+    raw[16:] = np.arange(128)
+    w = _q4k_weights(raw)
+    l = np.arange(32)
+    for c in range(4):
+        assert np.array_equal(w[2 * c], l & 15)
+        assert np.array_equal(w[2 * c + 1], 2 * c + (l >= 16))
+
+
+def test_q6_K_hand_block_bits():
+    raw = np.zeros(210, np.uint8)
+    raw[0:128] = 0x5A
+    raw[128:192] = 0xE4
+    raw[192:208] = 1
+    raw[208:210] = [0x00, 0x3C]
+    w = oracle.dequantize(oracle.Q6_K, raw, 1, 256)[0].reshape(2, 4, 32)
+    for h in range(2):
+        for g, v in enumerate([-22, -6, 5, 21]):
+            assert (w[h, g] == v).all()
+
+
+def test_q6_K_hand_block_byte_order():
+    raw = np.zeros(210, np.uint8)
+    raw[0:128] = np.arange(128)
+    raw[192:208] = 1
+    raw[208:210] = [0x00, 0x3C]
+    w = oracle.dequantize(oracle.Q6_K, raw, 1, 256)[0]
+    l = np.arange(32)
+    lo = (l & 15) - 32
+    hi = (l >= 16).astype(int)
+    expect = np.concatenate([lo, lo, -32 + hi, -30 + hi, lo, lo, -28 + hi, -26 + hi])
+    assert np.array_equal(w, expect)
+
+
+# ---------------------------------------------------------------- round trips with the independent packer
+
+@pytest.mark.parametrize("t", TYPES)
+def test_unpack_round_trip(t):
+    r = np.random.Generator(np.random.PCG64(100 + t))
+    for _ in range(50):
+        f = gp.random_fields(t, r)
+        q, sc, mn, d = oracle.unpack_block(t, gp.pack(t, f))
+        if t == oracle.Q8_0:
+            assert np.array_equal(q, f["q"]) and list(sc) == [1]
+            assert d[0] == np.float32(gp.f16_val(f["d"]))
+        elif t == oracle.Q4_K:
+            assert np.array_equal(q, f["nib"]) and np.array_equal(sc, f["sc"]) and np.array_equal(mn, f["mn"])
+            assert d[0] == np.float32(gp.f16_val(f["d"])) and d[1] == np.float32(gp.f16_val(f["dmin"]))
+        else:
+            assert np.array_equal(q, f["q6"]) and np.array_equal(sc, f["sc"])
+            assert d[0] == np.float32(gp.f16_val(f["d"]))
+
+
+@pytest.mark.parametrize("t", TYPES)
+def test_dequantize_vs_fields(t):
+    """Every dequantized value equals the float64 field formula rounded once to fp32 (bf16: then RNE)."""
+    r = np.random.Generator(np.random.PCG64(200 + t))
+    qk = oracle.block_len(t)
+    blocks, ref = [], []
+    for _ in range(64):
+        f = gp.random_fields(t, r)
+        blocks.append(gp.pack(t, f))
+        ref.append(gp.weights_f64(t, f))
+    W = np.concatenate(blocks).reshape(8, -1)
+    K = 8 * qk
+    ref = np.concatenate(ref).reshape(8, K).astype(np.float32)
+    got = oracle.dequantize(t, W, 8, K)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    gotb = oracle.dequantize(t, W, 8, K, oracle.BF16)
+    refb = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(gotb, refb)
+
+
+# ---------------------------------------------------------------- integer dots and the quantized dot
+
+def _packed_matrix(t, N, nblk, seed):
+    r = np.random.Generator(np.random.PCG64(seed))
+    fields = [[gp.random_fields(t, r) for _ in range(nblk)] for _ in range(N)]
+    W = np.stack([np.concatenate([gp.pack(t, f) for f in row]) for row in fields])
+    return W, fields
+
+
+@pytest.mark.parametrize("t", TYPES)
+def test_block_dots_brute_force(t):
+    qk, g = oracle.block_len(t), oracle.group_len(t)
+    nblk = 4 if qk == 256 else 8
+    N, M, K = 5, 3, nblk * qk
+    W, fields = _packed_matrix(t, N, nblk, 300 + t)
+    x = inputs.gen_act(M, K, 301, "f32")
+    q8 = oracle.quantize_q8_1(x)
+    got = oracle.block_dots(t, W, N, K, q8, M)
+    for m in range(M):
+        _, _, qa = gp.parse_q8_1(q8[m])
+        for n in range(N):
+            wq = np.concatenate([gp.dot_quants(t, f) for f in fields[n]])
+            ref = (wq * qa.astype(np.int64)).reshape(-1, g).sum(axis=1)
+            assert np.array_equal(got[m, n], ref)
+
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("K_blocks", [1, 2, 4])
+def test_quantized_dot_identity_fp64(t, K_blocks):
+    """O5(W, x) == sum_i w_i * (d8 * qa)_i in float64, to ~2^-20 of sum |terms|.
+
+    Exact in real arithmetic because s8 = d8 * sum(qa); the only differences
+    are the fp32 rounding of s8, fp64 summation order and the final fp32."""
+    qk = oracle.block_len(t)
+    nblk = K_blocks if qk == 256 else 8 * K_blocks
+    N, M, K = 24, 5, nblk * qk
+    W, fields = _packed_matrix(t, N, nblk, 400 + 10 * t + K_blocks)
+    x = inputs.gen_act(M, K, 401 + K_blocks, "f32")
+    x[1] *= 1e-3
+    x[2, :] = 0.0
+    y = oracle.mul_mat(t, W, N, K, x)
+    q8 = oracle.quantize_q8_1(x)
+    for m in range(M):
+        d8, _, qa = gp.parse_q8_1(q8[m])
+        a = np.repeat(d8.astype(np.float64), 32) * qa.astype(np.float64)
+        for n in range(N):
+            w = np.concatenate([gp.weights_f64(t, f) for f in fields[n]])
+            terms = w * a
+            ref = terms.sum()
+            tol = 2.0 ** -20 * np.abs(terms).sum() + 2.0 ** -23 * abs(ref) + 1e-30
+            assert abs(float(y[m, n]) - ref) <= tol, (m, n, float(y[m, n]), ref)
+    assert not y[2].any()
+
+
+def test_mul_mat_bf16_and_q8_1_inputs_agree():
+    t, N, K, M = oracle.Q4_K, 16, 512, 3
+    W = inputs.gen_q4_K(N, K, 5)
+    xb = inputs.gen_act(M, K, 6, "bf16")
+    q8 = oracle.quantize_q8_1(xb)
+    y1 = oracle.mul_mat(t, W, N, K, xb)
+    y2 = oracle.mul_mat(t, W, N, K, q8, xdt=oracle.Q8_1)
+    assert np.array_equal(y1, y2)
+    rows = np.array([15, 0, 7])
+    y3 = oracle.mul_mat(t, W, N, K, xb, rows=rows)
+    assert np.array_equal(y3, y1[:, rows])
+
+
+# ---------------------------------------------------------------- routed experts
+
+def _moe_small(seed=9):
+    E, N, K, T, top_k = 6, 16, 256, 5, 3
+    W = inputs.gen_experts(oracle.Q4_K, E, N, K, seed)
+    stride = W.shape[1] * W.shape[2]
+    x = inputs.gen_act(T, K, seed + 1, "f32")
+    ids = np.array([[0, 2, 5], [1, 1, 4], [-1, 3, 3], [5, 7, 0], [2, 2, 2]], np.int32)  # dup, inactive, out of range
+    w = inputs.rng(seed + 2).uniform(0.1, 1.0, (T, top_k)).astype(np.float32)
+    return E, N, K, T, top_k, W, stride, x, ids, w
+
+
+def test_mul_mat_id_reduces_to_mul_mat():
+    E, N, K, T, top_k, W, stride, x, ids, w = _moe_small()
+    y = oracle.mul_mat_id(oracle.Q4_K, W, E, N, K, stride, x, T, 0, ids, top_k)
+    for t in range(T):
+        for k in range(top_k):
+            e = ids[t, k]
+            if 0 <= e < E:
+                ref = oracle.mul_mat(oracle.Q4_K, W[e], N, K, x[t:t + 1])[0]
+                assert np.array_equal(y[t, k], ref)
+            else:
+                assert not y[t, k].any()
+
+
+def test_mul_mat_id_gather_form_and_tokens():
+    E, N, K, T, top_k, W, stride, _, ids, w = _moe_small(19)
+    xr = inputs.gen_act(T * top_k, K, 77, "bf16").reshape(T, top_k, K)
+    y = oracle.mul_mat_id(oracle.Q4_K, W, E, N, K, stride, xr, T, 1, ids, top_k)
+    for t in range(T):
+        for k in range(top_k):
+            e = ids[t, k]
+            if 0 <= e < E:
+                assert np.array_equal(y[t, k], oracle.mul_mat(oracle.Q4_K, W[e], N, K, xr[t, k:k + 1])[0])
+    toks = np.array([4, 1])
+    ys = oracle.mul_mat_id(oracle.Q4_K, W, E, N, K, stride, xr, T, 1, ids, top_k, tokens=toks)
+    assert np.array_equal(ys, y[toks])
+
+
+def test_mul_mat_id_swiglu_and_weighted_sum():
+    E, N, K, T, top_k, W, stride, x, ids, w = _moe_small(29)
+    o = oracle.mul_mat_id(oracle.Q4_K, W, E, N, K, stride, x, T, 0, ids, top_k).astype(np.float64)
+    g, u = o[..., :N // 2], o[..., N // 2:]
+    h_ref = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+    h = oracle.mul_mat_id(oracle.Q4_K, W, E, N, K, stride, x, T, 0, ids, top_k, epi=oracle.EPI_SWIGLU)
+    assert np.array_equal(h, h_ref)
+    ys = oracle.mul_mat_id(oracle.Q4_K, W, E, N, K, stride, x, T, 0, ids, top_k, route_w=w)
+    active = ((ids >= 0) & (ids < E)).astype(np.float64)
+    ref = np.zeros((T, N))
+    for t in range(T):
+        for k in range(top_k):                      # ascending k, fp64
+            ref[t] += active[t, k] * float(w[t, k]) * o[t, k].astype(np.float32).astype(np.float64)
+    assert np.array_equal(ys, ref.astype(np.float32))
+
+
+def test_routing_generator():
+    ids, w = inputs.gen_routing(64, 256, 8, 504)
+    assert ids.shape == (64, 8) and ids.min() >= 0 and ids.max() < 256
+    assert all(len(set(r)) == 8 for r in ids)
+    assert (np.diff(w, axis=1) <= 0).all() and (w > 0).all() and (w.sum(axis=1) < 1).all()
