@@ -1,0 +1,335 @@
+"""Benchmark of the GGUF block-quantized matmul hot path on one MI355X.
+
+Default (the headline): Q4_K 4096 x 4096 decode at M = 1 (bf16 activations
+quantized to q8_1 on the fly, MMVQ, bf16 out).  One step = one full call
+(q8_1 quantization + MMVQ) against the next of 120 weight copies (1.13 GB),
+so every step streams its weights from HBM rather than the 256 MB MALL; the K
+timed steps are captured in one HIP graph so launch overhead is not timed.
+value = algorithmic bytes per step x K / time (GB/s).
+
+The same JSON line carries, under "also", the other workloads of the
+benchmark set, each timed the same way: Q4_K 4096x4096 at M = 2, 4, 8; the
+Q4_K 8192 x 2048 prefill at M = 8192 (MMQ, TOPS) and its M = 16..64 sweep on
+both paths; the Q6_K 248320 x 2048 lm_head at M = 1 (GB/s) and M = 2048
+(TOPS); the E = 256, top-8 MoE layer (gate_up Q4_K + SwiGLU, down Q6_K +
+route-weighted sum) at T = 16 and T = 8192.
+
+roofline: the dominant kernel's algorithmic bytes (or int8 ops) per launch over
+its mean launch duration, measured with HIP events recorded on the launch
+stream around each launch, against MI355X peaks (HBM 8 TB/s; dense int8 MFMA
+5.0 POP/s).  cpu_baseline: the CPU oracle on a bounded sample of the headline
+workload, on this host's cores.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gguf_block_quantized_q8_amd as g  # noqa: E402
+from gguf_block_quantized_q8_amd import inputs  # noqa: E402
+
+METRIC = "MMVQ GB/s @M=1 and MMQ/mul_mat_id TOPS @M=8192 (Q4_K,Q6_K), % of roofline"
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+ROTATE_BYTES = 1 << 30
+PROFILE_TRAFFIC = {}      # filled from committed rocprofv3 counter runs when present
+
+
+def vp(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def bf16(a, dev):
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def check(rc, what):
+    if rc != 0:
+        raise RuntimeError(f"{what}: {g.lib().ggq_last_error().decode()}")
+
+
+class Ctx:
+    def __init__(self, dev):
+        self.dev = dev
+        self.L = g.lib()
+        self.stream = torch.cuda.current_stream(dev)
+
+    @property
+    def s(self):
+        return ctypes.c_void_p(torch.cuda.current_stream(self.dev).cuda_stream)
+
+
+def time_steps(step, K, W, graph):
+    """W untimed warmup steps, then exactly K timed steps (optionally as one HIP graph)."""
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    if graph:
+        gr = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step(0)                        # side-stream warm call before capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            for i in range(K):
+                step(i)
+        gr.replay()                        # untimed first replay (uploads the graph)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gr.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        del gr
+        return dt
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def time_launches(launch, n):
+    """Mean duration of one launch: HIP events recorded on the launch stream around each launch."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    launch(0)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        launch(i)
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(ms)) * 1e-3
+
+
+def roofline_bytes(nbytes, sec, kernel):
+    a = nbytes / sec / 1e9
+    return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": PROFILE_TRAFFIC.get(kernel), "kernel": kernel,
+            "kernel_us": round(sec * 1e6, 3)}
+
+
+def roofline_ops(ops, sec, kernel):
+    a = ops / sec / 1e12
+    return {"bound": "mfma", "achieved": round(a, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+            "frac": round(a / INT8_PEAK_TOPS, 4), "traffic": PROFILE_TRAFFIC.get(kernel), "kernel": kernel,
+            "kernel_us": round(sec * 1e6, 3), "ops_note": "int8 ops = 2*M*N*K, peak = dense int8 MFMA"}
+
+
+# ------------------------------------------------------------------ dense decode (MMVQ)
+
+def bench_decode(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, rotate=True):
+    dev = ctx.dev
+    rb = g.row_bytes(wt, K)
+    wbytes = N * rb
+    R = max(1, -(-ROTATE_BYTES // wbytes)) if rotate else 1
+    W0 = torch.from_numpy(inputs.gen_weights(wt, N, K, seed_w)).to(dev)
+    Wr = W0.unsqueeze(0).repeat(R, 1, 1).contiguous() if R > 1 else W0.unsqueeze(0)
+    del W0
+    x = bf16(inputs.gen_act(M, K, seed_x, "bf16"), dev)
+    y = torch.empty((M, N), dtype=ydt, device=dev)
+    ydt_c = g.F32 if ydt == torch.float32 else g.BF16
+    wsb = ctx.L.ggq_mul_mat_ws(wt, N, K, g.BF16, M, g.PATH_MMVQ)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    q8 = torch.empty(M * (K // 32) * 40, dtype=torch.uint8, device=dev)
+
+    def step(i):
+        check(ctx.L.ggq_mul_mat(wt, vp(Wr[i % R]), N, K, vp(x), g.BF16, M, K, vp(y), ydt_c, N, vp(ws), wsb,
+                                g.PATH_MMVQ, ctx.s), "mul_mat")
+
+    check(ctx.L.ggq_quantize_q8_1(vp(x), g.BF16, M, K, K, vp(q8), ctx.s), "quantize")
+
+    def kernel_only(i):
+        check(ctx.L.ggq_mul_mat(wt, vp(Wr[i % R]), N, K, vp(q8), g.Q8_1, M, K, vp(y), ydt_c, N, None, 0,
+                                g.PATH_MMVQ, ctx.s), "mul_mat q8_1")
+
+    dt = time_steps(step, steps, warmup, graph=True)
+    ysz = 4 if ydt == torch.float32 else 2
+    step_bytes = wbytes + M * K * 2 + 2 * M * (K // 32) * 40 + M * N * ysz
+    kern_bytes = wbytes + M * (K // 32) * 40 + M * N * ysz
+    ksec = time_launches(kernel_only, min(200, 4 * R))
+    del Wr
+    return {"value": step_bytes * steps / dt / 1e9, "unit": "GB/s", "ms_per_step": dt / steps * 1e3,
+            "step_bytes": step_bytes, "rotating_copies": R,
+            "roofline": roofline_bytes(kern_bytes, ksec, "mmvq_kernel")}
+
+
+# ------------------------------------------------------------------ dense prefill (MMQ)
+
+def bench_prefill(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, path=g.PATH_AUTO):
+    dev = ctx.dev
+    W = torch.from_numpy(inputs.gen_weights(wt, N, K, seed_w)).to(dev)
+    x = bf16(inputs.gen_act(M, K, seed_x, "bf16"), dev)
+    y = torch.empty((M, N), dtype=ydt, device=dev)
+    ydt_c = g.F32 if ydt == torch.float32 else g.BF16
+    wsb = ctx.L.ggq_mul_mat_ws(wt, N, K, g.BF16, M, path)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        check(ctx.L.ggq_mul_mat(wt, vp(W), N, K, vp(x), g.BF16, M, K, vp(y), ydt_c, N, vp(ws), wsb, path, ctx.s),
+              "mul_mat")
+
+    graph = M * N * K < 2e11
+    dt = time_steps(step, steps, warmup, graph=graph)
+    ops = 2.0 * M * N * K
+    res = {"value": ops * steps / dt / 1e12, "unit": "TOPS", "ms_per_step": dt / steps * 1e3}
+    if path != g.PATH_MMVQ and M > 8:
+        # kernel alone: pre-quantized planar operands are produced inside the call, so time the
+        # whole call and subtract the quantize kernel measured on its own
+        q8 = torch.empty(M * (K // 32) * 40, dtype=torch.uint8, device=dev)
+        tq = time_launches(lambda i: check(ctx.L.ggq_quantize_q8_1(vp(x), g.BF16, M, K, K, vp(q8), ctx.s), "q"), 20)
+        tc = time_launches(step, 20)
+        res["roofline"] = roofline_ops(ops, max(tc - tq, 1e-9), "mmq_kernel")
+        res["quantize_us"] = round(tq * 1e6, 2)
+    return res
+
+
+# ------------------------------------------------------------------ MoE layer
+
+def bench_moe(ctx, Tn, steps, warmup):
+    dev = ctx.dev
+    E, H, I, top_k = 256, 2048, 512, 8
+    Wgu = torch.from_numpy(inputs.gen_experts(g.Q4_K, E, 2 * I, H, 501)).to(dev)
+    Wd = torch.from_numpy(inputs.gen_experts(g.Q6_K, E, H, I, 502)).to(dev)
+    x = bf16(inputs.gen_act(Tn, H, 503, "bf16"), dev)
+    ids_np, w_np = inputs.gen_routing(Tn, E, top_k, 504)
+    ids = torch.from_numpy(ids_np).to(dev)
+    w = torch.from_numpy(w_np).to(dev)
+    h = torch.empty((Tn, top_k, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((Tn, H), dtype=torch.bfloat16, device=dev)
+    L = ctx.L
+    ws1b = L.ggq_mul_mat_id_ws(g.Q4_K, E, 2 * I, H, g.BF16, Tn, 0, top_k, g.EPI_SWIGLU, 0, g.PATH_AUTO)
+    ws2b = L.ggq_mul_mat_id_ws(g.Q6_K, E, H, I, g.BF16, Tn, 1, top_k, g.EPI_NONE, 1, g.PATH_AUTO)
+    ws1 = torch.empty(ws1b, dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(ws2b, dtype=torch.uint8, device=dev)
+    s_gu = Wgu.stride(0)
+    s_d = Wd.stride(0)
+
+    def gate_up(i):
+        check(L.ggq_mul_mat_id(g.Q4_K, vp(Wgu), E, 2 * I, H, s_gu, vp(x), g.BF16, Tn, 0, vp(ids), top_k, None,
+                               g.EPI_SWIGLU, vp(h), g.BF16, vp(ws1), ws1b, g.PATH_AUTO, ctx.s), "gate_up")
+
+    def down(i):
+        check(L.ggq_mul_mat_id(g.Q6_K, vp(Wd), E, H, I, s_d, vp(h), g.BF16, Tn, 1, vp(ids), top_k, vp(w),
+                               g.EPI_NONE, vp(y), g.BF16, vp(ws2), ws2b, g.PATH_AUTO, ctx.s), "down")
+
+    def step(i):
+        gate_up(i)
+        down(i)
+
+    dt = time_steps(step, steps, warmup, graph=Tn <= 64)
+    R = Tn * top_k
+    res = {"ms_per_step": dt / steps * 1e3}
+    tg = time_launches(gate_up, 20)
+    td = time_launches(down, 20)
+    if Tn <= 64:
+        distinct = len(np.unique(ids_np))
+        moved = distinct * (Wgu.stride(0) + Wd.stride(0)) + Tn * H * 2 * 2 + R * I * 2 * 2
+        res.update({"value": moved * steps / dt / 1e9, "unit": "GB/s", "distinct_experts": int(distinct),
+                    "roofline": roofline_bytes(distinct * Wgu.stride(0), tg, "mmvq_id gate_up (call)"),
+                    "down_call_us": round(td * 1e6, 2)})
+    else:
+        ops_gu = 2.0 * R * 2 * I * H
+        ops_d = 2.0 * R * H * I
+        res.update({"value": (ops_gu + ops_d) * steps / dt / 1e12, "unit": "TOPS",
+                    "roofline": roofline_ops(ops_gu, tg, "mmq_id gate_up (call)"),
+                    "down": roofline_ops(ops_d, td, "mmq_id down (call)")})
+    return res
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(seconds=10.0):
+    import oracle
+    N, K = 4096, 4096
+    W = inputs.gen_q4_K(N, K, 201)
+    x = inputs.gen_act(1, K, 202, "bf16")
+    rows = N // 4                      # bounded sample: a quarter of the rows per call
+    sel = np.arange(rows, dtype=np.int64)
+    oracle.mul_mat(oracle.Q4_K, W, N, K, x, rows=sel)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        oracle.mul_mat(oracle.Q4_K, W, N, K, x, rows=sel)
+        n += 1
+    dt = time.perf_counter() - t0
+    moved = rows * g.row_bytes(g.Q4_K, K) + K * 2 + 2 * (K // 32) * 40 + rows * 2
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(moved * n / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"q4_K 4096x4096 M=1: {rows} of 4096 weight rows per call (quantize + fp64 quantized dot), "
+                      f"{n} calls in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ctx = Ctx(dev)
+    K, W = args.steps, args.warmup
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    log("headline: q4_K 4096x4096 decode M=1")
+    head = bench_decode(ctx, g.Q4_K, 4096, 4096, 1, 201, 202, torch.bfloat16, K, W)
+    also = []
+    if not args.only_headline:
+        for M in (2, 4, 8):
+            log(f"q4_K 4096x4096 decode M={M}")
+            r = bench_decode(ctx, g.Q4_K, 4096, 4096, M, 201, 202, torch.bfloat16, K, W)
+            also.append({"workload": "q4_K_4096x4096_decode", "M": M, **r})
+        log("q4_K 8192x2048 prefill M=8192")
+        r = bench_prefill(ctx, g.Q4_K, 8192, 2048, 8192, 301, 302, torch.bfloat16, max(5, K // 20), max(2, W // 10))
+        also.append({"workload": "q4_K_8192x2048_prefill", "M": 8192, **r})
+        for M in (16, 24, 32, 64):
+            for path, pn in ((g.PATH_MMVQ, "mmvq"), (g.PATH_MMQ, "mmq")):
+                log(f"q4_K 8192x2048 sweep M={M} {pn}")
+                r = bench_prefill(ctx, g.Q4_K, 8192, 2048, M, 301, 302, torch.bfloat16, max(20, K // 4), W, path)
+                also.append({"workload": "q4_K_8192x2048_prefill_sweep", "M": M, "path": pn, **r})
+        log("q6_K 248320x2048 lm_head M=1")
+        r = bench_decode(ctx, g.Q6_K, 248320, 2048, 1, 401, 402, torch.float32, max(20, K // 4), W, rotate=False)
+        also.append({"workload": "q6_K_248320x2048_lm_head", "M": 1, **r})
+        log("q6_K 248320x2048 lm_head M=2048")
+        r = bench_prefill(ctx, g.Q6_K, 248320, 2048, 2048, 401, 402, torch.float32, max(3, K // 40), 1)
+        also.append({"workload": "q6_K_248320x2048_lm_head", "M": 2048, **r})
+        torch.cuda.empty_cache()
+        for Tn in (16, 8192):
+            log(f"moe T={Tn}")
+            r = bench_moe(ctx, Tn, max(5, K // (1 if Tn <= 64 else 20)), max(2, W // 4))
+            also.append({"workload": "moe_e256_top8_h2048_i512", "T": Tn, **r})
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+    line = {
+        "metric": METRIC, "value": round(head["value"], 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(head["ms_per_step"], 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "q4_K_4096x4096_decode", "M": 1, "N": 4096, "K": 4096, "weights": "Q4_K",
+                   "activations": "bf16 -> q8_1", "output": "bf16", "rotating_weight_copies": head["rotating_copies"],
+                   "step_bytes": head["step_bytes"]},
+        "roofline": head["roofline"], "cpu_baseline": cpu, "also": also,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

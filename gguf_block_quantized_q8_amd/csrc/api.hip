@@ -1,0 +1,374 @@
+// C ABI: argument validation, workspace carving, path dispatch.  All checks
+// run on the host before anything is launched; nothing here synchronizes.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.hpp"
+#include "../../include/ggq.h"
+
+using namespace ggq;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(GGQ_ERR_HIP, "%s: HIP error %s", what, hipGetErrorString(e));
+    return GGQ_OK;
+}
+
+const char *tname(int t) {
+    return t == GGQ_Q8_0 ? "Q8_0" : t == GGQ_Q4_K ? "Q4_K" : t == GGQ_Q6_K ? "Q6_K" : "?";
+}
+
+bool known_type(int t) { return t == GGQ_Q8_0 || t == GGQ_Q4_K || t == GGQ_Q6_K; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// activation rows quantized on the fly (MMVQ: q8_1 blocks; MMQ: planar fp16 + d + s)
+size_t act_bytes(bool mmq, int64_t rows, int64_t K) {
+    if (mmq) return align256((size_t)rows * K * 2) + 2 * align256((size_t)rows * (K / 32) * 4);
+    return align256((size_t)rows * (K / 32) * Q8_1_BYTES);
+}
+
+struct Carve {
+    uint8_t *base;
+    size_t off = 0;
+    explicit Carve(void *b) : base(static_cast<uint8_t *>(b)) {}
+    template <class T> T *take(size_t bytes) {
+        T *p = reinterpret_cast<T *>(base ? base + off : nullptr);
+        off += align256(bytes);
+        return p;
+    }
+};
+
+struct Planar {
+    _Float16 *xq;
+    float *xd, *xs;
+};
+
+Planar carve_planar(Carve &c, int64_t rows, int64_t K) {
+    Planar p;
+    p.xq = c.take<_Float16>((size_t)rows * K * 2);
+    p.xd = c.take<float>((size_t)rows * (K / 32) * 4);
+    p.xs = c.take<float>((size_t)rows * (K / 32) * 4);
+    return p;
+}
+
+// Dense dispatch: MMVQ for up to 8 activation rows (and always for Q8_0), MMQ above.
+constexpr int64_t MMVQ_MAX_ROWS = 8;
+// Routed dispatch: MMVQ-id up to this many tokens, MMQ-id above.
+constexpr int64_t MMVQ_ID_MAX_TOKENS = 32;
+constexpr int MMVQ_ID_J = 8;
+
+bool use_mmq(int wt, int64_t M, int path) {
+    if (path == GGQ_PATH_MMQ) return true;
+    if (path == GGQ_PATH_MMVQ) return false;
+    return wt != GGQ_Q8_0 && M > MMVQ_MAX_ROWS;
+}
+
+bool use_mmq_id(int wt, int64_t T, int path) {
+    if (path == GGQ_PATH_MMQ) return true;
+    if (path == GGQ_PATH_MMVQ) return false;
+    return wt != GGQ_Q8_0 && T > MMVQ_ID_MAX_TOKENS;
+}
+
+int check_weights(int wt, int64_t N, int64_t K) {
+    if (!known_type(wt)) return fail(GGQ_ERR_UNSUPPORTED, "ggml type %d is not supported (Q8_0=8, Q4_K=12, Q6_K=14)", wt);
+    if (N < 0 || K <= 0) return fail(GGQ_ERR_INVALID, "ggml type %s: bad shape N=%lld K=%lld", tname(wt), (long long)N, (long long)K);
+    if (K % block_len(wt) != 0)
+        return fail(GGQ_ERR_INVALID, "ggml type %s K=%lld is not a multiple of the block length %lld", tname(wt),
+                    (long long)K, (long long)block_len(wt));
+    return GGQ_OK;
+}
+
+int nc_for(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+
+}  // namespace
+
+extern "C" {
+
+const char *ggq_last_error(void) { return g_err; }
+
+size_t ggq_row_bytes(int type, int64_t K) {
+    if (!known_type(type) || K < 0 || K % block_len(type)) return 0;
+    return (size_t)(K / block_len(type) * block_bytes(type));
+}
+
+size_t ggq_q8_1_bytes(int64_t M, int64_t K) {
+    if (M < 0 || K < 0) return 0;
+    return (size_t)M * (size_t)(K / 32) * Q8_1_BYTES;
+}
+
+int ggq_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, void *q8, void *stream) {
+    g_err[0] = 0;
+    if (xdt != GGQ_F32 && xdt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "quantize_q8_1: input dtype %d must be F32 or BF16", xdt);
+    if (M < 0 || K < 0 || K % 32) return fail(GGQ_ERR_INVALID, "quantize_q8_1: K=%lld must be a non-negative multiple of 32", (long long)K);
+    if (ldx < K) return fail(GGQ_ERR_INVALID, "quantize_q8_1: ldx=%lld < K=%lld", (long long)ldx, (long long)K);
+    if (M == 0 || K == 0) return GGQ_OK;
+    if (!x || !q8) return fail(GGQ_ERR_INVALID, "quantize_q8_1: null pointer");
+    if (!aligned16(x) || !aligned16(q8)) return fail(GGQ_ERR_INVALID, "quantize_q8_1: pointers must be 16-byte aligned");
+    return hip_status(launch_quantize(x, xdt, M, K, ldx, static_cast<uint8_t *>(q8), nullptr, nullptr, nullptr,
+                                      static_cast<hipStream_t>(stream)), "quantize_q8_1");
+}
+
+int ggq_dequantize(int wt, const void *W, int64_t rows, int64_t K, void *y, int ydt, void *stream) {
+    g_err[0] = 0;
+    int rc = check_weights(wt, rows, K);
+    if (rc) return rc;
+    if (ydt != GGQ_F32 && ydt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "dequantize: output dtype %d must be F32 or BF16", ydt);
+    if (rows == 0) return GGQ_OK;
+    if (!W || !y) return fail(GGQ_ERR_INVALID, "dequantize: null pointer");
+    if (!aligned16(W) || !aligned16(y)) return fail(GGQ_ERR_INVALID, "dequantize: pointers must be 16-byte aligned");
+    return hip_status(launch_dequant(wt, static_cast<const uint8_t *>(W), rows, K, y, ydt, static_cast<hipStream_t>(stream)),
+                      "dequantize");
+}
+
+size_t ggq_mul_mat_ws(int wt, int64_t N, int64_t K, int xdt, int64_t M, int path) {
+    if (!known_type(wt) || M <= 0 || N <= 0 || K <= 0 || K % block_len(wt)) return 0;
+    const bool mmq = use_mmq(wt, M, path);
+    if (!mmq && xdt == GGQ_Q8_1) return 0;
+    return act_bytes(mmq, M, K);
+}
+
+int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int xdt, int64_t M, int64_t ldx, void *y,
+                int ydt, int64_t ldy, void *ws, size_t ws_bytes, int path, void *stream) {
+    g_err[0] = 0;
+    int rc = check_weights(wt, N, K);
+    if (rc) return rc;
+    if (xdt != GGQ_F32 && xdt != GGQ_BF16 && xdt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: input dtype %d", xdt);
+    if (ydt != GGQ_F32 && ydt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: output dtype %d must be F32 or BF16", ydt);
+    if (path != GGQ_PATH_AUTO && path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "mul_mat: bad path %d", path);
+    if (path == GGQ_PATH_MMQ && wt == GGQ_Q8_0) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: MMQ path has no Q8_0 kernel; use MMVQ");
+    if (M < 0) return fail(GGQ_ERR_INVALID, "mul_mat: M=%lld < 0", (long long)M);
+    if (xdt != GGQ_Q8_1 && ldx < K) return fail(GGQ_ERR_INVALID, "mul_mat: ldx=%lld < K=%lld", (long long)ldx, (long long)K);
+    if (ldy < N) return fail(GGQ_ERR_INVALID, "mul_mat: ldy=%lld < N=%lld", (long long)ldy, (long long)N);
+    if (M == 0 || N == 0) return GGQ_OK;
+    if (!W || !x || !y) return fail(GGQ_ERR_INVALID, "mul_mat: null pointer");
+    if (!aligned16(W) || !aligned16(x) || !aligned16(y)) return fail(GGQ_ERR_INVALID, "mul_mat: pointers must be 16-byte aligned");
+    const size_t need = ggq_mul_mat_ws(wt, N, K, xdt, M, path);
+    if (ws_bytes < need || (need && !ws)) return fail(GGQ_ERR_WORKSPACE, "mul_mat: workspace %zu bytes < %zu required", ws_bytes, need);
+    if (need && !aligned16(ws)) return fail(GGQ_ERR_INVALID, "mul_mat: workspace must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool mmq = use_mmq(wt, M, path);
+    const int64_t rb = (int64_t)ggq_row_bytes(wt, K);
+    Carve c(ws);
+    if (!mmq) {
+        const uint8_t *q8 = static_cast<const uint8_t *>(x);
+        if (xdt != GGQ_Q8_1) {
+            uint8_t *q = c.take<uint8_t>((size_t)M * (K / 32) * Q8_1_BYTES);
+            rc = hip_status(launch_quantize(x, xdt, M, K, ldx, q, nullptr, nullptr, nullptr, s), "mul_mat quantize");
+            if (rc) return rc;
+            q8 = q;
+        }
+        MmvqParams p{};
+        p.W = static_cast<const uint8_t *>(W);
+        p.row_bytes = rb;
+        p.N = N;
+        p.Np = N;
+        p.npairs = (N + 1) / 2;
+        p.units = (int)(K / block_len(wt) * (wt == GGQ_Q4_K ? 8 : wt == GGQ_Q6_K ? 4 : 1));
+        p.q8 = q8;
+        p.q8_row = (K / 32) * Q8_1_BYTES;
+        p.M = M;
+        p.y = y;
+        p.ldy = ldy;
+        const int nc = nc_for(M);
+        return hip_status(launch_mmvq(wt, nc, false, GGQ_EPI_NONE, ydt, p, (M + nc - 1) / nc, s), "mul_mat mmvq");
+    }
+    Planar pl = carve_planar(c, M, K);
+    if (xdt == GGQ_Q8_1) rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), M, K, pl.xq, pl.xd, pl.xs, s), "mul_mat expand");
+    else rc = hip_status(launch_quantize(x, xdt, M, K, ldx, nullptr, pl.xq, pl.xd, pl.xs, s), "mul_mat quantize");
+    if (rc) return rc;
+    MmqParams p{};
+    p.W = static_cast<const uint8_t *>(W);
+    p.row_bytes = rb;
+    p.N = N;
+    p.Np = N;
+    p.K = K;
+    p.xq = pl.xq;
+    p.xd = pl.xd;
+    p.xs = pl.xs;
+    p.M = M;
+    p.m_tiles = (M + MMQ_MT - 1) / MMQ_MT;
+    p.n_tiles = (N + MMQ_NT - 1) / MMQ_NT;
+    p.y = y;
+    p.ldy = ldy;
+    return hip_status(launch_mmq(wt, false, GGQ_EPI_NONE, ydt, p, s), "mul_mat mmq");
+}
+
+// ---------------------------------------------------------------------------
+// routed experts
+// ---------------------------------------------------------------------------
+namespace {
+
+struct IdLayout {
+    RouteTables rt;
+    int64_t max_tiles;
+    uint8_t *act;      // q8_1 rows (MMVQ) or planar base (MMQ)
+    Planar pl;
+    float *acc32;
+    size_t total;
+};
+
+IdLayout id_layout(void *ws, int wt, int64_t E, int64_t N, int64_t K, int64_t T, int x_per_route, int64_t top_k,
+                   int epi, bool weighted, bool mmq) {
+    IdLayout L{};
+    const int64_t R = T * top_k;
+    const int J = mmq ? MMQ_MT : MMVQ_ID_J;
+    L.max_tiles = route_max_tiles(R, E, J);
+    const int64_t Np = epi == GGQ_EPI_SWIGLU ? N / 2 : N;
+    const int64_t rows = x_per_route ? R : T;
+    Carve c(ws);
+    L.rt.bad = c.take<uint32_t>(4);                       // offset 0
+    L.rt.counts = c.take<uint32_t>((size_t)E * 4);
+    L.rt.offsets = c.take<uint32_t>((size_t)(E + 1) * 4);
+    L.rt.tile_off = c.take<uint32_t>((size_t)(E + 1) * 4);
+    L.rt.ntiles = c.take<uint32_t>(4);
+    L.rt.rank = c.take<int32_t>((size_t)R * 4);
+    L.rt.perm = c.take<int32_t>((size_t)R * 4);
+    L.rt.tiles = c.take<int4>((size_t)L.max_tiles * 16);
+    if (mmq) L.pl = carve_planar(c, rows, K);
+    else L.act = c.take<uint8_t>((size_t)rows * (K / 32) * Q8_1_BYTES);
+    L.acc32 = weighted ? c.take<float>((size_t)T * Np * 4) : nullptr;
+    L.total = c.off;
+    (void)wt;
+    return L;
+}
+
+}  // namespace
+
+size_t ggq_mul_mat_id_ws(int wt, int64_t E, int64_t N, int64_t K, int xdt, int64_t T, int x_per_route, int64_t top_k,
+                         int epi, int weighted, int path) {
+    (void)xdt;
+    if (!known_type(wt) || E <= 0 || N <= 0 || K <= 0 || K % block_len(wt) || T < 0 || top_k <= 0) return 0;
+    return id_layout(nullptr, wt, E, N, K, T, x_per_route, top_k, epi, weighted != 0, use_mmq_id(wt, T, path)).total;
+}
+
+int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64_t expert_stride, const void *x, int xdt,
+                   int64_t T, int x_per_route, const int32_t *ids, int64_t top_k, const float *route_w, int epi, void *y,
+                   int ydt, void *ws, size_t ws_bytes, int path, void *stream) {
+    g_err[0] = 0;
+    int rc = check_weights(wt, N, K);
+    if (rc) return rc;
+    if (xdt != GGQ_F32 && xdt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: input dtype %d must be F32 or BF16", xdt);
+    if (ydt != GGQ_F32 && ydt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: output dtype %d must be F32 or BF16", ydt);
+    if (epi != GGQ_EPI_NONE && epi != GGQ_EPI_SWIGLU) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad epilogue %d", epi);
+    if (epi == GGQ_EPI_SWIGLU && N % 2) return fail(GGQ_ERR_INVALID, "mul_mat_id: SwiGLU needs an even N (gate rows then up rows), N=%lld", (long long)N);
+    if (path != GGQ_PATH_AUTO && path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad path %d", path);
+    if (path == GGQ_PATH_MMQ && wt == GGQ_Q8_0) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: MMQ path has no Q8_0 kernel; use MMVQ");
+    if (E <= 0 || T < 0 || top_k <= 0) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad E=%lld T=%lld top_k=%lld", (long long)E, (long long)T, (long long)top_k);
+    if (x_per_route != 0 && x_per_route != 1) return fail(GGQ_ERR_INVALID, "mul_mat_id: x_per_route must be 0 or 1");
+    const int64_t rb = (int64_t)ggq_row_bytes(wt, K);
+    if (expert_stride < rb * N || expert_stride % 16) return fail(GGQ_ERR_INVALID, "mul_mat_id: expert_stride=%lld must be >= N*row_bytes=%lld and a multiple of 16", (long long)expert_stride, (long long)(rb * N));
+    if (T * top_k > INT32_MAX || E > INT32_MAX) return fail(GGQ_ERR_INVALID, "mul_mat_id: too many routes");
+    if (T == 0 || N == 0) return GGQ_OK;
+    if (!W || !x || !ids || !y) return fail(GGQ_ERR_INVALID, "mul_mat_id: null pointer");
+    if (!aligned16(W) || !aligned16(x) || !aligned16(y) || !aligned16(ids)) return fail(GGQ_ERR_INVALID, "mul_mat_id: pointers must be 16-byte aligned");
+    const bool mmq = use_mmq_id(wt, T, path);
+    const bool weighted = route_w != nullptr;
+    IdLayout L = id_layout(ws, wt, E, N, K, T, x_per_route, top_k, epi, weighted, mmq);
+    if (!ws || ws_bytes < L.total) return fail(GGQ_ERR_WORKSPACE, "mul_mat_id: workspace %zu bytes < %zu required", ws_bytes, L.total);
+    if (!aligned16(ws)) return fail(GGQ_ERR_INVALID, "mul_mat_id: workspace must be 16-byte aligned");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t R = T * top_k;
+    const int64_t Np = epi == GGQ_EPI_SWIGLU ? N / 2 : N;
+    const int64_t rows = x_per_route ? R : T;
+    const int J = mmq ? MMQ_MT : MMVQ_ID_J;
+    rc = hip_status(launch_route_build(ids, R, E, J, L.rt, s), "mul_mat_id routes");
+    if (rc) return rc;
+    if (weighted) rc = hip_status(launch_fill_u32(reinterpret_cast<uint32_t *>(L.acc32), T * Np, 0u, s), "mul_mat_id zero");
+    else rc = hip_status(launch_zero_inactive(ids, R, E, Np, y, ydt, s), "mul_mat_id zero");
+    if (rc) return rc;
+
+    if (!mmq) {
+        rc = hip_status(launch_quantize(x, xdt, rows, K, K, L.act, nullptr, nullptr, nullptr, s), "mul_mat_id quantize");
+        if (rc) return rc;
+        MmvqParams p{};
+        p.W = static_cast<const uint8_t *>(W);
+        p.row_bytes = rb;
+        p.expert_stride = expert_stride;
+        p.N = N;
+        p.Np = Np;
+        p.npairs = epi == GGQ_EPI_SWIGLU ? Np : (N + 1) / 2;
+        p.units = (int)(K / block_len(wt) * (wt == GGQ_Q4_K ? 8 : wt == GGQ_Q6_K ? 4 : 1));
+        p.q8 = L.act;
+        p.q8_row = (K / 32) * Q8_1_BYTES;
+        p.y = y;
+        p.perm = L.rt.perm;
+        p.groups = L.rt.tiles;
+        p.ngroups = L.rt.ntiles;
+        p.top_k = (int)top_k;
+        p.x_per_route = x_per_route;
+        p.route_w = route_w;
+        p.acc32 = L.acc32;
+        rc = hip_status(launch_mmvq(wt, MMVQ_ID_J, true, epi, ydt, p, L.max_tiles, s), "mul_mat_id mmvq");
+    } else {
+        rc = hip_status(launch_quantize(x, xdt, rows, K, K, nullptr, L.pl.xq, L.pl.xd, L.pl.xs, s), "mul_mat_id quantize");
+        if (rc) return rc;
+        MmqParams p{};
+        p.W = static_cast<const uint8_t *>(W);
+        p.row_bytes = rb;
+        p.expert_stride = expert_stride;
+        p.N = N;
+        p.Np = Np;
+        p.K = K;
+        p.xq = L.pl.xq;
+        p.xd = L.pl.xd;
+        p.xs = L.pl.xs;
+        p.m_tiles = L.max_tiles;
+        p.n_tiles = epi == GGQ_EPI_SWIGLU ? (Np + 63) / 64 : (N + MMQ_NT - 1) / MMQ_NT;
+        p.y = y;
+        p.perm = L.rt.perm;
+        p.tiles = L.rt.tiles;
+        p.ntiles = L.rt.ntiles;
+        p.top_k = (int)top_k;
+        p.x_per_route = x_per_route;
+        p.route_w = route_w;
+        p.acc32 = L.acc32;
+        rc = hip_status(launch_mmq(wt, true, epi, ydt, p, s), "mul_mat_id mmq");
+    }
+    if (rc) return rc;
+    if (weighted) rc = hip_status(launch_finalize(L.acc32, T * Np, y, ydt, s), "mul_mat_id finalize");
+    return rc;
+}
+
+size_t ggq_test_block_dots_ws(int wt, int64_t K, int64_t M, int path) {
+    if (path != GGQ_PATH_MMQ || !known_type(wt) || M <= 0 || K <= 0) return 0;
+    return act_bytes(true, M, K);
+}
+
+int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K, const void *q8, int64_t M, int32_t *out,
+                        void *ws, size_t ws_bytes, int path, void *stream) {
+    g_err[0] = 0;
+    int rc = check_weights(wt, N, K);
+    if (rc) return rc;
+    if (path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "test_block_dots: path must be MMVQ or MMQ");
+    if (path == GGQ_PATH_MMQ && wt == GGQ_Q8_0) return fail(GGQ_ERR_UNSUPPORTED, "test_block_dots: MMQ path has no Q8_0 kernel");
+    if (M < 0) return fail(GGQ_ERR_INVALID, "test_block_dots: M < 0");
+    if (M == 0 || N == 0) return GGQ_OK;
+    if (!W || !q8 || !out) return fail(GGQ_ERR_INVALID, "test_block_dots: null pointer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (path == GGQ_PATH_MMVQ)
+        return hip_status(launch_mmvq_dots(wt, static_cast<const uint8_t *>(W), N, K, static_cast<const uint8_t *>(q8), M, out, s),
+                          "test_block_dots mmvq");
+    const size_t need = ggq_test_block_dots_ws(wt, K, M, path);
+    if (!ws || ws_bytes < need) return fail(GGQ_ERR_WORKSPACE, "test_block_dots: workspace %zu bytes < %zu required", ws_bytes, need);
+    Carve c(ws);
+    Planar pl = carve_planar(c, M, K);
+    rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(q8), M, K, pl.xq, pl.xd, pl.xs, s), "test_block_dots expand");
+    if (rc) return rc;
+    return hip_status(launch_mmq_dots(wt, static_cast<const uint8_t *>(W), N, K, pl.xq, M, out, s), "test_block_dots mmq");
+}
+
+}  // extern "C"

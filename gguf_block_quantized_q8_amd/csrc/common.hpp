@@ -1,0 +1,90 @@
+// Shared device helpers for the gfx950 kernels: scalar codecs, block
+// geometry, byte loads from 2-byte aligned block fields, wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ggq {
+
+enum : int { T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_Q8_1 = 2 };
+
+constexpr int QK8_1 = 32;
+constexpr int Q8_1_BYTES = 40;   // float d, float s, int8 qs[32]
+
+template <int T> struct Geom;
+template <> struct Geom<T_Q8_0> { static constexpr int QK = 32,  BYTES = 34,  G = 32; };
+template <> struct Geom<T_Q4_K> { static constexpr int QK = 256, BYTES = 144, G = 32; };
+template <> struct Geom<T_Q6_K> { static constexpr int QK = 256, BYTES = 210, G = 16; };
+
+__host__ __device__ inline int64_t block_len(int t) { return t == T_Q8_0 ? 32 : (t == T_Q4_K || t == T_Q6_K) ? 256 : 0; }
+__host__ __device__ inline int64_t block_bytes(int t) { return t == T_Q8_0 ? 34 : t == T_Q4_K ? 144 : t == T_Q6_K ? 210 : 0; }
+__host__ __device__ inline int64_t group_len(int t) { return t == T_Q6_K ? 16 : 32; }
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v4i_a4 __attribute__((ext_vector_type(4), aligned(4)));  // 16 B, dword alignment
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// ---- scalar codecs ----
+__device__ __forceinline__ float fp16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);   // v_cvt_f32_f16: exact, subnormals kept
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __builtin_bit_cast(float, b << 16);
+}
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- loads ----
+__device__ __forceinline__ uint32_t ld_u16(const uint8_t *p) {
+    return *reinterpret_cast<const uint16_t *>(p);
+}
+
+// Read 16 bytes starting at a 2-byte aligned address p as 4 little-endian
+// dwords.  Touches only [p, p + 16) when p is 4-byte aligned, and
+// [p - 2, p + 16) otherwise (the last two bytes come from a 16-bit load), so a
+// field never pulls in bytes past its own end.
+__device__ __forceinline__ v4i ld16_a2(const uint8_t *p) {
+    uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if (a & 2) {
+        const uint32_t *q = reinterpret_cast<const uint32_t *>(a - 2);
+        uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
+        uint32_t w4 = *reinterpret_cast<const uint16_t *>(p + 14);
+        return v4i{(int)__builtin_amdgcn_alignbyte(w1, w0, 2), (int)__builtin_amdgcn_alignbyte(w2, w1, 2),
+                   (int)__builtin_amdgcn_alignbyte(w3, w2, 2), (int)__builtin_amdgcn_alignbyte(w4, w3, 2)};
+    }
+    return *reinterpret_cast<const v4i_a4 *>(p);
+}
+
+// 4 bytes at a 2-byte aligned address; touches [p, p + 4) or [p - 2, p + 4).
+__device__ __forceinline__ uint32_t ld4_a2(const uint8_t *p) {
+    uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    if (a & 2) {
+        uint32_t w0 = *reinterpret_cast<const uint32_t *>(a - 2);
+        uint32_t w1 = *reinterpret_cast<const uint16_t *>(p + 2);
+        return __builtin_amdgcn_alignbyte(w1, w0, 2);
+    }
+    return *reinterpret_cast<const uint32_t *>(p);
+}
+
+// ---- packed int8 dot ----
+__device__ __forceinline__ int dot4(int a, int b, int c) {
+    return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// ---- wave reductions over aligned segments of `width` lanes (power of two) ----
+__device__ __forceinline__ float seg_sum(float v, int width) {
+    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+}  // namespace ggq

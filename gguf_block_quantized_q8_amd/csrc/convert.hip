@@ -1,0 +1,284 @@
+// q8_1 quantization of activations, dequantization of weight blocks, and the
+// small fill / finalize kernels used around the matmuls.
+#include "kernels.hpp"
+
+namespace ggq {
+
+// ---------------------------------------------------------------------------
+// q8_1: 8 lanes per 32-value block, 4 values per lane.
+//   d = amax / 127 (IEEE fp32 division), q = roundf(x / d) (half away from
+//   zero), all-zero block -> d = s = 0, s = d * (float)sum(q).
+// Output either 40-byte blocks (q8 != nullptr) and/or the planar operand
+// layout of the MMQ kernels: fp16 quants [rows][K], d [rows][K/32],
+// s [rows][K/32] (xq != nullptr).
+// ---------------------------------------------------------------------------
+template <int XDT, bool VEC>
+__global__ __launch_bounds__(256) void quantize_q8_1_kernel(const void *__restrict__ x, int64_t M, int64_t K,
+                                                            int64_t ldx, uint8_t *__restrict__ q8,
+                                                            _Float16 *__restrict__ xq, float *__restrict__ xd,
+                                                            float *__restrict__ xs) {
+    const int64_t nb = K / QK8_1;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t b = gid >> 3;            // block index over M * nb
+    const int sub = threadIdx.x & 7;
+    const bool valid = b < M * nb;
+    const int64_t m = valid ? b / nb : 0;
+    const int64_t blk = valid ? b - m * nb : 0;
+    const int64_t e0 = m * ldx + blk * QK8_1 + sub * 4;
+
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+        if (XDT == DT_F32) {
+            const float *xf = static_cast<const float *>(x) + e0;
+            if (VEC) {
+                v4f t = *reinterpret_cast<const v4f *>(xf);
+                v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+            } else {
+                for (int i = 0; i < 4; i++) v[i] = xf[i];
+            }
+        } else {
+            const uint16_t *xb = static_cast<const uint16_t *>(x) + e0;
+            if (VEC) {
+                v2i t = *reinterpret_cast<const v2i *>(xb);
+                v[0] = bf16_bits_to_f32((uint32_t)t.x & 0xffffu);
+                v[1] = bf16_bits_to_f32((uint32_t)t.x >> 16);
+                v[2] = bf16_bits_to_f32((uint32_t)t.y & 0xffffu);
+                v[3] = bf16_bits_to_f32((uint32_t)t.y >> 16);
+            } else {
+                for (int i = 0; i < 4; i++) v[i] = bf16_bits_to_f32(xb[i]);
+            }
+        }
+    }
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    float d = amax / 127.0f;
+    int q[4];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        int qi = 0;
+        if (amax != 0.0f) {
+            float r = roundf(v[i] / d);
+            r = fminf(fmaxf(r, -127.0f), 127.0f);
+            qi = (int)r;
+        }
+        q[i] = qi;
+        sum += qi;
+    }
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    sum += __shfl_xor(sum, 4, 64);
+    if (amax == 0.0f) d = 0.0f;
+    const float s = d * (float)sum;
+    if (!valid) return;
+    if (q8) {
+        uint8_t *out = q8 + b * Q8_1_BYTES;
+        uint32_t packed = (uint32_t)(q[0] & 0xff) | ((uint32_t)(q[1] & 0xff) << 8) |
+                          ((uint32_t)(q[2] & 0xff) << 16) | ((uint32_t)(q[3] & 0xff) << 24);
+        reinterpret_cast<uint32_t *>(out + 8)[sub] = packed;
+        if (sub == 0) *reinterpret_cast<float2 *>(out) = make_float2(d, s);
+    }
+    if (xq) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        h4 hv = {(_Float16)q[0], (_Float16)q[1], (_Float16)q[2], (_Float16)q[3]};
+        *reinterpret_cast<h4 *>(xq + m * K + blk * QK8_1 + sub * 4) = hv;
+        if (sub == 0) {
+            xd[m * nb + blk] = d;
+            xs[m * nb + blk] = s;
+        }
+    }
+}
+
+// q8_1 blocks -> planar MMQ operand layout (for pre-quantized input).
+__global__ __launch_bounds__(256) void q8_1_to_planar_kernel(const uint8_t *__restrict__ q8, int64_t M, int64_t K,
+                                                             _Float16 *__restrict__ xq, float *__restrict__ xd,
+                                                             float *__restrict__ xs) {
+    const int64_t nb = K / QK8_1;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t b = gid >> 3;
+    const int sub = threadIdx.x & 7;
+    if (b >= M * nb) return;
+    const uint8_t *in = q8 + b * Q8_1_BYTES;
+    uint32_t w = reinterpret_cast<const uint32_t *>(in + 8)[sub];
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    h4 hv = {(_Float16)(int8_t)(w & 0xff), (_Float16)(int8_t)((w >> 8) & 0xff),
+             (_Float16)(int8_t)((w >> 16) & 0xff), (_Float16)(int8_t)(w >> 24)};
+    *reinterpret_cast<h4 *>(xq + b * QK8_1 + sub * 4) = hv;
+    if (sub == 0) {
+        float2 ds = *reinterpret_cast<const float2 *>(in);
+        xd[b] = ds.x;
+        xs[b] = ds.y;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: one thread per 16 consecutive weights of a row.
+//   Q8_0: d*q; Q4_K: (d*sc)*nib - dmin*m; Q6_K: (d*sc)*(q-32).
+// Every product is exact in fp32; the Q4_K subtraction rounds once.
+// ---------------------------------------------------------------------------
+template <int T, int YDT>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ W, int64_t rows, int64_t K,
+                                                      void *__restrict__ y) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_row = K / 16;
+    if (gid >= rows * per_row) return;
+    const int64_t r = gid / per_row;
+    const int64_t i0 = (gid - r * per_row) * 16;         // first weight index in the row
+    constexpr int QK = Geom<T>::QK, BB = Geom<T>::BYTES;
+    const uint8_t *blk = W + r * (K / QK) * BB + (i0 / QK) * BB;
+    const int ib = (int)(i0 % QK);                       // index inside the block
+    float w[16];
+    if (T == T_Q8_0) {
+        const float d = fp16_bits_to_f32(ld_u16(blk));
+        v4i q = ld16_a2(blk + 2 + ib);
+        for (int i = 0; i < 16; i++) w[i] = d * (float)(int8_t)((q[i / 4] >> (8 * (i % 4))) & 0xff);
+    } else if (T == T_Q4_K) {
+        const uint8_t *s = blk + 4;
+        const float d = fp16_bits_to_f32(ld_u16(blk)), dmin = fp16_bits_to_f32(ld_u16(blk + 2));
+        const int j = ib / 32;
+        int sc, mn;
+        if (j < 4) { sc = s[j] & 63; mn = s[j + 4] & 63; }
+        else { sc = (s[j + 4] & 0x0f) | ((s[j - 4] >> 6) << 4); mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4); }
+        const int c = ib / 64, r64 = ib % 64;
+        const bool hi = r64 >= 32;
+        v4i q = *reinterpret_cast<const v4i *>(blk + 16 + 32 * c + (r64 & 31));
+        const float a = d * (float)sc, m = dmin * (float)mn;
+        for (int i = 0; i < 16; i++) {
+            int byte = (q[i / 4] >> (8 * (i % 4))) & 0xff;
+            int nib = hi ? (byte >> 4) : (byte & 15);
+            w[i] = a * (float)nib - m;
+        }
+    } else {
+        const float d = fp16_bits_to_f32(ld_u16(blk + 208));
+        const int h = ib / 128, rr = ib % 128, g = rr / 32, l = rr % 32;
+        v4i ql = ld16_a2(blk + 64 * h + 32 * (g & 1) + l);
+        v4i qh = ld16_a2(blk + 128 + 32 * h + l);
+        const int sc = (int8_t)blk[192 + ib / 16];
+        const float a = d * (float)sc;
+        for (int i = 0; i < 16; i++) {
+            int lo = (ql[i / 4] >> (8 * (i % 4))) & 0xff;
+            lo = g < 2 ? (lo & 15) : (lo >> 4);
+            int hb = ((qh[i / 4] >> (8 * (i % 4))) >> (2 * g)) & 3;
+            w[i] = a * (float)((lo | (hb << 4)) - 32);
+        }
+    }
+    const int64_t o = r * K + i0;
+    if (YDT == DT_F32) {
+        v4f *yo = reinterpret_cast<v4f *>(static_cast<float *>(y) + o);
+        for (int i = 0; i < 4; i++) yo[i] = v4f{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+    } else {
+        v4i *yo = reinterpret_cast<v4i *>(static_cast<uint16_t *>(y) + o);
+        for (int i = 0; i < 2; i++) {
+            v4i t;
+            for (int k = 0; k < 4; k++)
+                t[k] = (int)(f32_to_bf16_bits(w[8 * i + 2 * k]) | (f32_to_bf16_bits(w[8 * i + 2 * k + 1]) << 16));
+            yo[i] = t;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small helpers
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n, uint32_t v) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t st = (int64_t)gridDim.x * blockDim.x;
+    for (; i < n; i += st) p[i] = v;
+}
+
+// fp32 accumulator -> output dtype.
+template <int YDT>
+__global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__ acc, int64_t n, void *__restrict__ y) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t st = (int64_t)gridDim.x * blockDim.x;
+    for (; i < n; i += st) {
+        if (YDT == DT_F32) static_cast<float *>(y)[i] = acc[i];
+        else static_cast<uint16_t *>(y)[i] = (uint16_t)f32_to_bf16_bits(acc[i]);
+    }
+}
+
+// Zero the output rows of inactive routes (id < 0 or id >= E) in the
+// unweighted mul_mat_id output y[T*top_k][Np].
+template <int YDT>
+__global__ __launch_bounds__(256) void zero_inactive_kernel(const int32_t *__restrict__ ids, int64_t R, int64_t E,
+                                                            int64_t Np, void *__restrict__ y) {
+    const int64_t r = blockIdx.x;
+    if (r >= R) return;
+    const int32_t e = ids[r];
+    if (e >= 0 && e < E) return;
+    for (int64_t n = threadIdx.x; n < Np; n += blockDim.x) {
+        if (YDT == DT_F32) static_cast<float *>(y)[r * Np + n] = 0.0f;
+        else static_cast<uint16_t *>(y)[r * Np + n] = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
+
+hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, uint8_t *q8, _Float16 *xq,
+                           float *xd, float *xs, hipStream_t s) {
+    const int64_t threads = M * (K / QK8_1) * 8;
+    if (threads == 0) return hipSuccess;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x);
+    const bool vec = xdt == DT_F32 ? ((ldx % 4) == 0 && (a % 16) == 0) : ((ldx % 4) == 0 && (a % 8) == 0);
+    dim3 g(grid_for(threads)), b(256);
+    if (xdt == DT_F32) {
+        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
+        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
+    } else {
+        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
+        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float16 *xq, float *xd, float *xs,
+                                 hipStream_t s) {
+    const int64_t threads = M * (K / QK8_1) * 8;
+    if (threads == 0) return hipSuccess;
+    hipLaunchKernelGGL(q8_1_to_planar_kernel, dim3(grid_for(threads)), dim3(256), 0, s, q8, M, K, xq, xd, xs);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, void *y, int ydt, hipStream_t s) {
+    const int64_t threads = rows * (K / 16);
+    if (threads == 0) return hipSuccess;
+    dim3 g(grid_for(threads)), b(256);
+#define GGQ_DQ(TT)                                                                                         \
+    if (t == TT) {                                                                                         \
+        if (ydt == DT_F32) hipLaunchKernelGGL((dequant_kernel<TT, DT_F32>), g, b, 0, s, W, rows, K, y);     \
+        else hipLaunchKernelGGL((dequant_kernel<TT, DT_BF16>), g, b, 0, s, W, rows, K, y);                 \
+    }
+    GGQ_DQ(T_Q8_0) GGQ_DQ(T_Q4_K) GGQ_DQ(T_Q6_K)
+#undef GGQ_DQ
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const unsigned g = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(g), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float *acc, int64_t n, void *y, int ydt, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const unsigned g = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
+    if (ydt == DT_F32) hipLaunchKernelGGL(finalize_kernel<DT_F32>, dim3(g), dim3(256), 0, s, acc, n, y);
+    else hipLaunchKernelGGL(finalize_kernel<DT_BF16>, dim3(g), dim3(256), 0, s, acc, n, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_inactive(const int32_t *ids, int64_t R, int64_t E, int64_t Np, void *y, int ydt,
+                                hipStream_t s) {
+    if (R == 0) return hipSuccess;
+    if (ydt == DT_F32) hipLaunchKernelGGL(zero_inactive_kernel<DT_F32>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
+    else hipLaunchKernelGGL(zero_inactive_kernel<DT_BF16>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
+    return hipGetLastError();
+}
+
+}  // namespace ggq

@@ -1,0 +1,98 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <algorithm>
+#include "common.hpp"
+
+namespace ggq {
+
+// ---- convert.hip ----
+hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, uint8_t *q8, _Float16 *xq,
+                           float *xd, float *xs, hipStream_t s);
+hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float16 *xq, float *xd, float *xs,
+                                 hipStream_t s);
+hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, void *y, int ydt, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s);
+hipError_t launch_finalize(const float *acc, int64_t n, void *y, int ydt, hipStream_t s);
+hipError_t launch_zero_inactive(const int32_t *ids, int64_t R, int64_t E, int64_t Np, void *y, int ydt,
+                                hipStream_t s);
+
+// ---- route.hip ----
+// Work list of (expert, first sorted route, route count) triples, one per
+// tile of at most J routes of one expert; built on the device from ids.
+struct RouteTables {
+    uint32_t *bad;        // count of ids >= E (workspace offset 0)
+    uint32_t *counts;     // [E]
+    uint32_t *offsets;    // [E + 1] exclusive scan of counts
+    uint32_t *tile_off;   // [E + 1] exclusive scan of ceil(count / J)
+    uint32_t *ntiles;     // [1] total tiles
+    int32_t *rank;        // [R] position of a route inside its expert list (-1: inactive)
+    int32_t *perm;        // [R] routes sorted by expert
+    int4 *tiles;          // [max_tiles] {expert, start, count, 0}
+};
+int64_t route_max_tiles(int64_t R, int64_t E, int J);
+hipError_t launch_route_build(const int32_t *ids, int64_t R, int64_t E, int J, const RouteTables &rt,
+                              hipStream_t s);
+
+// ---- mmvq.hip ----
+struct MmvqParams {
+    const uint8_t *W;
+    int64_t row_bytes;
+    int64_t expert_stride;
+    int64_t N;            // weight rows of one matrix
+    int64_t Np;           // output rows (N, or N/2 with SwiGLU)
+    int64_t npairs;       // row pairs handled (ceil(N/2), or Np with SwiGLU)
+    int units;            // lane work units per row
+    int seg;              // lanes per row segment (power of two, <= 64)
+    int64_t row_blocks;   // blocks along the row-pair axis
+    const uint8_t *q8;    // activation rows as q8_1 blocks
+    int64_t q8_row;       // bytes per activation row
+    int64_t M;            // dense: activation rows (columns of y^T)
+    void *y;
+    int64_t ldy;
+    // routed experts
+    const int32_t *perm;
+    const int4 *groups;
+    const uint32_t *ngroups;
+    int top_k;
+    int x_per_route;
+    const float *route_w;
+    float *acc32;
+};
+hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqParams &p, int64_t ngroups_bound,
+                       hipStream_t s);
+hipError_t launch_mmvq_dots(int t, const uint8_t *W, int64_t N, int64_t K, const uint8_t *q8, int64_t M,
+                            int32_t *out, hipStream_t s);
+
+// ---- mmq.hip ----
+struct MmqParams {
+    const uint8_t *W;
+    int64_t row_bytes;
+    int64_t expert_stride;
+    int64_t N;            // weight rows of one matrix
+    int64_t Np;           // output rows (N, or N/2 with SwiGLU)
+    int64_t K;
+    const _Float16 *xq;   // planar activations: fp16 quants [rows][K]
+    const float *xd;      // [rows][K/32] q8_1 d
+    const float *xs;      // [rows][K/32] q8_1 s
+    int64_t M;            // dense: activation rows
+    int64_t m_tiles;      // dense: tiles along M; routed: tile-list bound
+    int64_t n_tiles;      // tiles along the output rows
+    void *y;
+    int64_t ldy;
+    // routed experts
+    const int32_t *perm;
+    const int4 *tiles;
+    const uint32_t *ntiles;
+    int top_k;
+    int x_per_route;
+    const float *route_w;
+    float *acc32;
+};
+constexpr int MMQ_NT = 128;   // weight rows per workgroup tile
+constexpr int MMQ_MT = 128;   // activation rows (routes) per workgroup tile
+hipError_t launch_mmq(int t, bool moe, int epi, int ydt, const MmqParams &p, hipStream_t s);
+hipError_t launch_mmq_dots(int t, const uint8_t *W, int64_t N, int64_t K, const _Float16 *xq, int64_t M,
+                           int32_t *out, hipStream_t s);
+
+}  // namespace ggq

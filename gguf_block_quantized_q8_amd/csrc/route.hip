@@ -1,0 +1,98 @@
+// Routed-expert work list built on the device, with no host synchronization:
+// histogram of expert ids -> exclusive scans -> scatter of routes by expert ->
+// flat list of (expert, route tile) pairs of width J.  Only the tiles that hold
+// routes are listed; the kernels that consume the list are launched with the
+// host-side bound route_max_tiles() and blocks past the device count exit.
+#include "kernels.hpp"
+
+namespace ggq {
+
+int64_t route_max_tiles(int64_t R, int64_t E, int J) {
+    // sum_e ceil(c_e / J) <= sum_e (c_e / J + 1 for c_e > 0) <= R / J + min(E, R)
+    return R / J + std::min<int64_t>(E, R) + 1;
+}
+
+__global__ __launch_bounds__(256) void route_count_kernel(const int32_t *__restrict__ ids, int64_t R, int64_t E,
+                                                          uint32_t *__restrict__ counts, int32_t *__restrict__ rank,
+                                                          uint32_t *__restrict__ bad) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= R) return;
+    const int32_t e = ids[r];
+    if (e >= 0 && e < E) {
+        rank[r] = (int32_t)atomicAdd(&counts[e], 1u);
+    } else {
+        rank[r] = -1;
+        if (e >= E) atomicAdd(bad, 1u);
+    }
+}
+
+// Single workgroup: exclusive scans of the counts and of the tile counts,
+// then the tile list.
+__global__ __launch_bounds__(1024) void route_scan_kernel(const uint32_t *__restrict__ counts, int64_t E, int J,
+                                                          uint32_t *__restrict__ offsets, uint32_t *__restrict__ tile_off,
+                                                          uint32_t *__restrict__ ntiles, int4 *__restrict__ tiles) {
+    __shared__ uint32_t s_c[1024], s_t[1024];
+    __shared__ uint32_t carry_c, carry_t;
+    const int tid = threadIdx.x;
+    if (tid == 0) { carry_c = 0; carry_t = 0; }
+    __syncthreads();
+    for (int64_t base = 0; base < E; base += 1024) {
+        const int64_t e = base + tid;
+        const uint32_t c = e < E ? counts[e] : 0u;
+        const uint32_t nt = (c + (uint32_t)J - 1) / (uint32_t)J;
+        s_c[tid] = c;
+        s_t[tid] = nt;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {      // inclusive Hillis-Steele scan
+            uint32_t vc = tid >= off ? s_c[tid - off] : 0u;
+            uint32_t vt = tid >= off ? s_t[tid - off] : 0u;
+            __syncthreads();
+            s_c[tid] += vc;
+            s_t[tid] += vt;
+            __syncthreads();
+        }
+        const uint32_t oc = carry_c + s_c[tid] - c;     // exclusive
+        const uint32_t ot = carry_t + s_t[tid] - nt;
+        if (e < E) {
+            offsets[e] = oc;
+            tile_off[e] = ot;
+            for (uint32_t i = 0; i < nt; i++)
+                tiles[ot + i] = int4{(int)e, (int)(oc + i * (uint32_t)J), (int)min((uint32_t)J, c - i * (uint32_t)J), 0};
+        }
+        __syncthreads();
+        if (tid == 1023) { carry_c += s_c[1023]; carry_t += s_t[1023]; }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        offsets[E] = carry_c;
+        tile_off[E] = carry_t;
+        *ntiles = carry_t;
+    }
+}
+
+__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t *__restrict__ ids, int64_t R,
+                                                            const uint32_t *__restrict__ offsets,
+                                                            const int32_t *__restrict__ rank,
+                                                            int32_t *__restrict__ perm) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= R) return;
+    const int32_t k = rank[r];
+    if (k < 0) return;
+    perm[offsets[ids[r]] + k] = (int32_t)r;
+}
+
+hipError_t launch_route_build(const int32_t *ids, int64_t R, int64_t E, int J, const RouteTables &rt,
+                              hipStream_t s) {
+    hipError_t err = launch_fill_u32(rt.counts, E, 0u, s);
+    if (err != hipSuccess) return err;
+    err = launch_fill_u32(rt.bad, 1, 0u, s);
+    if (err != hipSuccess) return err;
+    const unsigned g = (unsigned)((R + 255) / 256);
+    if (R > 0) hipLaunchKernelGGL(route_count_kernel, dim3(g), dim3(256), 0, s, ids, R, E, rt.counts, rt.rank, rt.bad);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, rt.counts, E, J, rt.offsets, rt.tile_off,
+                       rt.ntiles, rt.tiles);
+    if (R > 0) hipLaunchKernelGGL(route_scatter_kernel, dim3(g), dim3(256), 0, s, ids, R, rt.offsets, rt.rank, rt.perm);
+    return hipGetLastError();
+}
+
+}  // namespace ggq

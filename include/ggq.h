@@ -1,0 +1,143 @@
+/*
+ * ggq.h -- C ABI of the MI355X (gfx950) GGUF block-quantized matmul library.
+ *
+ * Matrix multiplication against GGUF block-quantized weights (Q8_0, Q4_K,
+ * Q6_K) with activations quantized on the fly to q8_1 blocks; results come
+ * out in the activation dtype (or the requested output dtype) with fp32
+ * accumulation.  This is the operation FreeToken PR #690 "feat(gguf): serve
+ * GGUF checkpoints on vendored ggml-cuda kernels" describes in "What the ggml
+ * patch changes" (fp32/bf16 activations quantized directly to q8_1, fp32
+ * accumulation, MMVQ for small batches and MMQ above, a routed-MoE grid over
+ * only the (expert, column tile) pairs that hold routes with no host sync).
+ *
+ * Conventions for every entry point:
+ *   - All buffers are device memory owned by the caller (the library
+ *     allocates nothing on the device and keeps no pointer after returning).
+ *     Base pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous on it and never synchronize the host.
+ *   - Weights are row-major GGUF blocks: row n of an N x K matrix starts at
+ *     byte n * ggq_row_bytes(type, K).  Kernels never read outside
+ *     [W, W + N * row_bytes) (no tail padding needed); all offsets are 64-bit.
+ *   - Element types: GGQ_F32 = IEEE fp32, GGQ_BF16 = bfloat16 (output rounded
+ *     to nearest even), GGQ_Q8_1 = pre-quantized q8_1 blocks (input only).
+ *   - q8_1 block (40 bytes, 32 values): float d = amax/127 (fp32 division),
+ *     float s = d * (sum of the quants), int8 qs[32] = x/d (fp32 division)
+ *     rounded half away from zero; an all-zero block has d = s = 0.
+ *   - Return value: GGQ_OK or an error code; ggq_last_error() gives a
+ *     message for the calling thread's last failure.  All checks are on
+ *     the host and nothing is launched when a check fails.  M, N or T equal
+ *     to 0 is a valid no-op.
+ */
+#ifndef GGQ_H
+#define GGQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* GGUF tensor type ids (public GGUF numbering). */
+typedef enum { GGQ_Q8_0 = 8, GGQ_Q4_K = 12, GGQ_Q6_K = 14 } ggq_type;
+typedef enum { GGQ_F32 = 0, GGQ_BF16 = 1, GGQ_Q8_1 = 2 } ggq_dtype;
+/* Kernel choice: AUTO picks MMVQ for few activation rows, MMQ above. */
+typedef enum { GGQ_PATH_AUTO = 0, GGQ_PATH_MMVQ = 1, GGQ_PATH_MMQ = 2 } ggq_path;
+typedef enum { GGQ_EPI_NONE = 0, GGQ_EPI_SWIGLU = 1 } ggq_epilogue;
+typedef enum {
+    GGQ_OK = 0,
+    GGQ_ERR_INVALID = 1,     /* bad argument: null pointer, bad K, shape, stride, alignment */
+    GGQ_ERR_UNSUPPORTED = 2, /* type / dtype / path combination not provided (no fallback) */
+    GGQ_ERR_WORKSPACE = 3,   /* workspace smaller than the matching *_ws() size */
+    GGQ_ERR_HIP = 4          /* a HIP launch failed */
+} ggq_status;
+
+/* Bytes of one row of K weights of `type`; 0 if K is not a multiple of the
+ * block length (32 for Q8_0, 256 for Q4_K / Q6_K) or the type is unknown. */
+size_t ggq_row_bytes(int type, int64_t K);
+
+/* Bytes of M rows of K activations as q8_1 blocks: M * (K/32) * 40. */
+size_t ggq_q8_1_bytes(int64_t M, int64_t K);
+
+/* q8_1 quantization of activations (PR #690, "What the ggml patch changes":
+ * activations quantized to q8_1 directly).
+ *   x   : [M][ldx] elements of xdt (GGQ_F32 or GGQ_BF16); K % 32 == 0, ldx >= K.
+ *   q8  : output, [M][K/32] blocks of 40 bytes (ggq_q8_1_bytes(M, K)).
+ * Bit-exact: the same blocks as the definition above. */
+int ggq_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx,
+                      void *q8, void *stream);
+
+/* Dense quantized matmul: y[m][n] = sum_k W[n][k] * x[m][k] for n < N.
+ *   W   : N rows of K weights of type wt (Q8_0, Q4_K, Q6_K).
+ *   x   : [M][ldx] of xdt (GGQ_F32 / GGQ_BF16), or, with xdt = GGQ_Q8_1,
+ *         M rows of K/32 q8_1 blocks (ldx ignored) -- one quantization can
+ *         be reused for several weight matrices (PR #690, second item).
+ *   y   : [M][ldy] of ydt (GGQ_F32 / GGQ_BF16), ldy >= N; columns >= N are
+ *         not written.
+ *   ws  : workspace of at least ggq_mul_mat_ws(...) bytes (may be NULL when
+ *         that is 0).
+ *   path: AUTO, or force MMVQ / MMQ (MMQ: Q4_K and Q6_K only).
+ * fp32 accumulation; per-block integer dots are exact. */
+size_t ggq_mul_mat_ws(int wt, int64_t N, int64_t K, int xdt, int64_t M, int path);
+int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
+                const void *x, int xdt, int64_t M, int64_t ldx,
+                void *y, int ydt, int64_t ldy,
+                void *ws, size_t ws_bytes, int path, void *stream);
+
+/* Routed-expert matmul (MoE mul_mat_id; PR #690: "MoE MMQ runs a flat grid
+ * over only the (expert, column tile) pairs that hold routes, so it needs no
+ * host sync"; fused GLU and MoE weighted sum are the ops PR #690 lists next
+ * to mul_mat).
+ *   W            : E experts; expert e starts at byte e * expert_stride and
+ *                  holds N rows of K weights of type wt.  expert_stride >=
+ *                  N * row_bytes and a multiple of 16.
+ *   x            : x_per_route == 0: [T][K] (each route of token t uses x[t]);
+ *                  x_per_route == 1: [T][top_k][K] (route (t,k) uses x[t][k]).
+ *                  Element type xdt (GGQ_F32 / GGQ_BF16), rows contiguous.
+ *   ids          : [T][top_k] int32 expert ids.  id < 0: inactive route
+ *                  (contributes nothing).  id >= E: skipped and counted in
+ *                  the uint32 at workspace offset 0 (readable after the call).
+ *                  Repeated ids within a token are independent routes.
+ *   epi          : GGQ_EPI_SWIGLU: o' = silu(o[:N/2]) * o[N/2:] (gate rows
+ *                  first, then up rows), N' = N/2 (N even).  Otherwise N' = N.
+ *   route_w      : NULL: y is [T][top_k][N'] (inactive routes -> 0);
+ *                  else [T][top_k] fp32 weights and y is [T][N'] =
+ *                  sum_k route_w[t][k] * o'[t][k] (fp32 accumulation).
+ *   y            : output of ydt (GGQ_F32 / GGQ_BF16), contiguous.
+ *   ws           : at least ggq_mul_mat_id_ws(...) bytes.
+ * Tokens, routes and tiles are grouped on the device; no host sync. */
+size_t ggq_mul_mat_id_ws(int wt, int64_t E, int64_t N, int64_t K, int xdt,
+                         int64_t T, int x_per_route, int64_t top_k,
+                         int epi, int weighted, int path);
+int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K,
+                   int64_t expert_stride,
+                   const void *x, int xdt, int64_t T, int x_per_route,
+                   const int32_t *ids, int64_t top_k, const float *route_w, int epi,
+                   void *y, int ydt,
+                   void *ws, size_t ws_bytes, int path, void *stream);
+
+/* Dequantize (convert) rows of weights: y[r][k] = exact block value in fp32,
+ * or its round-to-nearest-even bf16 (PR #690 lists dequantize among its ops).
+ * y: [rows][K] of ydt (GGQ_F32 / GGQ_BF16).  Bit-exact. */
+int ggq_dequantize(int wt, const void *W, int64_t rows, int64_t K,
+                   void *y, int ydt, void *stream);
+
+/* Message describing the calling thread's last failing call ("" if none). */
+const char *ggq_last_error(void);
+
+/* Test hook (not part of the product API): per-group int32 dots of raw weight
+ * quants with q8_1 quants, out[M][N][K/g] (g = 32 for Q8_0 / Q4_K: nibbles
+ * without the min; g = 16 for Q6_K: values minus 32), computed by the same
+ * device unpack and dot code as the named path (GGQ_PATH_MMVQ: the v_dot4
+ * units; GGQ_PATH_MMQ: the staged fp16 tiles and the MFMA, Q4_K / Q6_K only).
+ * q8 is M rows of K/32 q8_1 blocks; ws needs ggq_test_block_dots_ws() bytes. */
+size_t ggq_test_block_dots_ws(int wt, int64_t K, int64_t M, int path);
+int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K,
+                        const void *q8, int64_t M, int32_t *out,
+                        void *ws, size_t ws_bytes, int path, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,117 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every symbol the
+header declares, and its host-side validation returns the documented error
+codes without touching a GPU (every call here fails a check before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gguf_block_quantized_q8_amd as g
+from gguf_block_quantized_q8_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ggq.h")
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced: every call below fails a check first
+
+
+@pytest.fixture(scope="module")
+def L():
+    newest_src = max(os.path.getmtime(s) for s in _build.sources())
+    if not os.path.exists(g.LIB_PATH) or os.path.getmtime(g.LIB_PATH) < newest_src:
+        _build.build()
+    return g.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ggq_\w+)\s*\(", text)))
+
+
+def test_exports_every_header_symbol(L):
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == sorted(g.EXPORTS)
+
+
+def test_geometry(L):
+    assert L.ggq_row_bytes(g.Q8_0, 512) == 16 * 34
+    assert L.ggq_row_bytes(g.Q4_K, 2048) == 8 * 144
+    assert L.ggq_row_bytes(g.Q6_K, 2048) == 8 * 210
+    assert L.ggq_row_bytes(g.Q4_K, 300) == 0
+    assert L.ggq_row_bytes(2, 256) == 0
+    assert L.ggq_q8_1_bytes(3, 64) == 3 * 2 * 40
+
+
+def err(L):
+    return L.ggq_last_error().decode()
+
+
+def test_unsupported_type(L):
+    rc = L.ggq_mul_mat(2, FAKE, 16, 2816, FAKE, g.F32, 1, 2816, FAKE, g.F32, 16, None, 0, 0, None)
+    assert rc == g.ERR_UNSUPPORTED and "type 2" in err(L)
+    assert L.ggq_dequantize(42, FAKE, 1, 256, FAKE, g.F32, None) == g.ERR_UNSUPPORTED
+
+
+def test_bad_K(L):
+    rc = L.ggq_mul_mat(g.Q4_K, FAKE, 16, 300, FAKE, g.F32, 1, 300, FAKE, g.F32, 16, None, 0, 0, None)
+    assert rc == g.ERR_INVALID and "K=300" in err(L)
+    assert L.ggq_quantize_q8_1(FAKE, g.F32, 1, 33, 33, FAKE, None) == g.ERR_INVALID
+
+
+def test_bad_strides_and_pointers(L):
+    assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, g.F32, 1, 128, FAKE, g.F32, 16, None, 0, 0, None) == g.ERR_INVALID
+    assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, g.F32, 1, 256, FAKE, g.F32, 8, None, 0, 0, None) == g.ERR_INVALID
+    assert L.ggq_mul_mat(g.Q4_K, None, 16, 256, FAKE, g.F32, 1, 256, FAKE, g.F32, 16, None, 0, 0, None) == g.ERR_INVALID
+    mis = ctypes.c_void_p(0x10002)
+    assert L.ggq_mul_mat(g.Q4_K, mis, 16, 256, FAKE, g.F32, 1, 256, FAKE, g.F32, 16, None, 0, 0, None) == g.ERR_INVALID
+    assert L.ggq_quantize_q8_1(FAKE, g.F32, 4, 64, 32, FAKE, None) == g.ERR_INVALID
+
+
+def test_bad_dtypes_and_paths(L):
+    assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, 7, 1, 256, FAKE, g.F32, 16, None, 0, 0, None) == g.ERR_UNSUPPORTED
+    assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, g.F32, 1, 256, FAKE, g.Q8_1, 16, None, 0, 0, None) == g.ERR_UNSUPPORTED
+    assert L.ggq_mul_mat(g.Q8_0, FAKE, 16, 256, FAKE, g.F32, 64, 256, FAKE, g.F32, 16, None, 0, g.PATH_MMQ, None) == g.ERR_UNSUPPORTED
+    assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, g.F32, 1, 256, FAKE, g.F32, 16, None, 0, 9, None) == g.ERR_INVALID
+
+
+def test_workspace_too_small(L):
+    need = L.ggq_mul_mat_ws(g.Q4_K, 64, 256, g.BF16, 100, g.PATH_AUTO)
+    assert need > 0
+    rc = L.ggq_mul_mat(g.Q4_K, FAKE, 64, 256, FAKE, g.BF16, 100, 256, FAKE, g.BF16, 64, FAKE, need - 1, 0, None)
+    assert rc == g.ERR_WORKSPACE
+    assert L.ggq_mul_mat_ws(g.Q4_K, 64, 256, g.Q8_1, 1, g.PATH_AUTO) == 0   # pre-quantized MMVQ needs none
+
+
+def test_noops(L):
+    assert L.ggq_mul_mat(g.Q4_K, None, 0, 256, None, g.F32, 0, 256, None, g.F32, 0, None, 0, 0, None) == g.OK
+    assert L.ggq_quantize_q8_1(None, g.F32, 0, 64, 64, None, None) == g.OK
+    assert L.ggq_dequantize(g.Q6_K, None, 0, 256, None, g.F32, None) == g.OK
+
+
+def test_mul_mat_id_validation(L):
+    i64 = ctypes.c_int64
+    def call(wt=g.Q4_K, E=4, N=32, K=256, stride=None, T=2, xpr=0, top_k=2, epi=0, ws_bytes=1 << 20, path=0, ws=FAKE):
+        stride = stride if stride is not None else N * L.ggq_row_bytes(wt, K)
+        return L.ggq_mul_mat_id(wt, FAKE, E, N, K, stride, FAKE, g.F32, T, xpr, FAKE, top_k, None, epi,
+                                FAKE, g.F32, ws, ws_bytes, path, None)
+    assert call(stride=32 * 144 - 16) == g.ERR_INVALID          # stride < N * row_bytes
+    assert call(stride=32 * 144 + 8) == g.ERR_INVALID           # stride % 16
+    assert call(N=33, epi=g.EPI_SWIGLU) == g.ERR_INVALID        # SwiGLU needs even N
+    assert call(xpr=2) == g.ERR_INVALID
+    assert call(ws_bytes=64) == g.ERR_WORKSPACE
+    assert call(wt=g.Q8_0, K=64, path=g.PATH_MMQ) == g.ERR_UNSUPPORTED
+    assert call(T=0) == g.OK
+    ws_small = L.ggq_mul_mat_id_ws(g.Q4_K, 256, 1024, 2048, g.BF16, 16, 0, 8, 1, 0, 0)
+    ws_big = L.ggq_mul_mat_id_ws(g.Q4_K, 256, 1024, 2048, g.BF16, 8192, 0, 8, 1, 0, 0)
+    assert 0 < ws_small < ws_big
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(g, "_lib", None)
+    monkeypatch.setattr(g, "LIB_PATH", "/nonexistent/libggq.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        g.lib()

@@ -1,0 +1,352 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bars: q8_1 blocks, per-group int32 dots and dequantized weights bit-exact;
+fp32 outputs max|gpu - ref| / max|ref| <= 1e-5; bf16 outputs <= 8e-3, where
+ref is the oracle's fp64-accumulated result (rounded to fp32, then to bf16 for
+bf16 outputs).  Full-size workloads are checked on seeded samples of output
+rows / tokens, computed one by one by the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import gguf_block_quantized_q8_amd as g
+from gguf_block_quantized_q8_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 8e-3}
+TYPES = [g.Q8_0, g.Q4_K, g.Q6_K]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def T(a, dev):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def host(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-30))
+
+
+def ref_out(y32, kind):
+    """Oracle fp32 result as the output dtype would hold it."""
+    if kind == "f32":
+        return y32
+    return torch.from_numpy(y32).to(torch.bfloat16).float().numpy()
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ q8_1
+
+@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+@pytest.mark.parametrize("M,K,ldx", [(1, 32, 32), (7, 512, 512), (33, 2048, 2080), (300, 4096, 4096)])
+def test_quantize_bit_exact(dev, xdt, M, K, ldx):
+    log("quantize", xdt, M, K, ldx)
+    x = inputs.gen_act(M, ldx, 1000 + M, xdt)
+    if M > 3:
+        x[3, :64] = 0                       # all-zero blocks
+    xt = T(x, dev)[:, :K] if ldx != K else T(x, dev)
+    q = host(g.quantize_q8_1(xt))
+    ref = oracle.quantize_q8_1(np.ascontiguousarray(x[:, :K]))
+    assert np.array_equal(q, ref)
+
+
+def test_quantize_ties_and_scales(dev):
+    x = np.zeros((4, 64), np.float32)
+    x[0, :7] = [127, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5]
+    x[1] = np.float32(2.5) * np.arange(-32, 32)
+    x[2] = np.float32(1e-30) * np.arange(64)                 # tiny values
+    x[3] = np.float32(3e37) * np.sin(np.arange(64))          # huge values
+    assert np.array_equal(host(g.quantize_q8_1(T(x, dev))), oracle.quantize_q8_1(x))
+
+
+# ------------------------------------------------------------------ dequantize
+
+@pytest.mark.parametrize("wt", TYPES)
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
+def test_dequantize_bit_exact(dev, wt, ydt):
+    log("dequant", wt, ydt)
+    K = 512 if wt == g.Q8_0 else 1024
+    W = inputs.gen_weights(wt, 37, K, 7 + wt)
+    y = g.dequantize(T(W, dev), wt, K, ydt)
+    if ydt == torch.float32:
+        assert np.array_equal(host(y).view(np.uint32), oracle.dequantize(wt, W, 37, K).view(np.uint32))
+    else:
+        ref = oracle.dequantize(wt, W, 37, K, oracle.BF16)
+        assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
+def test_dequantize_q6_K_large_scales(dev):
+    """Q6_K with full-range int8 scales (-128..127), beyond the [-64, 63] draw."""
+    W = inputs.gen_q6_K(16, 512, 9)
+    r = inputs.rng(10)
+    W.reshape(-1, 210)[:, 192:208] = r.integers(-128, 128, (W.size // 210, 16), dtype=np.int8).view(np.uint8)
+    y = g.dequantize(T(W, dev), g.Q6_K, 512)
+    assert np.array_equal(host(y).view(np.uint32), oracle.dequantize(g.Q6_K, W, 16, 512).view(np.uint32))
+
+
+# ------------------------------------------------------------------ per-group int dots
+
+@pytest.mark.parametrize("wt,path", [(g.Q8_0, "mmvq"), (g.Q4_K, "mmvq"), (g.Q6_K, "mmvq"), (g.Q4_K, "mmq"), (g.Q6_K, "mmq")])
+def test_block_dots_bit_exact(dev, wt, path):
+    log("dots", wt, path)
+    N, K, M = 131, (512 if wt == g.Q8_0 else 768), 133      # ragged against the 128 x 128 MMQ tiles
+    W = inputs.gen_weights(wt, N, K, 20 + wt)
+    x = inputs.gen_act(M, K, 21, "f32")
+    x[5] *= 1e3
+    q8 = oracle.quantize_q8_1(x)
+    d = host(g.test_block_dots(T(W, dev), wt, T(q8, dev), K, path))
+    assert np.array_equal(d, oracle.block_dots(wt, W, N, K, q8, M))
+
+
+def test_block_dots_q6_K_large_scales_mmq(dev):
+    W = inputs.gen_q6_K(64, 512, 30)
+    W.reshape(-1, 210)[:, 192:208] = inputs.rng(31).integers(-128, 128, (W.size // 210, 16), dtype=np.int8).view(np.uint8)
+    x = inputs.gen_act(40, 512, 32, "f32")
+    q8 = oracle.quantize_q8_1(x)
+    d = host(g.test_block_dots(T(W, dev), g.Q6_K, T(q8, dev), 512, "mmq"))
+    assert np.array_equal(d, oracle.block_dots(g.Q6_K, W, 64, 512, q8, 40))
+
+
+# ------------------------------------------------------------------ dense mul_mat, small / ragged
+
+def _check_mul_mat(dev, wt, N, K, M, xdt, ydt, path, seed, rows=None, W=None):
+    W = inputs.gen_weights(wt, N, K, seed) if W is None else W
+    x = inputs.gen_act(M, K, seed + 1, xdt)
+    y = g.mul_mat(T(W, dev), wt, T(x, dev), out_dtype=torch.float32 if ydt == "f32" else torch.bfloat16, path=path)
+    yh = host(y)
+    if rows is not None:
+        yh = yh[:, rows]
+    ref = ref_out(oracle.mul_mat(wt, W, N, K, x, rows=rows), ydt)
+    r = rel(yh, ref)
+    log(f"mul_mat type={wt} N={N} K={K} M={M} {xdt}->{ydt} path={path} rel={r:.3g}")
+    assert r <= TOL[ydt], r
+    return r
+
+
+@pytest.mark.parametrize("wt", TYPES)
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+def test_mmvq_small(dev, wt, M):
+    K = 512 if wt == g.Q8_0 else 768
+    _check_mul_mat(dev, wt, 97, K, M, "f32", "f32", "mmvq", 40 + wt)
+
+
+@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K])
+@pytest.mark.parametrize("K", [256, 512])
+def test_mmvq_short_rows(dev, wt, K):
+    _check_mul_mat(dev, wt, 300, K, 4, "bf16", "bf16", "mmvq", 50 + K)
+
+
+def test_mmvq_many_columns(dev):
+    """M above the 8 columns of one MMVQ group (Q8_0 always takes MMVQ)."""
+    _check_mul_mat(dev, g.Q8_0, 64, 256, 21, "f32", "f32", "auto", 60)
+
+
+@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K])
+@pytest.mark.parametrize("M,N,K", [(1, 5, 256), (40, 100, 512), (129, 257, 768), (300, 128, 1024)])
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+def test_mmq_small_ragged(dev, wt, M, N, K, ydt):
+    _check_mul_mat(dev, wt, N, K, M, "bf16", ydt, "mmq", 70 + M + wt)
+
+
+def test_mmq_q6_K_large_scales(dev):
+    W = inputs.gen_q6_K(200, 512, 80)
+    W.reshape(-1, 210)[:, 192:208] = inputs.rng(81).integers(-128, 128, (W.size // 210, 16), dtype=np.int8).view(np.uint8)
+    _check_mul_mat(dev, g.Q6_K, 200, 512, 150, "f32", "f32", "mmq", 82, W=W)
+    _check_mul_mat(dev, g.Q6_K, 200, 512, 3, "f32", "f32", "mmvq", 83, W=W)
+
+
+def test_q8_1_input_reuse(dev):
+    """Pre-quantized q8_1 input gives the same result as float input, on both paths."""
+    W = inputs.gen_q4_K(96, 512, 90)
+    x = inputs.gen_act(20, 512, 91, "bf16")
+    xt = T(x, dev)
+    q8 = g.quantize_q8_1(xt)
+    for path in ("mmvq", "mmq"):
+        a = g.mul_mat(T(W, dev), g.Q4_K, xt, out_dtype=torch.float32, path=path)
+        b = g.mul_mat(T(W, dev), g.Q4_K, q8, K=512, path=path)
+        assert torch.equal(a, b), path
+
+
+def test_output_row_stride(dev):
+    W = inputs.gen_q6_K(64, 256, 92)
+    x = inputs.gen_act(12, 256, 93, "f32")
+    out = torch.full((12, 80), 7.0, device=dev)
+    for path in ("mmvq", "mmq"):
+        g.mul_mat(T(W, dev), g.Q6_K, T(x, dev), path=path, out=out[:, :64])
+        assert (out[:, 64:] == 7.0).all()
+        assert rel(host(out[:, :64]), oracle.mul_mat(g.Q6_K, W, 64, 256, x)) <= 1e-5
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled)
+
+def test_c1_q8_0_matvec(dev):
+    for M in (1, 4):
+        _check_mul_mat(dev, g.Q8_0, 256, 512, M, "f32", "f32", "auto", 101)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_c2_q4_K_decode(dev, M):
+    W = inputs.gen_q4_K(4096, 4096, 201)
+    x = inputs.gen_act(M, 4096, 202, "bf16")
+    y = host(g.mul_mat(T(W, dev), g.Q4_K, T(x, dev)))
+    r = rel(y, ref_out(oracle.mul_mat(g.Q4_K, W, 4096, 4096, x), "bf16"))
+    log("C2 M", M, "rel", r)
+    assert r <= TOL["bf16"]
+
+
+def test_c3_q4_K_prefill_sampled(dev):
+    W = inputs.gen_q4_K(8192, 2048, 301)
+    x = inputs.gen_act(8192, 2048, 302, "bf16")
+    y = host(g.mul_mat(T(W, dev), g.Q4_K, T(x, dev)))
+    rows = inputs.sample_rows(8192, 256, 303)
+    r = rel(y[:, rows], ref_out(oracle.mul_mat(g.Q4_K, W, 8192, 2048, x, rows=rows), "bf16"))
+    log("C3 sampled rel", r)
+    assert r <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("M", [16, 24, 32, 64])
+def test_c3_crossover_sweep_both_paths(dev, M):
+    W = inputs.gen_q4_K(8192, 2048, 301)
+    x = inputs.gen_act(M, 2048, 302, "bf16")
+    ref = ref_out(oracle.mul_mat(g.Q4_K, W, 8192, 2048, x), "bf16")
+    for path in ("mmvq", "mmq"):
+        r = rel(host(g.mul_mat(T(W, dev), g.Q4_K, T(x, dev), path=path)), ref)
+        log("C3 sweep M", M, path, r)
+        assert r <= TOL["bf16"]
+
+
+def test_c4_q6_K_lm_head_m1_all_rows(dev):
+    W = inputs.gen_q6_K(248320, 2048, 401)
+    x = inputs.gen_act(1, 2048, 402, "bf16")
+    y = host(g.mul_mat(T(W, dev), g.Q6_K, T(x, dev), out_dtype=torch.float32))
+    r = rel(y, oracle.mul_mat(g.Q6_K, W, 248320, 2048, x))
+    log("C4 M=1 rel", r)
+    assert r <= TOL["f32"]
+
+
+def test_c4_q6_K_lm_head_m2048_sampled(dev):
+    W = inputs.gen_q6_K(248320, 2048, 401)
+    x = inputs.gen_act(2048, 2048, 402, "bf16")
+    y = g.mul_mat(T(W, dev), g.Q6_K, T(x, dev), out_dtype=torch.float32)
+    rows = inputs.sample_rows(248320, 4096, 403)
+    yh = y[:, torch.from_numpy(rows).to(dev)].cpu().numpy()
+    del y
+    r = rel(yh, oracle.mul_mat(g.Q6_K, W, 248320, 2048, x, rows=rows))
+    log("C4 M=2048 sampled rel", r)
+    assert r <= TOL["f32"]
+
+
+# ------------------------------------------------------------------ routed experts
+
+def _moe_ref(wt, W, K, x, ids, top_k, route_w=None, epi=oracle.EPI_NONE, x_per_route=False, tokens=None):
+    E, N = W.shape[0], W.shape[1]
+    Tn = ids.shape[0]
+    return oracle.mul_mat_id(wt, W, E, N, K, W.shape[1] * W.shape[2], x, Tn, int(x_per_route), ids, top_k,
+                             route_w=route_w, epi=epi, tokens=tokens)
+
+
+@pytest.mark.parametrize("path", ["mmvq", "mmq"])
+@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K])
+def test_moe_edge_routes(dev, path, wt):
+    """Duplicate ids in a token, inactive (-1) and out-of-range ids, experts with no routes."""
+    E, N, K, Tn, top_k = 9, 96, 512, 37, 4
+    W = inputs.gen_experts(wt, E, N, K, 500 + wt)
+    x = inputs.gen_act(Tn, K, 501, "f32")
+    ids = inputs.rng(502).integers(0, 5, (Tn, top_k)).astype(np.int32)   # experts 5..8 get nothing
+    ids[0] = [1, 1, 1, 1]
+    ids[1, 2] = -1
+    ids[2, 0] = 12                                                      # >= E: skipped and counted
+    ids[3] = [-1, -1, -1, -1]
+    y, ws = g.mul_mat_id(T(W, dev), wt, T(x, dev), T(ids, dev), K, out_dtype=torch.float32, path=path,
+                         return_workspace=True)
+    ref = _moe_ref(wt, W, K, x, ids, top_k)
+    r = rel(host(y), ref)
+    log("moe edges", wt, path, r)
+    assert r <= TOL["f32"]
+    assert (host(y)[1, 2] == 0).all() and (host(y)[3] == 0).all() and (host(y)[2, 0] == 0).all()
+    assert int(ws[:4].view(torch.int32).item()) == 1
+
+
+@pytest.mark.parametrize("path", ["mmvq", "mmq"])
+def test_moe_all_routes_one_expert(dev, path):
+    E, N, K, Tn, top_k = 4, 64, 256, 300, 2
+    W = inputs.gen_experts(g.Q4_K, E, N, K, 510)
+    x = inputs.gen_act(Tn, K, 511, "bf16")
+    ids = np.full((Tn, top_k), 2, np.int32)
+    y = g.mul_mat_id(T(W, dev), g.Q4_K, T(x, dev), T(ids, dev), K, out_dtype=torch.float32, path=path)
+    assert rel(host(y), _moe_ref(g.Q4_K, W, K, x, ids, top_k)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("path", ["mmvq", "mmq"])
+def test_moe_swiglu_and_weighted_gather(dev, path):
+    E, H, I, Tn, top_k = 16, 512, 256, 45, 4
+    Wgu = inputs.gen_experts(g.Q4_K, E, 2 * I, H, 520)
+    Wd = inputs.gen_experts(g.Q6_K, E, H, I, 521)
+    x = inputs.gen_act(Tn, H, 522, "bf16")
+    ids, w = inputs.gen_routing(Tn, E, top_k, 523)
+    h = g.mul_mat_id(T(Wgu, dev), g.Q4_K, T(x, dev), T(ids, dev), H, epi=g.EPI_SWIGLU, path=path)
+    h_ref32 = _moe_ref(g.Q4_K, Wgu, H, x, ids, top_k, epi=oracle.EPI_SWIGLU)
+    r = rel(host(h), ref_out(h_ref32, "bf16"))
+    log("swiglu", path, r)
+    assert r <= TOL["bf16"]
+    # down projection on identical inputs (the oracle's bf16 h) -> same q8_1 decisions
+    h_in = oracle.fp32_to_bf16_array(h_ref32)
+    y = g.mul_mat_id(T(Wd, dev), g.Q6_K, T(h_in, dev), T(ids, dev), I, route_w=T(w, dev), x_per_route=True,
+                     out_dtype=torch.float32, path=path)
+    r = rel(host(y), _moe_ref(g.Q6_K, Wd, I, h_in, ids, top_k, route_w=w, x_per_route=True))
+    log("weighted down", path, r)
+    assert r <= TOL["f32"]
+
+
+def _c5(dev, Tn, path, tokens=None):
+    E, H, I, top_k = 256, 2048, 512, 8
+    Wgu = inputs.gen_experts(g.Q4_K, E, 2 * I, H, 501)
+    Wd = inputs.gen_experts(g.Q6_K, E, H, I, 502)
+    x = inputs.gen_act(Tn, H, 503, "bf16")
+    ids, w = inputs.gen_routing(Tn, E, top_k, 504)
+    h = g.mul_mat_id(T(Wgu, dev), g.Q4_K, T(x, dev), T(ids, dev), H, epi=g.EPI_SWIGLU, path=path)
+    y = g.mul_mat_id(T(Wd, dev), g.Q6_K, h, T(ids, dev), I, route_w=T(w, dev), x_per_route=True, path=path)
+    hh = host(h)
+    yh = host(y)
+    sel = slice(None) if tokens is None else tokens
+    h_ref32 = _moe_ref(g.Q4_K, Wgu, H, x, ids, top_k, epi=oracle.EPI_SWIGLU, tokens=tokens)
+    r_h = rel(hh[sel], ref_out(h_ref32, "bf16"))
+    # down on the GPU's own h (identical inputs for the oracle)
+    h_gpu = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    y_ref32 = _moe_ref(g.Q6_K, Wd, I, h_gpu, ids, top_k, route_w=w, x_per_route=True, tokens=tokens)
+    r_y = rel(yh[sel], ref_out(y_ref32, "bf16"))
+    log(f"C5 T={Tn} path={path} gate_up rel={r_h:.3g} down rel={r_y:.3g}")
+    assert r_h <= TOL["bf16"] and r_y <= TOL["bf16"]
+
+
+def test_c5_moe_t16(dev):
+    _c5(dev, 16, "auto")
+
+
+def test_c5_moe_t16_mmq(dev):
+    _c5(dev, 16, "mmq")
+
+
+def test_c5_moe_t8192_sampled(dev):
+    toks = inputs.sample_rows(8192, 512, 505)
+    _c5(dev, 8192, "auto", tokens=toks)
