@@ -276,6 +276,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--workloads", default="all",
+                    help="comma list of: decode, prefill, sweep, lmhead1, lmhead2048, moe16, moe8192 (default all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -294,27 +296,36 @@ def main():
     log("headline: q4_K 4096x4096 decode M=1")
     head = bench_decode(ctx, g.Q4_K, 4096, 4096, 1, 201, 202, torch.bfloat16, K, W)
     also = []
-    if not args.only_headline:
+    sel = set(args.workloads.split(",")) if args.workloads != "all" else {
+        "decode", "prefill", "sweep", "lmhead1", "lmhead2048", "moe16", "moe8192"}
+    if args.only_headline:
+        sel = set()
+    if "decode" in sel:
         for M in (2, 4, 8):
             log(f"q4_K 4096x4096 decode M={M}")
             r = bench_decode(ctx, g.Q4_K, 4096, 4096, M, 201, 202, torch.bfloat16, K, W)
             also.append({"workload": "q4_K_4096x4096_decode", "M": M, **r})
+    if "prefill" in sel:
         log("q4_K 8192x2048 prefill M=8192")
         r = bench_prefill(ctx, g.Q4_K, 8192, 2048, 8192, 301, 302, torch.bfloat16, max(5, K // 20), max(2, W // 10))
         also.append({"workload": "q4_K_8192x2048_prefill", "M": 8192, **r})
+    if "sweep" in sel:
         for M in (16, 24, 32, 64):
             for path, pn in ((g.PATH_MMVQ, "mmvq"), (g.PATH_MMQ, "mmq")):
                 log(f"q4_K 8192x2048 sweep M={M} {pn}")
                 r = bench_prefill(ctx, g.Q4_K, 8192, 2048, M, 301, 302, torch.bfloat16, max(20, K // 4), W, path)
                 also.append({"workload": "q4_K_8192x2048_prefill_sweep", "M": M, "path": pn, **r})
+    if "lmhead1" in sel:
         log("q6_K 248320x2048 lm_head M=1")
         r = bench_decode(ctx, g.Q6_K, 248320, 2048, 1, 401, 402, torch.float32, max(20, K // 4), W, rotate=False)
         also.append({"workload": "q6_K_248320x2048_lm_head", "M": 1, **r})
+    if "lmhead2048" in sel:
         log("q6_K 248320x2048 lm_head M=2048")
         r = bench_prefill(ctx, g.Q6_K, 248320, 2048, 2048, 401, 402, torch.float32, max(3, K // 40), 1)
         also.append({"workload": "q6_K_248320x2048_lm_head", "M": 2048, **r})
-        torch.cuda.empty_cache()
-        for Tn in (16, 8192):
+    torch.cuda.empty_cache()
+    for Tn in (16, 8192):
+        if f"moe{Tn}" in sel:
             log(f"moe T={Tn}")
             r = bench_moe(ctx, Tn, max(5, K // (1 if Tn <= 64 else 20)), max(2, W // 4))
             also.append({"workload": "moe_e256_top8_h2048_i512", "T": Tn, **r})

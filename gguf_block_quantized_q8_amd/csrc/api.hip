@@ -37,7 +37,7 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // activation rows quantized on the fly (MMVQ: q8_1 blocks; MMQ: planar fp16 + d + s)
 size_t act_bytes(bool mmq, int64_t rows, int64_t K) {
     if (mmq) return align256((size_t)rows * K * 2) + 2 * align256((size_t)rows * (K / 32) * 4);
-    return align256((size_t)rows * (K / 32) * Q8_1_BYTES);
+    return 0;   // MMVQ stages its activations in LDS
 }
 
 struct Carve {
@@ -68,7 +68,6 @@ Planar carve_planar(Carve &c, int64_t rows, int64_t K) {
 constexpr int64_t MMVQ_MAX_ROWS = 8;
 // Routed dispatch: MMVQ-id up to this many tokens, MMQ-id above.
 constexpr int64_t MMVQ_ID_MAX_TOKENS = 32;
-constexpr int MMVQ_ID_J = 8;
 
 bool use_mmq(int wt, int64_t M, int path) {
     if (path == GGQ_PATH_MMQ) return true;
@@ -92,6 +91,12 @@ int check_weights(int wt, int64_t N, int64_t K) {
 }
 
 int nc_for(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+
+// Routes per MMVQ-id group: a little above the mean routes per expert, so an
+// expert's weights are rarely read twice and few columns sit idle.
+int mmvq_id_cols(int64_t R, int64_t E, int64_t K) {
+    return std::min(nc_for((R + E - 1) / E + 1), mmvq_max_cols(K));
+}
 
 }  // namespace
 
@@ -135,9 +140,7 @@ int ggq_dequantize(int wt, const void *W, int64_t rows, int64_t K, void *y, int 
 
 size_t ggq_mul_mat_ws(int wt, int64_t N, int64_t K, int xdt, int64_t M, int path) {
     if (!known_type(wt) || M <= 0 || N <= 0 || K <= 0 || K % block_len(wt)) return 0;
-    const bool mmq = use_mmq(wt, M, path);
-    if (!mmq && xdt == GGQ_Q8_1) return 0;
-    return act_bytes(mmq, M, K);
+    return act_bytes(use_mmq(wt, M, path), M, K);
 }
 
 int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int xdt, int64_t M, int64_t ldx, void *y,
@@ -163,26 +166,25 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
     const int64_t rb = (int64_t)ggq_row_bytes(wt, K);
     Carve c(ws);
     if (!mmq) {
-        const uint8_t *q8 = static_cast<const uint8_t *>(x);
-        if (xdt != GGQ_Q8_1) {
-            uint8_t *q = c.take<uint8_t>((size_t)M * (K / 32) * Q8_1_BYTES);
-            rc = hip_status(launch_quantize(x, xdt, M, K, ldx, q, nullptr, nullptr, nullptr, s), "mul_mat quantize");
-            if (rc) return rc;
-            q8 = q;
-        }
+        // MMVQ quantizes (or copies) the activations into LDS in its prologue: no workspace.
         MmvqParams p{};
         p.W = static_cast<const uint8_t *>(W);
         p.row_bytes = rb;
         p.N = N;
         p.Np = N;
         p.npairs = (N + 1) / 2;
+        p.K = K;
         p.units = (int)(K / block_len(wt) * (wt == GGQ_Q4_K ? 8 : wt == GGQ_Q6_K ? 4 : 1));
-        p.q8 = q8;
+        p.xsrc = xdt;
+        p.x = x;
+        p.ldx = ldx;
+        p.q8 = static_cast<const uint8_t *>(x);
         p.q8_row = (K / 32) * Q8_1_BYTES;
         p.M = M;
         p.y = y;
         p.ldy = ldy;
-        const int nc = nc_for(M);
+        p.w_bytes = N * rb;
+        const int nc = std::min(nc_for(M), mmvq_max_cols(K));
         return hip_status(launch_mmvq(wt, nc, false, GGQ_EPI_NONE, ydt, p, (M + nc - 1) / nc, s), "mul_mat mmvq");
     }
     Planar pl = carve_planar(c, M, K);
@@ -214,7 +216,6 @@ namespace {
 struct IdLayout {
     RouteTables rt;
     int64_t max_tiles;
-    uint8_t *act;      // q8_1 rows (MMVQ) or planar base (MMQ)
     Planar pl;
     float *acc32;
     size_t total;
@@ -224,7 +225,7 @@ IdLayout id_layout(void *ws, int wt, int64_t E, int64_t N, int64_t K, int64_t T,
                    int epi, bool weighted, bool mmq) {
     IdLayout L{};
     const int64_t R = T * top_k;
-    const int J = mmq ? MMQ_MT : MMVQ_ID_J;
+    const int J = mmq ? MMQ_MT : mmvq_id_cols(R, E, K);
     L.max_tiles = route_max_tiles(R, E, J);
     const int64_t Np = epi == GGQ_EPI_SWIGLU ? N / 2 : N;
     const int64_t rows = x_per_route ? R : T;
@@ -238,7 +239,6 @@ IdLayout id_layout(void *ws, int wt, int64_t E, int64_t N, int64_t K, int64_t T,
     L.rt.perm = c.take<int32_t>((size_t)R * 4);
     L.rt.tiles = c.take<int4>((size_t)L.max_tiles * 16);
     if (mmq) L.pl = carve_planar(c, rows, K);
-    else L.act = c.take<uint8_t>((size_t)rows * (K / 32) * Q8_1_BYTES);
     L.acc32 = weighted ? c.take<float>((size_t)T * Np * 4) : nullptr;
     L.total = c.off;
     (void)wt;
@@ -284,7 +284,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     const int64_t R = T * top_k;
     const int64_t Np = epi == GGQ_EPI_SWIGLU ? N / 2 : N;
     const int64_t rows = x_per_route ? R : T;
-    const int J = mmq ? MMQ_MT : MMVQ_ID_J;
+    const int J = mmq ? MMQ_MT : mmvq_id_cols(R, E, K);
     rc = hip_status(launch_route_build(ids, R, E, J, L.rt, s), "mul_mat_id routes");
     if (rc) return rc;
     if (weighted) rc = hip_status(launch_fill_u32(reinterpret_cast<uint32_t *>(L.acc32), T * Np, 0u, s), "mul_mat_id zero");
@@ -292,8 +292,6 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     if (rc) return rc;
 
     if (!mmq) {
-        rc = hip_status(launch_quantize(x, xdt, rows, K, K, L.act, nullptr, nullptr, nullptr, s), "mul_mat_id quantize");
-        if (rc) return rc;
         MmvqParams p{};
         p.W = static_cast<const uint8_t *>(W);
         p.row_bytes = rb;
@@ -301,9 +299,11 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.N = N;
         p.Np = Np;
         p.npairs = epi == GGQ_EPI_SWIGLU ? Np : (N + 1) / 2;
+        p.K = K;
         p.units = (int)(K / block_len(wt) * (wt == GGQ_Q4_K ? 8 : wt == GGQ_Q6_K ? 4 : 1));
-        p.q8 = L.act;
-        p.q8_row = (K / 32) * Q8_1_BYTES;
+        p.xsrc = xdt;
+        p.x = x;
+        p.ldx = K;
         p.y = y;
         p.perm = L.rt.perm;
         p.groups = L.rt.tiles;
@@ -312,7 +312,8 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.x_per_route = x_per_route;
         p.route_w = route_w;
         p.acc32 = L.acc32;
-        rc = hip_status(launch_mmvq(wt, MMVQ_ID_J, true, epi, ydt, p, L.max_tiles, s), "mul_mat_id mmvq");
+        p.w_bytes = (E - 1) * expert_stride + N * rb;
+        rc = hip_status(launch_mmvq(wt, J, true, epi, ydt, p, L.max_tiles, s), "mul_mat_id mmvq");
     } else {
         rc = hip_status(launch_quantize(x, xdt, rows, K, K, nullptr, L.pl.xq, L.pl.xd, L.pl.xs, s), "mul_mat_id quantize");
         if (rc) return rc;

@@ -81,9 +81,48 @@ __device__ __forceinline__ int dot4(int a, int b, int c) {
     return __builtin_amdgcn_sdot4(a, b, c, false);
 }
 
-// ---- wave reductions over aligned segments of `width` lanes (power of two) ----
+// ---- cross-lane reductions ----
+// DPP / permlane based: no LDS traffic.  dpp(v, ctrl) reads lane-permuted v.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <- 7 - i within 8 lanes
+constexpr int DPP_MIRROR = 0x140;       // lane i <- 15 - i within 16 lanes
+constexpr int DPP_ROW_BCAST15 = 0x142;  // lane 15 of each row -> next row
+constexpr int DPP_ROW_BCAST31 = 0x143;  // lane 31 -> rows 2 and 3
+
+// Max / sum over aligned groups of 8 lanes, result in every lane of the group.
+__device__ __forceinline__ float max8(float v) {
+    v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+    v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+    return fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+}
+__device__ __forceinline__ int sum8(int v) {
+    v += dpp_i<DPP_XOR1>(v);
+    v += dpp_i<DPP_XOR2>(v);
+    return v + dpp_i<DPP_HALF_MIRROR>(v);
+}
+
+// Sum over aligned segments of `width` lanes (a power of two <= 64), with the
+// segment total in the LAST lane of each segment (width <= 16: in every lane).
+// Within a 16-lane row: DPP butterflies; across rows: DPP row broadcasts
+// (lane 15 of a row into the next row, lane 31 into rows 2 and 3).
 __device__ __forceinline__ float seg_sum(float v, int width) {
-    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (width >= 2) v += dpp_f<DPP_XOR1>(v);
+    if (width >= 4) v += dpp_f<DPP_XOR2>(v);
+    if (width >= 8) v += dpp_f<DPP_HALF_MIRROR>(v);
+    if (width >= 16) v += dpp_f<DPP_MIRROR>(v);
+    if (width >= 32)                        // rows 1, 3 += lane 15 of rows 0, 2
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), DPP_ROW_BCAST15, 0xA, 0xF, false));
+    if (width >= 64)                        // rows 2, 3 += lane 31
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), DPP_ROW_BCAST31, 0xC, 0xF, false));
     return v;
 }
 

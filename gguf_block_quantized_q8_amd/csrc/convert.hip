@@ -49,10 +49,7 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const void *__restri
             }
         }
     }
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    const float amax = max8(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     float d = amax / 127.0f;
     int q[4];
     int sum = 0;
@@ -67,9 +64,7 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const void *__restri
         q[i] = qi;
         sum += qi;
     }
-    sum += __shfl_xor(sum, 1, 64);
-    sum += __shfl_xor(sum, 2, 64);
-    sum += __shfl_xor(sum, 4, 64);
+    sum = sum8(sum);
     if (amax == 0.0f) d = 0.0f;
     const float s = d * (float)sum;
     if (!valid) return;
