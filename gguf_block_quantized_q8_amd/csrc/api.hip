@@ -94,8 +94,8 @@ int nc_for(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
 // Routes per MMVQ-id group: a little above the mean routes per expert, so an
 // expert's weights are rarely read twice and few columns sit idle.
-int mmvq_id_cols(int64_t R, int64_t E, int64_t K) {
-    return std::min(nc_for((R + E - 1) / E + 1), mmvq_max_cols(K));
+int mmvq_id_cols(int wt, int64_t R, int64_t E, int64_t K) {
+    return std::min(nc_for((R + E - 1) / E + 1), mmvq_max_cols(wt, K));
 }
 
 }  // namespace
@@ -174,7 +174,6 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
         p.Np = N;
         p.npairs = (N + 1) / 2;
         p.K = K;
-        p.units = (int)(K / block_len(wt) * (wt == GGQ_Q4_K ? 8 : wt == GGQ_Q6_K ? 4 : 1));
         p.xsrc = xdt;
         p.x = x;
         p.ldx = ldx;
@@ -184,7 +183,7 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
         p.y = y;
         p.ldy = ldy;
         p.w_bytes = N * rb;
-        const int nc = std::min(nc_for(M), mmvq_max_cols(K));
+        const int nc = std::min(nc_for(M), mmvq_max_cols(wt, K));
         return hip_status(launch_mmvq(wt, nc, false, GGQ_EPI_NONE, ydt, p, (M + nc - 1) / nc, s), "mul_mat mmvq");
     }
     Planar pl = carve_planar(c, M, K);
@@ -225,7 +224,7 @@ IdLayout id_layout(void *ws, int wt, int64_t E, int64_t N, int64_t K, int64_t T,
                    int epi, bool weighted, bool mmq) {
     IdLayout L{};
     const int64_t R = T * top_k;
-    const int J = mmq ? MMQ_MT : mmvq_id_cols(R, E, K);
+    const int J = mmq ? MMQ_MT : mmvq_id_cols(wt, R, E, K);
     L.max_tiles = route_max_tiles(R, E, J);
     const int64_t Np = epi == GGQ_EPI_SWIGLU ? N / 2 : N;
     const int64_t rows = x_per_route ? R : T;
@@ -284,7 +283,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     const int64_t R = T * top_k;
     const int64_t Np = epi == GGQ_EPI_SWIGLU ? N / 2 : N;
     const int64_t rows = x_per_route ? R : T;
-    const int J = mmq ? MMQ_MT : mmvq_id_cols(R, E, K);
+    const int J = mmq ? MMQ_MT : mmvq_id_cols(wt, R, E, K);
     rc = hip_status(launch_route_build(ids, R, E, J, L.rt, s), "mul_mat_id routes");
     if (rc) return rc;
     if (weighted) rc = hip_status(launch_fill_u32(reinterpret_cast<uint32_t *>(L.acc32), T * Np, 0u, s), "mul_mat_id zero");
@@ -300,7 +299,6 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.Np = Np;
         p.npairs = epi == GGQ_EPI_SWIGLU ? Np : (N + 1) / 2;
         p.K = K;
-        p.units = (int)(K / block_len(wt) * (wt == GGQ_Q4_K ? 8 : wt == GGQ_Q6_K ? 4 : 1));
         p.xsrc = xdt;
         p.x = x;
         p.ldx = K;

@@ -31,6 +31,9 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // ---- scalar codecs ----
+// int bits -> float.  Takes its argument by value: clang's __builtin_bit_cast
+// applied directly to an ext_vector element (v.y, v[i]) reads element 0.
+__device__ __forceinline__ float as_float(int bits) { return __builtin_bit_cast(float, bits); }
 __device__ __forceinline__ float fp16_bits_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);   // v_cvt_f32_f16: exact, subnormals kept
 }

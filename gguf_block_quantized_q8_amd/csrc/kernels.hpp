@@ -43,8 +43,10 @@ struct MmvqParams {
     int64_t Np;           // output rows (N, or N/2 with SwiGLU)
     int64_t npairs;       // row pairs handled (ceil(N/2), or Np with SwiGLU)
     int64_t K;
-    int units;            // lane work units per row
+    // work geometry (set by the launcher)
+    int units;            // decode units per row
     int seg;              // lanes per row segment (power of two, <= 64)
+    int upl;              // units per lane per work item
     // activations: float rows quantized in the kernel prologue (xsrc = DT_F32 /
     // DT_BF16, x with row stride ldx elements) or q8_1 rows copied (xsrc =
     // DT_Q8_1, q8 with q8_row bytes per row)
@@ -67,11 +69,12 @@ struct MmvqParams {
     // set by the launcher
     int64_t w_bytes;        // readable weight bytes from W (N*row_bytes, or up to the last expert's last row)
     int64_t act_lds_bytes;  // LDS bytes of the activation region (set by the launcher)
+    int stage_bpc;          // blocks per staged row chunk (set by the launcher)
     int stage_cps;          // 16-byte pieces per staged row chunk (set by the launcher)
     int stage_ninst;        // 1 KB copy instructions per work item (set by the launcher)
 };
-constexpr size_t MMVQ_LDS_MAX = 96 * 1024;     // activation bytes staged per block
-int mmvq_max_cols(int64_t K);                 // largest column group (8, 4, 2, 1) whose q8_1 rows fit in LDS
+constexpr size_t MMVQ_LDS_MAX = 64 * 1024;     // activation bytes staged per block
+int mmvq_max_cols(int t, int64_t K);          // largest column group (8, 4, 2, 1) whose activations fit in LDS
 hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqParams &p, int64_t ngroups_bound,
                        hipStream_t s);
 hipError_t launch_mmvq_dots(int t, const uint8_t *W, int64_t N, int64_t K, const uint8_t *q8, int64_t M,
