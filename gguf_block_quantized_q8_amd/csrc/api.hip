@@ -179,6 +179,7 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
         p.ldx = ldx;
         p.q8 = static_cast<const uint8_t *>(x);
         p.q8_row = (K / 32) * Q8_1_BYTES;
+        p.x_bytes = xdt == GGQ_Q8_1 ? M * p.q8_row : ((M - 1) * ldx + K) * (xdt == GGQ_F32 ? 4 : 2);
         p.M = M;
         p.y = y;
         p.ldy = ldy;
@@ -302,6 +303,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.xsrc = xdt;
         p.x = x;
         p.ldx = K;
+        p.x_bytes = rows * K * (xdt == GGQ_F32 ? 4 : 2);
         p.y = y;
         p.perm = L.rt.perm;
         p.groups = L.rt.tiles;

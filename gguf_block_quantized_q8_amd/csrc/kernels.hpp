@@ -55,6 +55,7 @@ struct MmvqParams {
     int64_t ldx;
     const uint8_t *q8;
     int64_t q8_row;
+    int64_t x_bytes;      // readable bytes from x (or q8): the activation buffer's extent
     int64_t M;            // dense: activation rows (columns of y^T)
     void *y;
     int64_t ldy;
@@ -72,6 +73,7 @@ struct MmvqParams {
     int stage_bpc;          // blocks per staged row chunk (set by the launcher)
     int stage_cps;          // 16-byte pieces per staged row chunk (set by the launcher)
     int stage_ninst;        // 1 KB copy instructions per work item (set by the launcher)
+    int act_dma;            // activation rows copied to LDS by DMA in the prologue (set by the launcher)
 };
 constexpr size_t MMVQ_LDS_MAX = 64 * 1024;     // activation bytes staged per block
 int mmvq_max_cols(int t, int64_t K);          // largest column group (8, 4, 2, 1) whose activations fit in LDS

@@ -30,16 +30,28 @@ constexpr int MMVQ_MAXI = 12;   // DMA instructions (1 KB each) per work item, a
 
 #define AS3 __attribute__((address_space(3)))
 typedef const uint8_t AS3 *lds_bp;
-typedef v4i __attribute__((aligned(2))) v4i_u2;                // 16 B at 2-byte alignment
-typedef v2i __attribute__((aligned(2))) v2i_u2;
+typedef v4i __attribute__((aligned(4))) v4i_u4;                // 16 B at 4-byte alignment
 
-// ---- LDS loads (the hardware runs in unaligned mode: 2-aligned dwords are fine) ----
+// ---- LDS loads ----
+// A ds_read_b128 from a 2-byte (not 4-byte) aligned address is legal here but
+// several times slower than an aligned one, so fields of 2-byte aligned blocks
+// are read as aligned dwords and shifted into place with v_alignbyte.
 __device__ __forceinline__ v4i l128(lds_bp p) { return *(const v4i AS3 *)p; }          // 16-aligned
-__device__ __forceinline__ v4i l128u(lds_bp p) { return *(const v4i_u2 AS3 *)p; }       // 2-aligned
-__device__ __forceinline__ v2i l64u(lds_bp p) { return *(const v2i_u2 AS3 *)p; }
+__device__ __forceinline__ v4i l128w(lds_bp p) { return *(const v4i_u4 AS3 *)p; }      // 4-aligned
+__device__ __forceinline__ uint32_t l32(lds_bp p) { return *(const uint32_t AS3 *)p; }  // 4-aligned
 __device__ __forceinline__ uint32_t l16(lds_bp p) { return *(const uint16_t AS3 *)p; }
 __device__ __forceinline__ float lf(lds_bp p) { return *(const float AS3 *)p; }
 __device__ __forceinline__ v2i l64(lds_bp p) { return *(const v2i AS3 *)p; }           // 8-aligned
+
+__device__ __forceinline__ int abyte(uint32_t hi, uint32_t lo, uint32_t s) {
+    return (int)__builtin_amdgcn_alignbyte(hi, lo, s);              // bytes s .. s+3 of hi:lo
+}
+// 16 bytes at a + s (a 4-aligned, s in {0, 2}); reads [a, a + 20).
+__device__ __forceinline__ v4i l128s(lds_bp a, uint32_t s) {
+    const v4i w = l128w(a);
+    const uint32_t w4 = l32(a + 16);
+    return v4i{abyte(w.y, w.x, s), abyte(w.z, w.y, s), abyte(w.w, w.z, s), abyte(w4, w.w, s)};
+}
 
 // ---- per-type decode helpers (shared by the units and the test hook) ----
 
@@ -93,8 +105,8 @@ struct Unit<T_Q4_K, NC> {
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             const lds_bp blk = rows[i] + sb * 144;
-            const v4i hdr = l128u(blk);
-            const v4i q0 = l128u(blk + 16 + 32 * p), q1 = l128u(blk + 32 + 32 * p);
+            const v4i hdr = l128(blk);                                // Q4_K blocks stay 16-aligned
+            const v4i q0 = l128(blk + 16 + 32 * p), q1 = l128(blk + 32 + 32 * p);
             d[i] = fp16_bits_to_f32((uint32_t)hdr.x & 0xffffu);
             dm[i] = fp16_bits_to_f32((uint32_t)hdr.x >> 16);
             int a, b, c, e;
@@ -145,11 +157,14 @@ struct Unit<T_Q6_K, NC> {
         float dsc[2][4];
 #pragma unroll
         for (int i = 0; i < 2; i++) {
-            const lds_bp blk = rows[i] + sb * 210;
-            const v4i ql0 = l128u(blk + 64 * hh + 16 * t);
-            const v4i ql1 = l128u(blk + 64 * hh + 32 + 16 * t);
-            const v4i qh = l128u(blk + 128 + 32 * hh + 16 * t);
-            const v2i scw = l64u(blk + 192 + 8 * hh);                 // scales 8hh .. 8hh+7
+            const lds_bp blk = rows[i] + sb * 210;                    // 2-byte aligned for odd sb
+            const uint32_t s = (uint32_t)(uintptr_t)blk & 3;
+            const lds_bp ba = blk - s;
+            const v4i ql0 = l128s(ba + 64 * hh + 16 * t, s);
+            const v4i ql1 = l128s(ba + 64 * hh + 32 + 16 * t, s);
+            const v4i qh = l128s(ba + 128 + 32 * hh + 16 * t, s);
+            const uint32_t c0 = l32(ba + 192 + 8 * hh), c1 = l32(ba + 196 + 8 * hh), c2 = l32(ba + 200 + 8 * hh);
+            const v2i scw = {abyte(c1, c0, s), abyte(c2, c1, s)};       // scales 8hh .. 8hh+7
             const float d = fp16_bits_to_f32(l16(blk + 208));
 #pragma unroll
             for (int g = 0; g < 4; g++) {
@@ -165,8 +180,8 @@ struct Unit<T_Q6_K, NC> {
             if (col >= ncols) break;
             const int b0 = sb * 8 + 4 * hh;                            // q8_1 block of g = 0
             const lds_bp qa = A.qa + col * A.K + b0 * 32 + 16 * t;
-            const v4i dv = l128u(A.d8 + (col * A.nb + b0) * 4);
-            const v4i hv = l128u(A.h16 + ((col * 2 + t) * A.nb + b0) * 4);
+            const v4i dv = l128(A.d8 + (col * A.nb + b0) * 4);
+            const v4i hv = l128(A.h16 + ((col * 2 + t) * A.nb + b0) * 4);
 #pragma unroll
             for (int g = 0; g < 4; g++) {
                 const v4i a = l128(qa + 32 * g);
@@ -192,10 +207,14 @@ struct Unit<T_Q8_0, NC> {
         float d[2];
 #pragma unroll
         for (int i = 0; i < 2; i++) {
-            const lds_bp blk = rows[i] + u * 34;
+            const lds_bp blk = rows[i] + u * 34;                      // 2-byte aligned
             d[i] = fp16_bits_to_f32(l16(blk));
-            q[i][0] = l128u(blk + 2);
-            q[i][1] = l128u(blk + 18);
+            const uint32_t s = (uint32_t)(uintptr_t)(blk + 2) & 3;
+            const lds_bp qa = blk + 2 - s;
+            const v4i w0 = l128w(qa), w1 = l128w(qa + 16);
+            const uint32_t w2 = l32(qa + 32);
+            q[i][0] = v4i{abyte(w0.y, w0.x, s), abyte(w0.z, w0.y, s), abyte(w0.w, w0.z, s), abyte(w1.x, w0.w, s)};
+            q[i][1] = v4i{abyte(w1.y, w1.x, s), abyte(w1.z, w1.y, s), abyte(w1.w, w1.z, s), abyte(w2, w1.w, s)};
         }
 #pragma unroll
         for (int col = 0; col < NC; col++) {
@@ -231,50 +250,116 @@ __device__ __forceinline__ int sum4(int v) {
     return v + dpp_i<DPP_XOR2>(v);
 }
 
-// Quantize (or copy) the activation rows of this block's columns into the
-// planar LDS layout: the same arithmetic as the standalone quantizer (IEEE
-// division, round half away from zero), 8 lanes per 32-value block, the loads
-// of four passes issued together.
+// q = round-half-away(x / d) in fp32 with d = amax / 127, as the quantizer
+// defines it, without an IEEE division per value: with inv an approximate
+// reciprocal (v_rcp, about 1 ulp), r = x * inv is within about 4 ulp of the
+// correctly rounded quotient, so both round to the same integer unless r lies
+// within a few ulp of a half-integer (then any nearest rounding of r is that
+// integer, rint included).  Those rare values, and non-finite r, take the
+// exact division.
+__device__ __forceinline__ int quant_one(float x, float d, float inv) {
+    const float r = x * inv;
+    float q = __builtin_rintf(r);
+    if (!(fabsf(r - q) < 0.5f - fabsf(r) * 0x1p-20f - 0x1p-30f)) {
+        const float z = x / d;
+        const float t = __builtin_truncf(z);
+        q = fabsf(z - t) >= 0.5f ? t + __builtin_copysignf(1.0f, z) : t;
+    }
+    return (int)__builtin_amdgcn_fmed3f(q, -127.0f, 127.0f);
+}
+
+// Activation rows of this block's columns -> planar q8_1 in LDS, 8 lanes per
+// 32-value block, PASSES blocks per lane per batch.  load() issues the global
+// loads of one batch into registers; store() quantizes them (or takes the
+// given q8_1 block) and writes the LDS layout: the same arithmetic as the
+// standalone quantizer (amax / 127 with IEEE division, round half away from
+// zero, s = d * sum(q)).
 template <int NC, bool H16>
-__device__ __forceinline__ void stage_acts(uint8_t *lds, const MmvqParams &p, const int64_t *xrow, int ncols) {
-    const int K = (int)p.K, nb = K / QK8_1;
-    uint8_t *qa = lds;
-    float *d8 = reinterpret_cast<float *>(lds + NC * K);
-    float *s8 = d8 + NC * nb;
-    int *h16 = reinterpret_cast<int *>(s8 + NC * nb);
-    const int sub = threadIdx.x & 7;
-    const int total = ncols * nb;
-    constexpr int PASSES = 4;
-    const int per_pass = blockDim.x / 8;
-    for (int base = 0; base < total; base += PASSES * per_pass) {   // block-uniform trip count
-        int q[PASSES];           // 4 packed int8 quants
-        int qsum[PASSES];
-        float dv[PASSES], sv[PASSES];
+struct ActStage {
+    static constexpr int PASSES = 4;
+    // Raw loads, converted in store(): two 8-byte loads per pass, the same
+    // instructions for every source type (no branch between load and use, so
+    // nothing waits on them before store()):
+    //   f32: values at lo.x lo.y hi.x hi.y;  bf16: lo (hi repeats lo);
+    //   q8_1: d, s at lo, the lane's 4 quants at hi.y.
+    v2i lo[PASSES], hi[PASSES];
+    uint32_t nb_magic;            // b / nb == umulhi(b, nb_magic) for every block index b used here
+
+    __device__ void init(int nb) { nb_magic = 0xffffffffu / (uint32_t)nb + 1u; }
+    __device__ int col_of(int b) const { return (int)__umulhi((uint32_t)b, nb_magic); }
+
+    __device__ void load(const MmvqParams &p, const int64_t *xrow, int total, int nb, int base) {
+        const int sub = threadIdx.x & 7, per_pass = blockDim.x >> 3;
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ps++) {
+            if (base + ps * per_pass >= total) break;                  // block-uniform
+            const int b = min(base + ps * per_pass + (int)(threadIdx.x >> 3), total - 1);
+            const int c = col_of(b), blk = b - c * nb;
+            const uint8_t *a0, *a1;
+            if (p.xsrc == DT_Q8_1) {
+                a0 = p.q8 + xrow[c] * p.q8_row + (int64_t)blk * Q8_1_BYTES;
+                a1 = a0 + 4 + 4 * sub;                                // [4 + 4 sub, 12 + 4 sub) of the block
+            } else {
+                const int64_t e0 = xrow[c] * p.ldx + blk * QK8_1 + sub * 4;
+                const int esz = p.xsrc == DT_F32 ? 4 : 2;
+                a0 = static_cast<const uint8_t *>(p.x) + e0 * esz;
+                a1 = p.xsrc == DT_F32 ? a0 + 8 : a0;
+            }
+            lo[ps] = *reinterpret_cast<const v2i *>(a0);
+            hi[ps] = *reinterpret_cast<const v2i *>(a1);
+        }
+    }
+
+    // Same as load(), from raw activation rows already copied into LDS at
+    // `raw` (column c at c * K * esz, or c * nb * 40 for q8_1 blocks).
+    __device__ void load_lds(const MmvqParams &p, const uint8_t *raw, int K, int total, int nb, int base) {
+        const int sub = threadIdx.x & 7, per_pass = blockDim.x >> 3;
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ps++) {
+            if (base + ps * per_pass >= total) break;                  // block-uniform
+            const int b = min(base + ps * per_pass + (int)(threadIdx.x >> 3), total - 1);
+            const int c = col_of(b), blk = b - c * nb;
+            lds_bp a0, a1;
+            if (p.xsrc == DT_Q8_1) {
+                a0 = (lds_bp)raw + (c * nb + blk) * Q8_1_BYTES;
+                a1 = a0 + 4 + 4 * sub;
+            } else {
+                const int esz = p.xsrc == DT_F32 ? 4 : 2;
+                a0 = (lds_bp)raw + (c * K + blk * QK8_1 + sub * 4) * esz;
+                a1 = p.xsrc == DT_F32 ? a0 + 8 : a0;
+            }
+            lo[ps] = l64(a0);
+            hi[ps] = l64(a1);
+        }
+    }
+
+    __device__ void store(uint8_t *lds, const MmvqParams &p, int K, int total, int nb, int base) {
+        uint8_t *qa = lds;
+        float *d8 = reinterpret_cast<float *>(lds + NC * K);
+        float *s8 = d8 + NC * nb;
+        int *h16 = reinterpret_cast<int *>(s8 + NC * nb);
+        const int sub = threadIdx.x & 7, per_pass = blockDim.x >> 3;
+        int q[PASSES], qsum[PASSES];
+        float dq[PASSES], sq[PASSES];
+        const int npass = min(PASSES, (total - base + per_pass - 1) / per_pass);   // block-uniform
         if (p.xsrc == DT_Q8_1) {
 #pragma unroll
             for (int ps = 0; ps < PASSES; ps++) {
-                const int b = min(base + ps * per_pass + (int)(threadIdx.x >> 3), total - 1);
-                const int c = b / nb, blk = b - c * nb;
-                const uint8_t *src = p.q8 + xrow[c] * p.q8_row + (int64_t)blk * Q8_1_BYTES;
-                q[ps] = reinterpret_cast<const int *>(src + 8)[sub];
-                const float2 ds = *reinterpret_cast<const float2 *>(src);
-                dv[ps] = ds.x;
-                sv[ps] = ds.y;
+                if (ps >= npass) break;
+                q[ps] = hi[ps].y;
+                dq[ps] = as_float(lo[ps].x);
+                sq[ps] = as_float(lo[ps].y);
+                qsum[ps] = dot4(q[ps], 0x01010101, 0);
             }
-#pragma unroll
-            for (int ps = 0; ps < PASSES; ps++) qsum[ps] = dot4(q[ps], 0x01010101, 0);
         } else {
             float v[PASSES][4];
 #pragma unroll
             for (int ps = 0; ps < PASSES; ps++) {
-                const int b = min(base + ps * per_pass + (int)(threadIdx.x >> 3), total - 1);
-                const int c = b / nb, blk = b - c * nb;
-                const int64_t e0 = xrow[c] * p.ldx + blk * QK8_1 + sub * 4;
+                if (ps >= npass) break;
+                const v2i t = lo[ps], u = hi[ps];
                 if (p.xsrc == DT_F32) {
-                    const v4f t = *reinterpret_cast<const v4f *>(static_cast<const float *>(p.x) + e0);
-                    v[ps][0] = t.x; v[ps][1] = t.y; v[ps][2] = t.z; v[ps][3] = t.w;
+                    v[ps][0] = as_float(t.x); v[ps][1] = as_float(t.y); v[ps][2] = as_float(u.x); v[ps][3] = as_float(u.y);
                 } else {
-                    const v2i t = *reinterpret_cast<const v2i *>(static_cast<const uint16_t *>(p.x) + e0);
                     v[ps][0] = bf16_bits_to_f32((uint32_t)t.x & 0xffffu);
                     v[ps][1] = bf16_bits_to_f32((uint32_t)t.x >> 16);
                     v[ps][2] = bf16_bits_to_f32((uint32_t)t.y & 0xffffu);
@@ -283,43 +368,44 @@ __device__ __forceinline__ void stage_acts(uint8_t *lds, const MmvqParams &p, co
             }
 #pragma unroll
             for (int ps = 0; ps < PASSES; ps++) {
+                if (ps >= npass) break;
                 const float amax = max8(fmaxf(fmaxf(fabsf(v[ps][0]), fabsf(v[ps][1])), fmaxf(fabsf(v[ps][2]), fabsf(v[ps][3]))));
-                float d = amax / 127.0f;
+                const float d = amax / 127.0f;
+                const float inv = __builtin_amdgcn_rcpf(d);
                 int packed = 0, sum = 0;
+                if (amax != 0.0f) {
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    int qi = 0;
-                    if (amax != 0.0f) qi = (int)fminf(fmaxf(roundf(v[ps][i] / d), -127.0f), 127.0f);
-                    packed |= (qi & 0xff) << (8 * i);
-                    sum += qi;
+                    for (int i = 0; i < 4; i++) {
+                        const int qi = quant_one(v[ps][i], d, inv);
+                        packed |= (qi & 0xff) << (8 * i);
+                        sum += qi;
+                    }
                 }
-                if (amax == 0.0f) d = 0.0f;
                 q[ps] = packed;
                 qsum[ps] = sum;
-                dv[ps] = d;
+                dq[ps] = amax != 0.0f ? d : 0.0f;
             }
 #pragma unroll
-            for (int ps = 0; ps < PASSES; ps++) {
-                const int s = sum8(qsum[ps]);
-                sv[ps] = dv[ps] * (float)s;
-            }
+            for (int ps = 0; ps < PASSES; ps++)
+                if (ps < npass) sq[ps] = dq[ps] * (float)sum8(qsum[ps]);
         }
 #pragma unroll
         for (int ps = 0; ps < PASSES; ps++) {
+            if (ps >= npass) break;
             const int b = base + ps * per_pass + (int)(threadIdx.x >> 3);
             const int half = H16 ? sum4(qsum[ps]) : 0;              // lanes 0..3: quants 0..15, 4..7: 16..31
             if (b < total) {
-                const int c = b / nb, blk = b - c * nb;
+                const int c = col_of(b), blk = b - c * nb;
                 reinterpret_cast<int *>(qa + c * K + blk * QK8_1)[sub] = q[ps];
                 if (sub == 0) {
-                    d8[c * nb + blk] = dv[ps];
-                    s8[c * nb + blk] = sv[ps];
+                    d8[c * nb + blk] = dq[ps];
+                    s8[c * nb + blk] = sq[ps];
                 }
                 if (H16 && (sub & 3) == 0) h16[(c * 2 + (sub >> 2)) * nb + blk] = -32 * half;
             }
         }
     }
-}
+};
 
 // ---- LDS weight staging ----
 extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(v4i rsrc, AS3 uint32_t *lds, int size, int voffset,
@@ -328,7 +414,36 @@ extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(v4i rsrc, AS3 uint32_
 
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }    // vmcnt(0)
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+// vmcnt(n) for a wave-uniform n in 0..MMVQ_MAXI: everything but the last n
+// vector-memory instructions of this wave has completed.
+__device__ __forceinline__ void wait_vm_n(int n) {
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    }
+}
 __device__ __forceinline__ void compiler_fence() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+// Workgroup barrier for LDS data only: this wave's LDS writes are complete,
+// then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
+// global loads (the weight copy in flight); LDS written by DMA must be waited
+// for explicitly (vmcnt) before it.
+__device__ __forceinline__ void lds_barrier() {
+    wait_lgkm();
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
 
 // One work item of a wave = (group of spw row pairs, K-chunk kc): the 2*spw
 // rows ("slots") of the group, blocks [kc*bpc, (kc+1)*bpc) of each.  With A
@@ -347,8 +462,13 @@ struct Stage {
     uint32_t off[MMVQ_MAXI];     // rel_s * row_bytes + 16 * piece of this lane's piece in instruction k
 };
 
+// FIXED: issue all MMVQ_MAXI instructions, the ones past ninst reading
+// nothing (offset past the range) into the 1 KB `sink`, so the number of
+// vector-memory instructions is known at compile time and the compiler's own
+// waits for older loads (the activations in the prologue) count past them.
+template <bool FIXED = false>
 __device__ __forceinline__ void stage_issue(const uint8_t *A, const uint8_t *wend, uint8_t *buf, const Stage &S,
-                                            int ninst) {
+                                            int ninst, uint8_t *sink = nullptr) {
     const uint32_t phi = (uint32_t)(reinterpret_cast<uintptr_t>(A) & 15);
     const uint8_t *base = A - phi;
     const int64_t avail = wend - base;
@@ -358,10 +478,16 @@ __device__ __forceinline__ void stage_issue(const uint8_t *A, const uint8_t *wen
 #pragma unroll
     for (int i = 0; i < 4; i++) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);   // wave-uniform descriptor
 #pragma unroll
-    for (int k = 0; k < MMVQ_MAXI; k++)
-        if (k < ninst)
+    for (int k = 0; k < MMVQ_MAXI; k++) {
+        if (FIXED) {
+            const bool use = k < ninst;
+            llvm_amdgcn_raw_buffer_load_lds(rsrc, (AS3 uint32_t *)(use ? buf + 1024 * k : sink), 16,
+                                            (int)((phi + (use ? S.off[k] : STAGE_UNUSED)) & ~15u), 0, 0, 0);
+        } else if (k < ninst) {
             llvm_amdgcn_raw_buffer_load_lds(rsrc, (AS3 uint32_t *)(buf + 1024 * k), 16, (int)((phi + S.off[k]) & ~15u),
                                             0, 0, 0);
+        }
+    }
 }
 
 // wend is 2-byte aligned; when it is not 4-byte aligned the dword holding its
@@ -389,23 +515,35 @@ __device__ __forceinline__ int64_t slot_rel(int s, int64_t Np) {
     return EPI == EPI_SWIGLU ? (int64_t)(s >> 1) + (s & 1) * Np : (int64_t)s;
 }
 
-// grid: (blocks_x, column groups).  Each block stages its columns' q8_1
-// activations in LDS, then each wave walks its work items (spw row pairs x
-// K-chunks), copying item i+1 into its second LDS buffer while it computes
-// item i from the first.
+// Largest workgroup per column count: up to 16 waves (one workgroup per CU
+// quantizes the activations once for all of them) while the registers of the
+// wider column groups still allow it.
+template <int NC>
+struct MaxWaves { static constexpr int value = NC <= 2 ? 16 : NC == 4 ? 8 : 4; };
+
+// grid: (blocks_x, column groups), blockDim = 64 x waves.  Each block stages
+// its columns' q8_1 activations in LDS, then each wave walks its work items
+// (spw row pairs x K-chunks), copying item i+1 into its second LDS buffer
+// while it computes item i from the first.
 template <int T, int NC, bool MOE, int EPI, int YDT>
-__global__ __launch_bounds__(256) void mmvq_kernel(const MmvqParams p) {
+__global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const MmvqParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ int64_t xrow[NC];
     __shared__ int32_t route_s[NC];
     typedef Unit<T, NC> U;
     constexpr int BB = Geom<T>::BYTES;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int wpb = blockDim.x >> 6;
     const int seg = p.seg, upl = p.upl, lane_in = lane & (seg - 1), spw = 64 / seg, sid = lane / seg;
     const int64_t grp = blockIdx.y;
     const int ninst = p.stage_ninst, cps = p.stage_cps, bpc = p.stage_bpc;
     const int bufsz = ninst * 1024;
-    uint8_t *wbuf = lds + p.act_lds_bytes + wave * 2 * bufsz;
+    // item buffers: first buffers of all waves, then their second buffers (which
+    // hold the raw activation rows during the prologue), then a 1 KB sink
+    uint8_t *wbuf = lds + p.act_lds_bytes + wave * bufsz;
+    const int bstride = wpb * bufsz;
+    uint8_t *raw = lds + p.act_lds_bytes + bstride;
+    uint8_t *sink = raw + bstride;
 
     // ---- columns of this group ----
     const uint8_t *W = p.W;
@@ -428,31 +566,76 @@ __global__ __launch_bounds__(256) void mmvq_kernel(const MmvqParams p) {
     }
     const uint8_t *wend = p.W + p.w_bytes;
     const int64_t rb = p.row_bytes;
+    __syncthreads();                                            // xrow / route_s visible
 
     // ---- per-lane staging tables ----
     Stage S;
+    {
+        int slot = lane / cps, c = lane - slot * cps;            // piece idx = lane + 64k -> (slot, c)
+        const int q64 = 64 / cps, r64 = 64 - q64 * cps;
 #pragma unroll
-    for (int k = 0; k < MMVQ_MAXI; k++) {
-        const int idx = lane + 64 * k, slot = idx / cps, c = idx - slot * cps;
-        S.off[k] = slot < 2 * spw ? (uint32_t)(slot_rel<EPI>(slot, p.Np) * rb) + 16u * (uint32_t)c : STAGE_UNUSED;
+        for (int k = 0; k < MMVQ_MAXI; k++) {
+            S.off[k] = slot < 2 * spw ? (uint32_t)(slot_rel<EPI>(slot, p.Np) * rb) + 16u * (uint32_t)c : STAGE_UNUSED;
+            c += r64;
+            slot += q64;
+            if (c >= cps) { c -= cps; slot++; }
+        }
     }
     const uint32_t relrb0 = (uint32_t)(slot_rel<EPI>(2 * sid, p.Np) * rb);
     const uint32_t relrb1 = (uint32_t)(slot_rel<EPI>(2 * sid + 1, p.Np) * rb);
     const int nkc = (p.units + seg * upl - 1) / (seg * upl);    // K-chunks per row
-    const int64_t wave_stride = (int64_t)gridDim.x * 4 * spw;
-    const int64_t pw0 = ((int64_t)blockIdx.x * 4 + wave) * spw;
+    const int64_t wave_stride = (int64_t)gridDim.x * wpb * spw;
+    const int64_t pw0 = ((int64_t)blockIdx.x * wpb + wave) * spw;
     // address of chunk kc in the first row of the group starting at pair pw
     auto chunk_addr = [&](int64_t pw, int kc) {
         return W + (EPI == EPI_SWIGLU ? pw : 2 * pw) * rb + (int64_t)kc * bpc * BB;
     };
 
-    if (pw0 < p.npairs) stage_issue(chunk_addr(pw0, 0), wend, wbuf, S, ninst);   // first weights in flight
-    __syncthreads();
-    stage_acts<NC, T == T_Q6_K>(lds, p, xrow, ncols);
-    __syncthreads();
+    // Prologue: the activation loads of the first batch go out first, then the
+    // first weight item, so the quantization below runs while the weights are
+    // in flight (waiting only for the activation loads, which are older).
+    ActStage<NC, T == T_Q6_K> AS;
+    const int K = (int)p.K, nb = K / QK8_1, total = ncols * nb;
+    AS.init(nb);
+    const int batch = ActStage<NC, T == T_Q6_K>::PASSES * (int)(blockDim.x >> 3);
+    const bool first = pw0 < p.npairs;
+    if (p.act_dma) {
+        // raw activation rows -> LDS by the same DMA path (older than the weight
+        // copy, so waiting for all but the weight instructions covers them)
+        const int rowb = p.xsrc == DT_Q8_1 ? nb * Q8_1_BYTES : K * (p.xsrc == DT_F32 ? 4 : 2);
+        const int ppc = rowb / 16, pieces = ncols * ppc;
+        const int64_t xstride = p.xsrc == DT_Q8_1 ? p.q8_row : p.ldx * (p.xsrc == DT_F32 ? 4 : 2);
+        const uint8_t *xb = p.xsrc == DT_Q8_1 ? p.q8 : static_cast<const uint8_t *>(p.x);
+        struct { const void *q; uint32_t range; uint32_t cfg; } r = {xb, (uint32_t)p.x_bytes, 0x00020000u};
+        v4i rsrc = __builtin_bit_cast(v4i, r);
+#pragma unroll
+        for (int i = 0; i < 4; i++) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+        for (int i = 0; (i * wpb + wave) * 64 < pieces; i++) {
+            const int j = (i * wpb + wave) * 64 + lane, c = j / ppc;
+            const uint32_t voff = j < pieces ? (uint32_t)(xrow[c] * xstride) + 16u * (uint32_t)(j - c * ppc) : STAGE_UNUSED;
+            llvm_amdgcn_raw_buffer_load_lds(rsrc, (AS3 uint32_t *)(raw + (i * wpb + wave) * 1024), 16, (int)voff, 0, 0, 0);
+        }
+        if (first) stage_issue(chunk_addr(pw0, 0), wend, wbuf, S, ninst);
+        wait_vm_n(first ? ninst : 0);
+        lds_barrier();                                          // every wave's share has landed
+        for (int base = 0; base < total; base += batch) {
+            AS.load_lds(p, raw, K, total, nb, base);
+            AS.store(lds, p, K, total, nb, base);
+        }
+    } else {
+        AS.load(p, xrow, total, nb, 0);
+        if (first) stage_issue<true>(chunk_addr(pw0, 0), wend, wbuf, S, ninst, sink);
+        else stage_issue<true>(chunk_addr(0, 0), wend, wbuf, S, 0, sink);
+        AS.store(lds, p, K, total, nb, 0);
+        for (int base = batch; base < total; base += batch) {     // larger column groups: further batches
+            AS.load(p, xrow, total, nb, base);
+            AS.store(lds, p, K, total, nb, base);
+        }
+    }
+    lds_barrier();                                              // planar activations complete
     ActL A;
-    A.K = (int)p.K;
-    A.nb = A.K / QK8_1;
+    A.K = K;
+    A.nb = nb;
     A.qa = (lds_bp)lds;
     A.d8 = A.qa + NC * A.K;
     A.s8 = A.d8 + NC * A.nb * 4;
@@ -477,18 +660,18 @@ __global__ __launch_bounds__(256) void mmvq_kernel(const MmvqParams p) {
         const uint8_t *Acur = chunk_addr(pw, kc);
 
         wait_vm();                                              // item (pw, kc) has landed
-        if (patch) stage_patch(Acur, wend, wbuf + cur * bufsz, S, ninst, lane);
+        if (patch) stage_patch(Acur, wend, wbuf + cur * bstride, S, ninst, lane);
         compiler_fence();
         // next item into the other buffer (its previous contents were consumed last iteration)
         int64_t npw = pw;
         int nkc_next = kc + 1;
         if (nkc_next == nkc) { nkc_next = 0; npw = pw + wave_stride; }
-        if (npw < p.npairs) stage_issue(chunk_addr(npw, nkc_next), wend, wbuf + (cur ^ 1) * bufsz, S, ninst);
+        if (npw < p.npairs) stage_issue(chunk_addr(npw, nkc_next), wend, wbuf + (cur ^ 1) * bstride, S, ninst);
 
         // this lane's units of the chunk, for both rows of its pair
         if (pvalid) {
             const uint32_t phi = (uint32_t)(reinterpret_cast<uintptr_t>(Acur) & 15);
-            const uint8_t *b = wbuf + cur * bufsz;
+            const uint8_t *b = wbuf + cur * bstride;
             // slot data sits at ((phi + rel*rb) & 15); shift back by the chunk's first
             // block so the unit index addresses whole rows
             const int back = kc * bpc * BB;
@@ -601,33 +784,34 @@ static void raise_lds_limit(K kernel, size_t lds) {
 }
 
 template <int T, int NC, bool MOE, int EPI, int YDT>
-static void launch_one(const MmvqParams &p, dim3 g, size_t lds, hipStream_t s) {
+static void launch_one(const MmvqParams &p, dim3 g, int waves, size_t lds, hipStream_t s) {
     auto k = mmvq_kernel<T, NC, MOE, EPI, YDT>;
     raise_lds_limit(k, lds);
-    hipLaunchKernelGGL(k, g, dim3(256), lds, s, p);
+    hipLaunchKernelGGL(k, g, dim3(64 * waves), lds, s, p);
 }
 
 template <int T, int NC>
-static void launch_nc(bool moe, int epi, int ydt, const MmvqParams &p, dim3 g, size_t lds, hipStream_t s) {
+static void launch_nc(bool moe, int epi, int ydt, const MmvqParams &p, dim3 g, int waves, size_t lds, hipStream_t s) {
     if (!moe) {
-        if (ydt == DT_F32) launch_one<T, NC, false, EPI_NONE, DT_F32>(p, g, lds, s);
-        else launch_one<T, NC, false, EPI_NONE, DT_BF16>(p, g, lds, s);
+        if (ydt == DT_F32) launch_one<T, NC, false, EPI_NONE, DT_F32>(p, g, waves, lds, s);
+        else launch_one<T, NC, false, EPI_NONE, DT_BF16>(p, g, waves, lds, s);
     } else if (epi == EPI_SWIGLU) {
-        if (ydt == DT_F32) launch_one<T, NC, true, EPI_SWIGLU, DT_F32>(p, g, lds, s);
-        else launch_one<T, NC, true, EPI_SWIGLU, DT_BF16>(p, g, lds, s);
+        if (ydt == DT_F32) launch_one<T, NC, true, EPI_SWIGLU, DT_F32>(p, g, waves, lds, s);
+        else launch_one<T, NC, true, EPI_SWIGLU, DT_BF16>(p, g, waves, lds, s);
     } else {
-        if (ydt == DT_F32) launch_one<T, NC, true, EPI_NONE, DT_F32>(p, g, lds, s);
-        else launch_one<T, NC, true, EPI_NONE, DT_BF16>(p, g, lds, s);
+        if (ydt == DT_F32) launch_one<T, NC, true, EPI_NONE, DT_F32>(p, g, waves, lds, s);
+        else launch_one<T, NC, true, EPI_NONE, DT_BF16>(p, g, waves, lds, s);
     }
 }
 
 template <int T>
-static void launch_t(int nc, bool moe, int epi, int ydt, const MmvqParams &p, dim3 g, size_t lds, hipStream_t s) {
+static void launch_t(int nc, bool moe, int epi, int ydt, const MmvqParams &p, dim3 g, int waves, size_t lds,
+                     hipStream_t s) {
     switch (nc) {
-    case 1: launch_nc<T, 1>(moe, epi, ydt, p, g, lds, s); break;
-    case 2: launch_nc<T, 2>(moe, epi, ydt, p, g, lds, s); break;
-    case 4: launch_nc<T, 4>(moe, epi, ydt, p, g, lds, s); break;
-    default: launch_nc<T, 8>(moe, epi, ydt, p, g, lds, s); break;
+    case 1: launch_nc<T, 1>(moe, epi, ydt, p, g, waves, lds, s); break;
+    case 2: launch_nc<T, 2>(moe, epi, ydt, p, g, waves, lds, s); break;
+    case 4: launch_nc<T, 4>(moe, epi, ydt, p, g, waves, lds, s); break;
+    default: launch_nc<T, 8>(moe, epi, ydt, p, g, waves, lds, s); break;
     }
 }
 
@@ -692,17 +876,34 @@ hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqPara
     // staging offsets are 32-bit from the first row of an item
     if ((epi == EPI_SWIGLU ? p.Np + spw : 2 * spw) * p.row_bytes + G.cps * 16 >= (int64_t(1) << 31))
         return hipErrorInvalidValue;
-    const size_t lds = act + 4 * 2 * (size_t)G.ninst * 1024;
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
-    // one round of resident blocks (each quantizes its activations once)
-    const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (int64_t)(160 * 1024) / (int64_t)lds));
-    const int64_t pairs_per_block = 4 * spw;
-    const int64_t need = (p.npairs + pairs_per_block - 1) / pairs_per_block;
+    // Waves per block: as many as LDS (two item buffers per wave) and registers
+    // allow, so that one resident block per CU quantizes the activations once
+    // for all its waves; fewer when the row groups would not fill them.
+    const size_t per_wave = 2 * (size_t)G.ninst * 1024;
+    const size_t lds_cap = 160 * 1024 - 256;                    // room for the static LDS of the kernel
+    const int max_waves = nc <= 2 ? MaxWaves<1>::value : nc == 4 ? MaxWaves<4>::value : MaxWaves<8>::value;
+    if (act + per_wave + 1024 > lds_cap) return hipErrorInvalidValue;
+    int waves = (int)std::min<size_t>((size_t)max_waves, (lds_cap - act - 1024) / per_wave);
+    const int64_t groups = (p.npairs + spw - 1) / spw;          // row groups (one wave's worth per K-chunk)
+    const int64_t fill = (groups + 255) / 256;                   // waves per block to give every CU one block
+    if (fill < waves) waves = (int)std::max<int64_t>(fill, std::min<int64_t>(waves, 4));
+    const size_t lds = act + (size_t)waves * per_wave + 1024;   // + the prologue's 1 KB sink
+    // raw activation rows through LDS when they fit the waves' second buffers and
+    // every row starts 16-byte aligned at a 32-bit offset
+    {
+        const int64_t nb = p.K / QK8_1;
+        const int64_t rowb = p.xsrc == DT_Q8_1 ? nb * Q8_1_BYTES : p.K * (p.xsrc == DT_F32 ? 4 : 2);
+        const int64_t stride = p.xsrc == DT_Q8_1 ? p.q8_row : p.ldx * (p.xsrc == DT_F32 ? 4 : 2);
+        p.act_dma = rowb % 16 == 0 && stride % 16 == 0 && (int64_t)nc * rowb <= (int64_t)waves * G.ninst * 1024 &&
+                    p.x_bytes > 0 && p.x_bytes < 0x7fffff00LL;
+    }
+    const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (int64_t)lds_cap / (int64_t)lds));
+    const int64_t need = (groups + waves - 1) / waves;
     const int64_t cap = std::max<int64_t>(1, 256 * per_cu / ngroups_bound);
     const dim3 g((unsigned)std::min<int64_t>(need, cap), (unsigned)ngroups_bound);
-    if (t == T_Q4_K) launch_t<T_Q4_K>(nc, moe, epi, ydt, p, g, lds, s);
-    else if (t == T_Q6_K) launch_t<T_Q6_K>(nc, moe, epi, ydt, p, g, lds, s);
-    else launch_t<T_Q8_0>(nc, moe, epi, ydt, p, g, lds, s);
+    if (t == T_Q4_K) launch_t<T_Q4_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
+    else if (t == T_Q6_K) launch_t<T_Q6_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
+    else launch_t<T_Q8_0>(nc, moe, epi, ydt, p, g, waves, lds, s);
     return hipGetLastError();
 }
 
