@@ -36,11 +36,37 @@ sys.path.insert(0, ROOT)
 import gguf_block_quantized_q8_amd as g  # noqa: E402
 from gguf_block_quantized_q8_amd import inputs  # noqa: E402
 
+TNAME = {8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}
 METRIC = "MMVQ GB/s @M=1 and MMQ/mul_mat_id TOPS @M=8192 (Q4_K,Q6_K), % of roofline"
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 ROTATE_BYTES = 1 << 30
-PROFILE_TRAFFIC = {}      # filled from committed rocprofv3 counter runs when present
+# HBM bytes per launch from rocprofv3 counter runs (2.0 x FETCH_SIZE + 1.0 x WRITE_SIZE,
+# calibrated on a plain copy; profiles/hbm_counter_calibration_copy256MiB.md), keyed
+# by kernel, with the hash of the kernel sources they were measured on: reported
+# as null once those sources change.
+PROFILE_TRAFFIC = {
+    "mmvq_kernel<Q4_K,NC=1>": (9785549, "aff3358b48c02ee6"),
+    "mmvq_kernel<Q6_K,NC=1>": (419493222, "aff3358b48c02ee6"),
+}
+KERNEL_SOURCES = {"mmvq": ("mmvq.hip", "common.hpp", "kernels.hpp")}
+
+
+def source_hash(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "gguf_block_quantized_q8_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(kernel):
+    rec = PROFILE_TRAFFIC.get(kernel)
+    if rec is None:
+        return None
+    kind = kernel.split("_")[0]
+    return rec[0] if kind in KERNEL_SOURCES and source_hash(kind) == rec[1] else None
 
 
 def vp(t):
@@ -68,7 +94,11 @@ class Ctx:
 
 
 def time_steps(step, K, W, graph):
-    """W untimed warmup steps, then exactly K timed steps (optionally as one HIP graph)."""
+    """W untimed warmup steps, then exactly K timed steps (optionally as one HIP graph).
+
+    Returns (wall seconds from perf_counter between two synchronizations, GPU
+    seconds between HIP events recorded on the launch stream around the timed
+    region)."""
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
@@ -85,18 +115,24 @@ def time_steps(step, K, W, graph):
                 step(i)
         gr.replay()                        # untimed first replay (uploads the graph)
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record()
         gr.replay()
+        e1.record()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         del gr
-        return dt
+        return dt, e0.elapsed_time(e1) * 1e-3
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     for i in range(K):
         step(i)
+    e1.record()
     torch.cuda.synchronize()
-    return time.perf_counter() - t0
+    return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
 
 
 def time_launches(launch, n):
@@ -116,14 +152,14 @@ def time_launches(launch, n):
 def roofline_bytes(nbytes, sec, kernel):
     a = nbytes / sec / 1e9
     return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": PROFILE_TRAFFIC.get(kernel), "kernel": kernel,
+            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic(kernel), "kernel": kernel,
             "kernel_us": round(sec * 1e6, 3)}
 
 
 def roofline_ops(ops, sec, kernel):
     a = ops / sec / 1e12
     return {"bound": "mfma", "achieved": round(a, 2), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-            "frac": round(a / INT8_PEAK_TOPS, 4), "traffic": PROFILE_TRAFFIC.get(kernel), "kernel": kernel,
+            "frac": round(a / INT8_PEAK_TOPS, 4), "traffic": traffic(kernel), "kernel": kernel,
             "kernel_us": round(sec * 1e6, 3), "ops_note": "int8 ops = 2*M*N*K, peak = dense int8 MFMA"}
 
 
@@ -142,27 +178,19 @@ def bench_decode(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, rotate=Tr
     ydt_c = g.F32 if ydt == torch.float32 else g.BF16
     wsb = ctx.L.ggq_mul_mat_ws(wt, N, K, g.BF16, M, g.PATH_MMVQ)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    q8 = torch.empty(M * (K // 32) * 40, dtype=torch.uint8, device=dev)
 
     def step(i):
         check(ctx.L.ggq_mul_mat(wt, vp(Wr[i % R]), N, K, vp(x), g.BF16, M, K, vp(y), ydt_c, N, vp(ws), wsb,
                                 g.PATH_MMVQ, ctx.s), "mul_mat")
 
-    check(ctx.L.ggq_quantize_q8_1(vp(x), g.BF16, M, K, K, vp(q8), ctx.s), "quantize")
-
-    def kernel_only(i):
-        check(ctx.L.ggq_mul_mat(wt, vp(Wr[i % R]), N, K, vp(q8), g.Q8_1, M, K, vp(y), ydt_c, N, None, 0,
-                                g.PATH_MMVQ, ctx.s), "mul_mat q8_1")
-
-    dt = time_steps(step, steps, warmup, graph=True)
+    # one step is one launch of the MMVQ kernel (it quantizes the activations itself)
+    dt, gpu = time_steps(step, steps, warmup, graph=True)
     ysz = 4 if ydt == torch.float32 else 2
-    step_bytes = wbytes + M * K * 2 + 2 * M * (K // 32) * 40 + M * N * ysz
-    kern_bytes = wbytes + M * (K // 32) * 40 + M * N * ysz
-    ksec = time_launches(kernel_only, min(200, 4 * R))
+    step_bytes = wbytes + M * K * 2 + M * N * ysz     # weights + bf16 activations + output
     del Wr
     return {"value": step_bytes * steps / dt / 1e9, "unit": "GB/s", "ms_per_step": dt / steps * 1e3,
             "step_bytes": step_bytes, "rotating_copies": R,
-            "roofline": roofline_bytes(kern_bytes, ksec, "mmvq_kernel")}
+            "roofline": roofline_bytes(step_bytes, gpu / steps, f"mmvq_kernel<{TNAME[wt]},NC={min(8, M)}>")}
 
 
 # ------------------------------------------------------------------ dense prefill (MMQ)
@@ -181,7 +209,7 @@ def bench_prefill(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, path=g.P
               "mul_mat")
 
     graph = M * N * K < 2e11
-    dt = time_steps(step, steps, warmup, graph=graph)
+    dt, _ = time_steps(step, steps, warmup, graph=graph)
     ops = 2.0 * M * N * K
     res = {"value": ops * steps / dt / 1e12, "unit": "TOPS", "ms_per_step": dt / steps * 1e3}
     if path != g.PATH_MMVQ and M > 8:
@@ -228,7 +256,7 @@ def bench_moe(ctx, Tn, steps, warmup):
         gate_up(i)
         down(i)
 
-    dt = time_steps(step, steps, warmup, graph=Tn <= 64)
+    dt, _ = time_steps(step, steps, warmup, graph=Tn <= 64)
     R = Tn * top_k
     res = {"ms_per_step": dt / steps * 1e3}
     tg = time_launches(gate_up, 20)
@@ -280,6 +308,8 @@ def main():
                     help="comma list of: decode, prefill, sweep, lmhead1, lmhead2048, moe16, moe8192 (default all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 256 MiB device copy 10 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -289,6 +319,14 @@ def main():
     torch.cuda.set_device(dev)
     ctx = Ctx(dev)
     K, W = args.steps, args.warmup
+    if args.calib_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": a.numel(), "calib_copy_bytes_written": b.numel(), "launches": 10}))
+        return
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
