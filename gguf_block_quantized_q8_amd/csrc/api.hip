@@ -217,7 +217,7 @@ struct IdLayout {
     RouteTables rt;
     int64_t max_tiles;
     Planar pl;
-    float *acc32;
+    float *o32;           // weighted: per-route fp32 outputs [R][Np]
     size_t total;
 };
 
@@ -239,7 +239,7 @@ IdLayout id_layout(void *ws, int wt, int64_t E, int64_t N, int64_t K, int64_t T,
     L.rt.perm = c.take<int32_t>((size_t)R * 4);
     L.rt.tiles = c.take<int4>((size_t)L.max_tiles * 16);
     if (mmq) L.pl = carve_planar(c, rows, K);
-    L.acc32 = weighted ? c.take<float>((size_t)T * Np * 4) : nullptr;
+    L.o32 = weighted ? c.take<float>((size_t)R * Np * 4) : nullptr;
     L.total = c.off;
     (void)wt;
     return L;
@@ -287,9 +287,10 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     const int J = mmq ? MMQ_MT : mmvq_id_cols(wt, R, E, K);
     rc = hip_status(launch_route_build(ids, R, E, J, L.rt, s), "mul_mat_id routes");
     if (rc) return rc;
-    if (weighted) rc = hip_status(launch_fill_u32(reinterpret_cast<uint32_t *>(L.acc32), T * Np, 0u, s), "mul_mat_id zero");
-    else rc = hip_status(launch_zero_inactive(ids, R, E, Np, y, ydt, s), "mul_mat_id zero");
-    if (rc) return rc;
+    if (!weighted) {
+        rc = hip_status(launch_zero_inactive(ids, R, E, Np, y, ydt, s), "mul_mat_id zero");
+        if (rc) return rc;
+    }
 
     if (!mmq) {
         MmvqParams p{};
@@ -311,7 +312,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.top_k = (int)top_k;
         p.x_per_route = x_per_route;
         p.route_w = route_w;
-        p.acc32 = L.acc32;
+        p.o32 = L.o32;
         p.w_bytes = (E - 1) * expert_stride + N * rb;
         rc = hip_status(launch_mmvq(wt, J, true, epi, ydt, p, L.max_tiles, s), "mul_mat_id mmvq");
     } else {
@@ -336,11 +337,11 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.top_k = (int)top_k;
         p.x_per_route = x_per_route;
         p.route_w = route_w;
-        p.acc32 = L.acc32;
+        p.o32 = L.o32;
         rc = hip_status(launch_mmq(wt, true, epi, ydt, p, s), "mul_mat_id mmq");
     }
     if (rc) return rc;
-    if (weighted) rc = hip_status(launch_finalize(L.acc32, T * Np, y, ydt, s), "mul_mat_id finalize");
+    if (weighted) rc = hip_status(launch_route_sum(L.o32, ids, route_w, T, (int)top_k, E, Np, y, ydt, s), "mul_mat_id route sum");
     return rc;
 }
 

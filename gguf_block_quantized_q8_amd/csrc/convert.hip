@@ -183,14 +183,47 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
     for (; i < n; i += st) p[i] = v;
 }
 
-// fp32 accumulator -> output dtype.
-template <int YDT>
-__global__ __launch_bounds__(256) void finalize_kernel(const float *__restrict__ acc, int64_t n, void *__restrict__ y) {
+// Route-weighted sum of per-route fp32 outputs:
+//   y[t][n] = sum over k in ascending order of w[t][k] * o[t*top_k + k][n]
+// for the active routes of token t (0 <= id < E), accumulated in fp32, then
+// stored in the output dtype.  One thread per V consecutive n (V = 4 when Np
+// is a multiple of 4, else 1).
+template <int YDT, int V>
+__global__ __launch_bounds__(256) void route_sum_kernel(const float *__restrict__ o, const int32_t *__restrict__ ids,
+                                                        const float *__restrict__ w, int64_t T, int top_k, int64_t E,
+                                                        int64_t Np, void *__restrict__ y) {
+    const int64_t q = Np / V;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t st = (int64_t)gridDim.x * blockDim.x;
-    for (; i < n; i += st) {
-        if (YDT == DT_F32) static_cast<float *>(y)[i] = acc[i];
-        else static_cast<uint16_t *>(y)[i] = (uint16_t)f32_to_bf16_bits(acc[i]);
+    for (; i < T * q; i += st) {
+        const int64_t t = i / q, n = V * (i - t * q);
+        float acc[V];
+        for (int c = 0; c < V; c++) acc[c] = 0.0f;
+        for (int k = 0; k < top_k; k++) {
+            const int64_t r = t * top_k + k;
+            const int32_t e = ids[r];
+            if (e < 0 || e >= E) continue;
+            const float wk = w[r];
+            if (V == 4) {
+                const v4f v = *reinterpret_cast<const v4f *>(o + r * Np + n);
+                for (int c = 0; c < V; c++) acc[c] = __builtin_fmaf(wk, v[c], acc[c]);
+            } else {
+                acc[0] = __builtin_fmaf(wk, o[r * Np + n], acc[0]);
+            }
+        }
+        const int64_t idx = t * Np + n;
+        if (V == 4) {
+            if (YDT == DT_F32) {
+                *reinterpret_cast<v4f *>(static_cast<float *>(y) + idx) = v4f{acc[0], acc[1], acc[2], acc[3]};
+            } else {
+                const v2i b = {(int)(f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16)),
+                               (int)(f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16))};
+                *reinterpret_cast<v2i *>(static_cast<uint16_t *>(y) + idx) = b;
+            }
+        } else {
+            if (YDT == DT_F32) static_cast<float *>(y)[idx] = acc[0];
+            else static_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_bf16_bits(acc[0]);
+        }
     }
 }
 
@@ -260,11 +293,19 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const float *acc, int64_t n, void *y, int ydt, hipStream_t s) {
+hipError_t launch_route_sum(const float *o, const int32_t *ids, const float *w, int64_t T, int top_k, int64_t E,
+                            int64_t Np, void *y, int ydt, hipStream_t s) {
+    const bool vec = Np % 4 == 0;
+    const int64_t n = T * (vec ? Np / 4 : Np);
     if (n == 0) return hipSuccess;
-    const unsigned g = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
-    if (ydt == DT_F32) hipLaunchKernelGGL(finalize_kernel<DT_F32>, dim3(g), dim3(256), 0, s, acc, n, y);
-    else hipLaunchKernelGGL(finalize_kernel<DT_BF16>, dim3(g), dim3(256), 0, s, acc, n, y);
+    const dim3 g((unsigned)std::min<int64_t>((n + 255) / 256, 16384)), b(256);
+    if (ydt == DT_F32) {
+        if (vec) hipLaunchKernelGGL((route_sum_kernel<DT_F32, 4>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
+        else hipLaunchKernelGGL((route_sum_kernel<DT_F32, 1>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
+    } else {
+        if (vec) hipLaunchKernelGGL((route_sum_kernel<DT_BF16, 4>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
+        else hipLaunchKernelGGL((route_sum_kernel<DT_BF16, 1>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
+    }
     return hipGetLastError();
 }
 

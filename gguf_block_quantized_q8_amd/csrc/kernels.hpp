@@ -13,7 +13,8 @@ hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float
                                  hipStream_t s);
 hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, void *y, int ydt, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s);
-hipError_t launch_finalize(const float *acc, int64_t n, void *y, int ydt, hipStream_t s);
+hipError_t launch_route_sum(const float *o, const int32_t *ids, const float *w, int64_t T, int top_k, int64_t E,
+                            int64_t Np, void *y, int ydt, hipStream_t s);
 hipError_t launch_zero_inactive(const int32_t *ids, int64_t R, int64_t E, int64_t Np, void *y, int ydt,
                                 hipStream_t s);
 
@@ -66,7 +67,7 @@ struct MmvqParams {
     int top_k;
     int x_per_route;
     const float *route_w;
-    float *acc32;
+    float *o32;           // weighted: per-route fp32 outputs [R][Np]
     // set by the launcher
     int64_t w_bytes;        // readable weight bytes from W (N*row_bytes, or up to the last expert's last row)
     int64_t act_lds_bytes;  // LDS bytes of the activation region (set by the launcher)
@@ -105,7 +106,7 @@ struct MmqParams {
     int top_k;
     int x_per_route;
     const float *route_w;
-    float *acc32;
+    float *o32;           // weighted: per-route fp32 outputs [R][Np]
 };
 constexpr int MMQ_NT = 128;   // weight rows per workgroup tile
 constexpr int MMQ_MT = 128;   // activation rows (routes) per workgroup tile

@@ -2,39 +2,41 @@
 // operands.
 //
 // Why fp16 MFMA and not int8 MFMA: each output needs one fp32 rescale per
-// 32-wide q8_1 block (weight sub-scale x activation scale), and on gfx950 the
-// int8 MFMA and the VALU barely overlap.  With int8 MFMA the rescale costs
-// cvt + int multiply by the sub-scale + fma per output per block; here the
-// integer sub-scale is folded into the fp16 weight operand instead
-// (Q4_K: sc * nibble <= 945, Q6_K: sc * (q - 32) split into two exact fp16
-// parts), the MFMA accumulates the block's dot in fp32 exactly, and only one
-// fma per output per block remains (times the activation scale d8).  Every
-// product and partial sum is an integer below 2^24, so the per-block dot is
-// exact, as with int8.
+// 32-wide q8_1 block (weight sub-scale x activation scale), and the VALU does
+// one wave64 operation per 4 cycles per SIMD, about the time a 32x32 MFMA
+// needs for its 1024 outputs.  With int8 MFMA the rescale costs cvt + int
+// multiply by the sub-scale + fma per output per block; here the integer
+// sub-scale is folded into the fp16 weight operand instead (Q4_K: sc * nibble
+// <= 945, Q6_K: sc * (q - 32) split into two exact fp16 parts), the MFMA sums
+// the block's dot in fp32 exactly, and one fma per output per block remains
+// (times the activation scale d8).  Every product and partial sum is an
+// integer below 2^24, so the per-block dot is exact, as with int8.
 //
 // Tiles: 128 weight rows x 128 activation rows per workgroup, 4 waves of
-// 64 x 64 (2 x 2 MFMA 32x32x16 tiles).  K is staged 64 at a time through LDS
-// (fp16, row stride 72 halves: conflict-free 16-byte fragment reads); per
-// 256-wide super-block the weight scales and the activation d8 are staged once.
-// Q4_K's min term  -dmin * sum_j m_j * s8_j  runs as a bf16 MFMA with s8
-// split exactly into three bf16 parts.
+// 64 x 64 (2 x 2 MFMA 32x32x16 tiles).  K advances one q8_1 block (32) per
+// stage, software-pipelined: each thread holds the next stage's raw weight
+// bytes and activation quants in registers while the current stage computes
+// from one of two LDS buffers, and a stage ends with an LDS-only barrier (no
+// wait on the global loads in flight).  Per 256-wide super-block the weight
+// d / dmin and the activation d8 / s8 are staged once.  Q4_K's min term
+// -dmin * sum_j m_j * s8_j runs as a bf16 MFMA with s8 split exactly into
+// three bf16 parts.
 #include "kernels.hpp"
 
 namespace ggq {
 
-constexpr int NT = MMQ_NT, MT = MMQ_MT, KS = 64, LDA = KS + 8, LDM = 40;
+constexpr int NT = MMQ_NT, MT = MMQ_MT, KS = 32, LDA = KS + 8, LDM = 40;
 constexpr int EPI_NONE_ = 0, EPI_SWIGLU_ = 1;
 
 template <int T>
 struct __attribute__((aligned(16))) MmqSmem {
     static constexpr int NA = T == T_Q6_K ? 2 : 1;       // Q6_K: high and low parts of sc*(q-32)
     static constexpr int NMIN = T == T_Q4_K ? 1 : 0;
-    _Float16 A[NA][NT][LDA];
-    _Float16 B[MT][LDA];
+    _Float16 A[2][NA][NT][LDA];   // two stage buffers
+    _Float16 B[2][MT][LDA];
+    float d8[2][8][MT];           // by super-block parity; [block][column]: conflict-free column reads
     float wd[NT];
     float wdmin[NT];
-    int8_t sc[NT][16];
-    float d8[MT][8];
     __bf16 Amin[NMIN ? NT : 1][LDM];
     __bf16 Bmin[NMIN ? MT : 1][LDM];
     int32_t xrow[MT];     // activation row of each tile column (-1: none)
@@ -54,153 +56,177 @@ __device__ __forceinline__ void split3_bf16(float v, __bf16 &p0, __bf16 &p1, __b
     p2 = __builtin_bit_cast(__bf16, (uint16_t)(__builtin_bit_cast(uint32_t, r2) >> 16));
 }
 
-__device__ __forceinline__ void q4k_scale_min_b(int j, const uint8_t *s, int &sc, int &mn) {
-    if (j < 4) {
-        sc = s[j] & 63;
-        mn = s[j + 4] & 63;
-    } else {
-        sc = (s[j + 4] & 0x0f) | ((s[j - 4] >> 6) << 4);
-        mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
-    }
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2v as_h2(uint32_t u) { return __builtin_bit_cast(h2v, u); }
+__device__ __forceinline__ uint32_t h2_bits(h2v h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Bytes 0,1 (sel = 0x00050004) or 2,3 (sel = 0x00070006) of x, each as the low
+// byte of a 16-bit half whose high byte is 0x64: read through `mask`, the half
+// is the fp16 number 1024 + (byte & low bits of mask).
+__device__ __forceinline__ uint32_t spread2(uint32_t x, uint32_t sel, uint32_t mask) {
+    return __builtin_amdgcn_perm(x, 0x64646464u, sel) & mask;
 }
 
-// Per super-block metadata: weight scales (threads 0..127 = weight rows) and
-// activation d8 / s8 (threads 128..255 = tile columns).  UNIT: all integer
-// sub-scales forced to 1 (test hook: raw per-group dots).
+// Q4_K: 8 packed 6-bit values (scales or mins) of the 12 header bytes
+// s0..s2, one per byte: groups 0..3 in `lo`, 4..7 in `hi`.
+__device__ __forceinline__ void q4k_pack(uint32_t s0, uint32_t s1, uint32_t s2, uint32_t &sc_lo, uint32_t &sc_hi,
+                                         uint32_t &mn_lo, uint32_t &mn_hi) {
+    sc_lo = s0 & 0x3f3f3f3fu;
+    mn_lo = s1 & 0x3f3f3f3fu;
+    sc_hi = (s2 & 0x0f0f0f0fu) | ((s0 >> 2) & 0x30303030u);
+    mn_hi = ((s2 >> 4) & 0x0f0f0f0fu) | ((s1 >> 2) & 0x30303030u);
+}
+
+// 16-byte global load (the pointer may have come through LDS, so name the
+// address space: a flat load would also count against the LDS counter).
+__device__ __forceinline__ v4i gld16(const uint8_t *p) {
+    return *(const v4i __attribute__((address_space(1))) *)p;
+}
+
+// One stage's raw operands in registers: thread t stages weight row t/2 (16
+// of the stage's 32 K values, half t&1) and tile column t/2 (same split).
+// Rows and columns past the matrix read a valid row instead (their results
+// are never stored), so staging has no branches.
+// UNIT: all sub-scales 1 and no activation scales (test hook: raw dots).
 template <int T, bool UNIT>
-__device__ __forceinline__ void stage_meta(MmqSmem<T> &sm, int sb, int64_t K, const float *__restrict__ xd,
-                                           const float *__restrict__ xs) {
-    const int tid = threadIdx.x;
-    if (tid < NT) {
-        const uint8_t *row = sm.wrow[tid];
-        if (T == T_Q4_K) {
-            float d = 0.f, dmin = 0.f;
-            uint8_t s[12] = {};
-            if (row) {
-                const uint8_t *blk = row + (int64_t)sb * 144;
-                const v4i hdr = *reinterpret_cast<const v4i *>(blk);
-                d = fp16_bits_to_f32((uint32_t)hdr.x & 0xffffu);
-                dmin = fp16_bits_to_f32((uint32_t)hdr.x >> 16);
-                for (int k = 0; k < 12; k++) s[k] = (uint8_t)(((uint32_t)hdr[1 + k / 4] >> (8 * (k & 3))) & 0xffu);
-            }
-            sm.wd[tid] = d;
-            sm.wdmin[tid] = dmin;
-            for (int j = 0; j < 8; j++) {
-                int sc = 0, mn = 0;
-                if (row) q4k_scale_min_b(j, s, sc, mn);
-                sm.sc[tid][j] = (int8_t)(UNIT ? 1 : sc);
-                const __bf16 mb = (__bf16)(float)mn;
-                sm.Amin[tid][3 * j] = mb;
-                sm.Amin[tid][3 * j + 1] = mb;
-                sm.Amin[tid][3 * j + 2] = mb;
-            }
-            for (int k = 24; k < 32; k++) sm.Amin[tid][k] = (__bf16)0.0f;
-        } else if (T == T_Q6_K) {
-            float d = 0.f;
-            v4i scw = {0, 0, 0, 0};
-            if (row) {
-                const uint8_t *blk = row + (int64_t)sb * 210;
-                d = fp16_bits_to_f32(ld_u16(blk + 208));
-                scw = ld16_a2(blk + 192);
-            }
-            sm.wd[tid] = d;
-            for (int j = 0; j < 16; j++)
-                sm.sc[tid][j] = UNIT ? (int8_t)1 : (int8_t)(((uint32_t)scw[j / 4] >> (8 * (j & 3))) & 0xffu);
-        }
-    } else {
-        const int i = tid - NT;
-        const int32_t xr = sm.xrow[i];
-        const int64_t nb = K / QK8_1;
-        for (int j = 0; j < 8; j++) {
-            float d8 = 0.f, s8 = 0.f;
-            if (xr >= 0 && !UNIT) {
-                d8 = xd[(int64_t)xr * nb + sb * 8 + j];
-                if (T == T_Q4_K) s8 = xs[(int64_t)xr * nb + sb * 8 + j];
-            }
-            sm.d8[i][j] = d8;
-            if (T == T_Q4_K) split3_bf16(s8, sm.Bmin[i][3 * j], sm.Bmin[i][3 * j + 1], sm.Bmin[i][3 * j + 2]);
-        }
-        if (T == T_Q4_K)
-            for (int k = 24; k < 32; k++) sm.Bmin[i][k] = (__bf16)0.0f;
-    }
-}
+struct Stager {
+    const uint8_t *wrow;      // this thread's weight row
+    const _Float16 *xrow;     // this thread's activation row + 16 * half
+    const float *xd, *xs;     // d, s of this thread's activation row + 4 * half
+    v4i hdr;        // Q4_K: block header (d, dmin, 12 scale bytes); Q6_K: the 16 int8 scales
+    v4i q0, q1;     // Q4_K: 16 quant bytes (q0); Q6_K: 16 ql bytes (q0), 16 qh bytes (q1)
+    uint32_t d6;    // Q6_K: fp16 d
+    v4i b0, b1;     // 16 fp16 activation quants
+    v4f m;          // stage 0 of a super-block: 4 d8; stage 1 (Q4_K): 4 s8
 
-// Stage weights [NT][KS] for K offset 64*st of super-block sb: fp16 of the
-// integer sub-scale times the raw quant (Q4_K) or the two exact parts of
-// sc*(q-32) (Q6_K).  Thread: row = tid/2, 16 weights of each of two groups.
-template <int T>
-__device__ __forceinline__ void stage_A(MmqSmem<T> &sm, int sb, int st) {
-    const int tid = threadIdx.x, tr = tid >> 1, hf = tid & 1;
-    const uint8_t *row = sm.wrow[tr];
-    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-    if (T == T_Q4_K) {
-        h8 lo[2], hi[2];
-        if (row) {
-            const v4i qs = *reinterpret_cast<const v4i *>(row + (int64_t)sb * 144 + 16 + 32 * st + 16 * hf);
-            const int sc0 = sm.sc[tr][2 * st], sc1 = sm.sc[tr][2 * st + 1];
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int byte = (qs[i / 4] >> (8 * (i % 4))) & 0xff;
-                lo[i / 8][i % 8] = (_Float16)(float)(sc0 * (byte & 15));
-                hi[i / 8][i % 8] = (_Float16)(float)(sc1 * (byte >> 4));
-            }
+    __device__ void init(const uint8_t *row, const _Float16 *xq, const float *d, const float *sx, int64_t K,
+                         int64_t xr) {
+        const int hf = threadIdx.x & 1;
+        wrow = row;
+        xrow = xq + xr * K + 16 * hf;
+        const int64_t nb = K / QK8_1;
+        xd = UNIT ? nullptr : d + xr * nb + 4 * hf;
+        xs = (UNIT || T != T_Q4_K) ? nullptr : sx + xr * nb + 4 * hf;
+    }
+
+    __device__ void load(int s) {
+        const int hf = threadIdx.x & 1;
+        const int sb = s >> 3, j = s & 7;
+        if (T == T_Q4_K) {
+            const uint8_t *blk = wrow + (int64_t)sb * 144;
+            hdr = gld16(blk);
+            q0 = gld16(blk + 16 + 32 * (j >> 1) + 16 * hf);
         } else {
-            lo[0] = lo[1] = hi[0] = hi[1] = h8{};
+            const uint8_t *blk = wrow + (int64_t)sb * 210;
+            const int hh = j >> 2, g = j & 3;
+            q0 = ld16_a2(blk + 64 * hh + 32 * (g & 1) + 16 * hf);
+            q1 = ld16_a2(blk + 128 + 32 * hh + 16 * hf);
+            hdr = ld16_a2(blk + 192);
+            d6 = ld_u16(blk + 208);
         }
-        h8 *dlo = reinterpret_cast<h8 *>(&sm.A[0][tr][16 * hf]);
-        h8 *dhi = reinterpret_cast<h8 *>(&sm.A[0][tr][32 + 16 * hf]);
-        dlo[0] = lo[0]; dlo[1] = lo[1];
-        dhi[0] = hi[0]; dhi[1] = hi[1];
-    } else {
-        const int hh = st >> 1, g0 = 2 * (st & 1);
-        h8 ah[2][2], al[2][2];
-        if (row) {
-            const uint8_t *blk = row + (int64_t)sb * 210;
-            const v4i qla = ld16_a2(blk + 64 * hh + 16 * hf);
-            const v4i qlb = ld16_a2(blk + 64 * hh + 32 + 16 * hf);
-            const v4i qh = ld16_a2(blk + 128 + 32 * hh + 16 * hf);
+        const _Float16 *src = xrow + (int64_t)s * KS;
+        b0 = *reinterpret_cast<const v4i *>(src);
+        b1 = *reinterpret_cast<const v4i *>(src + 8);
+        if (!UNIT && j == 0) m = *reinterpret_cast<const v4f *>(xd + sb * 8);
+        if (!UNIT && T == T_Q4_K && j == 1) m = *reinterpret_cast<const v4f *>(xs + sb * 8);
+    }
+
+    __device__ void store(MmqSmem<T> &sm, int s) {
+        const int tid = threadIdx.x, tr = tid >> 1, hf = tid & 1;
+        const int sb = s >> 3, j = s & 7, buf = s & 1;
+        // ---- weights: fp16 of sub-scale x quant, built in packed halves ----
+        if (T == T_Q4_K) {
+            uint32_t sc_lo, sc_hi, mn_lo, mn_hi;
+            q4k_pack((uint32_t)hdr.y, (uint32_t)hdr.z, (uint32_t)hdr.w, sc_lo, sc_hi, mn_lo, mn_hi);
+            const int sc = UNIT ? 1 : (int)__builtin_amdgcn_ubfe(j < 4 ? sc_lo : sc_hi, 8 * (j & 3), 8);
+            // (1024 + nib) * sc - 1024 * sc = sc * nib, exact in one fused rounding
+            const _Float16 scf = (_Float16)(float)sc, off = (_Float16)(float)(-1024 * sc);
+            const h2v sc2 = {scf, scf}, off2 = {off, off};
+            uint32_t o[8];
 #pragma unroll
-            for (int gg = 0; gg < 2; gg++) {
-                const int g = g0 + gg;
-                const int sc = sm.sc[tr][8 * hh + 2 * g + hf];
-                const int sl = sc & 15, sh = sc - sl;
-                const v4i ql = gg == 0 ? qla : qlb;
+            for (int w = 0; w < 4; w++) {
+                const uint32_t x = (j & 1) ? ((uint32_t)q0[w] >> 4) : (uint32_t)q0[w];   // odd groups: high nibbles
+                o[2 * w] = h2_bits(__builtin_elementwise_fma(as_h2(spread2(x, 0x00050004u, 0x640f640fu)), sc2, off2));
+                o[2 * w + 1] = h2_bits(__builtin_elementwise_fma(as_h2(spread2(x, 0x00070006u, 0x640f640fu)), sc2, off2));
+            }
+            v4i *dst = reinterpret_cast<v4i *>(&sm.A[buf][0][tr][16 * hf]);
+            dst[0] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+            dst[1] = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+        } else {
+            const int hh = (j >> 2), g = j & 3;
+            const int sc = UNIT ? 1 : (int)(int8_t)__builtin_amdgcn_ubfe((uint32_t)hdr[(8 * hh + 2 * g + hf) >> 2],
+                                                                          8 * ((2 * g + hf) & 3), 8);
+            const int sl = sc & 15, shi = sc - sl;
+            const _Float16 shf = (_Float16)(float)shi, slf = (_Float16)(float)sl, moff = (_Float16)-1056.0f;
+            const h2v sh2 = {shf, shf}, sl2 = {slf, slf}, off2 = {moff, moff};
+            uint32_t oh[8], ol[8];
 #pragma unroll
-                for (int i = 0; i < 16; i++) {
-                    const int lb = (ql[i / 4] >> (8 * (i % 4))) & 0xff;
-                    const int lo = g < 2 ? (lb & 15) : (lb >> 4);
-                    const int hb = ((qh[i / 4] >> (8 * (i % 4))) >> (2 * g)) & 3;
-                    const int q = (lo | (hb << 4)) - 32;
-                    ah[gg][i / 8][i % 8] = (_Float16)(float)(sh * q);
-                    al[gg][i / 8][i % 8] = (_Float16)(float)(sl * q);
+            for (int w = 0; w < 4; w++) {
+                const uint32_t lo = g < 2 ? ((uint32_t)q0[w] & 0x0f0f0f0fu) : (((uint32_t)q0[w] >> 4) & 0x0f0f0f0fu);
+                const uint32_t q6 = lo | ((((uint32_t)q1[w] >> (2 * g)) & 0x03030303u) << 4);   // 0..63 per byte
+#pragma unroll
+                for (int hlf = 0; hlf < 2; hlf++) {
+                    const h2v v = as_h2(spread2(q6, hlf ? 0x00070006u : 0x00050004u, 0x643f643fu)) + off2;   // q - 32, exact
+                    oh[2 * w + hlf] = h2_bits(v * sh2);                                                        // exact
+                    ol[2 * w + hlf] = h2_bits(v * sl2);
                 }
             }
-        } else {
-            ah[0][0] = ah[0][1] = ah[1][0] = ah[1][1] = h8{};
-            al[0][0] = al[0][1] = al[1][0] = al[1][1] = h8{};
+            v4i *dh = reinterpret_cast<v4i *>(&sm.A[buf][0][tr][16 * hf]);
+            v4i *dl = reinterpret_cast<v4i *>(&sm.A[buf][1][tr][16 * hf]);
+            dh[0] = v4i{(int)oh[0], (int)oh[1], (int)oh[2], (int)oh[3]};
+            dh[1] = v4i{(int)oh[4], (int)oh[5], (int)oh[6], (int)oh[7]};
+            dl[0] = v4i{(int)ol[0], (int)ol[1], (int)ol[2], (int)ol[3]};
+            dl[1] = v4i{(int)ol[4], (int)ol[5], (int)ol[6], (int)ol[7]};
         }
+        // ---- activations ----
+        {
+            v4i *dst = reinterpret_cast<v4i *>(&sm.B[buf][tr][16 * hf]);
+            dst[0] = b0;
+            dst[1] = b1;
+        }
+        if (UNIT) return;
+        // ---- per super-block scales ----
+        if (j == 0)
+            for (int i = 0; i < 4; i++) sm.d8[sb & 1][4 * hf + i][tr] = m[i];
+        if (j == 1) {
+            if (hf == 0) {
+                if (T == T_Q4_K) {
+                    sm.wd[tr] = fp16_bits_to_f32((uint32_t)hdr.x & 0xffffu);
+                    sm.wdmin[tr] = fp16_bits_to_f32((uint32_t)hdr.x >> 16);
+                } else {
+                    sm.wd[tr] = fp16_bits_to_f32(d6);
+                }
+            }
+            if (T == T_Q4_K) {
+                uint32_t sc_lo, sc_hi, mn_lo, mn_hi;
+                q4k_pack((uint32_t)hdr.y, (uint32_t)hdr.z, (uint32_t)hdr.w, sc_lo, sc_hi, mn_lo, mn_hi);
+                const uint32_t mw = hf ? mn_hi : mn_lo;
 #pragma unroll
-        for (int gg = 0; gg < 2; gg++) {
-            h8 *dh = reinterpret_cast<h8 *>(&sm.A[0][tr][32 * gg + 16 * hf]);
-            h8 *dl = reinterpret_cast<h8 *>(&sm.A[MmqSmem<T>::NA - 1][tr][32 * gg + 16 * hf]);
-            dh[0] = ah[gg][0]; dh[1] = ah[gg][1];
-            dl[0] = al[gg][0]; dl[1] = al[gg][1];
+                for (int jj = 0; jj < 4; jj++) {
+                    const int g = 4 * hf + jj;
+                    const __bf16 mb = (__bf16)(float)(int)__builtin_amdgcn_ubfe(mw, 8 * jj, 8);
+                    sm.Amin[tr][3 * g] = mb;
+                    sm.Amin[tr][3 * g + 1] = mb;
+                    sm.Amin[tr][3 * g + 2] = mb;
+                    split3_bf16(m[jj], sm.Bmin[tr][3 * g], sm.Bmin[tr][3 * g + 1], sm.Bmin[tr][3 * g + 2]);
+                }
+                if (hf == 1)
+                    for (int k = 24; k < 32; k++) { sm.Amin[tr][k] = (__bf16)0.0f; sm.Bmin[tr][k] = (__bf16)0.0f; }
+            }
         }
     }
-}
+};
 
-// Stage activations [MT][KS] (fp16 quants) from the planar layout.
-template <int T>
-__device__ __forceinline__ void stage_B(MmqSmem<T> &sm, const _Float16 *__restrict__ xq, int64_t K, int64_t k0) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-        const int q = tid + 256 * c, i = q >> 3, part = q & 7;
-        const int32_t xr = sm.xrow[i];
-        v4i v = {0, 0, 0, 0};
-        if (xr >= 0) v = *reinterpret_cast<const v4i *>(xq + (int64_t)xr * K + k0 + 8 * part);
-        *reinterpret_cast<v4i *>(&sm.B[i][8 * part]) = v;
-    }
+// LDS-only workgroup barrier: this wave's LDS accesses are complete, then
+// s_barrier.  Global loads in flight (the next stage's operands) are not
+// waited for, unlike __syncthreads().
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
 template <int YDT>
@@ -221,14 +247,36 @@ __device__ __forceinline__ void store4(void *y, int64_t idx, const float *v, int
     }
 }
 
+// Tile order: workgroup b runs on XCD b % 8; the tiles of one XCD are a
+// contiguous range of the grouped order below, so the workgroups resident on
+// an XCD at one time share a few weight tiles and a few activation tiles in
+// that XCD's L2.  Grouped order: 8 weight tiles (bn) side by side, then the
+// activation tiles (bm), then the next 8 weight tiles.
+__device__ __forceinline__ void tile_of(int64_t b, int64_t m_tiles, int64_t n_tiles, int64_t &bm, int64_t &bn) {
+    const int64_t total = m_tiles * n_tiles;
+    const int64_t per = total / 8;                            // tiles per XCD in the balanced part
+    const int64_t t = b < 8 * per ? (b % 8) * per + b / 8 : b;
+    const int64_t G = 8;
+    const int64_t gsize = G * m_tiles;                        // tiles per group of G weight tiles
+    const int64_t grp = t / gsize, in = t % gsize;
+    const int64_t gw = min<int64_t>(G, n_tiles - grp * G);   // weight tiles in this group
+    bm = in / gw;
+    bn = grp * G + in % gw;
+}
+
 // grid: 1-D, m_tiles * n_tiles workgroups of 256 threads.
 template <int T, bool MOE, int EPI, int YDT>
 __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
     __shared__ MmqSmem<T> sm;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wn = wave & 1, wm = wave >> 1;
-    const int64_t bm = (int64_t)blockIdx.x % p.m_tiles;
-    const int64_t bn = (int64_t)blockIdx.x / p.m_tiles;
+    int64_t bm, bn;
+    if (MOE) {
+        bm = (int64_t)blockIdx.x % p.m_tiles;
+        bn = (int64_t)blockIdx.x / p.m_tiles;
+    } else {
+        tile_of(blockIdx.x, p.m_tiles, p.n_tiles, bm, bn);
+    }
 
     // ---- tile columns (activation rows / routes) ----
     int tile_count = MT;
@@ -269,107 +317,108 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
     }
     __syncthreads();
 
-    v16f acc[2][2], P[2][2];
+    v16f acc[2][2], P[2][2];                                  // P: this super-block, set at its first block
 #pragma unroll
     for (int a = 0; a < 2; a++)
 #pragma unroll
-        for (int b = 0; b < 2; b++) { acc[a][b] = v16f{}; P[a][b] = v16f{}; }
+        for (int b = 0; b < 2; b++) acc[a][b] = v16f{};
 
-    const int nsb = (int)(p.K / 256);
+    const int nst = (int)(p.K / KS);
     const int lr = lane & 31, kh = 8 * (lane >> 5);
+    Stager<T, false> S;
+    {
+        // rows / columns past the matrix stage row 0 / activation row 0 (never stored)
+        const uint8_t *wr = sm.wrow[tid >> 1];
+        const int32_t xr = sm.xrow[tid >> 1];
+        S.init(wr ? wr : W, p.xq, p.xd, p.xs, p.K, xr >= 0 ? xr : 0);
+    }
+    S.load(0);
+    S.store(sm, 0);
+    if (nst > 1) S.load(1);
+    lds_sync();
 #pragma unroll 1
-    for (int sb = 0; sb < nsb; sb++) {
-        __syncthreads();                                      // previous super-block's meta no longer read
-        stage_meta<T, false>(sm, sb, p.K, p.xd, p.xs);
-#pragma unroll 1
-        for (int st = 0; st < 4; st++) {
-            __syncthreads();                                  // meta visible / previous stage consumed
-            stage_A<T>(sm, sb, st);
-            stage_B<T>(sm, p.xq, p.K, (int64_t)sb * 256 + 64 * st);
-            __syncthreads();
+    for (int s = 0; s < nst; s++) {
+        const int buf = s & 1, j = s & 7;
+        if (s + 1 < nst) S.store(sm, s + 1);                 // into the other buffer
+        if (s + 2 < nst) S.load(s + 2);
+        // ---- this stage: one q8_1 block of every column ----
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                v16f C[2][2];
-#pragma unroll
-                for (int a = 0; a < 2; a++)
-#pragma unroll
-                    for (int b = 0; b < 2; b++) C[a][b] = v16f{};
-#pragma unroll
-                for (int kk = 0; kk < 2; kk++) {
-                    const int ko = 32 * j + 16 * kk + kh;
-                    v8h bf[2];
-#pragma unroll
-                    for (int mi = 0; mi < 2; mi++) bf[mi] = *reinterpret_cast<const v8h *>(&sm.B[64 * wm + 32 * mi + lr][ko]);
-#pragma unroll
-                    for (int x = 0; x < MmqSmem<T>::NA; x++) {
-                        v8h af[2];
-#pragma unroll
-                        for (int ni = 0; ni < 2; ni++) af[ni] = *reinterpret_cast<const v8h *>(&sm.A[x][64 * wn + 32 * ni + lr][ko]);
-#pragma unroll
-                        for (int ni = 0; ni < 2; ni++)
-#pragma unroll
-                            for (int mi = 0; mi < 2; mi++)
-                                C[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ni], bf[mi], C[ni][mi], 0, 0, 0);
-                    }
-                }
-#pragma unroll
-                for (int mi = 0; mi < 2; mi++) {
-                    const float d8 = sm.d8[64 * wm + 32 * mi + lr][2 * st + j];
-#pragma unroll
-                    for (int ni = 0; ni < 2; ni++)
-#pragma unroll
-                        for (int e = 0; e < 16; e++) P[ni][mi][e] = __builtin_fmaf(C[ni][mi][e], d8, P[ni][mi][e]);
-                }
-            }
-        }
-        // ---- end of super-block: P * d (- dmin * min term) into acc ----
-        if (T == T_Q4_K) {
-            v16f Q[2][2];
-#pragma unroll
-            for (int a = 0; a < 2; a++)
-#pragma unroll
-                for (int b = 0; b < 2; b++) Q[a][b] = v16f{};
+        for (int ni = 0; ni < 2; ni++) {
+            v16f C[2] = {v16f{}, v16f{}};
 #pragma unroll
             for (int kk = 0; kk < 2; kk++) {
                 const int ko = 16 * kk + kh;
-                v8bf am[2], bmv[2];
+                v8h bf[2];
 #pragma unroll
-                for (int ni = 0; ni < 2; ni++) am[ni] = *reinterpret_cast<const v8bf *>(&sm.Amin[64 * wn + 32 * ni + lr][ko]);
+                for (int mi = 0; mi < 2; mi++) bf[mi] = *reinterpret_cast<const v8h *>(&sm.B[buf][64 * wm + 32 * mi + lr][ko]);
 #pragma unroll
-                for (int mi = 0; mi < 2; mi++) bmv[mi] = *reinterpret_cast<const v8bf *>(&sm.Bmin[64 * wm + 32 * mi + lr][ko]);
+                for (int x = 0; x < MmqSmem<T>::NA; x++) {
+                    const v8h af = *reinterpret_cast<const v8h *>(&sm.A[buf][x][64 * wn + 32 * ni + lr][ko]);
+#pragma unroll
+                    for (int mi = 0; mi < 2; mi++) C[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[mi], C[mi], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int mi = 0; mi < 2; mi++) {
+                const float d8 = sm.d8[(s >> 3) & 1][j][64 * wm + 32 * mi + lr];
+                if (j == 0) {                                 // first block of a super-block starts P
+#pragma unroll
+                    for (int e = 0; e < 16; e++) P[ni][mi][e] = C[mi][e] * d8;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; e++) P[ni][mi][e] = __builtin_fmaf(C[mi][e], d8, P[ni][mi][e]);
+                }
+            }
+        }
+        if (j == 7) {
+            // ---- end of super-block: P * d (- dmin * min term) into acc ----
+            if (T == T_Q4_K) {
+                v16f Q[2][2];
+#pragma unroll
+                for (int a = 0; a < 2; a++)
+#pragma unroll
+                    for (int b = 0; b < 2; b++) Q[a][b] = v16f{};
+#pragma unroll
+                for (int kk = 0; kk < 2; kk++) {
+                    const int ko = 16 * kk + kh;
+                    v8bf am[2], bmv[2];
+#pragma unroll
+                    for (int ni = 0; ni < 2; ni++) am[ni] = *reinterpret_cast<const v8bf *>(&sm.Amin[64 * wn + 32 * ni + lr][ko]);
+#pragma unroll
+                    for (int mi = 0; mi < 2; mi++) bmv[mi] = *reinterpret_cast<const v8bf *>(&sm.Bmin[64 * wm + 32 * mi + lr][ko]);
+#pragma unroll
+                    for (int ni = 0; ni < 2; ni++)
+#pragma unroll
+                        for (int mi = 0; mi < 2; mi++)
+                            Q[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[ni], bmv[mi], Q[ni][mi], 0, 0, 0);
+                }
 #pragma unroll
                 for (int ni = 0; ni < 2; ni++)
 #pragma unroll
-                    for (int mi = 0; mi < 2; mi++)
-                        Q[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[ni], bmv[mi], Q[ni][mi], 0, 0, 0);
+                    for (int e = 0; e < 16; e++) {
+                        const int tr = 64 * wn + 32 * ni + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        const float d = sm.wd[tr], dm = sm.wdmin[tr];
+#pragma unroll
+                        for (int mi = 0; mi < 2; mi++) {
+                            acc[ni][mi][e] = __builtin_fmaf(P[ni][mi][e], d, acc[ni][mi][e]);
+                            acc[ni][mi][e] = __builtin_fmaf(Q[ni][mi][e], -dm, acc[ni][mi][e]);
+                        }
+                    }
+            } else {
+#pragma unroll
+                for (int ni = 0; ni < 2; ni++)
+#pragma unroll
+                    for (int e = 0; e < 16; e++) {
+                        const int tr = 64 * wn + 32 * ni + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        const float d = sm.wd[tr];
+#pragma unroll
+                        for (int mi = 0; mi < 2; mi++) {
+                            acc[ni][mi][e] = __builtin_fmaf(P[ni][mi][e], d, acc[ni][mi][e]);
+                        }
+                    }
             }
-#pragma unroll
-            for (int ni = 0; ni < 2; ni++)
-#pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const int tr = 64 * wn + 32 * ni + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    const float d = sm.wd[tr], dm = sm.wdmin[tr];
-#pragma unroll
-                    for (int mi = 0; mi < 2; mi++) {
-                        acc[ni][mi][e] = __builtin_fmaf(P[ni][mi][e], d, acc[ni][mi][e]);
-                        acc[ni][mi][e] = __builtin_fmaf(Q[ni][mi][e], -dm, acc[ni][mi][e]);
-                        P[ni][mi][e] = 0.0f;
-                    }
-                }
-        } else {
-#pragma unroll
-            for (int ni = 0; ni < 2; ni++)
-#pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const int tr = 64 * wn + 32 * ni + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    const float d = sm.wd[tr];
-#pragma unroll
-                    for (int mi = 0; mi < 2; mi++) {
-                        acc[ni][mi][e] = __builtin_fmaf(P[ni][mi][e], d, acc[ni][mi][e]);
-                        P[ni][mi][e] = 0.0f;
-                    }
-                }
         }
+        lds_sync();
     }
 
     // ---- epilogue ----
@@ -391,9 +440,8 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
                     store4<YDT>(p.y, (int64_t)xr * p.ldy + n0, v, nv);
                 }
             } else {
+                // weighted: per-route fp32 outputs, summed per token afterwards
                 const int64_t r = sm.route[col];
-                const int64_t t = r / p.top_k;
-                const float w = p.route_w ? p.route_w[r] : 0.0f;
                 if (EPI == EPI_SWIGLU_) {
                     const int64_t n0 = bn * 64 + 32 * wn + 8 * g + 4 * (lane >> 5);
                     if (n0 >= p.Np) continue;
@@ -404,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
                         const float gt = acc[0][mi][4 * g + i], up = acc[1][mi][4 * g + i];
                         h[i] = gt / (1.0f + expf(-gt)) * up;
                     }
-                    if (p.route_w) { for (int i = 0; i < nv; i++) atomicAdd(&p.acc32[t * p.Np + n0 + i], w * h[i]); }
+                    if (p.o32) store4<DT_F32>(p.o32, r * p.Np + n0, h, nv);
                     else store4<YDT>(p.y, r * p.Np + n0, h, nv);
                 } else {
 #pragma unroll
@@ -413,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
                         if (n0 >= p.N) continue;
                         const int nv = (int)min<int64_t>(4, p.N - n0);
                         float v[4] = {acc[ni][mi][4 * g], acc[ni][mi][4 * g + 1], acc[ni][mi][4 * g + 2], acc[ni][mi][4 * g + 3]};
-                        if (p.route_w) { for (int i = 0; i < nv; i++) atomicAdd(&p.acc32[t * p.Np + n0 + i], w * v[i]); }
+                        if (p.o32) store4<DT_F32>(p.o32, r * p.Np + n0, v, nv);
                         else store4<YDT>(p.y, r * p.Np + n0, v, nv);
                     }
                 }
@@ -423,7 +471,8 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
 }
 
 // ---- test hook: per-group int32 dots from the staged tiles and the MFMA ----
-// Same staging (sub-scales forced to 1) and fragment layout as mmq_kernel.
+// Same staging (sub-scales forced to 1) and fragment layout as mmq_kernel;
+// one stage per q8_1 block, the 16-wide MFMA K steps give Q6_K's 16-groups.
 template <int T>
 __global__ __launch_bounds__(256) void mmq_dots_kernel(const uint8_t *__restrict__ W, int64_t N, int64_t K,
                                                        const _Float16 *__restrict__ xq, int64_t M, int64_t m_tiles,
@@ -444,41 +493,42 @@ __global__ __launch_bounds__(256) void mmq_dots_kernel(const uint8_t *__restrict
     constexpr int G = Geom<T>::G;
     const int64_t gpr = K / G;
     const int lr = lane & 31, kh = 8 * (lane >> 5);
-    for (int sb = 0; sb < (int)(K / 256); sb++) {
+    Stager<T, true> S;
+    {
+        const uint8_t *wr = sm.wrow[tid >> 1];
+        const int32_t xr = sm.xrow[tid >> 1];
+        S.init(wr ? wr : W, xq, nullptr, nullptr, K, xr >= 0 ? xr : 0);
+    }
+    for (int s = 0; s < (int)(K / KS); s++) {
         __syncthreads();
-        stage_meta<T, true>(sm, sb, K, nullptr, nullptr);
-        for (int st = 0; st < 4; st++) {
-            __syncthreads();
-            stage_A<T>(sm, sb, st);
-            stage_B<T>(sm, xq, K, (int64_t)sb * 256 + 64 * st);
-            __syncthreads();
-            for (int q16 = 0; q16 < 4; q16++) {                // 16-wide K steps of this stage
-                v16f C[2][2];
-                for (int a = 0; a < 2; a++) for (int b = 0; b < 2; b++) C[a][b] = v16f{};
-                const int ko = 16 * q16 + kh;
-                v8h bf[2];
-                for (int mi = 0; mi < 2; mi++) bf[mi] = *reinterpret_cast<const v8h *>(&sm.B[64 * wm + 32 * mi + lr][ko]);
-                for (int x = 0; x < MmqSmem<T>::NA; x++) {
-                    v8h af[2];
-                    for (int ni = 0; ni < 2; ni++) af[ni] = *reinterpret_cast<const v8h *>(&sm.A[x][64 * wn + 32 * ni + lr][ko]);
-                    for (int ni = 0; ni < 2; ni++)
-                        for (int mi = 0; mi < 2; mi++)
-                            C[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ni], bf[mi], C[ni][mi], 0, 0, 0);
-                }
-                const int64_t kabs = (int64_t)sb * 256 + 64 * st + 16 * q16;
+        S.load(s);
+        S.store(sm, s);
+        __syncthreads();
+        const int buf = s & 1;
+        v16f C[2][2];
+        for (int a = 0; a < 2; a++) for (int b = 0; b < 2; b++) C[a][b] = v16f{};
+        for (int kk = 0; kk < 2; kk++) {
+            const int ko = 16 * kk + kh;
+            if (G == 16) for (int a = 0; a < 2; a++) for (int b = 0; b < 2; b++) C[a][b] = v16f{};
+            v8h bf[2];
+            for (int mi = 0; mi < 2; mi++) bf[mi] = *reinterpret_cast<const v8h *>(&sm.B[buf][64 * wm + 32 * mi + lr][ko]);
+            for (int x = 0; x < MmqSmem<T>::NA; x++) {
+                v8h af[2];
+                for (int ni = 0; ni < 2; ni++) af[ni] = *reinterpret_cast<const v8h *>(&sm.A[buf][x][64 * wn + 32 * ni + lr][ko]);
                 for (int ni = 0; ni < 2; ni++)
                     for (int mi = 0; mi < 2; mi++)
-                        for (int e = 0; e < 16; e++) {
-                            const int64_t n = bn * NT + 64 * wn + 32 * ni + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                            const int64_t m = bm * MT + 64 * wm + 32 * mi + lr;
-                            if (n >= N || m >= M) continue;
-                            int32_t *o = out + (m * N + n) * gpr + kabs / G;
-                            const int32_t v = (int32_t)C[ni][mi][e];
-                            if (G == 16) *o = v;
-                            else if ((q16 & 1) == 0) *o = v;
-                            else *o += v;                         // same thread wrote the first half
-                        }
+                        C[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ni], bf[mi], C[ni][mi], 0, 0, 0);
             }
+            if (G == 32 && kk == 0) continue;
+            const int64_t grp = G == 16 ? ((int64_t)s * KS + 16 * kk) / 16 : (int64_t)s;
+            for (int ni = 0; ni < 2; ni++)
+                for (int mi = 0; mi < 2; mi++)
+                    for (int e = 0; e < 16; e++) {
+                        const int64_t n = bn * NT + 64 * wn + 32 * ni + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                        const int64_t m = bm * MT + 64 * wm + 32 * mi + lr;
+                        if (n >= N || m >= M) continue;
+                        out[(m * N + n) * gpr + grp] = (int32_t)C[ni][mi][e];
+                    }
         }
     }
 }

@@ -704,16 +704,15 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
                     store_out<YDT>(p.y, col * p.ldy + r0, acc[0][c]);
                     if (v1) store_out<YDT>(p.y, col * p.ldy + r1, acc[1][c]);
                 } else {
+                    // weighted: per-route fp32 outputs, summed per token afterwards
                     const int64_t r = route_s[c];
-                    const int64_t t = r / p.top_k;
                     if (EPI == EPI_SWIGLU) {
                         const float h = silu_mul(acc[0][c], acc[1][c]);
-                        if (p.route_w) atomicAdd(&p.acc32[t * p.Np + r0], p.route_w[r] * h);
+                        if (p.o32) p.o32[r * p.Np + r0] = h;
                         else store_out<YDT>(p.y, r * p.Np + r0, h);
-                    } else if (p.route_w) {
-                        const float w = p.route_w[r];
-                        atomicAdd(&p.acc32[t * p.Np + r0], w * acc[0][c]);
-                        if (v1) atomicAdd(&p.acc32[t * p.Np + r1], w * acc[1][c]);
+                    } else if (p.o32) {
+                        p.o32[r * p.Np + r0] = acc[0][c];
+                        if (v1) p.o32[r * p.Np + r1] = acc[1][c];
                     } else {
                         store_out<YDT>(p.y, r * p.Np + r0, acc[0][c]);
                         if (v1) store_out<YDT>(p.y, r * p.Np + r1, acc[1][c]);

@@ -103,7 +103,10 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
  *                  first, then up rows), N' = N/2 (N even).  Otherwise N' = N.
  *   route_w      : NULL: y is [T][top_k][N'] (inactive routes -> 0);
  *                  else [T][top_k] fp32 weights and y is [T][N'] =
- *                  sum_k route_w[t][k] * o'[t][k] (fp32 accumulation).
+ *                  sum_k route_w[t][k] * o'[t][k] over the active routes,
+ *                  in ascending k with fp32 accumulation (deterministic: the
+ *                  per-route fp32 outputs go to the workspace, then one pass
+ *                  sums them per token).
  *   y            : output of ydt (GGQ_F32 / GGQ_BF16), contiguous.
  *   ws           : at least ggq_mul_mat_id_ws(...) bytes.
  * Tokens, routes and tiles are grouped on the device; no host sync. */
