@@ -313,6 +313,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.x_per_route = x_per_route;
         p.route_w = route_w;
         p.o32 = L.o32;
+        p.groups_expected = std::min<int64_t>(E, R);
         p.w_bytes = (E - 1) * expert_stride + N * rb;
         rc = hip_status(launch_mmvq(wt, J, true, epi, ydt, p, L.max_tiles, s), "mul_mat_id mmvq");
     } else {

@@ -68,6 +68,7 @@ struct MmvqParams {
     int x_per_route;
     const float *route_w;
     float *o32;           // weighted: per-route fp32 outputs [R][Np]
+    int64_t groups_expected;   // routed: expected active groups (min(E, routes))
     // set by the launcher
     int64_t w_bytes;        // readable weight bytes from W (N*row_bytes, or up to the last expert's last row)
     int64_t act_lds_bytes;  // LDS bytes of the activation region (set by the launcher)

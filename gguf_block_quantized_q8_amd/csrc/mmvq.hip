@@ -898,7 +898,10 @@ hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqPara
     }
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (int64_t)lds_cap / (int64_t)lds));
     const int64_t need = (groups + waves - 1) / waves;
-    const int64_t cap = std::max<int64_t>(1, 256 * per_cu / ngroups_bound);
+    // routed: about min(E, routes) groups are active, whatever the host-side bound;
+    // give them at least two workgroups per CU between them
+    const int64_t active = moe ? std::max<int64_t>(1, std::min<int64_t>(ngroups_bound, p.groups_expected)) : ngroups_bound;
+    const int64_t cap = std::max<int64_t>(1, (moe ? 512 : 256) * per_cu / active);
     const dim3 g((unsigned)std::min<int64_t>(need, cap), (unsigned)ngroups_bound);
     if (t == T_Q4_K) launch_t<T_Q4_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
     else if (t == T_Q6_K) launch_t<T_Q6_K>(nc, moe, epi, ydt, p, g, waves, lds, s);

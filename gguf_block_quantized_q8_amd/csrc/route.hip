@@ -81,8 +81,82 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t *__res
     perm[offsets[ids[r]] + k] = (int32_t)r;
 }
 
+// Small problems: the whole build in one workgroup (counts in LDS), one launch.
+constexpr int64_t ROUTE_SMALL_R = 16384;
+constexpr int64_t ROUTE_SMALL_E = 4096;
+
+__global__ __launch_bounds__(1024) void route_build_small_kernel(const int32_t *__restrict__ ids, int64_t R, int64_t E,
+                                                                 int J, uint32_t *__restrict__ counts,
+                                                                 uint32_t *__restrict__ offsets,
+                                                                 uint32_t *__restrict__ tile_off,
+                                                                 uint32_t *__restrict__ ntiles, int4 *__restrict__ tiles,
+                                                                 int32_t *__restrict__ rank, int32_t *__restrict__ perm,
+                                                                 uint32_t *__restrict__ bad) {
+    __shared__ uint32_t s_cnt[ROUTE_SMALL_E], s_off[ROUTE_SMALL_E];
+    __shared__ uint32_t s_c[1024], s_t[1024];
+    __shared__ uint32_t s_bad, carry_c, carry_t;
+    const int tid = threadIdx.x;
+    for (int64_t e = tid; e < E; e += 1024) s_cnt[e] = 0;
+    if (tid == 0) { s_bad = 0; carry_c = 0; carry_t = 0; }
+    __syncthreads();
+    // ranks within each expert (LDS atomics)
+    for (int64_t r = tid; r < R; r += 1024) {
+        const int32_t e = ids[r];
+        int32_t k = -1;
+        if (e >= 0 && e < E) k = (int32_t)atomicAdd(&s_cnt[e], 1u);
+        else if (e >= E) atomicAdd(&s_bad, 1u);
+        rank[r] = k;
+    }
+    __syncthreads();
+    // exclusive scans of the counts and of the tile counts, tile list
+    for (int64_t base = 0; base < E; base += 1024) {
+        const int64_t e = base + tid;
+        const uint32_t c = e < E ? s_cnt[e] : 0u;
+        const uint32_t nt = (c + (uint32_t)J - 1) / (uint32_t)J;
+        s_c[tid] = c;
+        s_t[tid] = nt;
+        __syncthreads();
+        for (int o = 1; o < 1024; o <<= 1) {
+            const uint32_t vc = tid >= o ? s_c[tid - o] : 0u;
+            const uint32_t vt = tid >= o ? s_t[tid - o] : 0u;
+            __syncthreads();
+            s_c[tid] += vc;
+            s_t[tid] += vt;
+            __syncthreads();
+        }
+        const uint32_t oc = carry_c + s_c[tid] - c, ot = carry_t + s_t[tid] - nt;
+        if (e < E) {
+            s_off[e] = oc;
+            counts[e] = c;
+            offsets[e] = oc;
+            tile_off[e] = ot;
+            for (uint32_t i = 0; i < nt; i++)
+                tiles[ot + i] = int4{(int)e, (int)(oc + i * (uint32_t)J), (int)min((uint32_t)J, c - i * (uint32_t)J), 0};
+        }
+        __syncthreads();
+        if (tid == 1023) { carry_c += s_c[1023]; carry_t += s_t[1023]; }
+        __syncthreads();
+    }
+    // scatter (each thread reads back the ranks it wrote)
+    for (int64_t r = tid; r < R; r += 1024) {
+        const int32_t k = rank[r];
+        if (k >= 0) perm[s_off[ids[r]] + k] = (int32_t)r;
+    }
+    if (tid == 0) {
+        offsets[E] = carry_c;
+        tile_off[E] = carry_t;
+        *ntiles = carry_t;
+        *bad = s_bad;
+    }
+}
+
 hipError_t launch_route_build(const int32_t *ids, int64_t R, int64_t E, int J, const RouteTables &rt,
                               hipStream_t s) {
+    if (R <= ROUTE_SMALL_R && E <= ROUTE_SMALL_E) {
+        hipLaunchKernelGGL(route_build_small_kernel, dim3(1), dim3(1024), 0, s, ids, R, E, J, rt.counts, rt.offsets,
+                           rt.tile_off, rt.ntiles, rt.tiles, rt.rank, rt.perm, rt.bad);
+        return hipGetLastError();
+    }
     hipError_t err = launch_fill_u32(rt.counts, E, 0u, s);
     if (err != hipSuccess) return err;
     err = launch_fill_u32(rt.bad, 1, 0u, s);
