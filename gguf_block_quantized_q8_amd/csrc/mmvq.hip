@@ -269,141 +269,104 @@ __device__ __forceinline__ int quant_one(float x, float d, float inv) {
 }
 
 // Activation rows of this block's columns -> planar q8_1 in LDS, 8 lanes per
-// 32-value block, PASSES blocks per lane per batch.  load() issues the global
-// loads of one batch into registers; store() quantizes them (or takes the
-// given q8_1 block) and writes the LDS layout: the same arithmetic as the
+// 32-value block (lane sub of a group holds values 4 sub .. 4 sub + 3), one
+// block per lane group per loop trip.  The loops stay rolled: every launch
+// starts with a cold instruction cache, so the prologue's cost follows its
+// code size more than its instruction count.  put() is the arithmetic of the
 // standalone quantizer (amax / 127 with IEEE division, round half away from
-// zero, s = d * sum(q)).
+// zero, s = d * sum(q)), or takes a given q8_1 block as is.
 template <int NC, bool H16>
 struct ActStage {
-    static constexpr int PASSES = 4;
-    // Raw loads, converted in store(): two 8-byte loads per pass, the same
-    // instructions for every source type (no branch between load and use, so
-    // nothing waits on them before store()):
-    //   f32: values at lo.x lo.y hi.x hi.y;  bf16: lo (hi repeats lo);
-    //   q8_1: d, s at lo, the lane's 4 quants at hi.y.
-    v2i lo[PASSES], hi[PASSES];
     uint32_t nb_magic;            // b / nb == umulhi(b, nb_magic) for every block index b used here
 
     __device__ void init(int nb) { nb_magic = 0xffffffffu / (uint32_t)nb + 1u; }
     __device__ int col_of(int b) const { return (int)__umulhi((uint32_t)b, nb_magic); }
 
-    __device__ void load(const MmvqParams &p, const int64_t *xrow, int total, int nb, int base) {
-        const int sub = threadIdx.x & 7, per_pass = blockDim.x >> 3;
-#pragma unroll
-        for (int ps = 0; ps < PASSES; ps++) {
-            if (base + ps * per_pass >= total) break;                  // block-uniform
-            const int b = min(base + ps * per_pass + (int)(threadIdx.x >> 3), total - 1);
-            const int c = col_of(b), blk = b - c * nb;
-            const uint8_t *a0, *a1;
-            if (p.xsrc == DT_Q8_1) {
-                a0 = p.q8 + xrow[c] * p.q8_row + (int64_t)blk * Q8_1_BYTES;
-                a1 = a0 + 4 + 4 * sub;                                // [4 + 4 sub, 12 + 4 sub) of the block
-            } else {
-                const int64_t e0 = xrow[c] * p.ldx + blk * QK8_1 + sub * 4;
-                const int esz = p.xsrc == DT_F32 ? 4 : 2;
-                a0 = static_cast<const uint8_t *>(p.x) + e0 * esz;
-                a1 = p.xsrc == DT_F32 ? a0 + 8 : a0;
-            }
-            lo[ps] = *reinterpret_cast<const v2i *>(a0);
-            hi[ps] = *reinterpret_cast<const v2i *>(a1);
+    // Raw bytes of block b for this lane, the same two 8-byte loads for every
+    // source type: f32 values at lo.x lo.y hi.x hi.y; bf16 values in lo (hi
+    // repeats lo); q8_1: d, s at lo, the lane's 4 quants at hi.y.
+    __device__ void fetch(const MmvqParams &p, const int64_t *xrow, int nb, int b, v2i &lo, v2i &hi) const {
+        const int sub = threadIdx.x & 7, c = col_of(b), blk = b - c * nb;
+        const uint8_t *a0, *a1;
+        if (p.xsrc == DT_Q8_1) {
+            a0 = p.q8 + xrow[c] * p.q8_row + (int64_t)blk * Q8_1_BYTES;
+            a1 = a0 + 4 + 4 * sub;                                    // [4 + 4 sub, 12 + 4 sub) of the block
+        } else {
+            const int64_t e0 = xrow[c] * p.ldx + blk * QK8_1 + sub * 4;
+            const int esz = p.xsrc == DT_F32 ? 4 : 2;
+            a0 = static_cast<const uint8_t *>(p.x) + e0 * esz;
+            a1 = p.xsrc == DT_F32 ? a0 + 8 : a0;
         }
+        lo = *reinterpret_cast<const v2i *>(a0);
+        hi = *reinterpret_cast<const v2i *>(a1);
     }
 
-    // Same as load(), from raw activation rows already copied into LDS at
+    // Same as fetch(), from raw activation rows already copied into LDS at
     // `raw` (column c at c * K * esz, or c * nb * 40 for q8_1 blocks).
-    __device__ void load_lds(const MmvqParams &p, const uint8_t *raw, int K, int total, int nb, int base) {
-        const int sub = threadIdx.x & 7, per_pass = blockDim.x >> 3;
-#pragma unroll
-        for (int ps = 0; ps < PASSES; ps++) {
-            if (base + ps * per_pass >= total) break;                  // block-uniform
-            const int b = min(base + ps * per_pass + (int)(threadIdx.x >> 3), total - 1);
-            const int c = col_of(b), blk = b - c * nb;
-            lds_bp a0, a1;
-            if (p.xsrc == DT_Q8_1) {
-                a0 = (lds_bp)raw + (c * nb + blk) * Q8_1_BYTES;
-                a1 = a0 + 4 + 4 * sub;
-            } else {
-                const int esz = p.xsrc == DT_F32 ? 4 : 2;
-                a0 = (lds_bp)raw + (c * K + blk * QK8_1 + sub * 4) * esz;
-                a1 = p.xsrc == DT_F32 ? a0 + 8 : a0;
-            }
-            lo[ps] = l64(a0);
-            hi[ps] = l64(a1);
+    __device__ void fetch_lds(const MmvqParams &p, const uint8_t *raw, int K, int nb, int b, v2i &lo, v2i &hi) const {
+        const int sub = threadIdx.x & 7, c = col_of(b), blk = b - c * nb;
+        lds_bp a0, a1;
+        if (p.xsrc == DT_Q8_1) {
+            a0 = (lds_bp)raw + (c * nb + blk) * Q8_1_BYTES;
+            a1 = a0 + 4 + 4 * sub;
+        } else {
+            const int esz = p.xsrc == DT_F32 ? 4 : 2;
+            a0 = (lds_bp)raw + (c * K + blk * QK8_1 + sub * 4) * esz;
+            a1 = p.xsrc == DT_F32 ? a0 + 8 : a0;
         }
+        lo = l64(a0);
+        hi = l64(a1);
     }
 
-    __device__ void store(uint8_t *lds, const MmvqParams &p, int K, int total, int nb, int base) {
+    // Quantize (or take) block b and write it to the planar layout.  All 8
+    // lanes of the group take part (cross-lane reductions within the group).
+    __device__ void put(uint8_t *lds, const MmvqParams &p, int K, int nb, int b, v2i lo, v2i hi) const {
         uint8_t *qa = lds;
         float *d8 = reinterpret_cast<float *>(lds + NC * K);
         float *s8 = d8 + NC * nb;
         int *h16 = reinterpret_cast<int *>(s8 + NC * nb);
-        const int sub = threadIdx.x & 7, per_pass = blockDim.x >> 3;
-        int q[PASSES], qsum[PASSES];
-        float dq[PASSES], sq[PASSES];
-        const int npass = min(PASSES, (total - base + per_pass - 1) / per_pass);   // block-uniform
+        const int sub = threadIdx.x & 7;
+        int q, qsum;
+        float dq, sq;
         if (p.xsrc == DT_Q8_1) {
-#pragma unroll
-            for (int ps = 0; ps < PASSES; ps++) {
-                if (ps >= npass) break;
-                q[ps] = hi[ps].y;
-                dq[ps] = as_float(lo[ps].x);
-                sq[ps] = as_float(lo[ps].y);
-                qsum[ps] = dot4(q[ps], 0x01010101, 0);
-            }
+            q = hi.y;
+            dq = as_float(lo.x);
+            sq = as_float(lo.y);
+            qsum = dot4(q, 0x01010101, 0);
         } else {
-            float v[PASSES][4];
+            float v[4];
+            if (p.xsrc == DT_F32) {
+                v[0] = as_float(lo.x); v[1] = as_float(lo.y); v[2] = as_float(hi.x); v[3] = as_float(hi.y);
+            } else {
+                v[0] = bf16_bits_to_f32((uint32_t)lo.x & 0xffffu);
+                v[1] = bf16_bits_to_f32((uint32_t)lo.x >> 16);
+                v[2] = bf16_bits_to_f32((uint32_t)lo.y & 0xffffu);
+                v[3] = bf16_bits_to_f32((uint32_t)lo.y >> 16);
+            }
+            const float amax = max8(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+            const float d = amax / 127.0f;
+            const float inv = __builtin_amdgcn_rcpf(d);
+            q = 0;
+            qsum = 0;
+            if (amax != 0.0f) {
 #pragma unroll
-            for (int ps = 0; ps < PASSES; ps++) {
-                if (ps >= npass) break;
-                const v2i t = lo[ps], u = hi[ps];
-                if (p.xsrc == DT_F32) {
-                    v[ps][0] = as_float(t.x); v[ps][1] = as_float(t.y); v[ps][2] = as_float(u.x); v[ps][3] = as_float(u.y);
-                } else {
-                    v[ps][0] = bf16_bits_to_f32((uint32_t)t.x & 0xffffu);
-                    v[ps][1] = bf16_bits_to_f32((uint32_t)t.x >> 16);
-                    v[ps][2] = bf16_bits_to_f32((uint32_t)t.y & 0xffffu);
-                    v[ps][3] = bf16_bits_to_f32((uint32_t)t.y >> 16);
+                for (int i = 0; i < 4; i++) {
+                    const int qi = quant_one(v[i], d, inv);
+                    q |= (qi & 0xff) << (8 * i);
+                    qsum += qi;
                 }
             }
-#pragma unroll
-            for (int ps = 0; ps < PASSES; ps++) {
-                if (ps >= npass) break;
-                const float amax = max8(fmaxf(fmaxf(fabsf(v[ps][0]), fabsf(v[ps][1])), fmaxf(fabsf(v[ps][2]), fabsf(v[ps][3]))));
-                const float d = amax / 127.0f;
-                const float inv = __builtin_amdgcn_rcpf(d);
-                int packed = 0, sum = 0;
-                if (amax != 0.0f) {
-#pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const int qi = quant_one(v[ps][i], d, inv);
-                        packed |= (qi & 0xff) << (8 * i);
-                        sum += qi;
-                    }
-                }
-                q[ps] = packed;
-                qsum[ps] = sum;
-                dq[ps] = amax != 0.0f ? d : 0.0f;
-            }
-#pragma unroll
-            for (int ps = 0; ps < PASSES; ps++)
-                if (ps < npass) sq[ps] = dq[ps] * (float)sum8(qsum[ps]);
+            dq = amax != 0.0f ? d : 0.0f;
+            sq = dq * (float)sum8(qsum);
         }
-#pragma unroll
-        for (int ps = 0; ps < PASSES; ps++) {
-            if (ps >= npass) break;
-            const int b = base + ps * per_pass + (int)(threadIdx.x >> 3);
-            const int half = H16 ? sum4(qsum[ps]) : 0;              // lanes 0..3: quants 0..15, 4..7: 16..31
-            if (b < total) {
-                const int c = col_of(b), blk = b - c * nb;
-                reinterpret_cast<int *>(qa + c * K + blk * QK8_1)[sub] = q[ps];
-                if (sub == 0) {
-                    d8[c * nb + blk] = dq[ps];
-                    s8[c * nb + blk] = sq[ps];
-                }
-                if (H16 && (sub & 3) == 0) h16[(c * 2 + (sub >> 2)) * nb + blk] = -32 * half;
-            }
+        const int half = H16 ? sum4(qsum) : 0;                      // lanes 0..3: quants 0..15, 4..7: 16..31
+        const int c = col_of(b), blk = b - c * nb;
+        reinterpret_cast<int *>(qa + c * K + blk * QK8_1)[sub] = q;
+        if (sub == 0) {
+            d8[c * nb + blk] = dq;
+            s8[c * nb + blk] = sq;
         }
+        if (H16 && (sub & 3) == 0) h16[(c * 2 + (sub >> 2)) * nb + blk] = -32 * half;
     }
 };
 
@@ -597,7 +560,7 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
     ActStage<NC, T == T_Q6_K> AS;
     const int K = (int)p.K, nb = K / QK8_1, total = ncols * nb;
     AS.init(nb);
-    const int batch = ActStage<NC, T == T_Q6_K>::PASSES * (int)(blockDim.x >> 3);
+    const int gstep = (int)(blockDim.x >> 3);                   // lane groups of the block
     const bool first = pw0 < p.npairs;
     if (p.act_dma) {
         // raw activation rows -> LDS by the same DMA path (older than the weight
@@ -618,18 +581,24 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
         if (first) stage_issue(chunk_addr(pw0, 0), wend, wbuf, S, ninst);
         wait_vm_n(first ? ninst : 0);
         lds_barrier();                                          // every wave's share has landed
-        for (int base = 0; base < total; base += batch) {
-            AS.load_lds(p, raw, K, total, nb, base);
-            AS.store(lds, p, K, total, nb, base);
+#pragma unroll 1
+        for (int b = (int)(threadIdx.x >> 3); b < total; b += gstep) {
+            v2i lo, hi;
+            AS.fetch_lds(p, raw, K, nb, b, lo, hi);
+            AS.put(lds, p, K, nb, b, lo, hi);
         }
     } else {
-        AS.load(p, xrow, total, nb, 0);
+        // the first block of every lane group is loaded ahead of the weight copy
+        const int b0 = (int)(threadIdx.x >> 3);
+        v2i lo, hi;
+        AS.fetch(p, xrow, nb, min(b0, total - 1), lo, hi);
         if (first) stage_issue<true>(chunk_addr(pw0, 0), wend, wbuf, S, ninst, sink);
         else stage_issue<true>(chunk_addr(0, 0), wend, wbuf, S, 0, sink);
-        AS.store(lds, p, K, total, nb, 0);
-        for (int base = batch; base < total; base += batch) {     // larger column groups: further batches
-            AS.load(p, xrow, total, nb, base);
-            AS.store(lds, p, K, total, nb, base);
+        if (b0 < total) AS.put(lds, p, K, nb, b0, lo, hi);
+#pragma unroll 1
+        for (int b = b0 + gstep; b < total; b += gstep) {          // larger column groups: further blocks
+            AS.fetch(p, xrow, nb, b, lo, hi);
+            AS.put(lds, p, K, nb, b, lo, hi);
         }
     }
     lds_barrier();                                              // planar activations complete
