@@ -76,6 +76,10 @@ struct MmvqParams {
     int stage_cps;          // 16-byte pieces per staged row chunk (set by the launcher)
     int stage_ninst;        // 1 KB copy instructions per work item (set by the launcher)
     int act_dma;            // activation rows copied to LDS by DMA in the prologue (set by the launcher)
+    uint32_t nb_magic;      // ceil(2^32 / (K / 32)): block index -> column by one high multiply (set by the launcher)
+    uint32_t cps_magic;     // ceil(2^32 / stage_cps): piece index -> row slot (set by the launcher)
+    uint32_t ppc_magic;     // ceil(2^32 / (raw activation row bytes / 16)) when act_dma (set by the launcher)
+    int64_t x_stride;       // bytes between activation rows (x or q8) (set by the launcher)
 };
 constexpr size_t MMVQ_LDS_MAX = 64 * 1024;     // activation bytes staged per block
 int mmvq_max_cols(int t, int64_t K);          // largest column group (8, 4, 2, 1) whose activations fit in LDS

@@ -250,21 +250,17 @@ __device__ __forceinline__ int sum4(int v) {
     return v + dpp_i<DPP_XOR2>(v);
 }
 
-// q = round-half-away(x / d) in fp32 with d = amax / 127, as the quantizer
-// defines it, without an IEEE division per value: with inv an approximate
-// reciprocal (v_rcp, about 1 ulp), r = x * inv is within about 4 ulp of the
-// correctly rounded quotient, so both round to the same integer unless r lies
-// within a few ulp of a half-integer (then any nearest rounding of r is that
-// integer, rint included).  Those rare values, and non-finite r, take the
-// exact division.
-__device__ __forceinline__ int quant_one(float x, float d, float inv) {
-    const float r = x * inv;
-    float q = __builtin_rintf(r);
-    if (!(fabsf(r - q) < 0.5f - fabsf(r) * 0x1p-20f - 0x1p-30f)) {
-        const float z = x / d;
-        const float t = __builtin_truncf(z);
-        q = fabsf(z - t) >= 0.5f ? t + __builtin_copysignf(1.0f, z) : t;
-    }
+// q = round-half-away(x / d) in fp32 with d = amax / 127 and the IEEE
+// quotient, as the quantizer defines it.  put() avoids this division per
+// value: with inv an approximate reciprocal (v_rcp, about 1 ulp), z = x * inv
+// is within about 4 ulp of the correctly rounded quotient, so both round to
+// the same integer unless z lies within a few ulp of a half-integer (then any
+// nearest rounding of z is that integer).  Lanes holding such a value, or a
+// non-finite one, take this exact path for their four values.
+__device__ __forceinline__ int quant_exact(float x, float d) {
+    const float z = x / d;
+    const float t = __builtin_truncf(z);
+    const float q = fabsf(z - t) >= 0.5f ? t + __builtin_copysignf(1.0f, z) : t;
     return (int)__builtin_amdgcn_fmed3f(q, -127.0f, 127.0f);
 }
 
@@ -279,7 +275,7 @@ template <int NC, bool H16>
 struct ActStage {
     uint32_t nb_magic;            // b / nb == umulhi(b, nb_magic) for every block index b used here
 
-    __device__ void init(int nb) { nb_magic = 0xffffffffu / (uint32_t)nb + 1u; }
+    __device__ void init(uint32_t magic) { nb_magic = magic; }
     __device__ int col_of(int b) const { return (int)__umulhi((uint32_t)b, nb_magic); }
 
     // Raw bytes of block b for this lane, the same two 8-byte loads for every
@@ -345,16 +341,29 @@ struct ActStage {
             }
             const float amax = max8(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
             const float d = amax / 127.0f;
-            const float inv = __builtin_amdgcn_rcpf(d);
             q = 0;
             qsum = 0;
             if (amax != 0.0f) {
+                // Adding 1.5 * 2^23 rounds |z| <= 128 to the nearest integer and
+                // leaves it, two's complement, in the low byte of the sum's bits.
+                constexpr float RM = 12582912.0f;
+                const float inv = __builtin_amdgcn_rcpf(d);
+                int qb[4];
+                bool bad = false;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int qi = quant_one(v[i], d, inv);
-                    q |= (qi & 0xff) << (8 * i);
-                    qsum += qi;
+                    const float z = v[i] * inv;
+                    const float r = z + RM;
+                    bad |= !(fabsf(z - (r - RM)) < 0.5f - fabsf(z) * 0x1p-20f - 0x1p-30f);
+                    qb[i] = __builtin_bit_cast(int, r);
                 }
+                if (bad) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) qb[i] = quant_exact(v[i], d);
+                }
+                q = (int)(__builtin_amdgcn_perm((uint32_t)qb[1], (uint32_t)qb[0], 0x0c0c0400u) |
+                          __builtin_amdgcn_perm((uint32_t)qb[3], (uint32_t)qb[2], 0x04000c0cu));
+                qsum = dot4(q, 0x01010101, 0);
             }
             dq = amax != 0.0f ? d : 0.0f;
             sq = dq * (float)sum8(qsum);
@@ -478,6 +487,14 @@ __device__ __forceinline__ int64_t slot_rel(int s, int64_t Np) {
     return EPI == EPI_SWIGLU ? (int64_t)(s >> 1) + (s & 1) * Np : (int64_t)s;
 }
 
+// Byte offset of row slot s from the first row of its group, in 32 bits (the
+// launcher bounds every such offset, row_bytes below 2^24 and np_rb = Np *
+// row_bytes below 2^31).
+template <int EPI>
+__device__ __forceinline__ uint32_t slot_off(uint32_t s, uint32_t rb, uint32_t np_rb) {
+    return EPI == EPI_SWIGLU ? __umul24(s >> 1, rb) + ((s & 1) ? np_rb : 0u) : __umul24(s, rb);
+}
+
 // Largest workgroup per column count: up to 16 waves (one workgroup per CU
 // quantizes the activations once for all of them) while the registers of the
 // wider column groups still allow it.
@@ -492,6 +509,7 @@ template <int T, int NC, bool MOE, int EPI, int YDT>
 __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const MmvqParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ int64_t xrow[NC];
+    __shared__ uint32_t xoff[NC];     // byte offset of each column's raw activation row (DMA prologue)
     __shared__ int32_t route_s[NC];
     typedef Unit<T, NC> U;
     constexpr int BB = Geom<T>::BYTES;
@@ -514,7 +532,11 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
     if (!MOE) {
         const int64_t c0 = grp * NC;
         ncols = (int)min<int64_t>(NC, p.M - c0);
-        if (threadIdx.x < NC) xrow[threadIdx.x] = c0 + (threadIdx.x < ncols ? threadIdx.x : 0);
+        if (threadIdx.x < NC) {
+            const int64_t r = c0 + (threadIdx.x < ncols ? threadIdx.x : 0);
+            xrow[threadIdx.x] = r;
+            xoff[threadIdx.x] = (uint32_t)(r * p.x_stride);
+        }
     } else {
         if (grp >= (int64_t)*p.ngroups) return;                 // block-uniform
         const int4 g = p.groups[grp];
@@ -524,7 +546,9 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
             const int c = threadIdx.x < ncols ? threadIdx.x : 0;
             const int32_t r = p.perm[g.y + c];
             route_s[threadIdx.x] = r;
-            xrow[threadIdx.x] = p.x_per_route ? r : r / p.top_k;
+            const int64_t xr = p.x_per_route ? r : r / p.top_k;
+            xrow[threadIdx.x] = xr;
+            xoff[threadIdx.x] = (uint32_t)(xr * p.x_stride);
         }
     }
     const uint8_t *wend = p.W + p.w_bytes;
@@ -533,19 +557,21 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
 
     // ---- per-lane staging tables ----
     Stage S;
+    const uint32_t rb32 = (uint32_t)rb, np_rb = (uint32_t)(p.Np * rb);
     {
-        int slot = lane / cps, c = lane - slot * cps;            // piece idx = lane + 64k -> (slot, c)
-        const int q64 = 64 / cps, r64 = 64 - q64 * cps;
+        // piece P = lane + 64 k of an item: row slot P / cps, bytes 16 (P mod cps) on of that slot's chunk
 #pragma unroll
         for (int k = 0; k < MMVQ_MAXI; k++) {
-            S.off[k] = slot < 2 * spw ? (uint32_t)(slot_rel<EPI>(slot, p.Np) * rb) + 16u * (uint32_t)c : STAGE_UNUSED;
-            c += r64;
-            slot += q64;
-            if (c >= cps) { c -= cps; slot++; }
+            S.off[k] = STAGE_UNUSED;
+            if (k < ninst) {
+                const uint32_t P = (uint32_t)(lane + 64 * k), slot = __umulhi(P, p.cps_magic);
+                const uint32_t c16 = 16u * P - __umul24(slot, 16u * (uint32_t)cps);
+                if (slot < 2u * (uint32_t)spw) S.off[k] = slot_off<EPI>(slot, rb32, np_rb) + c16;
+            }
         }
     }
-    const uint32_t relrb0 = (uint32_t)(slot_rel<EPI>(2 * sid, p.Np) * rb);
-    const uint32_t relrb1 = (uint32_t)(slot_rel<EPI>(2 * sid + 1, p.Np) * rb);
+    const uint32_t relrb0 = slot_off<EPI>(2 * sid, rb32, np_rb);
+    const uint32_t relrb1 = slot_off<EPI>(2 * sid + 1, rb32, np_rb);
     const int nkc = (p.units + seg * upl - 1) / (seg * upl);    // K-chunks per row
     const int64_t wave_stride = (int64_t)gridDim.x * wpb * spw;
     const int64_t pw0 = ((int64_t)blockIdx.x * wpb + wave) * spw;
@@ -559,24 +585,23 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
     // in flight (waiting only for the activation loads, which are older).
     ActStage<NC, T == T_Q6_K> AS;
     const int K = (int)p.K, nb = K / QK8_1, total = ncols * nb;
-    AS.init(nb);
+    AS.init(p.nb_magic);
     const int gstep = (int)(blockDim.x >> 3);                   // lane groups of the block
     const bool first = pw0 < p.npairs;
     if (p.act_dma) {
         // raw activation rows -> LDS by the same DMA path (older than the weight
         // copy, so waiting for all but the weight instructions covers them)
-        const int rowb = p.xsrc == DT_Q8_1 ? nb * Q8_1_BYTES : K * (p.xsrc == DT_F32 ? 4 : 2);
-        const int ppc = rowb / 16, pieces = ncols * ppc;
-        const int64_t xstride = p.xsrc == DT_Q8_1 ? p.q8_row : p.ldx * (p.xsrc == DT_F32 ? 4 : 2);
+        const uint32_t rowb = p.xsrc == DT_Q8_1 ? nb * Q8_1_BYTES : K * (p.xsrc == DT_F32 ? 4 : 2);
+        const uint32_t ppc = rowb / 16, pieces = ncols * ppc;
         const uint8_t *xb = p.xsrc == DT_Q8_1 ? p.q8 : static_cast<const uint8_t *>(p.x);
         struct { const void *q; uint32_t range; uint32_t cfg; } r = {xb, (uint32_t)p.x_bytes, 0x00020000u};
         v4i rsrc = __builtin_bit_cast(v4i, r);
 #pragma unroll
         for (int i = 0; i < 4; i++) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
-        for (int i = 0; (i * wpb + wave) * 64 < pieces; i++) {
-            const int j = (i * wpb + wave) * 64 + lane, c = j / ppc;
-            const uint32_t voff = j < pieces ? (uint32_t)(xrow[c] * xstride) + 16u * (uint32_t)(j - c * ppc) : STAGE_UNUSED;
-            llvm_amdgcn_raw_buffer_load_lds(rsrc, (AS3 uint32_t *)(raw + (i * wpb + wave) * 1024), 16, (int)voff, 0, 0, 0);
+        for (uint32_t j0 = (uint32_t)wave * 64; j0 < pieces; j0 += (uint32_t)wpb * 64) {
+            const uint32_t j = j0 + lane, c = __umulhi(j, p.ppc_magic);
+            const uint32_t voff = j < pieces ? xoff[c] + 16u * (j - __umul24(c, ppc)) : STAGE_UNUSED;
+            llvm_amdgcn_raw_buffer_load_lds(rsrc, (AS3 uint32_t *)(raw + j0 * 16), 16, (int)voff, 0, 0, 0);
         }
         if (first) stage_issue(chunk_addr(pw0, 0), wend, wbuf, S, ninst);
         wait_vm_n(first ? ninst : 0);
@@ -839,6 +864,9 @@ hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqPara
     p.stage_bpc = G.bpc;
     p.stage_cps = G.cps;
     p.stage_ninst = G.ninst;
+    p.cps_magic = (uint32_t)((((uint64_t)1 << 32) + G.cps - 1) / G.cps);
+    p.nb_magic = (uint32_t)((((uint64_t)1 << 32) + p.K / QK8_1 - 1) / (p.K / QK8_1));
+    if (p.row_bytes >= (int64_t(1) << 24)) return hipErrorInvalidValue;
     p.act_lds_bytes = (int64_t)act;
     const int spw = 64 / G.seg;
     // staging offsets are 32-bit from the first row of an item
@@ -864,6 +892,8 @@ hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqPara
         const int64_t stride = p.xsrc == DT_Q8_1 ? p.q8_row : p.ldx * (p.xsrc == DT_F32 ? 4 : 2);
         p.act_dma = rowb % 16 == 0 && stride % 16 == 0 && (int64_t)nc * rowb <= (int64_t)waves * G.ninst * 1024 &&
                     p.x_bytes > 0 && p.x_bytes < 0x7fffff00LL;
+        p.x_stride = stride;
+        p.ppc_magic = p.act_dma ? (uint32_t)((((uint64_t)1 << 32) + rowb / 16 - 1) / (rowb / 16)) : 0u;
     }
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (int64_t)lds_cap / (int64_t)lds));
     const int64_t need = (groups + waves - 1) / waves;
