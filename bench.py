@@ -46,10 +46,12 @@ ROTATE_BYTES = 1 << 30
 # by kernel, with the hash of the kernel sources they were measured on: reported
 # as null once those sources change.
 PROFILE_TRAFFIC = {
-    "mmvq_kernel<Q4_K,NC=1>": (9785549, "aff3358b48c02ee6"),
-    "mmvq_kernel<Q6_K,NC=1>": (419493222, "aff3358b48c02ee6"),
+    "mmvq_kernel<Q4_K,NC=1>": (9733427, "89b87ef4bab86844"),
+    "mmvq_kernel<Q6_K,NC=1>": (419547443, "89b87ef4bab86844"),
+    "mmq_kernel": (505481728, "a0071d9faa291d5c"),
 }
-KERNEL_SOURCES = {"mmvq": ("mmvq.hip", "common.hpp", "kernels.hpp")}
+KERNEL_SOURCES = {"mmvq": ("mmvq.hip", "common.hpp", "kernels.hpp"),
+                  "mmq": ("mmq.hip", "common.hpp", "kernels.hpp")}
 
 
 def source_hash(kind):
