@@ -264,7 +264,7 @@ __device__ __forceinline__ void tile_of(int64_t b, int64_t m_tiles, int64_t n_ti
     bn = grp * G + in % gw;
 }
 
-// grid: 1-D, m_tiles * n_tiles workgroups of 256 threads.
+// grid: 1-D, m_tiles * n_tiles workgroups of 256 threads (routed: m_tiles rounded up to 8).
 template <int T, bool MOE, int EPI, int YDT>
 __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
     __shared__ MmqSmem<T> sm;
@@ -272,8 +272,13 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
     const int wn = wave & 1, wm = wave >> 1;
     int64_t bm, bn;
     if (MOE) {
-        bm = (int64_t)blockIdx.x % p.m_tiles;
-        bn = (int64_t)blockIdx.x / p.m_tiles;
+        // Workgroup b runs on XCD b mod 8.  That XCD takes the route tiles
+        // t = b mod 8 (mod 8), each with all its weight tiles back to back, so a
+        // route tile's activations are read into one L2 once, and the tiles of
+        // one expert (neighbours in the list) spread evenly over the XCDs.
+        const int64_t b = blockIdx.x, x = b & 7, i = b >> 3;
+        bm = 8 * (i / p.n_tiles) + x;
+        bn = i % p.n_tiles;
     } else {
         tile_of(blockIdx.x, p.m_tiles, p.n_tiles, bm, bn);
     }
@@ -536,7 +541,10 @@ __global__ __launch_bounds__(256) void mmq_dots_kernel(const uint8_t *__restrict
 // ---------------------------------------------------------------------------
 template <int T>
 static void launch_t(bool moe, int epi, int ydt, const MmqParams &p, hipStream_t s) {
-    const dim3 g((unsigned)(p.m_tiles * p.n_tiles)), b(256);
+    // routed: route tiles rounded up to a multiple of 8 (the XCD interleave); the
+    // extra workgroups, like those past the device's tile count, exit at once
+    const int64_t mt = moe ? (p.m_tiles + 7) / 8 * 8 : p.m_tiles;
+    const dim3 g((unsigned)(mt * p.n_tiles)), b(256);
 #define GGQ_L(MOE, EPI, YDT) hipLaunchKernelGGL((mmq_kernel<T, MOE, EPI, YDT>), g, b, 0, s, p)
     if (!moe) {
         if (ydt == DT_F32) GGQ_L(false, EPI_NONE_, DT_F32); else GGQ_L(false, EPI_NONE_, DT_BF16);

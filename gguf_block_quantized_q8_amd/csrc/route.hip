@@ -26,6 +26,42 @@ __global__ __launch_bounds__(256) void route_count_kernel(const int32_t *__restr
     }
 }
 
+// Larger problems with E <= 4096: 4096 routes per workgroup, ranks from LDS
+// atomics on a per-workgroup histogram, then one global atomic per expert
+// present in the workgroup (instead of one per route on the few hot counters).
+constexpr int ROUTE_CHUNK = 4096;
+constexpr int64_t ROUTE_LDS_E = 4096;
+
+__global__ __launch_bounds__(1024) void route_count_lds_kernel(const int32_t *__restrict__ ids, int64_t R, int64_t E,
+                                                              uint32_t *__restrict__ counts, int32_t *__restrict__ rank,
+                                                              uint32_t *__restrict__ bad) {
+    __shared__ uint32_t s_cnt[ROUTE_LDS_E];
+    const int tid = threadIdx.x;
+    for (int64_t e = tid; e < E; e += 1024) s_cnt[e] = 0;
+    __syncthreads();
+    const int64_t r0 = (int64_t)blockIdx.x * ROUTE_CHUNK;
+    int32_t ex[ROUTE_CHUNK / 1024], k[ROUTE_CHUNK / 1024];
+#pragma unroll
+    for (int i = 0; i < ROUTE_CHUNK / 1024; i++) {
+        const int64_t r = r0 + i * 1024 + tid;
+        ex[i] = r < R ? ids[r] : -1;
+        k[i] = -1;
+        if (ex[i] >= 0 && ex[i] < E) k[i] = (int32_t)atomicAdd(&s_cnt[ex[i]], 1u);
+        else if (ex[i] >= E) atomicAdd(bad, 1u);
+    }
+    __syncthreads();
+    for (int64_t e = tid; e < E; e += 1024) {
+        const uint32_t c = s_cnt[e];
+        if (c) s_cnt[e] = atomicAdd(&counts[e], c);                // this workgroup's first rank in expert e
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ROUTE_CHUNK / 1024; i++) {
+        const int64_t r = r0 + i * 1024 + tid;
+        if (r < R) rank[r] = k[i] >= 0 ? (int32_t)s_cnt[ex[i]] + k[i] : -1;
+    }
+}
+
 // Single workgroup: exclusive scans of the counts and of the tile counts,
 // then the tile list.
 __global__ __launch_bounds__(1024) void route_scan_kernel(const uint32_t *__restrict__ counts, int64_t E, int J,
@@ -162,7 +198,11 @@ hipError_t launch_route_build(const int32_t *ids, int64_t R, int64_t E, int J, c
     err = launch_fill_u32(rt.bad, 1, 0u, s);
     if (err != hipSuccess) return err;
     const unsigned g = (unsigned)((R + 255) / 256);
-    if (R > 0) hipLaunchKernelGGL(route_count_kernel, dim3(g), dim3(256), 0, s, ids, R, E, rt.counts, rt.rank, rt.bad);
+    if (R > 0 && E <= ROUTE_LDS_E)
+        hipLaunchKernelGGL(route_count_lds_kernel, dim3((unsigned)((R + ROUTE_CHUNK - 1) / ROUTE_CHUNK)), dim3(1024), 0, s,
+                           ids, R, E, rt.counts, rt.rank, rt.bad);
+    else if (R > 0)
+        hipLaunchKernelGGL(route_count_kernel, dim3(g), dim3(256), 0, s, ids, R, E, rt.counts, rt.rank, rt.bad);
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, rt.counts, E, J, rt.offsets, rt.tile_off,
                        rt.ntiles, rt.tiles);
     if (R > 0) hipLaunchKernelGGL(route_scatter_kernel, dim3(g), dim3(256), 0, s, ids, R, rt.offsets, rt.rank, rt.perm);

@@ -288,6 +288,29 @@ def test_moe_edge_routes(dev, path, wt):
 
 
 @pytest.mark.parametrize("path", ["mmvq", "mmq"])
+def test_moe_edge_routes_many(dev, path):
+    """Over 16K routes (the multi-workgroup route build): hot and empty experts,
+    inactive and out-of-range ids, all counted and skipped as in the small case."""
+    E, N, K, Tn, top_k = 9, 96, 512, 5000, 4
+    W = inputs.gen_experts(g.Q4_K, E, N, K, 520)
+    x = inputs.gen_act(Tn, K, 521, "f32")
+    rng = inputs.rng(522)
+    ids = rng.integers(0, 6, (Tn, top_k)).astype(np.int32)             # experts 6..8 get nothing
+    ids[rng.random((Tn, top_k)) < 0.3] = 2                              # one hot expert
+    ids[rng.random((Tn, top_k)) < 0.02] = -1
+    bad = rng.random((Tn, top_k)) < 0.01
+    ids[bad] = 9 + rng.integers(0, 100, int(bad.sum())).astype(np.int32)
+    y, ws = g.mul_mat_id(T(W, dev), g.Q4_K, T(x, dev), T(ids, dev), K, out_dtype=torch.float32, path=path,
+                         return_workspace=True)
+    ref = _moe_ref(g.Q4_K, W, K, x, ids, top_k)
+    r = rel(host(y), ref)
+    log("moe edges, many routes", path, r, "bad", int(bad.sum()))
+    assert r <= TOL["f32"]
+    assert (host(y)[ids < 0] == 0).all() and (host(y)[ids >= E] == 0).all()
+    assert int(ws[:4].view(torch.int32).item()) == int(bad.sum())
+
+
+@pytest.mark.parametrize("path", ["mmvq", "mmq"])
 def test_moe_all_routes_one_expert(dev, path):
     E, N, K, Tn, top_k = 4, 64, 256, 300, 2
     W = inputs.gen_experts(g.Q4_K, E, N, K, 510)
