@@ -242,6 +242,18 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
     else static_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_bf16_bits(v);
 }
 
+// Outputs idx and idx + 1 (both valid): one store when they are aligned together.
+template <int YDT>
+__device__ __forceinline__ void store_out2(void *y, int64_t idx, float v0, float v1) {
+    if ((idx & 1) == 0) {
+        if (YDT == DT_F32) *reinterpret_cast<v2i *>(static_cast<float *>(y) + idx) = v2i{__builtin_bit_cast(int, v0), __builtin_bit_cast(int, v1)};
+        else *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(y) + idx) = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+    } else {
+        store_out<YDT>(y, idx, v0);
+        store_out<YDT>(y, idx + 1, v1);
+    }
+}
+
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // Sum over aligned quads of lanes, result in every lane of the quad.
@@ -695,8 +707,8 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
                 if (c >= ncols) break;
                 if (!MOE) {
                     const int64_t col = xrow[c];
-                    store_out<YDT>(p.y, col * p.ldy + r0, acc[0][c]);
-                    if (v1) store_out<YDT>(p.y, col * p.ldy + r1, acc[1][c]);
+                    if (v1) store_out2<YDT>(p.y, col * p.ldy + r0, acc[0][c], acc[1][c]);   // r1 = r0 + 1
+                    else store_out<YDT>(p.y, col * p.ldy + r0, acc[0][c]);
                 } else {
                     // weighted: per-route fp32 outputs, summed per token afterwards
                     const int64_t r = route_s[c];
