@@ -230,8 +230,14 @@ def bench_prefill(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, path=g.P
 def bench_moe(ctx, Tn, steps, warmup):
     dev = ctx.dev
     E, H, I, top_k = 256, 2048, 512, 8
-    Wgu = torch.from_numpy(inputs.gen_experts(g.Q4_K, E, 2 * I, H, 501)).to(dev)
-    Wd = torch.from_numpy(inputs.gen_experts(g.Q6_K, E, H, I, 502)).to(dev)
+    Wgu0 = torch.from_numpy(inputs.gen_experts(g.Q4_K, E, 2 * I, H, 501)).to(dev)
+    Wd0 = torch.from_numpy(inputs.gen_experts(g.Q6_K, E, H, I, 502)).to(dev)
+    # decode-sized batches stream the experts' weights: rotate copies (0.5 GB each)
+    # so that no step finds them in the 256 MB last-level cache
+    ncopy = 4 if Tn <= 64 else 1
+    Wgus = [Wgu0] + [Wgu0.clone() for _ in range(ncopy - 1)]
+    Wds = [Wd0] + [Wd0.clone() for _ in range(ncopy - 1)]
+    Wgu, Wd = Wgu0, Wd0
     x = bf16(inputs.gen_act(Tn, H, 503, "bf16"), dev)
     ids_np, w_np = inputs.gen_routing(Tn, E, top_k, 504)
     ids = torch.from_numpy(ids_np).to(dev)
@@ -247,11 +253,11 @@ def bench_moe(ctx, Tn, steps, warmup):
     s_d = Wd.stride(0)
 
     def gate_up(i):
-        check(L.ggq_mul_mat_id(g.Q4_K, vp(Wgu), E, 2 * I, H, s_gu, vp(x), g.BF16, Tn, 0, vp(ids), top_k, None,
+        check(L.ggq_mul_mat_id(g.Q4_K, vp(Wgus[i % ncopy]), E, 2 * I, H, s_gu, vp(x), g.BF16, Tn, 0, vp(ids), top_k, None,
                                g.EPI_SWIGLU, vp(h), g.BF16, vp(ws1), ws1b, g.PATH_AUTO, ctx.s), "gate_up")
 
     def down(i):
-        check(L.ggq_mul_mat_id(g.Q6_K, vp(Wd), E, H, I, s_d, vp(h), g.BF16, Tn, 1, vp(ids), top_k, vp(w),
+        check(L.ggq_mul_mat_id(g.Q6_K, vp(Wds[i % ncopy]), E, H, I, s_d, vp(h), g.BF16, Tn, 1, vp(ids), top_k, vp(w),
                                g.EPI_NONE, vp(y), g.BF16, vp(ws2), ws2b, g.PATH_AUTO, ctx.s), "down")
 
     def step(i):
@@ -267,6 +273,7 @@ def bench_moe(ctx, Tn, steps, warmup):
         distinct = len(np.unique(ids_np))
         moved = distinct * (Wgu.stride(0) + Wd.stride(0)) + Tn * H * 2 * 2 + R * I * 2 * 2
         res.update({"value": moved * steps / dt / 1e9, "unit": "GB/s", "distinct_experts": int(distinct),
+                    "rotating_weight_copies": ncopy,
                     "roofline": roofline_bytes(distinct * Wgu.stride(0), tg, "mmvq_id gate_up (call)"),
                     "down_call_us": round(td * 1e6, 2)})
     else:

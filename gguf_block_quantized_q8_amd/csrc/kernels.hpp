@@ -80,6 +80,7 @@ struct MmvqParams {
     uint32_t cps_magic;     // ceil(2^32 / stage_cps): piece index -> row slot (set by the launcher)
     uint32_t ppc_magic;     // ceil(2^32 / (raw activation row bytes / 16)) when act_dma (set by the launcher)
     int64_t x_stride;       // bytes between activation rows (x or q8) (set by the launcher)
+    uint32_t raw_region;    // LDS bytes after the first item buffers: second buffers, or the raw rows if larger (set by the launcher)
 };
 constexpr size_t MMVQ_LDS_MAX = 64 * 1024;     // activation bytes staged per block
 int mmvq_max_cols(int t, int64_t K);          // largest column group (8, 4, 2, 1) whose activations fit in LDS

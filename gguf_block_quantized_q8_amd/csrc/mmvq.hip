@@ -95,6 +95,14 @@ struct Unit;
 
 // ---- Q4_K: unit = (super-block sb, pair p): the 32 quant bytes of groups 2p
 // (low nibbles) and 2p+1 (high nibbles), 64 weights.
+// Wide column groups: finish a column's dots before the next column's
+// activation loads (else all NC x 16 registers of quants are live at once).
+// The empty asm takes the column's sums and orders memory accesses.
+template <int NC>
+__device__ __forceinline__ void col_fence(float &a0, float &a1) {
+    if (NC >= 4) asm volatile("" : "+v"(a0), "+v"(a1) :: "memory");
+}
+
 template <int NC>
 struct Unit<T_Q4_K, NC> {
     __device__ static void run(int u, lds_bp row0, lds_bp row1, const ActL &A, int ncols, float (&acc)[2][NC]) {
@@ -140,6 +148,7 @@ struct Unit<T_Q4_K, NC> {
                 acc[i][col] += d[i] * (sc0[i] * d80 * (float)D0 + sc1[i] * d81 * (float)D1) -
                                dm[i] * (mn0[i] * s80 + mn1[i] * s81);
             }
+            col_fence<NC>(acc[0][col], acc[1][col]);
         }
     }
 };
@@ -194,6 +203,7 @@ struct Unit<T_Q6_K, NC> {
                     acc[i][col] += dsc[i][g] * d8 * (float)D;
                 }
             }
+            col_fence<NC>(acc[0][col], acc[1][col]);
         }
     }
 };
@@ -232,6 +242,7 @@ struct Unit<T_Q8_0, NC> {
                 }
                 acc[i][col] += d[i] * d8 * (float)D;
             }
+            col_fence<NC>(acc[0][col], acc[1][col]);
         }
     }
 };
@@ -507,11 +518,10 @@ __device__ __forceinline__ uint32_t slot_off(uint32_t s, uint32_t rb, uint32_t n
     return EPI == EPI_SWIGLU ? __umul24(s >> 1, rb) + ((s & 1) ? np_rb : 0u) : __umul24(s, rb);
 }
 
-// Largest workgroup per column count: up to 16 waves (one workgroup per CU
-// quantizes the activations once for all of them) while the registers of the
-// wider column groups still allow it.
+// Largest workgroup: 16 waves (one workgroup per CU quantizes the activations
+// once for all of them); every column count fits 128 registers.
 template <int NC>
-struct MaxWaves { static constexpr int value = NC <= 2 ? 16 : NC == 4 ? 8 : 4; };
+struct MaxWaves { static constexpr int value = 16; };
 
 // grid: (blocks_x, column groups), blockDim = 64 x waves.  Each block stages
 // its columns' q8_1 activations in LDS, then each wave walks its work items
@@ -536,7 +546,7 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
     uint8_t *wbuf = lds + p.act_lds_bytes + wave * bufsz;
     const int bstride = wpb * bufsz;
     uint8_t *raw = lds + p.act_lds_bytes + bstride;
-    uint8_t *sink = raw + bstride;
+    uint8_t *sink = raw + p.raw_region;
 
     // ---- columns of this group ----
     const uint8_t *W = p.W;
@@ -895,24 +905,30 @@ hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqPara
     const int64_t groups = (p.npairs + spw - 1) / spw;          // row groups (one wave's worth per K-chunk)
     const int64_t fill = (groups + 255) / 256;                   // waves per block to give every CU one block
     if (fill < waves) waves = (int)std::max<int64_t>(fill, std::min<int64_t>(waves, 4));
-    const size_t lds = act + (size_t)waves * per_wave + 1024;   // + the prologue's 1 KB sink
-    // raw activation rows through LDS when they fit the waves' second buffers and
-    // every row starts 16-byte aligned at a 32-bit offset
+    // Raw activation rows through LDS when every row starts 16-byte aligned at a
+    // 32-bit offset and they fit the region after the first item buffers: the
+    // waves' second buffers, extended when the rows need more and LDS allows.
+    const size_t bufs = (size_t)waves * G.ninst * 1024;          // one buffer per wave
+    size_t region = bufs;
     {
         const int64_t nb = p.K / QK8_1;
         const int64_t rowb = p.xsrc == DT_Q8_1 ? nb * Q8_1_BYTES : p.K * (p.xsrc == DT_F32 ? 4 : 2);
         const int64_t stride = p.xsrc == DT_Q8_1 ? p.q8_row : p.ldx * (p.xsrc == DT_F32 ? 4 : 2);
-        p.act_dma = rowb % 16 == 0 && stride % 16 == 0 && (int64_t)nc * rowb <= (int64_t)waves * G.ninst * 1024 &&
+        const size_t raw_need = ((size_t)nc * (size_t)rowb + 1023) & ~size_t(1023);
+        p.act_dma = rowb % 16 == 0 && stride % 16 == 0 && act + bufs + std::max(bufs, raw_need) + 1024 <= lds_cap &&
                     p.x_bytes > 0 && p.x_bytes < 0x7fffff00LL;
+        if (p.act_dma) region = std::max(bufs, raw_need);
         p.x_stride = stride;
         p.ppc_magic = p.act_dma ? (uint32_t)((((uint64_t)1 << 32) + rowb / 16 - 1) / (rowb / 16)) : 0u;
     }
+    p.raw_region = (uint32_t)region;
+    const size_t lds = act + bufs + region + 1024;              // + the prologue's 1 KB sink
     const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(8, (int64_t)lds_cap / (int64_t)lds));
     const int64_t need = (groups + waves - 1) / waves;
     // routed: about min(E, routes) groups are active, whatever the host-side bound;
-    // give them at least two workgroups per CU between them
+    // spread one wave of workgroups over them (more only adds prologues: measured)
     const int64_t active = moe ? std::max<int64_t>(1, std::min<int64_t>(ngroups_bound, p.groups_expected)) : ngroups_bound;
-    const int64_t cap = std::max<int64_t>(1, (moe ? 512 : 256) * per_cu / active);
+    const int64_t cap = std::max<int64_t>(1, 256 * per_cu / active);
     const dim3 g((unsigned)std::min<int64_t>(need, cap), (unsigned)ngroups_bound);
     if (t == T_Q4_K) launch_t<T_Q4_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
     else if (t == T_Q6_K) launch_t<T_Q6_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
