@@ -195,6 +195,24 @@ def bench_decode(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, rotate=Tr
             "roofline": roofline_bytes(step_bytes, gpu / steps, f"mmvq_kernel<{TNAME[wt]},NC={min(8, M)}>")}
 
 
+def bench_get_rows(ctx, wt, rows, K, n, seed_w, seed_ids, ydt, steps, warmup):
+    """n random rows of a quantized table (the lm_head-shaped Q6_K table read as embeddings)."""
+    dev = ctx.dev
+    W = torch.from_numpy(inputs.gen_weights(wt, rows, K, seed_w)).to(dev)
+    ids = torch.from_numpy(inputs.rng(seed_ids).integers(0, rows, n).astype(np.int32)).to(dev)
+    y = torch.empty((n, K), dtype=ydt, device=dev)
+    ydt_c = g.F32 if ydt == torch.float32 else g.BF16
+
+    def step(i):
+        check(ctx.L.ggq_get_rows(wt, vp(W), rows, K, vp(ids), n, vp(y), ydt_c, K, ctx.s), "get_rows")
+
+    dt, gpu = time_steps(step, steps, warmup, graph=True)
+    step_bytes = n * (g.row_bytes(wt, K) + 4 + K * (4 if ydt == torch.float32 else 2))
+    return {"value": step_bytes * steps / dt / 1e9, "unit": "GB/s", "ms_per_step": dt / steps * 1e3,
+            "step_bytes": step_bytes,
+            "roofline": roofline_bytes(step_bytes, gpu / steps, f"dequant_kernel<{TNAME[wt]}> (get_rows)")}
+
+
 # ------------------------------------------------------------------ dense prefill (MMQ)
 
 def bench_prefill(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, path=g.PATH_AUTO):
@@ -314,7 +332,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--workloads", default="all",
-                    help="comma list of: decode, prefill, sweep, lmhead1, lmhead2048, moe16, moe8192 (default all)")
+                    help="comma list of: decode, prefill, sweep, lmhead1, lmhead2048, getrows, moe16, moe8192 (default all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -344,7 +362,7 @@ def main():
     head = bench_decode(ctx, g.Q4_K, 4096, 4096, 1, 201, 202, torch.bfloat16, K, W)
     also = []
     sel = set(args.workloads.split(",")) if args.workloads != "all" else {
-        "decode", "prefill", "sweep", "lmhead1", "lmhead2048", "moe16", "moe8192"}
+        "decode", "prefill", "sweep", "lmhead1", "lmhead2048", "getrows", "moe16", "moe8192"}
     if args.only_headline:
         sel = set()
     if "decode" in sel:
@@ -366,6 +384,10 @@ def main():
         log("q6_K 248320x2048 lm_head M=1")
         r = bench_decode(ctx, g.Q6_K, 248320, 2048, 1, 401, 402, torch.float32, max(20, K // 4), W, rotate=False)
         also.append({"workload": "q6_K_248320x2048_lm_head", "M": 1, **r})
+    if "getrows" in sel:
+        log("q6_K 248320x2048 get_rows n=8192")
+        r = bench_get_rows(ctx, g.Q6_K, 248320, 2048, 8192, 401, 404, torch.bfloat16, max(20, K // 4), W)
+        also.append({"workload": "q6_K_248320x2048_get_rows", "n": 8192, **r})
     if "lmhead2048" in sel:
         log("q6_K 248320x2048 lm_head M=2048")
         r = bench_prefill(ctx, g.Q6_K, 248320, 2048, 2048, 401, 402, torch.float32, max(3, K // 40), 1)

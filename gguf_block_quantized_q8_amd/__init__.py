@@ -25,7 +25,7 @@ _PATHS = {"auto": PATH_AUTO, "mmvq": PATH_MMVQ, "mmq": PATH_MMQ}
 _lib = None
 
 EXPORTS = ["ggq_row_bytes", "ggq_q8_1_bytes", "ggq_quantize_q8_1", "ggq_mul_mat_ws", "ggq_mul_mat",
-           "ggq_mul_mat_id_ws", "ggq_mul_mat_id", "ggq_dequantize", "ggq_last_error",
+           "ggq_mul_mat_id_ws", "ggq_mul_mat_id", "ggq_dequantize", "ggq_get_rows", "ggq_last_error",
            "ggq_test_block_dots_ws", "ggq_test_block_dots"]
 
 
@@ -56,6 +56,8 @@ def lib():
                                  vp, i32, vp, sz, i32, vp]
     L.ggq_dequantize.restype = i32
     L.ggq_dequantize.argtypes = [i32, vp, i64, i64, vp, i32, vp]
+    L.ggq_get_rows.restype = i32
+    L.ggq_get_rows.argtypes = [i32, vp, i64, i64, vp, i64, vp, i32, i64, vp]
     L.ggq_last_error.restype = ctypes.c_char_p
     L.ggq_last_error.argtypes = []
     L.ggq_test_block_dots_ws.restype = sz
@@ -202,6 +204,19 @@ def dequantize(W, wt, K, out_dtype=torch.float32):
     y = torch.empty((rows, K), dtype=out_dtype, device=W.device)
     rc = lib().ggq_dequantize(wt, _ptr(W), rows, K, _ptr(y), _ydt(out_dtype), _stream(W.device))
     _raise(rc, "dequantize")
+    return y
+
+
+def get_rows(W, wt, K, ids, out_dtype=torch.float32):
+    """Rows ids of the quantized table W, dequantized: [len(ids), K] (ids outside the table give zeros)."""
+    _check_gpu(W, ids)
+    if ids.dtype != torch.int32:
+        raise ValueError("get_rows: ids must be int32")
+    rows = W.shape[0] if W.dim() == 2 else W.numel() // row_bytes(wt, K)
+    n = ids.numel()
+    y = torch.empty((n, K), dtype=out_dtype, device=W.device)
+    rc = lib().ggq_get_rows(wt, _ptr(W), rows, K, _ptr(ids), n, _ptr(y), _ydt(out_dtype), K, _stream(W.device))
+    _raise(rc, "get_rows")
     return y
 
 

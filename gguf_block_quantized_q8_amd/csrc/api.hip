@@ -134,8 +134,27 @@ int ggq_dequantize(int wt, const void *W, int64_t rows, int64_t K, void *y, int 
     if (rows == 0) return GGQ_OK;
     if (!W || !y) return fail(GGQ_ERR_INVALID, "dequantize: null pointer");
     if (!aligned16(W) || !aligned16(y)) return fail(GGQ_ERR_INVALID, "dequantize: pointers must be 16-byte aligned");
-    return hip_status(launch_dequant(wt, static_cast<const uint8_t *>(W), rows, K, y, ydt, static_cast<hipStream_t>(stream)),
+    return hip_status(launch_dequant(wt, static_cast<const uint8_t *>(W), rows, K, nullptr, rows, y, ydt, K,
+                                     static_cast<hipStream_t>(stream)),
                       "dequantize");
+}
+
+int ggq_get_rows(int wt, const void *W, int64_t rows, int64_t K, const int32_t *ids, int64_t n, void *y, int ydt,
+                 int64_t ldy, void *stream) {
+    g_err[0] = 0;
+    int rc = check_weights(wt, rows, K);
+    if (rc) return rc;
+    if (ydt != GGQ_F32 && ydt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "get_rows: output dtype %d must be F32 or BF16", ydt);
+    if (n < 0) return fail(GGQ_ERR_INVALID, "get_rows: n=%lld < 0", (long long)n);
+    if (ldy < K) return fail(GGQ_ERR_INVALID, "get_rows: ldy=%lld < K=%lld", (long long)ldy, (long long)K);
+    if (ldy % (ydt == GGQ_F32 ? 4 : 8))
+        return fail(GGQ_ERR_INVALID, "get_rows: ldy=%lld must keep output rows 16-byte aligned", (long long)ldy);
+    if (n == 0) return GGQ_OK;
+    if (!W || !ids || !y) return fail(GGQ_ERR_INVALID, "get_rows: null pointer");
+    if (!aligned16(W) || !aligned16(y)) return fail(GGQ_ERR_INVALID, "get_rows: W and y must be 16-byte aligned");
+    return hip_status(launch_dequant(wt, static_cast<const uint8_t *>(W), rows, K, ids, n, y, ydt, ldy,
+                                     static_cast<hipStream_t>(stream)),
+                      "get_rows");
 }
 
 size_t ggq_mul_mat_ws(int wt, int64_t N, int64_t K, int xdt, int64_t M, int path) {

@@ -109,23 +109,29 @@ __global__ __launch_bounds__(256) void q8_1_to_planar_kernel(const uint8_t *__re
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize: one thread per 16 consecutive weights of a row.
+// Dequantize: one thread per 16 consecutive weights of an output row.
 //   Q8_0: d*q; Q4_K: (d*sc)*nib - dmin*m; Q6_K: (d*sc)*(q-32).
 // Every product is exact in fp32; the Q4_K subtraction rounds once.
+// Output row r (of n) holds table row ids[r] (r itself without ids); a row id
+// outside [0, rows) gives a row of zeros.  y rows are ldy elements apart.
 // ---------------------------------------------------------------------------
 template <int T, int YDT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ W, int64_t rows, int64_t K,
-                                                      void *__restrict__ y) {
+                                                      const int32_t *__restrict__ ids, int64_t n,
+                                                      void *__restrict__ y, int64_t ldy) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t per_row = K / 16;
-    if (gid >= rows * per_row) return;
+    if (gid >= n * per_row) return;
     const int64_t r = gid / per_row;
     const int64_t i0 = (gid - r * per_row) * 16;         // first weight index in the row
+    const int64_t src = ids ? (int64_t)ids[r] : r;
     constexpr int QK = Geom<T>::QK, BB = Geom<T>::BYTES;
-    const uint8_t *blk = W + r * (K / QK) * BB + (i0 / QK) * BB;
+    const uint8_t *blk = W + (src >= 0 && src < rows ? src : 0) * (K / QK) * BB + (i0 / QK) * BB;
     const int ib = (int)(i0 % QK);                       // index inside the block
     float w[16];
-    if (T == T_Q8_0) {
+    if (src < 0 || src >= rows) {
+        for (int i = 0; i < 16; i++) w[i] = 0.0f;
+    } else if (T == T_Q8_0) {
         const float d = fp16_bits_to_f32(ld_u16(blk));
         v4i q = ld16_a2(blk + 2 + ib);
         for (int i = 0; i < 16; i++) w[i] = d * (float)(int8_t)((q[i / 4] >> (8 * (i % 4))) & 0xff);
@@ -159,7 +165,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
             w[i] = a * (float)((lo | (hb << 4)) - 32);
         }
     }
-    const int64_t o = r * K + i0;
+    const int64_t o = r * ldy + i0;
     if (YDT == DT_F32) {
         v4f *yo = reinterpret_cast<v4f *>(static_cast<float *>(y) + o);
         for (int i = 0; i < 4; i++) yo[i] = v4f{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
@@ -272,14 +278,15 @@ hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float
     return hipGetLastError();
 }
 
-hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, void *y, int ydt, hipStream_t s) {
-    const int64_t threads = rows * (K / 16);
+hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, const int32_t *ids, int64_t n, void *y,
+                          int ydt, int64_t ldy, hipStream_t s) {
+    const int64_t threads = n * (K / 16);
     if (threads == 0) return hipSuccess;
     dim3 g(grid_for(threads)), b(256);
-#define GGQ_DQ(TT)                                                                                         \
-    if (t == TT) {                                                                                         \
-        if (ydt == DT_F32) hipLaunchKernelGGL((dequant_kernel<TT, DT_F32>), g, b, 0, s, W, rows, K, y);     \
-        else hipLaunchKernelGGL((dequant_kernel<TT, DT_BF16>), g, b, 0, s, W, rows, K, y);                 \
+#define GGQ_DQ(TT)                                                                                                    \
+    if (t == TT) {                                                                                                    \
+        if (ydt == DT_F32) hipLaunchKernelGGL((dequant_kernel<TT, DT_F32>), g, b, 0, s, W, rows, K, ids, n, y, ldy);   \
+        else hipLaunchKernelGGL((dequant_kernel<TT, DT_BF16>), g, b, 0, s, W, rows, K, ids, n, y, ldy);               \
     }
     GGQ_DQ(T_Q8_0) GGQ_DQ(T_Q4_K) GGQ_DQ(T_Q6_K)
 #undef GGQ_DQ

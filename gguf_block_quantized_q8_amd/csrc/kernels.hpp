@@ -11,7 +11,9 @@ hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t
                            float *xd, float *xs, hipStream_t s);
 hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float16 *xq, float *xd, float *xs,
                                  hipStream_t s);
-hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, void *y, int ydt, hipStream_t s);
+// y row r (of n) = table row ids[r] (r without ids), zeros for ids outside [0, rows); rows ldy apart
+hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, const int32_t *ids, int64_t n, void *y,
+                          int ydt, int64_t ldy, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t launch_route_sum(const float *o, const int32_t *ids, const float *w, int64_t T, int top_k, int64_t E,
                             int64_t Np, void *y, int ydt, hipStream_t s);

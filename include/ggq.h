@@ -126,6 +126,21 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K,
 int ggq_dequantize(int wt, const void *W, int64_t rows, int64_t K,
                    void *y, int ydt, void *stream);
 
+/* Gather rows of a quantized table (embeddings, or a tied lm_head read as
+ * rows), dequantized: y[i][k] = exact value of table row ids[i], weight k, in
+ * fp32, or its round-to-nearest-even bf16 -- the same values as
+ * ggq_dequantize (PR #690 lists get_rows among the ops its backend serves
+ * next to the matmuls).
+ *   W   : table of `rows` rows of ggq_row_bytes(wt, K) bytes, 16-byte aligned.
+ *   ids : [n] int32 row ids, device memory.  An id outside [0, rows) gives a
+ *         row of zeros (no fault, no error: ids are not read on the host).
+ *   y   : [n][ldy] of ydt (GGQ_F32 / GGQ_BF16); writes K values per row;
+ *         ldy >= K and ldy keeps rows 16-byte aligned (multiple of 4 for
+ *         fp32, 8 for bf16).
+ * n = 0 is a no-op.  Bit-exact.  Returns GGQ_OK or an error code. */
+int ggq_get_rows(int wt, const void *W, int64_t rows, int64_t K, const int32_t *ids, int64_t n,
+                 void *y, int ydt, int64_t ldy, void *stream);
+
 /* Message describing the calling thread's last failing call ("" if none). */
 const char *ggq_last_error(void);
 

@@ -110,6 +110,21 @@ def test_mul_mat_id_validation(L):
     assert 0 < ws_small < ws_big
 
 
+def test_get_rows_validation(L):
+    def call(wt=g.Q4_K, rows=8, K=256, ids=FAKE, n=3, y=FAKE, ydt=g.F32, ldy=256):
+        return L.ggq_get_rows(wt, FAKE, rows, K, ids, n, y, ydt, ldy, None)
+    assert call(wt=3) == g.ERR_UNSUPPORTED
+    assert call(K=300) == g.ERR_INVALID and "K=300" in err(L)
+    assert call(ydt=g.Q8_1) == g.ERR_UNSUPPORTED
+    assert call(n=-1) == g.ERR_INVALID
+    assert call(ldy=128) == g.ERR_INVALID                      # ldy < K
+    assert call(ldy=258) == g.ERR_INVALID                      # rows not 16-byte aligned (fp32)
+    assert call(ydt=g.BF16, ldy=260) == g.ERR_INVALID          # rows not 16-byte aligned (bf16)
+    assert call(ids=None) == g.ERR_INVALID
+    assert call(y=ctypes.c_void_p(0x10008)) == g.ERR_INVALID   # y not 16-byte aligned
+    assert call(n=0, ids=None, y=None) == g.OK
+
+
 def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(g, "_lib", None)
     monkeypatch.setattr(g, "LIB_PATH", "/nonexistent/libggq.so")

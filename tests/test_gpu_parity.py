@@ -104,6 +104,34 @@ def test_dequantize_q6_K_large_scales(dev):
     assert np.array_equal(host(y).view(np.uint32), oracle.dequantize(g.Q6_K, W, 16, 512).view(np.uint32))
 
 
+@pytest.mark.parametrize("wt", [g.Q8_0, g.Q4_K, g.Q6_K])
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
+def test_get_rows_bit_exact(dev, wt, ydt):
+    """Gathered rows equal the oracle's dequantized table rows bit for bit; ids
+    outside the table give zeros; repeated ids repeat the row."""
+    log("get_rows", wt, ydt)
+    rows, K = 300, 512
+    W = inputs.gen_weights(wt, rows, K, 40 + wt)
+    ids = inputs.rng(41).integers(-3, rows + 3, 97).astype(np.int32)
+    ids[:4] = [0, rows - 1, 5, 5]
+    y = g.get_rows(T(W, dev), wt, K, T(ids, dev), ydt)
+    kind = oracle.BF16 if ydt == torch.bfloat16 else oracle.F32
+    table = oracle.dequantize(wt, W, rows, K, kind)
+    ok = (ids >= 0) & (ids < rows)
+    ref = np.zeros((ids.size, K), table.dtype)
+    ref[ok] = table[ids[ok]]
+    got = host(y) if ydt == torch.float32 else y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got.view(np.uint32) if ydt == torch.float32 else got,
+                          ref.view(np.uint32) if ydt == torch.float32 else ref)
+
+
+def test_get_rows_empty_and_errors(dev):
+    W = T(inputs.gen_q4_K(8, 256, 42), dev)
+    assert g.get_rows(W, g.Q4_K, 256, torch.empty(0, dtype=torch.int32, device=dev)).shape == (0, 256)
+    with pytest.raises(ValueError):
+        g.get_rows(W, g.Q4_K, 200, torch.zeros(3, dtype=torch.int32, device=dev))   # K not a multiple of 256
+
+
 # ------------------------------------------------------------------ per-group int dots
 
 @pytest.mark.parametrize("wt,path", [(g.Q8_0, "mmvq"), (g.Q4_K, "mmvq"), (g.Q6_K, "mmvq"), (g.Q4_K, "mmq"), (g.Q6_K, "mmq")])
