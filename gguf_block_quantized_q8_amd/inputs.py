@@ -13,6 +13,8 @@ Distributions (one numpy PCG64 stream per seed):
     every 6-bit scale/min and every nibble uniform.
   * Q6_K super-blocks: ql and qh uniform random bytes, the 16 int8 scales
     uniform in [-64, 63], fp16 d ~ U(1e-4, 5e-3).
+  * Q4_0 blocks: fp16 d ~ U(1e-3, 2e-2), 16 uniform random quant bytes.
+  * Q5_K super-blocks: as Q4_K, plus 32 uniform random bytes of fifth bits.
   * Activations: fp32 N(0, 1); bf16 activations are those fp32 values
     rounded to bf16 by torch (returned as uint16 bit patterns).
   * Routing: router logits fp32 N(0, 1) [T, E] -> softmax in fp64 -> fp32
@@ -23,12 +25,14 @@ Block byte layouts follow the public GGUF format:
   Q8_0 (34 B / 32): fp16 d | 32 x int8
   Q4_K (144 B / 256): fp16 d | fp16 dmin | 12 B scales | 128 B quants
   Q6_K (210 B / 256): 128 B ql | 64 B qh | 16 x int8 scales | fp16 d
+  Q4_0 (18 B / 32): fp16 d | 16 B quants
+  Q5_K (176 B / 256): fp16 d | fp16 dmin | 12 B scales | 32 B fifth bits | 128 B quants
 """
 import numpy as np
 
-Q8_0, Q4_K, Q6_K = 8, 12, 14
-BLOCK = {Q8_0: (32, 34), Q4_K: (256, 144), Q6_K: (256, 210)}
-NAMES = {Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+Q4_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 8, 12, 13, 14
+BLOCK = {Q4_0: (32, 18), Q8_0: (32, 34), Q4_K: (256, 144), Q5_K: (256, 176), Q6_K: (256, 210)}
+NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q5_K: "Q5_K", Q6_K: "Q6_K"}
 
 
 def rng(seed):
@@ -74,8 +78,27 @@ def gen_q6_K(N, K, seed, dlo=1e-4, dhi=5e-3):
     return blk.reshape(N, row_bytes(Q6_K, K))
 
 
+def gen_q4_0(N, K, seed, dlo=1e-3, dhi=2e-2):
+    r = rng(seed)
+    nb = N * K // 32
+    blk = np.zeros((nb, 18), dtype=np.uint8)
+    blk[:, 0:2] = _fp16_bits(r, dlo, dhi, nb).view(np.uint8).reshape(nb, 2)
+    blk[:, 2:18] = r.integers(0, 256, size=(nb, 16), dtype=np.uint8)
+    return blk.reshape(N, row_bytes(Q4_0, K))
+
+
+def gen_q5_K(N, K, seed, dlo=1e-3, dhi=2e-2):
+    r = rng(seed)
+    nb = N * K // 256
+    blk = np.zeros((nb, 176), dtype=np.uint8)
+    blk[:, 0:2] = _fp16_bits(r, dlo, dhi, nb).view(np.uint8).reshape(nb, 2)
+    blk[:, 2:4] = _fp16_bits(r, dlo, dhi, nb).view(np.uint8).reshape(nb, 2)
+    blk[:, 4:176] = r.integers(0, 256, size=(nb, 172), dtype=np.uint8)
+    return blk.reshape(N, row_bytes(Q5_K, K))
+
+
 def gen_weights(t, N, K, seed):
-    return {Q8_0: gen_q8_0, Q4_K: gen_q4_K, Q6_K: gen_q6_K}[t](N, K, seed)
+    return {Q4_0: gen_q4_0, Q8_0: gen_q8_0, Q4_K: gen_q4_K, Q5_K: gen_q5_K, Q6_K: gen_q6_K}[t](N, K, seed)
 
 
 def gen_experts(t, E, N, K, seed):

@@ -16,7 +16,7 @@ import numpy as np
 
 from . import build as _build
 
-Q8_0, Q4_K, Q6_K = 8, 12, 14
+Q4_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 8, 12, 13, 14
 F32, BF16, Q8_1 = 0, 1, 2
 EPI_NONE, EPI_SWIGLU = 0, 1
 Q8_1_BYTES = 40

@@ -66,8 +66,10 @@ static uint16_t rd16(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8)); 
 
 int64_t ggqo_block_len(int type) {
     switch (type) {
+    case GGQO_Q4_0: return 32;
     case GGQO_Q8_0: return 32;
     case GGQO_Q4_K: return 256;
+    case GGQO_Q5_K: return 256;
     case GGQO_Q6_K: return 256;
     default: return 0;
     }
@@ -75,8 +77,10 @@ int64_t ggqo_block_len(int type) {
 
 int64_t ggqo_block_bytes(int type) {
     switch (type) {
+    case GGQO_Q4_0: return 2 + 16;                 /* fp16 d, 32 nibbles */
     case GGQO_Q8_0: return 2 + 32;                 /* fp16 d, 32 x int8 */
     case GGQO_Q4_K: return 2 + 2 + 12 + 128;       /* d, dmin, packed scales, nibbles */
+    case GGQO_Q5_K: return 2 + 2 + 12 + 32 + 128;  /* d, dmin, packed scales, fifth bits, nibbles */
     case GGQO_Q6_K: return 128 + 64 + 16 + 2;      /* ql, qh, int8 scales, d */
     default: return 0;
     }
@@ -84,8 +88,10 @@ int64_t ggqo_block_bytes(int type) {
 
 int64_t ggqo_group_len(int type) {
     switch (type) {
+    case GGQO_Q4_0: return 32;
     case GGQO_Q8_0: return 32;
     case GGQO_Q4_K: return 32;
+    case GGQO_Q5_K: return 32;
     case GGQO_Q6_K: return 16;
     default: return 0;
     }
@@ -164,6 +170,36 @@ static void unpack_q8_0(const uint8_t *blk, int32_t *q, int32_t *sc, int32_t *mn
     mn[0] = 0;
 }
 
+/* Q4_0: one group of 32: byte b of the 16 quant bytes gives weight b (low
+ * nibble) and weight 16 + b (high nibble); the value is d * (nibble - 8). */
+static void unpack_q4_0(const uint8_t *blk, int32_t *q, int32_t *sc, int32_t *mn, float *d) {
+    d[0] = ggqo_fp16_to_fp32(rd16(blk));
+    d[1] = 0.0f;
+    for (int i = 0; i < 16; i++) {
+        q[i] = blk[2 + i] & 0x0f;
+        q[16 + i] = blk[2 + i] >> 4;
+    }
+    sc[0] = 1;
+    mn[0] = 0;
+}
+
+/* The 6-bit scales and mins of the 8 groups of a Q4_K / Q5_K block, from
+ * the 12 packed bytes s: groups 0..3 use the low 6 bits of bytes 0..3
+ * (scales) and 4..7 (mins); groups 4..7 take their low 4 bits from the
+ * nibbles of bytes 8..11 and their top 2 bits from the top bits of bytes
+ * 0..3 (scales) and 4..7 (mins). */
+static void unpack_scales_k(const uint8_t *s, int32_t *sc, int32_t *mn) {
+    for (int j = 0; j < 8; j++) {
+        if (j < 4) {
+            sc[j] = s[j] & 63;
+            mn[j] = s[j + 4] & 63;
+        } else {
+            sc[j] = (s[j + 4] & 0x0f) | ((s[j - 4] >> 6) << 4);
+            mn[j] = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+        }
+    }
+}
+
 /* Q4_K: 8 groups of 32.  Groups 0..3 take their 6-bit scale and min from the
  * low 6 bits of bytes 0..3 and 4..7 of the packed area; groups 4..7 take the
  * low 4 bits from the nibbles of bytes 8..11 and the top 2 bits from the top
@@ -175,19 +211,29 @@ static void unpack_q4_K(const uint8_t *blk, int32_t *q, int32_t *sc, int32_t *mn
     const uint8_t *qs = blk + 16;
     d[0] = ggqo_fp16_to_fp32(rd16(blk));
     d[1] = ggqo_fp16_to_fp32(rd16(blk + 2));
-    for (int j = 0; j < 8; j++) {
-        if (j < 4) {
-            sc[j] = s[j] & 63;
-            mn[j] = s[j + 4] & 63;
-        } else {
-            sc[j] = (s[j + 4] & 0x0f) | ((s[j - 4] >> 6) << 4);
-            mn[j] = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
-        }
-    }
+    unpack_scales_k(s, sc, mn);
     for (int i = 0; i < 256; i++) {
         int c = i / 64, r = i % 64;
         if (r < 32) q[i] = qs[32 * c + r] & 0x0f;
         else        q[i] = qs[32 * c + r - 32] >> 4;
+    }
+}
+
+/* Q5_K: the Q4_K arrangement (same scales, mins and nibbles, the nibbles at
+ * byte 48) plus a fifth bit per weight: weight i of group j takes bit j of
+ * byte (i mod 32) of the 32 bytes at offset 16, as bit 4 of its value 0..31. */
+static void unpack_q5_K(const uint8_t *blk, int32_t *q, int32_t *sc, int32_t *mn, float *d) {
+    const uint8_t *s = blk + 4;
+    const uint8_t *qh = blk + 16;
+    const uint8_t *qs = blk + 48;
+    d[0] = ggqo_fp16_to_fp32(rd16(blk));
+    d[1] = ggqo_fp16_to_fp32(rd16(blk + 2));
+    unpack_scales_k(s, sc, mn);
+    for (int i = 0; i < 256; i++) {
+        int c = i / 64, r = i % 64, j = i / 32, l = i % 32;
+        int lo = (r < 32) ? (qs[32 * c + l] & 0x0f) : (qs[32 * c + l] >> 4);
+        int hi = (qh[l] >> j) & 1;
+        q[i] = lo | (hi << 4);
     }
 }
 
@@ -216,15 +262,23 @@ static void unpack_q6_K(const uint8_t *blk, int32_t *q, int32_t *sc, int32_t *mn
 int ggqo_unpack_block(int type, const uint8_t *blk, int32_t *q, int32_t *sc, int32_t *mn, float *d) {
     if (!blk || !q || !sc || !mn || !d) return -1;
     switch (type) {
+    case GGQO_Q4_0: unpack_q4_0(blk, q, sc, mn, d); return 0;
     case GGQO_Q8_0: unpack_q8_0(blk, q, sc, mn, d); return 0;
     case GGQO_Q4_K: unpack_q4_K(blk, q, sc, mn, d); return 0;
+    case GGQO_Q5_K: unpack_q5_K(blk, q, sc, mn, d); return 0;
     case GGQO_Q6_K: unpack_q6_K(blk, q, sc, mn, d); return 0;
     default: return -1;
     }
 }
 
-/* Signed weight quant entering the integer dot: Q6_K carries a -32 offset. */
-static int32_t dot_quant(int type, int32_t q) { return type == GGQO_Q6_K ? q - 32 : q; }
+/* Signed weight quant entering the integer dot: Q6_K carries a -32 offset,
+ * Q4_0 a -8 offset. */
+static int32_t dot_quant(int type, int32_t q) {
+    return type == GGQO_Q6_K ? q - 32 : type == GGQO_Q4_0 ? q - 8 : q;
+}
+
+/* Types with a per-group min subtracted (d*sc*q - dmin*m). */
+static int has_min(int type) { return type == GGQO_Q4_K || type == GGQO_Q5_K; }
 
 /* ------------------------------------------------------------------ */
 /* integer block dots                                                   */
@@ -280,8 +334,8 @@ static float q8_d(const uint8_t *row, int64_t blk) { float v; memcpy(&v, row + b
 static float q8_s(const uint8_t *row, int64_t blk) { float v; memcpy(&v, row + blk * Q8_1_BYTES + 4, 4); return v; }
 
 /* Contribution of one weight block to one output, fp64:
- *   Q8_0: d * d8 * D
- *   Q4_K: sum_j (d*sc_j) * d8_j * D_j - (dmin*m_j) * s8_j
+ *   Q8_0, Q4_0: d * d8 * D   (Q4_0: D over nibble - 8)
+ *   Q4_K, Q5_K: sum_j (d*sc_j) * d8_j * D_j - (dmin*m_j) * s8_j
  *   Q6_K: sum_j (d*sc_j) * d8_(j/2) * D_j                                  */
 static double block_contrib(int type, const int32_t *q, const int32_t *sc, const int32_t *mn,
                             const float *d, int64_t blk_k0, const uint8_t *q8row) {
@@ -292,7 +346,7 @@ static double block_contrib(int type, const int32_t *q, const int32_t *sc, const
         double dot = (double)group_dot(type, q, blk_k0, j, q8row);
         double wscale = (double)d[0] * (double)sc[j];
         acc += wscale * (double)q8_d(q8row, ablk) * dot;
-        if (type == GGQO_Q4_K)
+        if (has_min(type))
             acc -= ((double)d[1] * (double)mn[j]) * (double)q8_s(q8row, ablk);
     }
     return acc;
@@ -349,9 +403,10 @@ int ggqo_mul_mat(int type, const void *W, int64_t N, int64_t K,
 /* dequantize                                                           */
 /* ------------------------------------------------------------------ */
 
-/* Weight values in fp32: Q8_0 d*q; Q4_K (d*sc)*nib - dmin*m; Q6_K
- * (d*sc)*(q-32).  Every product is exact in fp32, so the only rounding is
- * the Q4_K subtraction. */
+/* Weight values in fp32: Q8_0 d*q; Q4_0 d*(nib-8); Q4_K / Q5_K
+ * (d*sc)*q - dmin*m; Q6_K (d*sc)*(q-32).  Every product is exact in fp32
+ * (at most 11 + 6 + 5 significant bits), so the only rounding is the
+ * subtraction of the min. */
 int ggqo_dequantize(int type, const void *W, int64_t rows, int64_t K, void *y, int ydt) {
     if (!W || !y || !check_w(type, rows, K)) return -1;
     if (ydt != GGQO_F32 && ydt != GGQO_BF16) return -1;
@@ -366,7 +421,7 @@ int ggqo_dequantize(int type, const void *W, int64_t rows, int64_t K, void *y, i
             for (int64_t i = 0; i < qk; i++) {
                 int64_t j = i / g;
                 float w;
-                if (type == GGQO_Q4_K) {
+                if (has_min(type)) {
                     float a = d[0] * (float)sc[j];
                     float m = d[1] * (float)mn[j];
                     float t = a * (float)q[i];

@@ -7,13 +7,14 @@
  * benchmark use it.  It shares no source with the GPU path.
  *
  * What it computes, and where that is defined:
- *  - Weights are GGUF blocks of type Q8_0, Q4_K or Q6_K, the quantized
- *    tensor types listed in FreeToken PR #690 "feat(gguf): serve GGUF
- *    checkpoints on vendored ggml-cuda kernels" (Summary, "Tensor types")
- *    and transformers PR #45977 "GgufLinear" ("What").  The pages give only
- *    block sizes (Q4_K 144 B and Q6_K 210 B per 256 weights, from the
- *    per-expert byte counts in FreeToken PR #196, Windows follow-up); the
- *    bit arrangement follows the public GGUF block layout.
+ *  - Weights are GGUF blocks of type Q8_0, Q4_K or Q6_K (and Q4_0, Q5_K),
+ *    quantized tensor types listed in FreeToken PR #690 "feat(gguf): serve
+ *    GGUF checkpoints on vendored ggml-cuda kernels" (Summary, "Tensor
+ *    types") and transformers PR #45977 "GgufLinear" ("What").  The pages
+ *    give only block sizes (Q4_K 144 B and Q6_K 210 B per 256 weights, from
+ *    the per-expert byte counts in FreeToken PR #196, Windows follow-up) and
+ *    the type id of Q4_0 (2); the bit arrangement, and the Q4_0 (18 B per
+ *    32) and Q5_K (176 B per 256) sizes, follow the public GGUF layout.
  *  - Activations are quantized on the fly to q8_1 blocks and results come
  *    out in the activation dtype with fp32 accumulation (PR #690, "What the
  *    ggml patch changes", first item).  This project's q8_1 block is
@@ -41,7 +42,7 @@ extern "C" {
 #endif
 
 /* GGUF tensor type ids (public GGUF numbering). */
-enum { GGQO_Q8_0 = 8, GGQO_Q4_K = 12, GGQO_Q6_K = 14 };
+enum { GGQO_Q4_0 = 2, GGQO_Q8_0 = 8, GGQO_Q4_K = 12, GGQO_Q5_K = 13, GGQO_Q6_K = 14 };
 /* Activation / output element types.  GGQO_Q8_1 = pre-quantized blocks. */
 enum { GGQO_F32 = 0, GGQO_BF16 = 1, GGQO_Q8_1 = 2 };
 /* Epilogues of mul_mat_id. */
@@ -66,17 +67,19 @@ int ggqo_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx
 
 /* ---- unpack ---- */
 /* One block into integer fields.
- *   q[QK]   : Q8_0 signed quants; Q4_K nibbles 0..15; Q6_K 6-bit values 0..63
- *             (the -32 offset is NOT applied here).
- *   sc[G]   : per-group integer scale (Q8_0: 1 group, value 1; Q4_K: 8 groups
- *             0..63; Q6_K: 16 groups, signed int8).
- *   mn[G]   : Q4_K mins 0..63, zero otherwise.
- *   d[2]    : fp32 of the fp16 super-scale d and (Q4_K) dmin. */
+ *   q[QK]   : Q8_0 signed quants; Q4_0 and Q4_K nibbles 0..15; Q5_K values
+ *             0..31; Q6_K 6-bit values 0..63 (the -8 / -32 offsets of Q4_0 /
+ *             Q6_K are NOT applied here).
+ *   sc[G]   : per-group integer scale (Q8_0, Q4_0: 1 group, value 1; Q4_K,
+ *             Q5_K: 8 groups 0..63; Q6_K: 16 groups, signed int8).
+ *   mn[G]   : Q4_K / Q5_K mins 0..63, zero otherwise.
+ *   d[2]    : fp32 of the fp16 super-scale d and (Q4_K, Q5_K) dmin. */
 int ggqo_unpack_block(int type, const uint8_t *blk, int32_t *q, int32_t *sc, int32_t *mn, float *d);
 
 /* ---- integer block dots ---- */
 /* out[M][N][K/g], g = ggqo_group_len(type): the int32 dot of raw weight quants
- * (Q4_K nibbles without the min, Q6_K values minus 32) with the q8_1 quants
+ * (Q4_K / Q5_K values without the min, Q6_K values minus 32, Q4_0 nibbles
+ * minus 8) with the q8_1 quants
  * of the same K positions. */
 int ggqo_block_dots(int type, const void *W, int64_t N, int64_t K,
                     const void *q8, int64_t M, int32_t *out);

@@ -19,7 +19,7 @@ from tests import gguf_pack as gp
 from gguf_block_quantized_q8_amd import inputs
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
-TYPES = [oracle.Q8_0, oracle.Q4_K, oracle.Q6_K]
+TYPES = [oracle.Q4_0, oracle.Q8_0, oracle.Q4_K, oracle.Q5_K, oracle.Q6_K]
 
 
 # ---------------------------------------------------------------- sizes
@@ -34,9 +34,9 @@ def test_page_bank_sizes():
 
 
 def test_geometry():
-    assert [oracle.block_len(t) for t in TYPES] == [32, 256, 256]
-    assert [oracle.block_bytes(t) for t in TYPES] == [34, 144, 210]
-    assert [oracle.group_len(t) for t in TYPES] == [32, 32, 16]
+    assert [oracle.block_len(t) for t in TYPES] == [32, 32, 256, 256, 256]
+    assert [oracle.block_bytes(t) for t in TYPES] == [18, 34, 144, 176, 210]
+    assert [oracle.group_len(t) for t in TYPES] == [32, 32, 32, 32, 16]
     assert oracle.row_bytes(oracle.Q4_K, 300) == 0
     assert oracle.row_bytes(oracle.Q8_0, 48) == 0
     assert oracle.row_bytes(99, 256) == 0
@@ -168,6 +168,50 @@ def test_q8_0_hand_block():
     assert oracle.mul_mat(oracle.Q8_0, blk, 1, 32, x)[0, 0] == -1016.0
 
 
+def test_q4_0_hand_block():
+    # d = 1.0; byte b holds weight b (low nibble b) and weight 16 + b (high nibble 15 - b)
+    blk = np.zeros(18, np.uint8)
+    blk[0:2] = [0x00, 0x3C]
+    blk[2:18] = [b | ((15 - b) << 4) for b in range(16)]
+    w = oracle.dequantize(oracle.Q4_0, blk, 1, 32)[0]
+    assert np.array_equal(w, np.concatenate([np.arange(16) - 8, 7 - np.arange(16)]).astype(np.float32))
+    x = np.full((1, 32), 127.0, np.float32)             # -> d8 = 1, qa = 127
+    q8 = oracle.quantize_q8_1(x)
+    assert oracle.block_dots(oracle.Q4_0, blk, 1, 32, q8, 1)[0, 0, 0] == 127 * -16
+    assert oracle.mul_mat(oracle.Q4_0, blk, 1, 32, x)[0, 0] == -2032.0
+
+
+def test_q5_K_hand_block_low_bits():
+    # no fifth bits: the Q4_K reading of the same scales, mins and nibbles (nibbles at byte 48)
+    raw = np.zeros(176, np.uint8)
+    raw[0:2] = [0x00, 0x3C]                             # d = 1.0
+    raw[2:4] = [0x00, 0x38]                             # dmin = 0.5
+    raw[4:16] = [1, 2, 3, 4, 5, 6, 7, 8, 0x21, 0x43, 0x65, 0x87]
+    raw[48:] = 0x21
+    q, sc, mn, d = oracle.unpack_block(oracle.Q5_K, raw)
+    assert list(sc) == [1, 2, 3, 4, 1, 3, 5, 7] and list(mn) == [5, 6, 7, 8, 2, 4, 6, 8]
+    w = oracle.dequantize(oracle.Q5_K, raw, 1, 256)[0].reshape(8, 32)
+    for j, v in enumerate([-1.5, 1.0, -0.5, 4.0, 0.0, 4.0, 2.0, 10.0]):
+        assert (w[j] == v).all(), j
+
+
+def test_q5_K_hand_block_fifth_bits():
+    # scales 1, mins 0, nibbles 0: group j holds 16 * (bit j of its byte of the 32 high-bit bytes)
+    raw = np.zeros(176, np.uint8)
+    raw[0:2] = [0x00, 0x3C]
+    raw[4:8] = 1
+    raw[12:16] = 1
+    raw[16:48] = 0xA5                                   # bits 0, 2, 5, 7
+    w = oracle.dequantize(oracle.Q5_K, raw, 1, 256)[0].reshape(8, 32)
+    for j, v in enumerate([16, 0, 16, 0, 0, 16, 0, 16]):
+        assert (w[j] == v).all(), j
+    raw[16:48] = np.arange(32)                          # byte l = l: weight l of group j is bit j of l
+    w = oracle.dequantize(oracle.Q5_K, raw, 1, 256)[0].reshape(8, 32)
+    l = np.arange(32)
+    for j in range(8):
+        assert np.array_equal(w[j], 16.0 * ((l >> j) & 1)), j
+
+
 def _q4k_weights(blk):
     return oracle.dequantize(oracle.Q4_K, blk, 1, 256)[0].reshape(8, 32)
 
@@ -251,6 +295,12 @@ def test_unpack_round_trip(t):
         if t == oracle.Q8_0:
             assert np.array_equal(q, f["q"]) and list(sc) == [1]
             assert d[0] == np.float32(gp.f16_val(f["d"]))
+        elif t == oracle.Q4_0:
+            assert np.array_equal(q, f["nib"]) and list(sc) == [1] and list(mn) == [0]
+            assert d[0] == np.float32(gp.f16_val(f["d"]))
+        elif t == oracle.Q5_K:
+            assert np.array_equal(q, f["q5"]) and np.array_equal(sc, f["sc"]) and np.array_equal(mn, f["mn"])
+            assert d[0] == np.float32(gp.f16_val(f["d"])) and d[1] == np.float32(gp.f16_val(f["dmin"]))
         elif t == oracle.Q4_K:
             assert np.array_equal(q, f["nib"]) and np.array_equal(sc, f["sc"]) and np.array_equal(mn, f["mn"])
             assert d[0] == np.float32(gp.f16_val(f["d"])) and d[1] == np.float32(gp.f16_val(f["dmin"]))
