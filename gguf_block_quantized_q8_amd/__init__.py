@@ -1,4 +1,4 @@
-"""GGUF block-quantized matmul (Q8_0 / Q4_K / Q6_K x q8_1) on MI355X.
+"""GGUF block-quantized matmul (Q4_0 / Q8_0 / Q4_K / Q5_K / Q6_K x q8_1) on MI355X.
 
 Thin Python binding over the C ABI in include/ggq.h (libggq.so, hand-written
 HIP for gfx950).  This module only marshals arguments: it takes torch tensors
@@ -12,7 +12,7 @@ import os
 
 import torch
 
-Q8_0, Q4_K, Q6_K = 8, 12, 14
+Q4_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 8, 12, 13, 14
 F32, BF16, Q8_1 = 0, 1, 2
 PATH_AUTO, PATH_MMVQ, PATH_MMQ = 0, 1, 2
 EPI_NONE, EPI_SWIGLU = 0, 1

@@ -27,10 +27,13 @@ int hip_status(hipError_t e, const char *what) {
 }
 
 const char *tname(int t) {
-    return t == GGQ_Q8_0 ? "Q8_0" : t == GGQ_Q4_K ? "Q4_K" : t == GGQ_Q6_K ? "Q6_K" : "?";
+    return t == GGQ_Q4_0 ? "Q4_0" : t == GGQ_Q8_0 ? "Q8_0" : t == GGQ_Q4_K ? "Q4_K" : t == GGQ_Q5_K ? "Q5_K"
+         : t == GGQ_Q6_K ? "Q6_K" : "?";
 }
 
-bool known_type(int t) { return t == GGQ_Q8_0 || t == GGQ_Q4_K || t == GGQ_Q6_K; }
+bool known_type(int t) { return t == GGQ_Q4_0 || t == GGQ_Q8_0 || t == GGQ_Q4_K || t == GGQ_Q5_K || t == GGQ_Q6_K; }
+// MMQ kernels exist for the super-block types; the 32-weight-block types run MMVQ at any M.
+bool has_mmq(int t) { return t == GGQ_Q4_K || t == GGQ_Q5_K || t == GGQ_Q6_K; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -72,17 +75,18 @@ constexpr int64_t MMVQ_ID_MAX_TOKENS = 32;
 bool use_mmq(int wt, int64_t M, int path) {
     if (path == GGQ_PATH_MMQ) return true;
     if (path == GGQ_PATH_MMVQ) return false;
-    return wt != GGQ_Q8_0 && M > MMVQ_MAX_ROWS;
+    return has_mmq(wt) && M > MMVQ_MAX_ROWS;
 }
 
 bool use_mmq_id(int wt, int64_t T, int path) {
     if (path == GGQ_PATH_MMQ) return true;
     if (path == GGQ_PATH_MMVQ) return false;
-    return wt != GGQ_Q8_0 && T > MMVQ_ID_MAX_TOKENS;
+    return has_mmq(wt) && T > MMVQ_ID_MAX_TOKENS;
 }
 
 int check_weights(int wt, int64_t N, int64_t K) {
-    if (!known_type(wt)) return fail(GGQ_ERR_UNSUPPORTED, "ggml type %d is not supported (Q8_0=8, Q4_K=12, Q6_K=14)", wt);
+    if (!known_type(wt))
+        return fail(GGQ_ERR_UNSUPPORTED, "ggml type %d is not supported (Q4_0=2, Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14)", wt);
     if (N < 0 || K <= 0) return fail(GGQ_ERR_INVALID, "ggml type %s: bad shape N=%lld K=%lld", tname(wt), (long long)N, (long long)K);
     if (K % block_len(wt) != 0)
         return fail(GGQ_ERR_INVALID, "ggml type %s K=%lld is not a multiple of the block length %lld", tname(wt),
@@ -170,7 +174,7 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
     if (xdt != GGQ_F32 && xdt != GGQ_BF16 && xdt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: input dtype %d", xdt);
     if (ydt != GGQ_F32 && ydt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: output dtype %d must be F32 or BF16", ydt);
     if (path != GGQ_PATH_AUTO && path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "mul_mat: bad path %d", path);
-    if (path == GGQ_PATH_MMQ && wt == GGQ_Q8_0) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: MMQ path has no Q8_0 kernel; use MMVQ");
+    if (path == GGQ_PATH_MMQ && !has_mmq(wt)) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: MMQ path has no %s kernel; use MMVQ", tname(wt));
     if (M < 0) return fail(GGQ_ERR_INVALID, "mul_mat: M=%lld < 0", (long long)M);
     if (xdt != GGQ_Q8_1 && ldx < K) return fail(GGQ_ERR_INVALID, "mul_mat: ldx=%lld < K=%lld", (long long)ldx, (long long)K);
     if (ldy < N) return fail(GGQ_ERR_INVALID, "mul_mat: ldy=%lld < N=%lld", (long long)ldy, (long long)N);
@@ -284,7 +288,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     if (epi != GGQ_EPI_NONE && epi != GGQ_EPI_SWIGLU) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad epilogue %d", epi);
     if (epi == GGQ_EPI_SWIGLU && N % 2) return fail(GGQ_ERR_INVALID, "mul_mat_id: SwiGLU needs an even N (gate rows then up rows), N=%lld", (long long)N);
     if (path != GGQ_PATH_AUTO && path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad path %d", path);
-    if (path == GGQ_PATH_MMQ && wt == GGQ_Q8_0) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: MMQ path has no Q8_0 kernel; use MMVQ");
+    if (path == GGQ_PATH_MMQ && !has_mmq(wt)) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: MMQ path has no %s kernel; use MMVQ", tname(wt));
     if (E <= 0 || T < 0 || top_k <= 0) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad E=%lld T=%lld top_k=%lld", (long long)E, (long long)T, (long long)top_k);
     if (x_per_route != 0 && x_per_route != 1) return fail(GGQ_ERR_INVALID, "mul_mat_id: x_per_route must be 0 or 1");
     const int64_t rb = (int64_t)ggq_row_bytes(wt, K);
@@ -376,7 +380,7 @@ int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K, const void 
     int rc = check_weights(wt, N, K);
     if (rc) return rc;
     if (path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "test_block_dots: path must be MMVQ or MMQ");
-    if (path == GGQ_PATH_MMQ && wt == GGQ_Q8_0) return fail(GGQ_ERR_UNSUPPORTED, "test_block_dots: MMQ path has no Q8_0 kernel");
+    if (path == GGQ_PATH_MMQ && !has_mmq(wt)) return fail(GGQ_ERR_UNSUPPORTED, "test_block_dots: MMQ path has no %s kernel", tname(wt));
     if (M < 0) return fail(GGQ_ERR_INVALID, "test_block_dots: M < 0");
     if (M == 0 || N == 0) return GGQ_OK;
     if (!W || !q8 || !out) return fail(GGQ_ERR_INVALID, "test_block_dots: null pointer");

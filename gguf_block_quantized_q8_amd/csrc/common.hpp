@@ -7,19 +7,25 @@
 
 namespace ggq {
 
-enum : int { T_Q8_0 = 8, T_Q4_K = 12, T_Q6_K = 14 };
+enum : int { T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14 };
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_Q8_1 = 2 };
 
 constexpr int QK8_1 = 32;
 constexpr int Q8_1_BYTES = 40;   // float d, float s, int8 qs[32]
 
 template <int T> struct Geom;
+template <> struct Geom<T_Q4_0> { static constexpr int QK = 32,  BYTES = 18,  G = 32; };
 template <> struct Geom<T_Q8_0> { static constexpr int QK = 32,  BYTES = 34,  G = 32; };
 template <> struct Geom<T_Q4_K> { static constexpr int QK = 256, BYTES = 144, G = 32; };
+template <> struct Geom<T_Q5_K> { static constexpr int QK = 256, BYTES = 176, G = 32; };
 template <> struct Geom<T_Q6_K> { static constexpr int QK = 256, BYTES = 210, G = 16; };
 
-__host__ __device__ inline int64_t block_len(int t) { return t == T_Q8_0 ? 32 : (t == T_Q4_K || t == T_Q6_K) ? 256 : 0; }
-__host__ __device__ inline int64_t block_bytes(int t) { return t == T_Q8_0 ? 34 : t == T_Q4_K ? 144 : t == T_Q6_K ? 210 : 0; }
+__host__ __device__ inline int64_t block_len(int t) {
+    return (t == T_Q4_0 || t == T_Q8_0) ? 32 : (t == T_Q4_K || t == T_Q5_K || t == T_Q6_K) ? 256 : 0;
+}
+__host__ __device__ inline int64_t block_bytes(int t) {
+    return t == T_Q4_0 ? 18 : t == T_Q8_0 ? 34 : t == T_Q4_K ? 144 : t == T_Q5_K ? 176 : t == T_Q6_K ? 210 : 0;
+}
 __host__ __device__ inline int64_t group_len(int t) { return t == T_Q6_K ? 16 : 32; }
 
 typedef int v2i __attribute__((ext_vector_type(2)));

@@ -110,8 +110,8 @@ __global__ __launch_bounds__(256) void q8_1_to_planar_kernel(const uint8_t *__re
 
 // ---------------------------------------------------------------------------
 // Dequantize: one thread per 16 consecutive weights of an output row.
-//   Q8_0: d*q; Q4_K: (d*sc)*nib - dmin*m; Q6_K: (d*sc)*(q-32).
-// Every product is exact in fp32; the Q4_K subtraction rounds once.
+//   Q8_0: d*q; Q4_0: d*(nib-8); Q4_K / Q5_K: (d*sc)*q - dmin*m; Q6_K: (d*sc)*(q-32).
+// Every product is exact in fp32; the subtraction of the min rounds once.
 // Output row r (of n) holds table row ids[r] (r itself without ids); a row id
 // outside [0, rows) gives a row of zeros.  y rows are ldy elements apart.
 // ---------------------------------------------------------------------------
@@ -131,6 +131,32 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     float w[16];
     if (src < 0 || src >= rows) {
         for (int i = 0; i < 16; i++) w[i] = 0.0f;
+    } else if (T == T_Q4_0) {
+        // weights 0..15: low nibbles of the 16 quant bytes, 16..31: high nibbles
+        const float d = fp16_bits_to_f32(ld_u16(blk));
+        const v4i q = ld16_a2(blk + 2);
+        for (int i = 0; i < 16; i++) {
+            const int byte = (q[i / 4] >> (8 * (i % 4))) & 0xff;
+            w[i] = d * (float)((ib ? byte >> 4 : byte & 15) - 8);
+        }
+    } else if (T == T_Q5_K) {
+        // the Q4_K fields (nibbles at byte 48) plus bit j of byte l of the 32 fifth-bit bytes
+        const uint8_t *s = blk + 4;
+        const float d = fp16_bits_to_f32(ld_u16(blk)), dmin = fp16_bits_to_f32(ld_u16(blk + 2));
+        const int j = ib / 32;
+        int sc, mn;
+        if (j < 4) { sc = s[j] & 63; mn = s[j + 4] & 63; }
+        else { sc = (s[j + 4] & 0x0f) | ((s[j - 4] >> 6) << 4); mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4); }
+        const int c = ib / 64, l0 = ib % 32;
+        const bool hi = (ib % 64) >= 32;
+        const v4i q = *reinterpret_cast<const v4i *>(blk + 48 + 32 * c + l0);
+        const v4i h = *reinterpret_cast<const v4i *>(blk + 16 + l0);
+        const float a = d * (float)sc, m = dmin * (float)mn;
+        for (int i = 0; i < 16; i++) {
+            const int byte = (q[i / 4] >> (8 * (i % 4))) & 0xff;
+            const int bit = (h[i / 4] >> (8 * (i % 4) + j)) & 1;
+            w[i] = a * (float)((hi ? (byte >> 4) : (byte & 15)) | (bit << 4)) - m;
+        }
     } else if (T == T_Q8_0) {
         const float d = fp16_bits_to_f32(ld_u16(blk));
         v4i q = ld16_a2(blk + 2 + ib);
@@ -288,7 +314,7 @@ hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, cons
         if (ydt == DT_F32) hipLaunchKernelGGL((dequant_kernel<TT, DT_F32>), g, b, 0, s, W, rows, K, ids, n, y, ldy);   \
         else hipLaunchKernelGGL((dequant_kernel<TT, DT_BF16>), g, b, 0, s, W, rows, K, ids, n, y, ldy);               \
     }
-    GGQ_DQ(T_Q8_0) GGQ_DQ(T_Q4_K) GGQ_DQ(T_Q6_K)
+    GGQ_DQ(T_Q4_0) GGQ_DQ(T_Q8_0) GGQ_DQ(T_Q4_K) GGQ_DQ(T_Q5_K) GGQ_DQ(T_Q6_K)
 #undef GGQ_DQ
     return hipGetLastError();
 }

@@ -7,7 +7,8 @@
 // needs for its 1024 outputs.  With int8 MFMA the rescale costs cvt + int
 // multiply by the sub-scale + fma per output per block; here the integer
 // sub-scale is folded into the fp16 weight operand instead (Q4_K: sc * nibble
-// <= 945, Q6_K: sc * (q - 32) split into two exact fp16 parts), the MFMA sums
+// <= 945, Q5_K: sc * value <= 1953, Q6_K: sc * (q - 32) split into two exact
+// fp16 parts), the MFMA sums
 // the block's dot in fp32 exactly, and one fma per output per block remains
 // (times the activation scale d8).  Every product and partial sum is an
 // integer below 2^24, so the per-block dot is exact, as with int8.
@@ -18,7 +19,7 @@
 // bytes and activation quants in registers while the current stage computes
 // from one of two LDS buffers, and a stage ends with an LDS-only barrier (no
 // wait on the global loads in flight).  Per 256-wide super-block the weight
-// d / dmin and the activation d8 / s8 are staged once.  Q4_K's min term
+// d / dmin and the activation d8 / s8 are staged once.  The Q4_K / Q5_K min term
 // -dmin * sum_j m_j * s8_j runs as a bf16 MFMA with s8 split exactly into
 // three bf16 parts.
 #include "kernels.hpp"
@@ -31,7 +32,7 @@ constexpr int EPI_NONE_ = 0, EPI_SWIGLU_ = 1;
 template <int T>
 struct __attribute__((aligned(16))) MmqSmem {
     static constexpr int NA = T == T_Q6_K ? 2 : 1;       // Q6_K: high and low parts of sc*(q-32)
-    static constexpr int NMIN = T == T_Q4_K ? 1 : 0;
+    static constexpr int NMIN = (T == T_Q4_K || T == T_Q5_K) ? 1 : 0;
     _Float16 A[2][NA][NT][LDA];   // two stage buffers
     _Float16 B[2][MT][LDA];
     float d8[2][8][MT];           // by super-block parity; [block][column]: conflict-free column reads
@@ -92,14 +93,16 @@ __device__ __forceinline__ v4i gld16(const uint8_t *p) {
 // UNIT: all sub-scales 1 and no activation scales (test hook: raw dots).
 template <int T, bool UNIT>
 struct Stager {
+    static constexpr bool HAS_MIN = T == T_Q4_K || T == T_Q5_K;   // d*sc*q - dmin*m types
     const uint8_t *wrow;      // this thread's weight row
     const _Float16 *xrow;     // this thread's activation row + 16 * half
     const float *xd, *xs;     // d, s of this thread's activation row + 4 * half
-    v4i hdr;        // Q4_K: block header (d, dmin, 12 scale bytes); Q6_K: the 16 int8 scales
-    v4i q0, q1;     // Q4_K: 16 quant bytes (q0); Q6_K: 16 ql bytes (q0), 16 qh bytes (q1)
+    v4i hdr;        // Q4_K / Q5_K: block header (d, dmin, 12 scale bytes); Q6_K: the 16 int8 scales
+    v4i q0, q1;     // Q4_K: 16 quant bytes (q0); Q5_K: also 16 fifth-bit bytes (q1);
+                    // Q6_K: 16 ql bytes (q0), 16 qh bytes (q1)
     uint32_t d6;    // Q6_K: fp16 d
     v4i b0, b1;     // 16 fp16 activation quants
-    v4f m;          // stage 0 of a super-block: 4 d8; stage 1 (Q4_K): 4 s8
+    v4f m;          // stage 0 of a super-block: 4 d8; stage 1 (Q4_K, Q5_K): 4 s8
 
     __device__ void init(const uint8_t *row, const _Float16 *xq, const float *d, const float *sx, int64_t K,
                          int64_t xr) {
@@ -108,7 +111,7 @@ struct Stager {
         xrow = xq + xr * K + 16 * hf;
         const int64_t nb = K / QK8_1;
         xd = UNIT ? nullptr : d + xr * nb + 4 * hf;
-        xs = (UNIT || T != T_Q4_K) ? nullptr : sx + xr * nb + 4 * hf;
+        xs = (UNIT || !HAS_MIN) ? nullptr : sx + xr * nb + 4 * hf;
     }
 
     __device__ void load(int s) {
@@ -118,6 +121,11 @@ struct Stager {
             const uint8_t *blk = wrow + (int64_t)sb * 144;
             hdr = gld16(blk);
             q0 = gld16(blk + 16 + 32 * (j >> 1) + 16 * hf);
+        } else if (T == T_Q5_K) {
+            const uint8_t *blk = wrow + (int64_t)sb * 176;
+            hdr = gld16(blk);
+            q0 = gld16(blk + 48 + 32 * (j >> 1) + 16 * hf);
+            q1 = gld16(blk + 16 + 16 * hf);                         // fifth bits of positions 16 hf ..
         } else {
             const uint8_t *blk = wrow + (int64_t)sb * 210;
             const int hh = j >> 2, g = j & 3;
@@ -130,14 +138,14 @@ struct Stager {
         b0 = *reinterpret_cast<const v4i *>(src);
         b1 = *reinterpret_cast<const v4i *>(src + 8);
         if (!UNIT && j == 0) m = *reinterpret_cast<const v4f *>(xd + sb * 8);
-        if (!UNIT && T == T_Q4_K && j == 1) m = *reinterpret_cast<const v4f *>(xs + sb * 8);
+        if (!UNIT && HAS_MIN && j == 1) m = *reinterpret_cast<const v4f *>(xs + sb * 8);
     }
 
     __device__ void store(MmqSmem<T> &sm, int s) {
         const int tid = threadIdx.x, tr = tid >> 1, hf = tid & 1;
         const int sb = s >> 3, j = s & 7, buf = s & 1;
         // ---- weights: fp16 of sub-scale x quant, built in packed halves ----
-        if (T == T_Q4_K) {
+        if (HAS_MIN) {
             uint32_t sc_lo, sc_hi, mn_lo, mn_hi;
             q4k_pack((uint32_t)hdr.y, (uint32_t)hdr.z, (uint32_t)hdr.w, sc_lo, sc_hi, mn_lo, mn_hi);
             const int sc = UNIT ? 1 : (int)__builtin_amdgcn_ubfe(j < 4 ? sc_lo : sc_hi, 8 * (j & 3), 8);
@@ -147,9 +155,16 @@ struct Stager {
             uint32_t o[8];
 #pragma unroll
             for (int w = 0; w < 4; w++) {
-                const uint32_t x = (j & 1) ? ((uint32_t)q0[w] >> 4) : (uint32_t)q0[w];   // odd groups: high nibbles
-                o[2 * w] = h2_bits(__builtin_elementwise_fma(as_h2(spread2(x, 0x00050004u, 0x640f640fu)), sc2, off2));
-                o[2 * w + 1] = h2_bits(__builtin_elementwise_fma(as_h2(spread2(x, 0x00070006u, 0x640f640fu)), sc2, off2));
+                uint32_t x = (j & 1) ? ((uint32_t)q0[w] >> 4) : (uint32_t)q0[w];   // odd groups: high nibbles
+                // Q5_K: value = nibble | fifth bit (bit j of the byte) << 4, at most 31, so sc * value
+                // stays below 2048 and exact in fp16 as well
+                uint32_t mask = 0x640f640fu;
+                if (T == T_Q5_K) {
+                    x = (x & 0x0f0f0f0fu) | ((((uint32_t)q1[w] >> j) & 0x01010101u) << 4);
+                    mask = 0x641f641fu;
+                }
+                o[2 * w] = h2_bits(__builtin_elementwise_fma(as_h2(spread2(x, 0x00050004u, mask)), sc2, off2));
+                o[2 * w + 1] = h2_bits(__builtin_elementwise_fma(as_h2(spread2(x, 0x00070006u, mask)), sc2, off2));
             }
             v4i *dst = reinterpret_cast<v4i *>(&sm.A[buf][0][tr][16 * hf]);
             dst[0] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
@@ -192,14 +207,14 @@ struct Stager {
             for (int i = 0; i < 4; i++) sm.d8[sb & 1][4 * hf + i][tr] = m[i];
         if (j == 1) {
             if (hf == 0) {
-                if (T == T_Q4_K) {
+                if (HAS_MIN) {
                     sm.wd[tr] = fp16_bits_to_f32((uint32_t)hdr.x & 0xffffu);
                     sm.wdmin[tr] = fp16_bits_to_f32((uint32_t)hdr.x >> 16);
                 } else {
                     sm.wd[tr] = fp16_bits_to_f32(d6);
                 }
             }
-            if (T == T_Q4_K) {
+            if (HAS_MIN) {
                 uint32_t sc_lo, sc_hi, mn_lo, mn_hi;
                 q4k_pack((uint32_t)hdr.y, (uint32_t)hdr.z, (uint32_t)hdr.w, sc_lo, sc_hi, mn_lo, mn_hi);
                 const uint32_t mw = hf ? mn_hi : mn_lo;
@@ -377,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
         }
         if (j == 7) {
             // ---- end of super-block: P * d (- dmin * min term) into acc ----
-            if (T == T_Q4_K) {
+            if (MmqSmem<T>::NMIN) {
                 v16f Q[2][2];
 #pragma unroll
                 for (int a = 0; a < 2; a++)
@@ -560,6 +575,7 @@ hipError_t launch_mmq(int t, bool moe, int epi, int ydt, const MmqParams &p, hip
     if (p.m_tiles == 0 || p.n_tiles == 0) return hipSuccess;
     if (t == T_Q4_K) launch_t<T_Q4_K>(moe, epi, ydt, p, s);
     else if (t == T_Q6_K) launch_t<T_Q6_K>(moe, epi, ydt, p, s);
+    else if (t == T_Q5_K) launch_t<T_Q5_K>(moe, epi, ydt, p, s);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -571,6 +587,7 @@ hipError_t launch_mmq_dots(int t, const uint8_t *W, int64_t N, int64_t K, const 
     const dim3 g((unsigned)(mt * nt)), b(256);
     if (t == T_Q4_K) hipLaunchKernelGGL(mmq_dots_kernel<T_Q4_K>, g, b, 0, s, W, N, K, xq, M, mt, out);
     else if (t == T_Q6_K) hipLaunchKernelGGL(mmq_dots_kernel<T_Q6_K>, g, b, 0, s, W, N, K, xq, M, mt, out);
+    else if (t == T_Q5_K) hipLaunchKernelGGL(mmq_dots_kernel<T_Q5_K>, g, b, 0, s, W, N, K, xq, M, mt, out);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

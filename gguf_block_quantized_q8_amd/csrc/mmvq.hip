@@ -72,6 +72,10 @@ __device__ __forceinline__ void q4k_scales(int p, uint32_t s0, uint32_t s1, uint
 __device__ __forceinline__ int nib_lo(int qs) { return qs & 0x0f0f0f0f; }
 __device__ __forceinline__ int nib_hi(int qs) { return (int)(((uint32_t)qs >> 4) & 0x0f0f0f0fu); }
 
+// Q5_K: the fifth bit (bit j of each byte of one qh dword) moved to bit 4 of
+// each byte, to be ORed onto the nibbles of group j.
+__device__ __forceinline__ int q5k_bit(uint32_t qh, int j) { return (int)(((qh >> j) & 0x01010101u) << 4); }
+
 // Q6_K: 4 packed 6-bit weights (0..63, before the -32 offset) of quarter g
 // from one dword of ql (low nibbles for g < 2, high for g >= 2) and one of qh
 // (bits 2g, 2g+1 of each byte).
@@ -124,6 +128,62 @@ struct Unit<T_Q4_K, NC> {
             for (int w = 0; w < 4; w++) {
                 lo[i][w] = nib_lo(q0[w]); lo[i][4 + w] = nib_lo(q1[w]);
                 hi[i][w] = nib_hi(q0[w]); hi[i][4 + w] = nib_hi(q1[w]);
+            }
+        }
+#pragma unroll
+        for (int col = 0; col < NC; col++) {
+            if (col >= ncols) break;
+            const int b0 = sb * 8 + 2 * p;                          // q8_1 block of group 2p
+            const lds_bp qa = A.qa + col * A.K + b0 * 32;
+            const v4i a0 = l128(qa), a1 = l128(qa + 16), a2 = l128(qa + 32), a3 = l128(qa + 48);
+            const v2i dd = l64(A.d8 + (col * A.nb + b0) * 4), ss = l64(A.s8 + (col * A.nb + b0) * 4);
+            const float d80 = as_float(dd.x), d81 = as_float(dd.y);
+            const float s80 = as_float(ss.x), s81 = as_float(ss.y);
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                int D0 = 0, D1 = 0;
+#pragma unroll
+                for (int w = 0; w < 4; w++) {
+                    D0 = dot4(lo[i][w], a0[w], D0);
+                    D0 = dot4(lo[i][4 + w], a1[w], D0);
+                    D1 = dot4(hi[i][w], a2[w], D1);
+                    D1 = dot4(hi[i][4 + w], a3[w], D1);
+                }
+                acc[i][col] += d[i] * (sc0[i] * d80 * (float)D0 + sc1[i] * d81 * (float)D1) -
+                               dm[i] * (mn0[i] * s80 + mn1[i] * s81);
+            }
+            col_fence<NC>(acc[0][col], acc[1][col]);
+        }
+    }
+};
+
+// ---- Q5_K: unit = (super-block sb, pair p), as Q4_K: groups 2p and 2p+1
+// from the low / high nibbles of 32 quant bytes (at byte 48 of the block) with
+// their fifth bits from bits 2p / 2p+1 of the 32 high-bit bytes (at byte 16).
+template <int NC>
+struct Unit<T_Q5_K, NC> {
+    __device__ static void run(int u, lds_bp row0, lds_bp row1, const ActL &A, int ncols, float (&acc)[2][NC]) {
+        const int sb = u >> 2, p = u & 3;
+        const lds_bp rows[2] = {row0, row1};
+        int lo[2][8], hi[2][8];
+        float d[2], dm[2], sc0[2], sc1[2], mn0[2], mn1[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const lds_bp blk = rows[i] + sb * 176;                    // Q5_K blocks stay 16-aligned
+            const v4i hdr = l128(blk);
+            const v4i h0 = l128(blk + 16), h1 = l128(blk + 32);
+            const v4i q0 = l128(blk + 48 + 32 * p), q1 = l128(blk + 64 + 32 * p);
+            d[i] = fp16_bits_to_f32((uint32_t)hdr.x & 0xffffu);
+            dm[i] = fp16_bits_to_f32((uint32_t)hdr.x >> 16);
+            int a, b, c, e;
+            q4k_scales(p, (uint32_t)hdr.y, (uint32_t)hdr.z, (uint32_t)hdr.w, a, b, c, e);
+            sc0[i] = (float)a; sc1[i] = (float)b; mn0[i] = (float)c; mn1[i] = (float)e;
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                lo[i][w] = nib_lo(q0[w]) | q5k_bit((uint32_t)h0[w], 2 * p);
+                lo[i][4 + w] = nib_lo(q1[w]) | q5k_bit((uint32_t)h1[w], 2 * p);
+                hi[i][w] = nib_hi(q0[w]) | q5k_bit((uint32_t)h0[w], 2 * p + 1);
+                hi[i][4 + w] = nib_hi(q1[w]) | q5k_bit((uint32_t)h1[w], 2 * p + 1);
             }
         }
 #pragma unroll
@@ -241,6 +301,49 @@ struct Unit<T_Q8_0, NC> {
                     D = dot4(q[i][1][w], a1[w], D);
                 }
                 acc[i][col] += d[i] * d8 * (float)D;
+            }
+            col_fence<NC>(acc[0][col], acc[1][col]);
+        }
+    }
+};
+
+// ---- Q4_0: unit = one 18-byte block (32 weights): byte b of the 16 quant
+// bytes holds weight b (low nibble) and weight 16 + b (high nibble), value
+// d * (nibble - 8).  The -8 enters through the block's activation sum:
+// d * (d8 * D - 8 * s8), D the dot of the raw nibbles.
+template <int NC>
+struct Unit<T_Q4_0, NC> {
+    __device__ static void run(int u, lds_bp row0, lds_bp row1, const ActL &A, int ncols, float (&acc)[2][NC]) {
+        const lds_bp rows[2] = {row0, row1};
+        v4i lo[2], hi[2];
+        float d[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const lds_bp blk = rows[i] + u * 18;                      // 2-byte aligned
+            d[i] = fp16_bits_to_f32(l16(blk));
+            const uint32_t s = (uint32_t)(uintptr_t)(blk + 2) & 3;
+            const v4i q = l128s(blk + 2 - s, s);
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                lo[i][w] = nib_lo(q[w]);
+                hi[i][w] = nib_hi(q[w]);
+            }
+        }
+#pragma unroll
+        for (int col = 0; col < NC; col++) {
+            if (col >= ncols) break;
+            const lds_bp qa = A.qa + col * A.K + u * 32;
+            const v4i a0 = l128(qa), a1 = l128(qa + 16);
+            const float d8 = lf(A.d8 + (col * A.nb + u) * 4), s8 = lf(A.s8 + (col * A.nb + u) * 4);
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                int D = 0;
+#pragma unroll
+                for (int w = 0; w < 4; w++) {
+                    D = dot4(lo[i][w], a0[w], D);
+                    D = dot4(hi[i][w], a1[w], D);
+                }
+                acc[i][col] += d[i] * (d8 * (float)D - 8.0f * s8);
             }
             col_fence<NC>(acc[0][col], acc[1][col]);
         }
@@ -766,6 +869,29 @@ __global__ __launch_bounds__(256) void mmvq_dots_kernel(const uint8_t *__restric
             const v4i qa = ld16_a2(a + 8 + 16 * h);
             for (int w = 0; w < 4; w++) D = dot4((jj & 1) ? nib_hi(qs[w]) : nib_lo(qs[w]), qa[w], D);
         }
+    } else if (T == T_Q5_K) {
+        const int sb = (int)(j / 8), jj = (int)(j % 8), p = jj >> 1;
+        const uint8_t *blk = row + sb * 176;
+        const uint8_t *a = arow + (int64_t)(sb * 8 + jj) * Q8_1_BYTES;
+        for (int h = 0; h < 2; h++) {
+            const v4i qs = ld16_a2(blk + 48 + 32 * p + 16 * h);
+            const v4i qh = ld16_a2(blk + 16 + 16 * h);
+            const v4i qa = ld16_a2(a + 8 + 16 * h);
+            for (int w = 0; w < 4; w++)
+                D = dot4(((jj & 1) ? nib_hi(qs[w]) : nib_lo(qs[w])) | q5k_bit((uint32_t)qh[w], jj), qa[w], D);
+        }
+    } else if (T == T_Q4_0) {
+        const uint8_t *blk = row + j * 18;
+        const uint8_t *a = arow + j * Q8_1_BYTES;
+        const v4i q = ld16_a2(blk + 2);
+        const v4i a0 = ld16_a2(a + 8), a1 = ld16_a2(a + 24);
+        int asum = 0;
+        for (int w = 0; w < 4; w++) {
+            asum = dot4(a0[w], 0x01010101, dot4(a1[w], 0x01010101, asum));
+            D = dot4(nib_lo(q[w]), a0[w], D);
+            D = dot4(nib_hi(q[w]), a1[w], D);
+        }
+        D -= 8 * asum;
     } else if (T == T_Q6_K) {
         const int sb = (int)(j / 16), jj = (int)(j % 16);          // 16-weight group
         const int hh = jj / 8, g = (jj % 8) / 2, t = jj & 1;
@@ -849,7 +975,7 @@ struct ItemGeo {
 };
 
 static ItemGeo item_geo(int t, int64_t K) {
-    const int upb = t == T_Q8_0 ? 1 : 4;                          // units per block
+    const int upb = (t == T_Q8_0 || t == T_Q4_0) ? 1 : 4;        // units per block
     const double ub = (double)block_bytes(t) / upb;                // bytes per unit
     ItemGeo G{};
     G.units = (int)(K / block_len(t)) * upb;
@@ -932,6 +1058,8 @@ hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqPara
     const dim3 g((unsigned)std::min<int64_t>(need, cap), (unsigned)ngroups_bound);
     if (t == T_Q4_K) launch_t<T_Q4_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
     else if (t == T_Q6_K) launch_t<T_Q6_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
+    else if (t == T_Q5_K) launch_t<T_Q5_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
+    else if (t == T_Q4_0) launch_t<T_Q4_0>(nc, moe, epi, ydt, p, g, waves, lds, s);
     else launch_t<T_Q8_0>(nc, moe, epi, ydt, p, g, waves, lds, s);
     return hipGetLastError();
 }
@@ -943,6 +1071,8 @@ hipError_t launch_mmvq_dots(int t, const uint8_t *W, int64_t N, int64_t K, const
     dim3 g((unsigned)((n + 255) / 256));
     if (t == T_Q4_K) hipLaunchKernelGGL(mmvq_dots_kernel<T_Q4_K>, g, dim3(256), 0, s, W, N, K, q8, M, out);
     else if (t == T_Q6_K) hipLaunchKernelGGL(mmvq_dots_kernel<T_Q6_K>, g, dim3(256), 0, s, W, N, K, q8, M, out);
+    else if (t == T_Q5_K) hipLaunchKernelGGL(mmvq_dots_kernel<T_Q5_K>, g, dim3(256), 0, s, W, N, K, q8, M, out);
+    else if (t == T_Q4_0) hipLaunchKernelGGL(mmvq_dots_kernel<T_Q4_0>, g, dim3(256), 0, s, W, N, K, q8, M, out);
     else hipLaunchKernelGGL(mmvq_dots_kernel<T_Q8_0>, g, dim3(256), 0, s, W, N, K, q8, M, out);
     return hipGetLastError();
 }

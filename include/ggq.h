@@ -2,7 +2,9 @@
  * ggq.h -- C ABI of the MI355X (gfx950) GGUF block-quantized matmul library.
  *
  * Matrix multiplication against GGUF block-quantized weights (Q8_0, Q4_K,
- * Q6_K) with activations quantized on the fly to q8_1 blocks; results come
+ * Q6_K, and Q4_0, Q5_K: types PR #690 lists in its Summary, with block
+ * layouts from the public GGUF format) with activations quantized on the fly
+ * to q8_1 blocks; results come
  * out in the activation dtype (or the requested output dtype) with fp32
  * accumulation.  This is the operation FreeToken PR #690 "feat(gguf): serve
  * GGUF checkpoints on vendored ggml-cuda kernels" describes in "What the ggml
@@ -40,7 +42,7 @@ extern "C" {
 #endif
 
 /* GGUF tensor type ids (public GGUF numbering). */
-typedef enum { GGQ_Q8_0 = 8, GGQ_Q4_K = 12, GGQ_Q6_K = 14 } ggq_type;
+typedef enum { GGQ_Q4_0 = 2, GGQ_Q8_0 = 8, GGQ_Q4_K = 12, GGQ_Q5_K = 13, GGQ_Q6_K = 14 } ggq_type;
 typedef enum { GGQ_F32 = 0, GGQ_BF16 = 1, GGQ_Q8_1 = 2 } ggq_dtype;
 /* Kernel choice: AUTO picks MMVQ for few activation rows, MMQ above. */
 typedef enum { GGQ_PATH_AUTO = 0, GGQ_PATH_MMVQ = 1, GGQ_PATH_MMQ = 2 } ggq_path;
@@ -54,7 +56,8 @@ typedef enum {
 } ggq_status;
 
 /* Bytes of one row of K weights of `type`; 0 if K is not a multiple of the
- * block length (32 for Q8_0, 256 for Q4_K / Q6_K) or the type is unknown. */
+ * block length (32 for Q4_0 / Q8_0, 256 for Q4_K / Q5_K / Q6_K) or the type
+ * is unknown.  Block bytes: Q4_0 18, Q8_0 34, Q4_K 144, Q5_K 176, Q6_K 210. */
 size_t ggq_row_bytes(int type, int64_t K);
 
 /* Bytes of M rows of K activations as q8_1 blocks: M * (K/32) * 40. */
@@ -69,7 +72,7 @@ int ggq_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx,
                       void *q8, void *stream);
 
 /* Dense quantized matmul: y[m][n] = sum_k W[n][k] * x[m][k] for n < N.
- *   W   : N rows of K weights of type wt (Q8_0, Q4_K, Q6_K).
+ *   W   : N rows of K weights of type wt (Q4_0, Q8_0, Q4_K, Q5_K, Q6_K).
  *   x   : [M][ldx] of xdt (GGQ_F32 / GGQ_BF16), or, with xdt = GGQ_Q8_1,
  *         M rows of K/32 q8_1 blocks (ldx ignored) -- one quantization can
  *         be reused for several weight matrices (PR #690, second item).
@@ -77,7 +80,8 @@ int ggq_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx,
  *         not written.
  *   ws  : workspace of at least ggq_mul_mat_ws(...) bytes (may be NULL when
  *         that is 0).
- *   path: AUTO, or force MMVQ / MMQ (MMQ: Q4_K and Q6_K only).
+ *   path: AUTO, or force MMVQ / MMQ (MMQ: Q4_K, Q5_K and Q6_K only; Q4_0
+ *         and Q8_0 run MMVQ at every M).
  * fp32 accumulation; per-block integer dots are exact. */
 size_t ggq_mul_mat_ws(int wt, int64_t N, int64_t K, int xdt, int64_t M, int path);
 int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
@@ -145,10 +149,11 @@ int ggq_get_rows(int wt, const void *W, int64_t rows, int64_t K, const int32_t *
 const char *ggq_last_error(void);
 
 /* Test hook (not part of the product API): per-group int32 dots of raw weight
- * quants with q8_1 quants, out[M][N][K/g] (g = 32 for Q8_0 / Q4_K: nibbles
- * without the min; g = 16 for Q6_K: values minus 32), computed by the same
- * device unpack and dot code as the named path (GGQ_PATH_MMVQ: the v_dot4
- * units; GGQ_PATH_MMQ: the staged fp16 tiles and the MFMA, Q4_K / Q6_K only).
+ * quants with q8_1 quants, out[M][N][K/g] (g = 32 for Q8_0, Q4_0 (nibbles
+ * minus 8), Q4_K / Q5_K (values without the min); g = 16 for Q6_K: values
+ * minus 32), computed by the same device unpack and dot code as the named
+ * path (GGQ_PATH_MMVQ: the v_dot4 units; GGQ_PATH_MMQ: the staged fp16 tiles
+ * and the MFMA, Q4_K / Q5_K / Q6_K only).
  * q8 is M rows of K/32 q8_1 blocks; ws needs ggq_test_block_dots_ws() bytes. */
 size_t ggq_test_block_dots_ws(int wt, int64_t K, int64_t M, int path);
 int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K,

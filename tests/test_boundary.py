@@ -41,8 +41,11 @@ def test_geometry(L):
     assert L.ggq_row_bytes(g.Q8_0, 512) == 16 * 34
     assert L.ggq_row_bytes(g.Q4_K, 2048) == 8 * 144
     assert L.ggq_row_bytes(g.Q6_K, 2048) == 8 * 210
+    assert L.ggq_row_bytes(g.Q4_0, 256) == 8 * 18
+    assert L.ggq_row_bytes(g.Q5_K, 2048) == 8 * 176
     assert L.ggq_row_bytes(g.Q4_K, 300) == 0
-    assert L.ggq_row_bytes(2, 256) == 0
+    assert L.ggq_row_bytes(g.Q4_0, 48) == 0
+    assert L.ggq_row_bytes(3, 256) == 0                                 # Q4_1: not provided
     assert L.ggq_q8_1_bytes(3, 64) == 3 * 2 * 40
 
 
@@ -51,8 +54,8 @@ def err(L):
 
 
 def test_unsupported_type(L):
-    rc = L.ggq_mul_mat(2, FAKE, 16, 2816, FAKE, g.F32, 1, 2816, FAKE, g.F32, 16, None, 0, 0, None)
-    assert rc == g.ERR_UNSUPPORTED and "type 2" in err(L)
+    rc = L.ggq_mul_mat(3, FAKE, 16, 2816, FAKE, g.F32, 1, 2816, FAKE, g.F32, 16, None, 0, 0, None)
+    assert rc == g.ERR_UNSUPPORTED and "type 3" in err(L)
     assert L.ggq_dequantize(42, FAKE, 1, 256, FAKE, g.F32, None) == g.ERR_UNSUPPORTED
 
 
@@ -75,6 +78,8 @@ def test_bad_dtypes_and_paths(L):
     assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, 7, 1, 256, FAKE, g.F32, 16, None, 0, 0, None) == g.ERR_UNSUPPORTED
     assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, g.F32, 1, 256, FAKE, g.Q8_1, 16, None, 0, 0, None) == g.ERR_UNSUPPORTED
     assert L.ggq_mul_mat(g.Q8_0, FAKE, 16, 256, FAKE, g.F32, 64, 256, FAKE, g.F32, 16, None, 0, g.PATH_MMQ, None) == g.ERR_UNSUPPORTED
+    assert L.ggq_mul_mat(g.Q4_0, FAKE, 16, 256, FAKE, g.F32, 64, 256, FAKE, g.F32, 16, None, 0, g.PATH_MMQ, None) == g.ERR_UNSUPPORTED
+    assert L.ggq_mul_mat_ws(g.Q4_0, 16, 256, g.F32, 4096, g.PATH_AUTO) == 0   # Q4_0 runs MMVQ at any M
     assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, g.F32, 1, 256, FAKE, g.F32, 16, None, 0, 9, None) == g.ERR_INVALID
 
 

@@ -18,7 +18,7 @@ from gguf_block_quantized_q8_amd import inputs
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 8e-3}
-TYPES = [g.Q8_0, g.Q4_K, g.Q6_K]
+TYPES = [g.Q8_0, g.Q4_K, g.Q6_K, g.Q4_0, g.Q5_K]
 
 
 @pytest.fixture(scope="module")
@@ -104,7 +104,7 @@ def test_dequantize_q6_K_large_scales(dev):
     assert np.array_equal(host(y).view(np.uint32), oracle.dequantize(g.Q6_K, W, 16, 512).view(np.uint32))
 
 
-@pytest.mark.parametrize("wt", [g.Q8_0, g.Q4_K, g.Q6_K])
+@pytest.mark.parametrize("wt", TYPES)
 @pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
 def test_get_rows_bit_exact(dev, wt, ydt):
     """Gathered rows equal the oracle's dequantized table rows bit for bit; ids
@@ -134,7 +134,8 @@ def test_get_rows_empty_and_errors(dev):
 
 # ------------------------------------------------------------------ per-group int dots
 
-@pytest.mark.parametrize("wt,path", [(g.Q8_0, "mmvq"), (g.Q4_K, "mmvq"), (g.Q6_K, "mmvq"), (g.Q4_K, "mmq"), (g.Q6_K, "mmq")])
+@pytest.mark.parametrize("wt,path", [(g.Q8_0, "mmvq"), (g.Q4_K, "mmvq"), (g.Q6_K, "mmvq"), (g.Q4_K, "mmq"), (g.Q6_K, "mmq"),
+                                     (g.Q4_0, "mmvq"), (g.Q5_K, "mmvq"), (g.Q5_K, "mmq")])
 def test_block_dots_bit_exact(dev, wt, path):
     log("dots", wt, path)
     N, K, M = 131, (512 if wt == g.Q8_0 else 768), 133      # ragged against the 128 x 128 MMQ tiles
@@ -174,22 +175,35 @@ def _check_mul_mat(dev, wt, N, K, M, xdt, ydt, path, seed, rows=None, W=None):
 @pytest.mark.parametrize("wt", TYPES)
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
 def test_mmvq_small(dev, wt, M):
-    K = 512 if wt == g.Q8_0 else 768
+    K = 512 if wt in (g.Q8_0, g.Q4_0) else 768
     _check_mul_mat(dev, wt, 97, K, M, "f32", "f32", "mmvq", 40 + wt)
 
 
-@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K])
+@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K, g.Q5_K])
 @pytest.mark.parametrize("K", [256, 512])
 def test_mmvq_short_rows(dev, wt, K):
     _check_mul_mat(dev, wt, 300, K, 4, "bf16", "bf16", "mmvq", 50 + K)
 
 
 def test_mmvq_many_columns(dev):
-    """M above the 8 columns of one MMVQ group (Q8_0 always takes MMVQ)."""
+    """M above the 8 columns of one MMVQ group (Q8_0 and Q4_0 always take MMVQ)."""
     _check_mul_mat(dev, g.Q8_0, 64, 256, 21, "f32", "f32", "auto", 60)
+    _check_mul_mat(dev, g.Q4_0, 64, 256, 21, "f32", "f32", "auto", 61)
 
 
-@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K])
+@pytest.mark.parametrize("wt", [g.Q4_0, g.Q5_K])
+def test_new_types_decode_shape(dev, wt):
+    """The 4096 x 4096 decode shape (bf16 in and out) at M = 1 and 8, and a prefill-sized
+    MMQ call for Q5_K, sampled rows against the oracle."""
+    W = inputs.gen_weights(wt, 4096, 4096, 90 + wt)
+    for M in (1, 8):
+        _check_mul_mat(dev, wt, 4096, 4096, M, "bf16", "bf16", "auto", 91 + wt + M, W=W)
+    if wt == g.Q5_K:
+        rows = inputs.sample_rows(4096, 128, 95)
+        _check_mul_mat(dev, wt, 4096, 4096, 512, "bf16", "bf16", "mmq", 96, rows=rows, W=W)
+
+
+@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K, g.Q5_K])
 @pytest.mark.parametrize("M,N,K", [(1, 5, 256), (40, 100, 512), (129, 257, 768), (300, 128, 1024)])
 @pytest.mark.parametrize("ydt", ["f32", "bf16"])
 def test_mmq_small_ragged(dev, wt, M, N, K, ydt):
@@ -293,8 +307,8 @@ def _moe_ref(wt, W, K, x, ids, top_k, route_w=None, epi=oracle.EPI_NONE, x_per_r
                              route_w=route_w, epi=epi, tokens=tokens)
 
 
-@pytest.mark.parametrize("path", ["mmvq", "mmq"])
-@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K])
+@pytest.mark.parametrize("path,wt", [("mmvq", g.Q4_K), ("mmq", g.Q4_K), ("mmvq", g.Q6_K), ("mmq", g.Q6_K),
+                                     ("mmvq", g.Q5_K), ("mmq", g.Q5_K), ("mmvq", g.Q4_0)])
 def test_moe_edge_routes(dev, path, wt):
     """Duplicate ids in a token, inactive (-1) and out-of-range ids, experts with no routes."""
     E, N, K, Tn, top_k = 9, 96, 512, 37, 4
