@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 import gguf_block_quantized_q8_amd as g  # noqa: E402
 from gguf_block_quantized_q8_amd import inputs  # noqa: E402
 
-TNAME = {8: "Q8_0", 12: "Q4_K", 14: "Q6_K"}
+TNAME = {2: "Q4_0", 8: "Q8_0", 12: "Q4_K", 13: "Q5_K", 14: "Q6_K"}
 METRIC = "MMVQ GB/s @M=1 and MMQ/mul_mat_id TOPS @M=8192 (Q4_K,Q6_K), % of roofline"
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
@@ -332,7 +332,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--workloads", default="all",
-                    help="comma list of: decode, prefill, sweep, lmhead1, lmhead2048, getrows, moe16, moe8192 (default all)")
+                    help="comma list of: decode, prefill, sweep, lmhead1, lmhead2048, getrows, types, moe16, moe8192 (default all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -362,7 +362,7 @@ def main():
     head = bench_decode(ctx, g.Q4_K, 4096, 4096, 1, 201, 202, torch.bfloat16, K, W)
     also = []
     sel = set(args.workloads.split(",")) if args.workloads != "all" else {
-        "decode", "prefill", "sweep", "lmhead1", "lmhead2048", "getrows", "moe16", "moe8192"}
+        "decode", "prefill", "sweep", "lmhead1", "lmhead2048", "getrows", "types", "moe16", "moe8192"}
     if args.only_headline:
         sel = set()
     if "decode" in sel:
@@ -384,6 +384,14 @@ def main():
         log("q6_K 248320x2048 lm_head M=1")
         r = bench_decode(ctx, g.Q6_K, 248320, 2048, 1, 401, 402, torch.float32, max(20, K // 4), W, rotate=False)
         also.append({"workload": "q6_K_248320x2048_lm_head", "M": 1, **r})
+    if "types" in sel:
+        for wt, name in ((g.Q4_0, "q4_0"), (g.Q5_K, "q5_K")):
+            log(f"{name} 4096x4096 decode M=1")
+            r = bench_decode(ctx, wt, 4096, 4096, 1, 201, 202, torch.bfloat16, K, W)
+            also.append({"workload": f"{name}_4096x4096_decode", "M": 1, **r})
+        log("q5_K 8192x2048 prefill M=8192")
+        r = bench_prefill(ctx, g.Q5_K, 8192, 2048, 8192, 301, 302, torch.bfloat16, max(5, K // 20), max(2, W // 10))
+        also.append({"workload": "q5_K_8192x2048_prefill", "M": 8192, **r})
     if "getrows" in sel:
         log("q6_K 248320x2048 get_rows n=8192")
         r = bench_get_rows(ctx, g.Q6_K, 248320, 2048, 8192, 401, 404, torch.bfloat16, max(20, K // 4), W)
