@@ -393,27 +393,20 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
         if (j == 7) {
             // ---- end of super-block: P * d (- dmin * min term) into acc ----
             if (MmqSmem<T>::NMIN) {
-                v16f Q[2][2];
+                // one weight half-tile (ni) at a time: 32 registers of min-term sums live, not 64
 #pragma unroll
-                for (int a = 0; a < 2; a++)
+                for (int ni = 0; ni < 2; ni++) {
+                    v16f Q[2] = {v16f{}, v16f{}};
 #pragma unroll
-                    for (int b = 0; b < 2; b++) Q[a][b] = v16f{};
+                    for (int kk = 0; kk < 2; kk++) {
+                        const int ko = 16 * kk + kh;
+                        const v8bf am = *reinterpret_cast<const v8bf *>(&sm.Amin[64 * wn + 32 * ni + lr][ko]);
 #pragma unroll
-                for (int kk = 0; kk < 2; kk++) {
-                    const int ko = 16 * kk + kh;
-                    v8bf am[2], bmv[2];
-#pragma unroll
-                    for (int ni = 0; ni < 2; ni++) am[ni] = *reinterpret_cast<const v8bf *>(&sm.Amin[64 * wn + 32 * ni + lr][ko]);
-#pragma unroll
-                    for (int mi = 0; mi < 2; mi++) bmv[mi] = *reinterpret_cast<const v8bf *>(&sm.Bmin[64 * wm + 32 * mi + lr][ko]);
-#pragma unroll
-                    for (int ni = 0; ni < 2; ni++)
-#pragma unroll
-                        for (int mi = 0; mi < 2; mi++)
-                            Q[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[ni], bmv[mi], Q[ni][mi], 0, 0, 0);
-                }
-#pragma unroll
-                for (int ni = 0; ni < 2; ni++)
+                        for (int mi = 0; mi < 2; mi++) {
+                            const v8bf bmv = *reinterpret_cast<const v8bf *>(&sm.Bmin[64 * wm + 32 * mi + lr][ko]);
+                            Q[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bmv, Q[mi], 0, 0, 0);
+                        }
+                    }
 #pragma unroll
                     for (int e = 0; e < 16; e++) {
                         const int tr = 64 * wn + 32 * ni + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
@@ -421,9 +414,10 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
 #pragma unroll
                         for (int mi = 0; mi < 2; mi++) {
                             acc[ni][mi][e] = __builtin_fmaf(P[ni][mi][e], d, acc[ni][mi][e]);
-                            acc[ni][mi][e] = __builtin_fmaf(Q[ni][mi][e], -dm, acc[ni][mi][e]);
+                            acc[ni][mi][e] = __builtin_fmaf(Q[mi][e], -dm, acc[ni][mi][e]);
                         }
                     }
+                }
             } else {
 #pragma unroll
                 for (int ni = 0; ni < 2; ni++)
