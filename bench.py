@@ -260,7 +260,10 @@ def bench_moe(ctx, Tn, steps, warmup):
     ids_np, w_np = inputs.gen_routing(Tn, E, top_k, 504)
     ids = torch.from_numpy(ids_np).to(dev)
     w = torch.from_numpy(w_np).to(dev)
+    # h between the projections: q8_1 blocks straight from the gate_up epilogue
+    # (the down projection's own input format), or bf16 (then quantized again)
     h = torch.empty((Tn, top_k, I), dtype=torch.bfloat16, device=dev)
+    hq = torch.empty((Tn, top_k, I // 32 * 40), dtype=torch.uint8, device=dev)
     y = torch.empty((Tn, H), dtype=torch.bfloat16, device=dev)
     L = ctx.L
     ws1b = L.ggq_mul_mat_id_ws(g.Q4_K, E, 2 * I, H, g.BF16, Tn, 0, top_k, g.EPI_SWIGLU, 0, g.PATH_AUTO)
@@ -270,23 +273,32 @@ def bench_moe(ctx, Tn, steps, warmup):
     s_gu = Wgu.stride(0)
     s_d = Wd.stride(0)
 
-    def gate_up(i):
+    def gate_up(i, q8=True):
         check(L.ggq_mul_mat_id(g.Q4_K, vp(Wgus[i % ncopy]), E, 2 * I, H, s_gu, vp(x), g.BF16, Tn, 0, vp(ids), top_k, None,
-                               g.EPI_SWIGLU, vp(h), g.BF16, vp(ws1), ws1b, g.PATH_AUTO, ctx.s), "gate_up")
+                               g.EPI_SWIGLU, vp(hq if q8 else h), g.Q8_1 if q8 else g.BF16, vp(ws1), ws1b,
+                               g.PATH_AUTO, ctx.s), "gate_up")
 
-    def down(i):
-        check(L.ggq_mul_mat_id(g.Q6_K, vp(Wds[i % ncopy]), E, H, I, s_d, vp(h), g.BF16, Tn, 1, vp(ids), top_k, vp(w),
-                               g.EPI_NONE, vp(y), g.BF16, vp(ws2), ws2b, g.PATH_AUTO, ctx.s), "down")
+    def down(i, q8=True):
+        check(L.ggq_mul_mat_id(g.Q6_K, vp(Wds[i % ncopy]), E, H, I, s_d, vp(hq if q8 else h), g.Q8_1 if q8 else g.BF16,
+                               Tn, 1, vp(ids), top_k, vp(w), g.EPI_NONE, vp(y), g.BF16, vp(ws2), ws2b, g.PATH_AUTO,
+                               ctx.s), "down")
 
     def step(i):
+        gate_up(i, False)
+        down(i, False)
+
+    def step_q8_h(i):
         gate_up(i)
         down(i)
 
     dt, _ = time_steps(step, steps, warmup, graph=Tn <= 64)
+    sq = max(steps // 2, 1)
+    dt_q, _ = time_steps(step_q8_h, sq, max(warmup // 2, 1), graph=Tn <= 64)
     R = Tn * top_k
-    res = {"ms_per_step": dt / steps * 1e3}
-    tg = time_launches(gate_up, 20)
-    td = time_launches(down, 20)
+    res = {"ms_per_step": dt / steps * 1e3, "h_between": "bf16",
+           "ms_per_step_q8_1_h": round(dt_q / sq * 1e3, 4)}
+    tg = time_launches(lambda i: gate_up(i, False), 20)
+    td = time_launches(lambda i: down(i, False), 20)
     if Tn <= 64:
         distinct = len(np.unique(ids_np))
         moved = distinct * (Wgu.stride(0) + Wd.stride(0)) + Tn * H * 2 * 2 + R * I * 2 * 2

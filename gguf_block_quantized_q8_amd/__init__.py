@@ -174,8 +174,11 @@ def mul_mat(W, wt, x, K=None, out_dtype=None, path="auto", out=None):
 def mul_mat_id(W, wt, x, ids, K, route_w=None, epi=EPI_NONE, x_per_route=False, out_dtype=None,
                path="auto", return_workspace=False):
     """Routed experts.  W: uint8 [E, N, row_bytes] (or [E, stride] with stride >= N*row_bytes);
-    x: [T, K] (broadcast) or [T, top_k, K] (x_per_route); ids: int32 [T, top_k].
-    Returns y [T, top_k, N'] (route_w None) or [T, N'] (route_w [T, top_k] float32)."""
+    x: [T, K] (broadcast) or [T, top_k, K] (x_per_route), float32 / bfloat16, or uint8 rows of
+    K/32 q8_1 blocks; ids: int32 [T, top_k].
+    Returns y [T, top_k, N'] (route_w None) or [T, N'] (route_w [T, top_k] float32).
+    out_dtype "q8_1" (route_w None): y is uint8 [T, top_k, N'/32*40], each route's outputs as
+    q8_1 blocks (rounded to bf16 first for bfloat16 x)."""
     _check_gpu(W, x, ids, route_w)
     E = W.shape[0]
     rb = row_bytes(wt, K)
@@ -184,15 +187,20 @@ def mul_mat_id(W, wt, x, ids, K, route_w=None, epi=EPI_NONE, x_per_route=False, 
     T, top_k = ids.shape
     Np = N // 2 if epi == EPI_SWIGLU else N
     if out_dtype is None:
-        out_dtype = x.dtype
-    shape = (T, Np) if route_w is not None else (T, top_k, Np)
-    y = torch.empty(shape, dtype=out_dtype, device=x.device)
+        out_dtype = x.dtype if _xdt(x) != Q8_1 else torch.float32
+    if out_dtype == "q8_1":
+        y = torch.empty((T, top_k, Np // 32 * Q8_1_BYTES), dtype=torch.uint8, device=x.device)
+        ydt = Q8_1
+    else:
+        shape = (T, Np) if route_w is not None else (T, top_k, Np)
+        y = torch.empty(shape, dtype=out_dtype, device=x.device)
+        ydt = _ydt(out_dtype)
     p = _PATHS[path]
     L = lib()
     wsb = L.ggq_mul_mat_id_ws(wt, E, N, K, _xdt(x), T, int(x_per_route), top_k, epi, int(route_w is not None), p)
     ws = _workspace(max(wsb, 256), x.device)
     rc = L.ggq_mul_mat_id(wt, _ptr(W), E, N, K, stride, _ptr(x), _xdt(x), T, int(x_per_route),
-                          _ptr(ids), top_k, _ptr(route_w), epi, _ptr(y), _ydt(out_dtype),
+                          _ptr(ids), top_k, _ptr(route_w), epi, _ptr(y), ydt,
                           _ptr(ws), ws.numel(), p, _stream(x.device))
     _raise(rc, "mul_mat_id")
     return (y, ws) if return_workspace else y

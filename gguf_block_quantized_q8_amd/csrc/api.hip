@@ -241,6 +241,7 @@ struct IdLayout {
     int64_t max_tiles;
     Planar pl;
     float *o32;           // weighted: per-route fp32 outputs [R][Np]
+    void *hstage;         // MMVQ, unweighted: outputs [R][Np] (fp32 room) before a q8_1 output's quantization
     size_t total;
 };
 
@@ -263,6 +264,7 @@ IdLayout id_layout(void *ws, int wt, int64_t E, int64_t N, int64_t K, int64_t T,
     L.rt.tiles = c.take<int4>((size_t)L.max_tiles * 16);
     if (mmq) L.pl = carve_planar(c, rows, K);
     L.o32 = weighted ? c.take<float>((size_t)R * Np * 4) : nullptr;
+    L.hstage = !mmq && !weighted ? c.take<float>((size_t)R * Np * 4) : nullptr;
     L.total = c.off;
     (void)wt;
     return L;
@@ -283,10 +285,13 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     g_err[0] = 0;
     int rc = check_weights(wt, N, K);
     if (rc) return rc;
-    if (xdt != GGQ_F32 && xdt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: input dtype %d must be F32 or BF16", xdt);
-    if (ydt != GGQ_F32 && ydt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: output dtype %d must be F32 or BF16", ydt);
+    if (xdt != GGQ_F32 && xdt != GGQ_BF16 && xdt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: input dtype %d", xdt);
+    if (ydt != GGQ_F32 && ydt != GGQ_BF16 && ydt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: output dtype %d", ydt);
     if (epi != GGQ_EPI_NONE && epi != GGQ_EPI_SWIGLU) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad epilogue %d", epi);
     if (epi == GGQ_EPI_SWIGLU && N % 2) return fail(GGQ_ERR_INVALID, "mul_mat_id: SwiGLU needs an even N (gate rows then up rows), N=%lld", (long long)N);
+    if (ydt == GGQ_Q8_1 && route_w) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: q8_1 output is per route (route_w must be NULL)");
+    if (ydt == GGQ_Q8_1 && (epi == GGQ_EPI_SWIGLU ? N / 2 : N) % QK8_1)
+        return fail(GGQ_ERR_INVALID, "mul_mat_id: q8_1 output needs output rows N'=%lld divisible by 32", (long long)(epi == GGQ_EPI_SWIGLU ? N / 2 : N));
     if (path != GGQ_PATH_AUTO && path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad path %d", path);
     if (path == GGQ_PATH_MMQ && !has_mmq(wt)) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: MMQ path has no %s kernel; use MMVQ", tname(wt));
     if (E <= 0 || T < 0 || top_k <= 0) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad E=%lld T=%lld top_k=%lld", (long long)E, (long long)T, (long long)top_k);
@@ -310,8 +315,14 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     const int J = mmq ? MMQ_MT : mmvq_id_cols(wt, R, E, K);
     rc = hip_status(launch_route_build(ids, R, E, J, L.rt, s), "mul_mat_id routes");
     if (rc) return rc;
+    // q8_1 output: MMQ quantizes in its epilogue; MMVQ writes the values (fp32,
+    // or bf16 for bf16 input) to the workspace and the q8_1 kernel follows
+    const bool q8_out = ydt == GGQ_Q8_1;
+    const int hdt = xdt == GGQ_BF16 ? GGQ_BF16 : GGQ_F32;
+    void *yk = q8_out && !mmq ? L.hstage : y;               // what the matmul kernel writes
+    const int ydt_k = q8_out && !mmq ? hdt : ydt;
     if (!weighted) {
-        rc = hip_status(launch_zero_inactive(ids, R, E, Np, y, ydt, s), "mul_mat_id zero");
+        rc = hip_status(launch_zero_inactive(ids, R, E, Np, yk, ydt_k, s), "mul_mat_id zero");
         if (rc) return rc;
     }
 
@@ -327,8 +338,10 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.xsrc = xdt;
         p.x = x;
         p.ldx = K;
-        p.x_bytes = rows * K * (xdt == GGQ_F32 ? 4 : 2);
-        p.y = y;
+        p.q8 = static_cast<const uint8_t *>(x);
+        p.q8_row = (K / 32) * Q8_1_BYTES;
+        p.x_bytes = xdt == GGQ_Q8_1 ? rows * p.q8_row : rows * K * (xdt == GGQ_F32 ? 4 : 2);
+        p.y = yk;
         p.perm = L.rt.perm;
         p.groups = L.rt.tiles;
         p.ngroups = L.rt.ntiles;
@@ -338,9 +351,16 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.o32 = L.o32;
         p.groups_expected = std::min<int64_t>(E, R);
         p.w_bytes = (E - 1) * expert_stride + N * rb;
-        rc = hip_status(launch_mmvq(wt, J, true, epi, ydt, p, L.max_tiles, s), "mul_mat_id mmvq");
+        rc = hip_status(launch_mmvq(wt, J, true, epi, ydt_k, p, L.max_tiles, s), "mul_mat_id mmvq");
+        if (!rc && q8_out)
+            rc = hip_status(launch_quantize(L.hstage, hdt, R, Np, Np, static_cast<uint8_t *>(y), nullptr, nullptr, nullptr, s),
+                            "mul_mat_id q8_1 output");
     } else {
-        rc = hip_status(launch_quantize(x, xdt, rows, K, K, nullptr, L.pl.xq, L.pl.xd, L.pl.xs, s), "mul_mat_id quantize");
+        if (xdt == GGQ_Q8_1)
+            rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), rows, K, L.pl.xq, L.pl.xd, L.pl.xs, s),
+                            "mul_mat_id expand");
+        else
+            rc = hip_status(launch_quantize(x, xdt, rows, K, K, nullptr, L.pl.xq, L.pl.xd, L.pl.xs, s), "mul_mat_id quantize");
         if (rc) return rc;
         MmqParams p{};
         p.W = static_cast<const uint8_t *>(W);
@@ -362,6 +382,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.x_per_route = x_per_route;
         p.route_w = route_w;
         p.o32 = L.o32;
+        p.q8_bf16 = q8_out && hdt == GGQ_BF16;
         rc = hip_status(launch_mmq(wt, true, epi, ydt, p, s), "mul_mat_id mmq");
     }
     if (rc) return rc;

@@ -53,6 +53,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// q8_1 quant of one value of a block whose largest magnitude is amax, with
+// d = amax / 127: x / d (IEEE fp32 division) rounded half away from zero; an
+// all-zero block gives 0.  |x / d| <= 127 (1 + 2^-23), so the clamp only
+// guards the rounding of that bound.
+__device__ __forceinline__ int q8_1_quant(float x, float d, float amax) {
+    if (amax == 0.0f) return 0;
+    return (int)fminf(fmaxf(roundf(x / d), -127.0f), 127.0f);
+}
+
 // ---- loads ----
 __device__ __forceinline__ uint32_t ld_u16(const uint8_t *p) {
     return *reinterpret_cast<const uint16_t *>(p);

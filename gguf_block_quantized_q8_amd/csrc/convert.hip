@@ -55,14 +55,8 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const void *__restri
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        int qi = 0;
-        if (amax != 0.0f) {
-            float r = roundf(v[i] / d);
-            r = fminf(fmaxf(r, -127.0f), 127.0f);
-            qi = (int)r;
-        }
-        q[i] = qi;
-        sum += qi;
+        q[i] = q8_1_quant(v[i], d, amax);
+        sum += q[i];
     }
     sum = sum8(sum);
     if (amax == 0.0f) d = 0.0f;
@@ -268,6 +262,13 @@ __global__ __launch_bounds__(256) void zero_inactive_kernel(const int32_t *__res
     if (r >= R) return;
     const int32_t e = ids[r];
     if (e >= 0 && e < E) return;
+    if (YDT == DT_Q8_1) {
+        // Np / 32 all-zero q8_1 blocks (d = s = 0, q = 0): what an all-zero row quantizes to
+        const int64_t words = Np / QK8_1 * (Q8_1_BYTES / 4);
+        uint32_t *o = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(y) + r * (Np / QK8_1) * Q8_1_BYTES);
+        for (int64_t i = threadIdx.x; i < words; i += blockDim.x) o[i] = 0u;
+        return;
+    }
     for (int64_t n = threadIdx.x; n < Np; n += blockDim.x) {
         if (YDT == DT_F32) static_cast<float *>(y)[r * Np + n] = 0.0f;
         else static_cast<uint16_t *>(y)[r * Np + n] = 0;
@@ -346,7 +347,8 @@ hipError_t launch_zero_inactive(const int32_t *ids, int64_t R, int64_t E, int64_
                                 hipStream_t s) {
     if (R == 0) return hipSuccess;
     if (ydt == DT_F32) hipLaunchKernelGGL(zero_inactive_kernel<DT_F32>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
-    else hipLaunchKernelGGL(zero_inactive_kernel<DT_BF16>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
+    else if (ydt == DT_BF16) hipLaunchKernelGGL(zero_inactive_kernel<DT_BF16>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
+    else hipLaunchKernelGGL(zero_inactive_kernel<DT_Q8_1>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
     return hipGetLastError();
 }
 

@@ -115,6 +115,7 @@ struct MmqParams {
     int x_per_route;
     const float *route_w;
     float *o32;           // weighted: per-route fp32 outputs [R][Np]
+    int q8_bf16;          // q8_1 output: round the values to bf16 before quantizing
 };
 constexpr int MMQ_NT = 128;   // weight rows per workgroup tile
 constexpr int MMQ_MT = 128;   // activation rows (routes) per workgroup tile

@@ -279,6 +279,66 @@ __device__ __forceinline__ void tile_of(int64_t b, int64_t m_tiles, int64_t n_ti
     bn = grp * G + in % gw;
 }
 
+// Routed output as q8_1 blocks, y[route][Np / 32] (Np % 32 == 0).  A block is
+// 32 consecutive outputs of one route: one 32-row MFMA tile row group of one
+// column, held 16 + 16 by lanes l and l + 32 (rows 8g + 4h + i, h = lane / 32),
+// so its amax and quant sum take one lane exchange.  The values are those the
+// fp32 / bf16 epilogue would store (SwiGLU applied, rounded to bf16 first when
+// p.q8_bf16), quantized as the q8_1 kernel does.
+template <int EPI, int T>
+__device__ __forceinline__ void store_q8_1(const MmqParams &p, const MmqSmem<T> &sm, const v16f (&acc)[2][2],
+                                           int64_t bn, int tile_count, int wn, int wm, int lane) {
+    const int lr = lane & 31, h = lane >> 5;
+    const int64_t bpr = p.Np / QK8_1;                       // blocks per route
+#pragma unroll
+    for (int mi = 0; mi < 2; mi++) {
+        const int col = 64 * wm + 32 * mi + lr;
+        const bool live = col < tile_count && sm.xrow[col] >= 0;   // the same in lanes l and l + 32
+        const int64_t r = live ? sm.route[col] : 0;
+#pragma unroll
+        for (int bi = 0; bi < (EPI == EPI_SWIGLU_ ? 1 : 2); bi++) {
+            const int64_t n0 = EPI == EPI_SWIGLU_ ? bn * 64 + 32 * wn : bn * NT + 64 * wn + 32 * bi;
+            float v[16];
+            float amax = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                float o;
+                if (EPI == EPI_SWIGLU_) {
+                    const float gt = acc[0][mi][e], up = acc[1][mi][e];
+                    o = gt / (1.0f + expf(-gt)) * up;
+                } else {
+                    o = acc[bi][mi][e];
+                }
+                if (p.q8_bf16) o = bf16_bits_to_f32(f32_to_bf16_bits(o));
+                v[e] = o;
+                amax = fmaxf(amax, fabsf(o));
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            float d = amax / 127.0f;
+            uint32_t qw[4];
+            int sum = 0;
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int q = q8_1_quant(v[4 * g + i], d, amax);
+                    sum += q;
+                    w |= (uint32_t)(q & 0xff) << (8 * i);
+                }
+                qw[g] = w;
+            }
+            sum += __shfl_xor(sum, 32);
+            if (amax == 0.0f) d = 0.0f;
+            if (!live || n0 >= p.Np) continue;
+            uint8_t *blk = static_cast<uint8_t *>(p.y) + (r * bpr + n0 / QK8_1) * Q8_1_BYTES;
+#pragma unroll
+            for (int g = 0; g < 4; g++) *reinterpret_cast<uint32_t *>(blk + 8 + 8 * g + 4 * h) = qw[g];
+            if (h == 0) *reinterpret_cast<float2 *>(blk) = make_float2(d, d * (float)sum);
+        }
+    }
+}
+
 // grid: 1-D, m_tiles * n_tiles workgroups of 256 threads (routed: m_tiles rounded up to 8).
 template <int T, bool MOE, int EPI, int YDT>
 __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
@@ -436,6 +496,10 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
     }
 
     // ---- epilogue ----
+    if (YDT == DT_Q8_1) {
+        store_q8_1<EPI>(p, sm, acc, bn, tile_count, wn, wm, lane);
+        return;
+    }
 #pragma unroll
     for (int mi = 0; mi < 2; mi++) {
         const int col = 64 * wm + 32 * mi + lr;
@@ -558,9 +622,13 @@ static void launch_t(bool moe, int epi, int ydt, const MmqParams &p, hipStream_t
     if (!moe) {
         if (ydt == DT_F32) GGQ_L(false, EPI_NONE_, DT_F32); else GGQ_L(false, EPI_NONE_, DT_BF16);
     } else if (epi == EPI_SWIGLU_) {
-        if (ydt == DT_F32) GGQ_L(true, EPI_SWIGLU_, DT_F32); else GGQ_L(true, EPI_SWIGLU_, DT_BF16);
+        if (ydt == DT_F32) GGQ_L(true, EPI_SWIGLU_, DT_F32);
+        else if (ydt == DT_BF16) GGQ_L(true, EPI_SWIGLU_, DT_BF16);
+        else GGQ_L(true, EPI_SWIGLU_, DT_Q8_1);
     } else {
-        if (ydt == DT_F32) GGQ_L(true, EPI_NONE_, DT_F32); else GGQ_L(true, EPI_NONE_, DT_BF16);
+        if (ydt == DT_F32) GGQ_L(true, EPI_NONE_, DT_F32);
+        else if (ydt == DT_BF16) GGQ_L(true, EPI_NONE_, DT_BF16);
+        else GGQ_L(true, EPI_NONE_, DT_Q8_1);
     }
 #undef GGQ_L
 }

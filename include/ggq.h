@@ -98,7 +98,8 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
  *                  N * row_bytes and a multiple of 16.
  *   x            : x_per_route == 0: [T][K] (each route of token t uses x[t]);
  *                  x_per_route == 1: [T][top_k][K] (route (t,k) uses x[t][k]).
- *                  Element type xdt (GGQ_F32 / GGQ_BF16), rows contiguous.
+ *                  Element type xdt (GGQ_F32 / GGQ_BF16), rows contiguous; or
+ *                  xdt = GGQ_Q8_1: the same rows as K/32 q8_1 blocks each.
  *   ids          : [T][top_k] int32 expert ids.  id < 0: inactive route
  *                  (contributes nothing).  id >= E: skipped and counted in
  *                  the uint32 at workspace offset 0 (readable after the call).
@@ -111,8 +112,17 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
  *                  in ascending k with fp32 accumulation (deterministic: the
  *                  per-route fp32 outputs go to the workspace, then one pass
  *                  sums them per token).
- *   y            : output of ydt (GGQ_F32 / GGQ_BF16), contiguous.
- *   ws           : at least ggq_mul_mat_id_ws(...) bytes.
+ *   y            : output of ydt (GGQ_F32 / GGQ_BF16), contiguous.  With
+ *                  route_w == NULL, ydt may be GGQ_Q8_1 (N' % 32 == 0): y is
+ *                  [T][top_k][N'/32] q8_1 blocks, the blocks ggq_quantize_q8_1
+ *                  makes from the plain output (bf16 for bf16 x, else fp32),
+ *                  bit for bit -- the SwiGLU h in the down projection's own
+ *                  input format (PR #690 keeps intermediates in the activation
+ *                  dtype and quantizes activations straight to q8_1).  The MMQ
+ *                  path quantizes in its epilogue; the MMVQ path stages the
+ *                  plain output in the workspace and quantizes after.
+ *   ws           : at least ggq_mul_mat_id_ws(...) bytes (includes that
+ *                  staging for MMVQ-path calls without route weights).
  * Tokens, routes and tiles are grouped on the device; no host sync. */
 size_t ggq_mul_mat_id_ws(int wt, int64_t E, int64_t N, int64_t K, int xdt,
                          int64_t T, int x_per_route, int64_t top_k,

@@ -99,10 +99,11 @@ def test_noops(L):
 
 def test_mul_mat_id_validation(L):
     i64 = ctypes.c_int64
-    def call(wt=g.Q4_K, E=4, N=32, K=256, stride=None, T=2, xpr=0, top_k=2, epi=0, ws_bytes=1 << 20, path=0, ws=FAKE):
+    def call(wt=g.Q4_K, E=4, N=32, K=256, stride=None, T=2, xpr=0, top_k=2, epi=0, ws_bytes=1 << 20, path=0, ws=FAKE,
+             xdt=g.F32, ydt=g.F32, route_w=None):
         stride = stride if stride is not None else N * L.ggq_row_bytes(wt, K)
-        return L.ggq_mul_mat_id(wt, FAKE, E, N, K, stride, FAKE, g.F32, T, xpr, FAKE, top_k, None, epi,
-                                FAKE, g.F32, ws, ws_bytes, path, None)
+        return L.ggq_mul_mat_id(wt, FAKE, E, N, K, stride, FAKE, xdt, T, xpr, FAKE, top_k, route_w, epi,
+                                FAKE, ydt, ws, ws_bytes, path, None)
     assert call(stride=32 * 144 - 16) == g.ERR_INVALID          # stride < N * row_bytes
     assert call(stride=32 * 144 + 8) == g.ERR_INVALID           # stride % 16
     assert call(N=33, epi=g.EPI_SWIGLU) == g.ERR_INVALID        # SwiGLU needs even N
@@ -110,6 +111,11 @@ def test_mul_mat_id_validation(L):
     assert call(ws_bytes=64) == g.ERR_WORKSPACE
     assert call(wt=g.Q8_0, K=64, path=g.PATH_MMQ) == g.ERR_UNSUPPORTED
     assert call(T=0) == g.OK
+    assert call(xdt=3) == g.ERR_UNSUPPORTED
+    assert call(ydt=3) == g.ERR_UNSUPPORTED
+    assert call(ydt=g.Q8_1, route_w=FAKE) == g.ERR_UNSUPPORTED    # q8_1 output is per route
+    assert call(ydt=g.Q8_1, N=48) == g.ERR_INVALID                  # N' % 32
+    assert call(ydt=g.Q8_1, N=64, epi=g.EPI_SWIGLU, ws_bytes=64) == g.ERR_WORKSPACE   # N' = 32 passes
     ws_small = L.ggq_mul_mat_id_ws(g.Q4_K, 256, 1024, 2048, g.BF16, 16, 0, 8, 1, 0, 0)
     ws_big = L.ggq_mul_mat_id_ws(g.Q4_K, 256, 1024, 2048, g.BF16, 8192, 0, 8, 1, 0, 0)
     assert 0 < ws_small < ws_big

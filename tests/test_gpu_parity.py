@@ -383,14 +383,95 @@ def test_moe_swiglu_and_weighted_gather(dev, path):
     assert r <= TOL["f32"]
 
 
+def _bits(y):
+    """Output tensor as the oracle's input array: bf16 bits (uint16) or float32."""
+    if y.dtype == torch.bfloat16:
+        return y.view(torch.int16).cpu().numpy().view(np.uint16)
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("path", ["mmvq", "mmq"])
+@pytest.mark.parametrize("epi", [g.EPI_NONE, g.EPI_SWIGLU])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_moe_q8_1_output(dev, path, epi, xdt):
+    """q8_1 output: each route's outputs as q8_1 blocks, equal bit for bit to the
+    oracle's q8_1 of the same call's plain output (bf16 for bf16 input, else
+    fp32).  Tiles cover partial weight tiles (N' = 160 and 192); inactive and
+    out-of-range routes give all-zero blocks."""
+    E, K, Tn, top_k = 9, 512, 41, 4
+    N = 320 if epi == g.EPI_SWIGLU else 192
+    Np = N // 2 if epi == g.EPI_SWIGLU else N
+    W = inputs.gen_experts(g.Q4_K, E, N, K, 530)
+    x = inputs.gen_act(Tn, K, 531, xdt)
+    ids = inputs.rng(532).integers(0, 6, (Tn, top_k)).astype(np.int32)
+    ids[0] = [2, 2, 2, 2]
+    ids[1, 1] = -1
+    ids[2, 3] = 40                                                      # >= E
+    kind = torch.bfloat16 if xdt == "bf16" else torch.float32
+    args = (T(W, dev), g.Q4_K, T(x, dev), T(ids, dev), K)
+    y = g.mul_mat_id(*args, epi=epi, out_dtype=kind, path=path)
+    q = g.mul_mat_id(*args, epi=epi, out_dtype="q8_1", path=path)
+    R = Tn * top_k
+    want = oracle.quantize_q8_1(_bits(y).reshape(R, Np))
+    got = q.cpu().numpy().reshape(R, -1)
+    log("q8_1 out", path, epi, xdt, "blocks equal:", np.array_equal(got, want))
+    assert np.array_equal(got, want)
+    dead = ((ids < 0) | (ids >= E)).reshape(R)
+    assert (got[dead] == 0).all()
+    ref = _moe_ref(g.Q4_K, W, K, x, ids, top_k, epi=epi)
+    assert rel(host(y), ref_out(ref, "bf16" if xdt == "bf16" else "f32")) <= TOL["bf16" if xdt == "bf16" else "f32"]
+
+
+@pytest.mark.parametrize("path", ["mmvq", "mmq"])
+@pytest.mark.parametrize("x_per_route", [False, True])
+def test_moe_q8_1_input(dev, path, x_per_route):
+    """q8_1 activations in: the same result as the oracle on the float rows
+    those blocks are the quantization of (identical q8_1 decisions)."""
+    E, N, K, Tn, top_k = 16, 256, 512, 45, 4
+    W = inputs.gen_experts(g.Q6_K, E, N, K, 540)
+    ids, w = inputs.gen_routing(Tn, E, top_k, 541)
+    ids[3, 0] = -1
+    rows = Tn * top_k if x_per_route else Tn
+    x = inputs.gen_act(rows, K, 542, "bf16")
+    q8 = oracle.quantize_q8_1(x)
+    xq = T(q8, dev).view(Tn, top_k, -1) if x_per_route else T(q8, dev)
+    xf = x.reshape(Tn, top_k, K) if x_per_route else x
+    y = g.mul_mat_id(T(W, dev), g.Q6_K, xq, T(ids, dev), K, x_per_route=x_per_route, out_dtype=torch.float32,
+                     path=path)
+    r = rel(host(y), _moe_ref(g.Q6_K, W, K, xf, ids, top_k, x_per_route=x_per_route))
+    yw = g.mul_mat_id(T(W, dev), g.Q6_K, xq, T(ids, dev), K, route_w=T(w, dev), x_per_route=x_per_route,
+                      out_dtype=torch.float32, path=path)
+    rw = rel(host(yw), _moe_ref(g.Q6_K, W, K, xf, ids, top_k, route_w=w, x_per_route=x_per_route))
+    log("q8_1 in", path, x_per_route, r, rw)
+    assert r <= TOL["f32"] and rw <= TOL["f32"]
+
+
+@pytest.mark.parametrize("path", ["mmvq", "mmq"])
+def test_moe_layer_q8_1_chain(dev, path):
+    """gate_up with SwiGLU straight to q8_1, then the weighted down projection
+    from those blocks: the same bits as the chain through a bf16 h."""
+    E, H, I, Tn, top_k = 16, 512, 256, 45, 4
+    Wgu = T(inputs.gen_experts(g.Q4_K, E, 2 * I, H, 550), dev)
+    Wd = T(inputs.gen_experts(g.Q6_K, E, H, I, 551), dev)
+    x = T(inputs.gen_act(Tn, H, 552, "bf16"), dev)
+    ids, w = inputs.gen_routing(Tn, E, top_k, 553)
+    ids, w = T(ids, dev), T(w, dev)
+    h = g.mul_mat_id(Wgu, g.Q4_K, x, ids, H, epi=g.EPI_SWIGLU, path=path)
+    y0 = g.mul_mat_id(Wd, g.Q6_K, h, ids, I, route_w=w, x_per_route=True, path=path)
+    hq = g.mul_mat_id(Wgu, g.Q4_K, x, ids, H, epi=g.EPI_SWIGLU, out_dtype="q8_1", path=path)
+    y1 = g.mul_mat_id(Wd, g.Q6_K, hq, ids, I, route_w=w, x_per_route=True, out_dtype=torch.bfloat16, path=path)
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
 def _c5(dev, Tn, path, tokens=None):
     E, H, I, top_k = 256, 2048, 512, 8
     Wgu = inputs.gen_experts(g.Q4_K, E, 2 * I, H, 501)
     Wd = inputs.gen_experts(g.Q6_K, E, H, I, 502)
     x = inputs.gen_act(Tn, H, 503, "bf16")
     ids, w = inputs.gen_routing(Tn, E, top_k, 504)
-    h = g.mul_mat_id(T(Wgu, dev), g.Q4_K, T(x, dev), T(ids, dev), H, epi=g.EPI_SWIGLU, path=path)
-    y = g.mul_mat_id(T(Wd, dev), g.Q6_K, h, T(ids, dev), I, route_w=T(w, dev), x_per_route=True, path=path)
+    Wgu_t, Wd_t, x_t, ids_t, w_t = T(Wgu, dev), T(Wd, dev), T(x, dev), T(ids, dev), T(w, dev)
+    h = g.mul_mat_id(Wgu_t, g.Q4_K, x_t, ids_t, H, epi=g.EPI_SWIGLU, path=path)
+    y = g.mul_mat_id(Wd_t, g.Q6_K, h, ids_t, I, route_w=w_t, x_per_route=True, path=path)
     hh = host(h)
     yh = host(y)
     sel = slice(None) if tokens is None else tokens
@@ -402,6 +483,11 @@ def _c5(dev, Tn, path, tokens=None):
     r_y = rel(yh[sel], ref_out(y_ref32, "bf16"))
     log(f"C5 T={Tn} path={path} gate_up rel={r_h:.3g} down rel={r_y:.3g}")
     assert r_h <= TOL["bf16"] and r_y <= TOL["bf16"]
+    # the layer through q8_1 h (fused quantization in the gate_up epilogue): the same bits
+    hq = g.mul_mat_id(Wgu_t, g.Q4_K, x_t, ids_t, H, epi=g.EPI_SWIGLU, out_dtype="q8_1", path=path)
+    assert np.array_equal(hq.cpu().numpy().reshape(Tn * top_k, -1), oracle.quantize_q8_1(h_gpu.reshape(Tn * top_k, I)))
+    yq = g.mul_mat_id(Wd_t, g.Q6_K, hq, ids_t, I, route_w=w_t, x_per_route=True, out_dtype=torch.bfloat16, path=path)
+    assert torch.equal(yq.view(torch.int16), y.view(torch.int16))
 
 
 def test_c5_moe_t16(dev):
