@@ -401,9 +401,10 @@ def main():
             log(f"{name} 4096x4096 decode M=1")
             r = bench_decode(ctx, wt, 4096, 4096, 1, 201, 202, torch.bfloat16, K, W)
             also.append({"workload": f"{name}_4096x4096_decode", "M": 1, **r})
-        log("q5_K 8192x2048 prefill M=8192")
-        r = bench_prefill(ctx, g.Q5_K, 8192, 2048, 8192, 301, 302, torch.bfloat16, max(5, K // 20), max(2, W // 10))
-        also.append({"workload": "q5_K_8192x2048_prefill", "M": 8192, **r})
+        for wt, name in ((g.Q5_K, "q5_K"), (g.Q8_0, "q8_0"), (g.Q4_0, "q4_0")):
+            log(f"{name} 8192x2048 prefill M=8192")
+            r = bench_prefill(ctx, wt, 8192, 2048, 8192, 301, 302, torch.bfloat16, max(5, K // 20), max(2, W // 10))
+            also.append({"workload": f"{name}_8192x2048_prefill", "M": 8192, **r})
     if "getrows" in sel:
         log("q6_K 248320x2048 get_rows n=8192")
         r = bench_get_rows(ctx, g.Q6_K, 248320, 2048, 8192, 401, 404, torch.bfloat16, max(20, K // 4), W)

@@ -32,8 +32,11 @@ const char *tname(int t) {
 }
 
 bool known_type(int t) { return t == GGQ_Q4_0 || t == GGQ_Q8_0 || t == GGQ_Q4_K || t == GGQ_Q5_K || t == GGQ_Q6_K; }
-// MMQ kernels exist for the super-block types; the 32-weight-block types run MMVQ at any M.
-bool has_mmq(int t) { return t == GGQ_Q4_K || t == GGQ_Q5_K || t == GGQ_Q6_K; }
+// MMQ kernels: every type; Q8_0 / Q4_0 (32-weight blocks) when K is a multiple of
+// 256 (the kernel stages activation scales 8 blocks at a time).
+bool has_mmq(int t, int64_t K) {
+    return t == GGQ_Q4_K || t == GGQ_Q5_K || t == GGQ_Q6_K || ((t == GGQ_Q8_0 || t == GGQ_Q4_0) && K % 256 == 0);
+}
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -67,21 +70,21 @@ Planar carve_planar(Carve &c, int64_t rows, int64_t K) {
     return p;
 }
 
-// Dense dispatch: MMVQ for up to 8 activation rows (and always for Q8_0), MMQ above.
+// Dense dispatch: MMVQ for up to 8 activation rows, MMQ above (when it has a kernel for the type and K).
 constexpr int64_t MMVQ_MAX_ROWS = 8;
 // Routed dispatch: MMVQ-id up to this many tokens, MMQ-id above.
 constexpr int64_t MMVQ_ID_MAX_TOKENS = 32;
 
-bool use_mmq(int wt, int64_t M, int path) {
+bool use_mmq(int wt, int64_t K, int64_t M, int path) {
     if (path == GGQ_PATH_MMQ) return true;
     if (path == GGQ_PATH_MMVQ) return false;
-    return has_mmq(wt) && M > MMVQ_MAX_ROWS;
+    return has_mmq(wt, K) && M > MMVQ_MAX_ROWS;
 }
 
-bool use_mmq_id(int wt, int64_t T, int path) {
+bool use_mmq_id(int wt, int64_t K, int64_t T, int path) {
     if (path == GGQ_PATH_MMQ) return true;
     if (path == GGQ_PATH_MMVQ) return false;
-    return has_mmq(wt) && T > MMVQ_ID_MAX_TOKENS;
+    return has_mmq(wt, K) && T > MMVQ_ID_MAX_TOKENS;
 }
 
 int check_weights(int wt, int64_t N, int64_t K) {
@@ -163,7 +166,7 @@ int ggq_get_rows(int wt, const void *W, int64_t rows, int64_t K, const int32_t *
 
 size_t ggq_mul_mat_ws(int wt, int64_t N, int64_t K, int xdt, int64_t M, int path) {
     if (!known_type(wt) || M <= 0 || N <= 0 || K <= 0 || K % block_len(wt)) return 0;
-    return act_bytes(use_mmq(wt, M, path), M, K);
+    return act_bytes(use_mmq(wt, K, M, path), M, K);
 }
 
 int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int xdt, int64_t M, int64_t ldx, void *y,
@@ -174,7 +177,8 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
     if (xdt != GGQ_F32 && xdt != GGQ_BF16 && xdt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: input dtype %d", xdt);
     if (ydt != GGQ_F32 && ydt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: output dtype %d must be F32 or BF16", ydt);
     if (path != GGQ_PATH_AUTO && path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "mul_mat: bad path %d", path);
-    if (path == GGQ_PATH_MMQ && !has_mmq(wt)) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: MMQ path has no %s kernel; use MMVQ", tname(wt));
+    if (path == GGQ_PATH_MMQ && !has_mmq(wt, K))
+        return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: MMQ path has no %s kernel for K=%lld (Q8_0 / Q4_0 need K %% 256 == 0); use MMVQ", tname(wt), (long long)K);
     if (M < 0) return fail(GGQ_ERR_INVALID, "mul_mat: M=%lld < 0", (long long)M);
     if (xdt != GGQ_Q8_1 && ldx < K) return fail(GGQ_ERR_INVALID, "mul_mat: ldx=%lld < K=%lld", (long long)ldx, (long long)K);
     if (ldy < N) return fail(GGQ_ERR_INVALID, "mul_mat: ldy=%lld < N=%lld", (long long)ldy, (long long)N);
@@ -185,7 +189,7 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
     if (ws_bytes < need || (need && !ws)) return fail(GGQ_ERR_WORKSPACE, "mul_mat: workspace %zu bytes < %zu required", ws_bytes, need);
     if (need && !aligned16(ws)) return fail(GGQ_ERR_INVALID, "mul_mat: workspace must be 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool mmq = use_mmq(wt, M, path);
+    const bool mmq = use_mmq(wt, K, M, path);
     const int64_t rb = (int64_t)ggq_row_bytes(wt, K);
     Carve c(ws);
     if (!mmq) {
@@ -276,7 +280,7 @@ size_t ggq_mul_mat_id_ws(int wt, int64_t E, int64_t N, int64_t K, int xdt, int64
                          int epi, int weighted, int path) {
     (void)xdt;
     if (!known_type(wt) || E <= 0 || N <= 0 || K <= 0 || K % block_len(wt) || T < 0 || top_k <= 0) return 0;
-    return id_layout(nullptr, wt, E, N, K, T, x_per_route, top_k, epi, weighted != 0, use_mmq_id(wt, T, path)).total;
+    return id_layout(nullptr, wt, E, N, K, T, x_per_route, top_k, epi, weighted != 0, use_mmq_id(wt, K, T, path)).total;
 }
 
 int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64_t expert_stride, const void *x, int xdt,
@@ -293,7 +297,8 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     if (ydt == GGQ_Q8_1 && (epi == GGQ_EPI_SWIGLU ? N / 2 : N) % QK8_1)
         return fail(GGQ_ERR_INVALID, "mul_mat_id: q8_1 output needs output rows N'=%lld divisible by 32", (long long)(epi == GGQ_EPI_SWIGLU ? N / 2 : N));
     if (path != GGQ_PATH_AUTO && path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad path %d", path);
-    if (path == GGQ_PATH_MMQ && !has_mmq(wt)) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: MMQ path has no %s kernel; use MMVQ", tname(wt));
+    if (path == GGQ_PATH_MMQ && !has_mmq(wt, K))
+        return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: MMQ path has no %s kernel for K=%lld (Q8_0 / Q4_0 need K %% 256 == 0); use MMVQ", tname(wt), (long long)K);
     if (E <= 0 || T < 0 || top_k <= 0) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad E=%lld T=%lld top_k=%lld", (long long)E, (long long)T, (long long)top_k);
     if (x_per_route != 0 && x_per_route != 1) return fail(GGQ_ERR_INVALID, "mul_mat_id: x_per_route must be 0 or 1");
     const int64_t rb = (int64_t)ggq_row_bytes(wt, K);
@@ -302,7 +307,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     if (T == 0 || N == 0) return GGQ_OK;
     if (!W || !x || !ids || !y) return fail(GGQ_ERR_INVALID, "mul_mat_id: null pointer");
     if (!aligned16(W) || !aligned16(x) || !aligned16(y) || !aligned16(ids)) return fail(GGQ_ERR_INVALID, "mul_mat_id: pointers must be 16-byte aligned");
-    const bool mmq = use_mmq_id(wt, T, path);
+    const bool mmq = use_mmq_id(wt, K, T, path);
     const bool weighted = route_w != nullptr;
     IdLayout L = id_layout(ws, wt, E, N, K, T, x_per_route, top_k, epi, weighted, mmq);
     if (!ws || ws_bytes < L.total) return fail(GGQ_ERR_WORKSPACE, "mul_mat_id: workspace %zu bytes < %zu required", ws_bytes, L.total);
@@ -401,7 +406,8 @@ int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K, const void 
     int rc = check_weights(wt, N, K);
     if (rc) return rc;
     if (path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "test_block_dots: path must be MMVQ or MMQ");
-    if (path == GGQ_PATH_MMQ && !has_mmq(wt)) return fail(GGQ_ERR_UNSUPPORTED, "test_block_dots: MMQ path has no %s kernel", tname(wt));
+    if (path == GGQ_PATH_MMQ && !has_mmq(wt, K))
+        return fail(GGQ_ERR_UNSUPPORTED, "test_block_dots: MMQ path has no %s kernel for K=%lld", tname(wt), (long long)K);
     if (M < 0) return fail(GGQ_ERR_INVALID, "test_block_dots: M < 0");
     if (M == 0 || N == 0) return GGQ_OK;
     if (!W || !q8 || !out) return fail(GGQ_ERR_INVALID, "test_block_dots: null pointer");

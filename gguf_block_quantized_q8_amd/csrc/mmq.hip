@@ -11,7 +11,9 @@
 // fp16 parts), the MFMA sums
 // the block's dot in fp32 exactly, and one fma per output per block remains
 // (times the activation scale d8).  Every product and partial sum is an
-// integer below 2^24, so the per-block dot is exact, as with int8.
+// integer below 2^24, so the per-block dot is exact, as with int8.  Q8_0 and
+// Q4_0 carry their fp16 scale per 32-weight block: their staged operand is the
+// plain quant (q, or nibble - 8), and each stage applies d * d8 per output.
 //
 // Tiles: 128 weight rows x 128 activation rows per workgroup, 4 waves of
 // 64 x 64 (2 x 2 MFMA 32x32x16 tiles).  K advances one q8_1 block (32) per
@@ -29,6 +31,9 @@ namespace ggq {
 constexpr int NT = MMQ_NT, MT = MMQ_MT, KS = 32, LDA = KS + 8, LDM = 40;
 constexpr int EPI_NONE_ = 0, EPI_SWIGLU_ = 1;
 
+// Q8_0 / Q4_0: one fp16 weight scale per 32-weight block, i.e. per stage.
+template <int T> constexpr bool kBlk32 = T == T_Q8_0 || T == T_Q4_0;
+
 template <int T>
 struct __attribute__((aligned(16))) MmqSmem {
     static constexpr int NA = T == T_Q6_K ? 2 : 1;       // Q6_K: high and low parts of sc*(q-32)
@@ -36,7 +41,7 @@ struct __attribute__((aligned(16))) MmqSmem {
     _Float16 A[2][NA][NT][LDA];   // two stage buffers
     _Float16 B[2][MT][LDA];
     float d8[2][8][MT];           // by super-block parity; [block][column]: conflict-free column reads
-    float wd[NT];
+    float wd[kBlk32<T> ? 2 : 1][NT];   // K-quants: d of the super-block; Q8_0 / Q4_0: d of the stage's block
     float wdmin[NT];
     __bf16 Amin[NMIN ? NT : 1][LDM];
     __bf16 Bmin[NMIN ? MT : 1][LDM];
@@ -99,8 +104,9 @@ struct Stager {
     const float *xd, *xs;     // d, s of this thread's activation row + 4 * half
     v4i hdr;        // Q4_K / Q5_K: block header (d, dmin, 12 scale bytes); Q6_K: the 16 int8 scales
     v4i q0, q1;     // Q4_K: 16 quant bytes (q0); Q5_K: also 16 fifth-bit bytes (q1);
-                    // Q6_K: 16 ql bytes (q0), 16 qh bytes (q1)
-    uint32_t d6;    // Q6_K: fp16 d
+                    // Q6_K: 16 ql bytes (q0), 16 qh bytes (q1); Q8_0: this half's 16 int8 quants;
+                    // Q4_0: the block's 16 nibble bytes (both halves)
+    uint32_t d6;    // Q6_K, Q8_0, Q4_0: fp16 d
     v4i b0, b1;     // 16 fp16 activation quants
     v4f m;          // stage 0 of a super-block: 4 d8; stage 1 (Q4_K, Q5_K): 4 s8
 
@@ -126,6 +132,14 @@ struct Stager {
             hdr = gld16(blk);
             q0 = gld16(blk + 48 + 32 * (j >> 1) + 16 * hf);
             q1 = gld16(blk + 16 + 16 * hf);                         // fifth bits of positions 16 hf ..
+        } else if (T == T_Q8_0) {
+            const uint8_t *blk = wrow + (int64_t)s * 34;           // one block per stage
+            q0 = ld16_a2(blk + 2 + 16 * hf);
+            d6 = ld_u16(blk);
+        } else if (T == T_Q4_0) {
+            const uint8_t *blk = wrow + (int64_t)s * 18;
+            q0 = ld16_a2(blk + 2);                                  // weights l (low nibble) and l + 16 (high)
+            d6 = ld_u16(blk);
         } else {
             const uint8_t *blk = wrow + (int64_t)sb * 210;
             const int hh = j >> 2, g = j & 3;
@@ -145,7 +159,23 @@ struct Stager {
         const int tid = threadIdx.x, tr = tid >> 1, hf = tid & 1;
         const int sb = s >> 3, j = s & 7, buf = s & 1;
         // ---- weights: fp16 of sub-scale x quant, built in packed halves ----
-        if (HAS_MIN) {
+        if (kBlk32<T>) {
+            // Q8_0: q + 128 as a byte, read as fp16 1024 + byte, minus 1152; Q4_0: nibble - 8 likewise
+            const _Float16 off = (_Float16)(T == T_Q8_0 ? -1152.0f : -1032.0f);
+            const h2v off2 = {off, off};
+            uint32_t o[8];
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                const uint32_t x = T == T_Q8_0 ? (uint32_t)q0[w] ^ 0x80808080u
+                                               : (hf ? ((uint32_t)q0[w] >> 4) : (uint32_t)q0[w]) & 0x0f0f0f0fu;
+                o[2 * w] = h2_bits(as_h2(__builtin_amdgcn_perm(x, 0x64646464u, 0x00050004u)) + off2);
+                o[2 * w + 1] = h2_bits(as_h2(__builtin_amdgcn_perm(x, 0x64646464u, 0x00070006u)) + off2);
+            }
+            v4i *dst = reinterpret_cast<v4i *>(&sm.A[buf][0][tr][16 * hf]);
+            dst[0] = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+            dst[1] = v4i{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+            if (!UNIT && hf == 0) sm.wd[buf][tr] = fp16_bits_to_f32(d6);
+        } else if (HAS_MIN) {
             uint32_t sc_lo, sc_hi, mn_lo, mn_hi;
             q4k_pack((uint32_t)hdr.y, (uint32_t)hdr.z, (uint32_t)hdr.w, sc_lo, sc_hi, mn_lo, mn_hi);
             const int sc = UNIT ? 1 : (int)__builtin_amdgcn_ubfe(j < 4 ? sc_lo : sc_hi, 8 * (j & 3), 8);
@@ -205,13 +235,13 @@ struct Stager {
         // ---- per super-block scales ----
         if (j == 0)
             for (int i = 0; i < 4; i++) sm.d8[sb & 1][4 * hf + i][tr] = m[i];
-        if (j == 1) {
+        if (j == 1 && !kBlk32<T>) {
             if (hf == 0) {
                 if (HAS_MIN) {
-                    sm.wd[tr] = fp16_bits_to_f32((uint32_t)hdr.x & 0xffffu);
+                    sm.wd[0][tr] = fp16_bits_to_f32((uint32_t)hdr.x & 0xffffu);
                     sm.wdmin[tr] = fp16_bits_to_f32((uint32_t)hdr.x >> 16);
                 } else {
-                    sm.wd[tr] = fp16_bits_to_f32(d6);
+                    sm.wd[0][tr] = fp16_bits_to_f32(d6);
                 }
             }
             if (HAS_MIN) {
@@ -438,6 +468,22 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
                     for (int mi = 0; mi < 2; mi++) C[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[mi], C[mi], 0, 0, 0);
                 }
             }
+            if (kBlk32<T>) {
+                // the block's weight scale per row, straight into acc: rows 8 q + 4 h + i of the half-tile
+                const float *dwr = &sm.wd[buf][64 * wn + 32 * ni + 4 * (lane >> 5)];
+#pragma unroll
+                for (int mi = 0; mi < 2; mi++) {
+                    const float d8 = sm.d8[(s >> 3) & 1][j][64 * wm + 32 * mi + lr];
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const v4f dw = *reinterpret_cast<const v4f *>(dwr + 8 * q);
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            acc[ni][mi][4 * q + i] = __builtin_fmaf(C[mi][4 * q + i], d8 * dw[i], acc[ni][mi][4 * q + i]);
+                    }
+                }
+                continue;
+            }
 #pragma unroll
             for (int mi = 0; mi < 2; mi++) {
                 const float d8 = sm.d8[(s >> 3) & 1][j][64 * wm + 32 * mi + lr];
@@ -450,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
                 }
             }
         }
-        if (j == 7) {
+        if (j == 7 && !kBlk32<T>) {
             // ---- end of super-block: P * d (- dmin * min term) into acc ----
             if (MmqSmem<T>::NMIN) {
                 // one weight half-tile (ni) at a time: 32 registers of min-term sums live, not 64
@@ -470,7 +516,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
 #pragma unroll
                     for (int e = 0; e < 16; e++) {
                         const int tr = 64 * wn + 32 * ni + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                        const float d = sm.wd[tr], dm = sm.wdmin[tr];
+                        const float d = sm.wd[0][tr], dm = sm.wdmin[tr];
 #pragma unroll
                         for (int mi = 0; mi < 2; mi++) {
                             acc[ni][mi][e] = __builtin_fmaf(P[ni][mi][e], d, acc[ni][mi][e]);
@@ -484,7 +530,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
 #pragma unroll
                     for (int e = 0; e < 16; e++) {
                         const int tr = 64 * wn + 32 * ni + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                        const float d = sm.wd[tr];
+                        const float d = sm.wd[0][tr];
 #pragma unroll
                         for (int mi = 0; mi < 2; mi++) {
                             acc[ni][mi][e] = __builtin_fmaf(P[ni][mi][e], d, acc[ni][mi][e]);
@@ -559,7 +605,7 @@ __global__ __launch_bounds__(256) void mmq_dots_kernel(const uint8_t *__restrict
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wn = wave & 1, wm = wave >> 1;
     const int64_t bm = (int64_t)blockIdx.x % m_tiles, bn = (int64_t)blockIdx.x / m_tiles;
-    const int64_t row_bytes = K / 256 * Geom<T>::BYTES;
+    const int64_t row_bytes = K / Geom<T>::QK * Geom<T>::BYTES;
     if (tid < MT) {
         const int64_t m = bm * MT + tid;
         sm.xrow[tid] = m < M ? (int32_t)m : -1;
@@ -638,6 +684,8 @@ hipError_t launch_mmq(int t, bool moe, int epi, int ydt, const MmqParams &p, hip
     if (t == T_Q4_K) launch_t<T_Q4_K>(moe, epi, ydt, p, s);
     else if (t == T_Q6_K) launch_t<T_Q6_K>(moe, epi, ydt, p, s);
     else if (t == T_Q5_K) launch_t<T_Q5_K>(moe, epi, ydt, p, s);
+    else if (t == T_Q8_0) launch_t<T_Q8_0>(moe, epi, ydt, p, s);
+    else if (t == T_Q4_0) launch_t<T_Q4_0>(moe, epi, ydt, p, s);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
@@ -650,6 +698,8 @@ hipError_t launch_mmq_dots(int t, const uint8_t *W, int64_t N, int64_t K, const 
     if (t == T_Q4_K) hipLaunchKernelGGL(mmq_dots_kernel<T_Q4_K>, g, b, 0, s, W, N, K, xq, M, mt, out);
     else if (t == T_Q6_K) hipLaunchKernelGGL(mmq_dots_kernel<T_Q6_K>, g, b, 0, s, W, N, K, xq, M, mt, out);
     else if (t == T_Q5_K) hipLaunchKernelGGL(mmq_dots_kernel<T_Q5_K>, g, b, 0, s, W, N, K, xq, M, mt, out);
+    else if (t == T_Q8_0) hipLaunchKernelGGL(mmq_dots_kernel<T_Q8_0>, g, b, 0, s, W, N, K, xq, M, mt, out);
+    else if (t == T_Q4_0) hipLaunchKernelGGL(mmq_dots_kernel<T_Q4_0>, g, b, 0, s, W, N, K, xq, M, mt, out);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -80,8 +80,8 @@ int ggq_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx,
  *         not written.
  *   ws  : workspace of at least ggq_mul_mat_ws(...) bytes (may be NULL when
  *         that is 0).
- *   path: AUTO, or force MMVQ / MMQ (MMQ: Q4_K, Q5_K and Q6_K only; Q4_0
- *         and Q8_0 run MMVQ at every M).
+ *   path: AUTO, or force MMVQ / MMQ (MMQ: every type; for Q4_0 and Q8_0
+ *         only when K % 256 == 0, else AUTO takes MMVQ at every M).
  * fp32 accumulation; per-block integer dots are exact. */
 size_t ggq_mul_mat_ws(int wt, int64_t N, int64_t K, int xdt, int64_t M, int path);
 int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
@@ -163,7 +163,7 @@ const char *ggq_last_error(void);
  * minus 8), Q4_K / Q5_K (values without the min); g = 16 for Q6_K: values
  * minus 32), computed by the same device unpack and dot code as the named
  * path (GGQ_PATH_MMVQ: the v_dot4 units; GGQ_PATH_MMQ: the staged fp16 tiles
- * and the MFMA, Q4_K / Q5_K / Q6_K only).
+ * and the MFMA, Q4_0 / Q8_0 with K % 256 == 0).
  * q8 is M rows of K/32 q8_1 blocks; ws needs ggq_test_block_dots_ws() bytes. */
 size_t ggq_test_block_dots_ws(int wt, int64_t K, int64_t M, int path);
 int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K,

@@ -77,9 +77,12 @@ def test_bad_strides_and_pointers(L):
 def test_bad_dtypes_and_paths(L):
     assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, 7, 1, 256, FAKE, g.F32, 16, None, 0, 0, None) == g.ERR_UNSUPPORTED
     assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, g.F32, 1, 256, FAKE, g.Q8_1, 16, None, 0, 0, None) == g.ERR_UNSUPPORTED
-    assert L.ggq_mul_mat(g.Q8_0, FAKE, 16, 256, FAKE, g.F32, 64, 256, FAKE, g.F32, 16, None, 0, g.PATH_MMQ, None) == g.ERR_UNSUPPORTED
-    assert L.ggq_mul_mat(g.Q4_0, FAKE, 16, 256, FAKE, g.F32, 64, 256, FAKE, g.F32, 16, None, 0, g.PATH_MMQ, None) == g.ERR_UNSUPPORTED
-    assert L.ggq_mul_mat_ws(g.Q4_0, 16, 256, g.F32, 4096, g.PATH_AUTO) == 0   # Q4_0 runs MMVQ at any M
+    # MMQ for the 32-weight-block types needs K % 256 == 0
+    assert L.ggq_mul_mat(g.Q8_0, FAKE, 16, 288, FAKE, g.F32, 64, 288, FAKE, g.F32, 16, None, 0, g.PATH_MMQ, None) == g.ERR_UNSUPPORTED
+    assert L.ggq_mul_mat(g.Q4_0, FAKE, 16, 288, FAKE, g.F32, 64, 288, FAKE, g.F32, 16, None, 0, g.PATH_MMQ, None) == g.ERR_UNSUPPORTED
+    assert L.ggq_mul_mat_ws(g.Q8_0, 16, 256, g.F32, 64, g.PATH_AUTO) > 0          # MMQ (planar operand)
+    assert L.ggq_mul_mat_ws(g.Q8_0, 16, 288, g.F32, 64, g.PATH_AUTO) == 0         # MMVQ
+    assert L.ggq_mul_mat_ws(g.Q4_0, 16, 288, g.F32, 4096, g.PATH_AUTO) == 0   # K % 256 != 0: MMVQ at any M
     assert L.ggq_mul_mat(g.Q4_K, FAKE, 16, 256, FAKE, g.F32, 1, 256, FAKE, g.F32, 16, None, 0, 9, None) == g.ERR_INVALID
 
 

@@ -135,7 +135,8 @@ def test_get_rows_empty_and_errors(dev):
 # ------------------------------------------------------------------ per-group int dots
 
 @pytest.mark.parametrize("wt,path", [(g.Q8_0, "mmvq"), (g.Q4_K, "mmvq"), (g.Q6_K, "mmvq"), (g.Q4_K, "mmq"), (g.Q6_K, "mmq"),
-                                     (g.Q4_0, "mmvq"), (g.Q5_K, "mmvq"), (g.Q5_K, "mmq")])
+                                     (g.Q4_0, "mmvq"), (g.Q5_K, "mmvq"), (g.Q5_K, "mmq"), (g.Q8_0, "mmq"),
+                                     (g.Q4_0, "mmq")])
 def test_block_dots_bit_exact(dev, wt, path):
     log("dots", wt, path)
     N, K, M = 131, (512 if wt == g.Q8_0 else 768), 133      # ragged against the 128 x 128 MMQ tiles
@@ -186,24 +187,38 @@ def test_mmvq_short_rows(dev, wt, K):
 
 
 def test_mmvq_many_columns(dev):
-    """M above the 8 columns of one MMVQ group (Q8_0 and Q4_0 always take MMVQ)."""
-    _check_mul_mat(dev, g.Q8_0, 64, 256, 21, "f32", "f32", "auto", 60)
-    _check_mul_mat(dev, g.Q4_0, 64, 256, 21, "f32", "f32", "auto", 61)
+    """M above the 8 columns of one MMVQ group; Q8_0 / Q4_0 with K not a multiple of
+    256 take MMVQ at any M under AUTO."""
+    _check_mul_mat(dev, g.Q8_0, 64, 256, 21, "f32", "f32", "mmvq", 60)
+    _check_mul_mat(dev, g.Q4_0, 64, 256, 21, "f32", "f32", "mmvq", 61)
+    _check_mul_mat(dev, g.Q8_0, 64, 288, 21, "f32", "f32", "auto", 62)
+    _check_mul_mat(dev, g.Q4_0, 64, 288, 21, "f32", "f32", "auto", 63)
 
 
-@pytest.mark.parametrize("wt", [g.Q4_0, g.Q5_K])
+@pytest.mark.parametrize("path", ["mmvq", "mmq"])
+def test_q8_0_full_int8_range(dev, path):
+    """Q8_0 quants of -128 (a valid int8 that the [-127, 127] draw never makes)."""
+    W = inputs.gen_q8_0(100, 512, 64)
+    blocks = W.reshape(-1, 34)
+    rng = inputs.rng(65)
+    hit = rng.random((blocks.shape[0], 32)) < 0.2
+    q = blocks[:, 2:].view(np.int8)
+    q[hit] = -128
+    _check_mul_mat(dev, g.Q8_0, 100, 512, 40, "f32", "f32", path, 66, W=W)
+
+
+@pytest.mark.parametrize("wt", [g.Q4_0, g.Q5_K, g.Q8_0])
 def test_new_types_decode_shape(dev, wt):
     """The 4096 x 4096 decode shape (bf16 in and out) at M = 1 and 8, and a prefill-sized
-    MMQ call for Q5_K, sampled rows against the oracle."""
+    MMQ call, sampled rows against the oracle."""
     W = inputs.gen_weights(wt, 4096, 4096, 90 + wt)
     for M in (1, 8):
         _check_mul_mat(dev, wt, 4096, 4096, M, "bf16", "bf16", "auto", 91 + wt + M, W=W)
-    if wt == g.Q5_K:
-        rows = inputs.sample_rows(4096, 128, 95)
-        _check_mul_mat(dev, wt, 4096, 4096, 512, "bf16", "bf16", "mmq", 96, rows=rows, W=W)
+    rows = inputs.sample_rows(4096, 128, 95)
+    _check_mul_mat(dev, wt, 4096, 4096, 512, "bf16", "bf16", "auto", 96, rows=rows, W=W)
 
 
-@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K, g.Q5_K])
+@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K, g.Q5_K, g.Q8_0, g.Q4_0])
 @pytest.mark.parametrize("M,N,K", [(1, 5, 256), (40, 100, 512), (129, 257, 768), (300, 128, 1024)])
 @pytest.mark.parametrize("ydt", ["f32", "bf16"])
 def test_mmq_small_ragged(dev, wt, M, N, K, ydt):
@@ -308,7 +323,8 @@ def _moe_ref(wt, W, K, x, ids, top_k, route_w=None, epi=oracle.EPI_NONE, x_per_r
 
 
 @pytest.mark.parametrize("path,wt", [("mmvq", g.Q4_K), ("mmq", g.Q4_K), ("mmvq", g.Q6_K), ("mmq", g.Q6_K),
-                                     ("mmvq", g.Q5_K), ("mmq", g.Q5_K), ("mmvq", g.Q4_0)])
+                                     ("mmvq", g.Q5_K), ("mmq", g.Q5_K), ("mmvq", g.Q4_0), ("mmq", g.Q4_0),
+                                     ("mmvq", g.Q8_0), ("mmq", g.Q8_0)])
 def test_moe_edge_routes(dev, path, wt):
     """Duplicate ids in a token, inactive (-1) and out-of-range ids, experts with no routes."""
     E, N, K, Tn, top_k = 9, 96, 512, 37, 4
