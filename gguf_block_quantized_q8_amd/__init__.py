@@ -13,7 +13,7 @@ import os
 import torch
 
 Q4_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 8, 12, 13, 14
-F32, BF16, Q8_1 = 0, 1, 2
+F32, BF16, Q8_1, F16 = 0, 1, 2, 3
 PATH_AUTO, PATH_MMVQ, PATH_MMQ = 0, 1, 2
 EPI_NONE, EPI_SWIGLU = 0, 1
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
@@ -96,9 +96,11 @@ def _xdt(x):
         return F32
     if x.dtype == torch.bfloat16:
         return BF16
+    if x.dtype == torch.float16:
+        return F16
     if x.dtype == torch.uint8:
         return Q8_1
-    raise TypeError(f"activations must be float32, bfloat16 or uint8 q8_1 blocks, got {x.dtype}")
+    raise TypeError(f"activations must be float32, bfloat16, float16 or uint8 q8_1 blocks, got {x.dtype}")
 
 
 def _ydt(dtype):
@@ -106,7 +108,9 @@ def _ydt(dtype):
         return F32
     if dtype == torch.bfloat16:
         return BF16
-    raise TypeError(f"output dtype must be float32 or bfloat16, got {dtype}")
+    if dtype == torch.float16:
+        return F16
+    raise TypeError(f"output dtype must be float32, bfloat16 or float16, got {dtype}")
 
 
 def _check_gpu(*ts):

@@ -37,6 +37,10 @@ bool known_type(int t) { return t == GGQ_Q4_0 || t == GGQ_Q8_0 || t == GGQ_Q4_K 
 bool has_mmq(int t, int64_t K) {
     return t == GGQ_Q4_K || t == GGQ_Q5_K || t == GGQ_Q6_K || ((t == GGQ_Q8_0 || t == GGQ_Q4_0) && K % 256 == 0);
 }
+// Float element types of activations and outputs: fp32, bf16, fp16.
+bool float_dt(int dt) { return dt == GGQ_F32 || dt == GGQ_BF16 || dt == GGQ_F16; }
+// Kernel instantiation for an output dtype: the 16-bit ones share one (fp16 by flag).
+int kernel_dt(int dt) { return dt == GGQ_F16 ? GGQ_BF16 : dt; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -123,7 +127,7 @@ size_t ggq_q8_1_bytes(int64_t M, int64_t K) {
 
 int ggq_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, void *q8, void *stream) {
     g_err[0] = 0;
-    if (xdt != GGQ_F32 && xdt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "quantize_q8_1: input dtype %d must be F32 or BF16", xdt);
+    if (!float_dt(xdt)) return fail(GGQ_ERR_UNSUPPORTED, "quantize_q8_1: input dtype %d must be F32, BF16 or F16", xdt);
     if (M < 0 || K < 0 || K % 32) return fail(GGQ_ERR_INVALID, "quantize_q8_1: K=%lld must be a non-negative multiple of 32", (long long)K);
     if (ldx < K) return fail(GGQ_ERR_INVALID, "quantize_q8_1: ldx=%lld < K=%lld", (long long)ldx, (long long)K);
     if (M == 0 || K == 0) return GGQ_OK;
@@ -137,7 +141,7 @@ int ggq_dequantize(int wt, const void *W, int64_t rows, int64_t K, void *y, int 
     g_err[0] = 0;
     int rc = check_weights(wt, rows, K);
     if (rc) return rc;
-    if (ydt != GGQ_F32 && ydt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "dequantize: output dtype %d must be F32 or BF16", ydt);
+    if (!float_dt(ydt)) return fail(GGQ_ERR_UNSUPPORTED, "dequantize: output dtype %d must be F32, BF16 or F16", ydt);
     if (rows == 0) return GGQ_OK;
     if (!W || !y) return fail(GGQ_ERR_INVALID, "dequantize: null pointer");
     if (!aligned16(W) || !aligned16(y)) return fail(GGQ_ERR_INVALID, "dequantize: pointers must be 16-byte aligned");
@@ -151,7 +155,7 @@ int ggq_get_rows(int wt, const void *W, int64_t rows, int64_t K, const int32_t *
     g_err[0] = 0;
     int rc = check_weights(wt, rows, K);
     if (rc) return rc;
-    if (ydt != GGQ_F32 && ydt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "get_rows: output dtype %d must be F32 or BF16", ydt);
+    if (!float_dt(ydt)) return fail(GGQ_ERR_UNSUPPORTED, "get_rows: output dtype %d must be F32, BF16 or F16", ydt);
     if (n < 0) return fail(GGQ_ERR_INVALID, "get_rows: n=%lld < 0", (long long)n);
     if (ldy < K) return fail(GGQ_ERR_INVALID, "get_rows: ldy=%lld < K=%lld", (long long)ldy, (long long)K);
     if (ldy % (ydt == GGQ_F32 ? 4 : 8))
@@ -174,8 +178,8 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
     g_err[0] = 0;
     int rc = check_weights(wt, N, K);
     if (rc) return rc;
-    if (xdt != GGQ_F32 && xdt != GGQ_BF16 && xdt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: input dtype %d", xdt);
-    if (ydt != GGQ_F32 && ydt != GGQ_BF16) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: output dtype %d must be F32 or BF16", ydt);
+    if (!float_dt(xdt) && xdt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: input dtype %d", xdt);
+    if (!float_dt(ydt)) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: output dtype %d must be F32, BF16 or F16", ydt);
     if (path != GGQ_PATH_AUTO && path != GGQ_PATH_MMVQ && path != GGQ_PATH_MMQ) return fail(GGQ_ERR_INVALID, "mul_mat: bad path %d", path);
     if (path == GGQ_PATH_MMQ && !has_mmq(wt, K))
         return fail(GGQ_ERR_UNSUPPORTED, "mul_mat: MMQ path has no %s kernel for K=%lld (Q8_0 / Q4_0 need K %% 256 == 0); use MMVQ", tname(wt), (long long)K);
@@ -210,9 +214,10 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
         p.M = M;
         p.y = y;
         p.ldy = ldy;
+        p.y_f16 = ydt == GGQ_F16;
         p.w_bytes = N * rb;
         const int nc = std::min(nc_for(M), mmvq_max_cols(wt, K));
-        return hip_status(launch_mmvq(wt, nc, false, GGQ_EPI_NONE, ydt, p, (M + nc - 1) / nc, s), "mul_mat mmvq");
+        return hip_status(launch_mmvq(wt, nc, false, GGQ_EPI_NONE, kernel_dt(ydt), p, (M + nc - 1) / nc, s), "mul_mat mmvq");
     }
     Planar pl = carve_planar(c, M, K);
     if (xdt == GGQ_Q8_1) rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), M, K, pl.xq, pl.xd, pl.xs, s), "mul_mat expand");
@@ -232,7 +237,8 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
     p.n_tiles = (N + MMQ_NT - 1) / MMQ_NT;
     p.y = y;
     p.ldy = ldy;
-    return hip_status(launch_mmq(wt, false, GGQ_EPI_NONE, ydt, p, s), "mul_mat mmq");
+    p.y_f16 = ydt == GGQ_F16;
+    return hip_status(launch_mmq(wt, false, GGQ_EPI_NONE, kernel_dt(ydt), p, s), "mul_mat mmq");
 }
 
 // ---------------------------------------------------------------------------
@@ -289,8 +295,8 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     g_err[0] = 0;
     int rc = check_weights(wt, N, K);
     if (rc) return rc;
-    if (xdt != GGQ_F32 && xdt != GGQ_BF16 && xdt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: input dtype %d", xdt);
-    if (ydt != GGQ_F32 && ydt != GGQ_BF16 && ydt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: output dtype %d", ydt);
+    if (!float_dt(xdt) && xdt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: input dtype %d", xdt);
+    if (!float_dt(ydt) && ydt != GGQ_Q8_1) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: output dtype %d", ydt);
     if (epi != GGQ_EPI_NONE && epi != GGQ_EPI_SWIGLU) return fail(GGQ_ERR_INVALID, "mul_mat_id: bad epilogue %d", epi);
     if (epi == GGQ_EPI_SWIGLU && N % 2) return fail(GGQ_ERR_INVALID, "mul_mat_id: SwiGLU needs an even N (gate rows then up rows), N=%lld", (long long)N);
     if (ydt == GGQ_Q8_1 && route_w) return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: q8_1 output is per route (route_w must be NULL)");
@@ -320,10 +326,10 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     const int J = mmq ? MMQ_MT : mmvq_id_cols(wt, R, E, K);
     rc = hip_status(launch_route_build(ids, R, E, J, L.rt, s), "mul_mat_id routes");
     if (rc) return rc;
-    // q8_1 output: MMQ quantizes in its epilogue; MMVQ writes the values (fp32,
-    // or bf16 for bf16 input) to the workspace and the q8_1 kernel follows
+    // q8_1 output: MMQ quantizes in its epilogue; MMVQ writes the values (in the
+    // 16-bit input's dtype, else fp32) to the workspace and the q8_1 kernel follows
     const bool q8_out = ydt == GGQ_Q8_1;
-    const int hdt = xdt == GGQ_BF16 ? GGQ_BF16 : GGQ_F32;
+    const int hdt = xdt == GGQ_BF16 || xdt == GGQ_F16 ? xdt : GGQ_F32;
     void *yk = q8_out && !mmq ? L.hstage : y;               // what the matmul kernel writes
     const int ydt_k = q8_out && !mmq ? hdt : ydt;
     if (!weighted) {
@@ -347,6 +353,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.q8_row = (K / 32) * Q8_1_BYTES;
         p.x_bytes = xdt == GGQ_Q8_1 ? rows * p.q8_row : rows * K * (xdt == GGQ_F32 ? 4 : 2);
         p.y = yk;
+        p.y_f16 = ydt_k == GGQ_F16;
         p.perm = L.rt.perm;
         p.groups = L.rt.tiles;
         p.ngroups = L.rt.ntiles;
@@ -356,7 +363,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.o32 = L.o32;
         p.groups_expected = std::min<int64_t>(E, R);
         p.w_bytes = (E - 1) * expert_stride + N * rb;
-        rc = hip_status(launch_mmvq(wt, J, true, epi, ydt_k, p, L.max_tiles, s), "mul_mat_id mmvq");
+        rc = hip_status(launch_mmvq(wt, J, true, epi, kernel_dt(ydt_k), p, L.max_tiles, s), "mul_mat_id mmvq");
         if (!rc && q8_out)
             rc = hip_status(launch_quantize(L.hstage, hdt, R, Np, Np, static_cast<uint8_t *>(y), nullptr, nullptr, nullptr, s),
                             "mul_mat_id q8_1 output");
@@ -387,8 +394,9 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.x_per_route = x_per_route;
         p.route_w = route_w;
         p.o32 = L.o32;
-        p.q8_bf16 = q8_out && hdt == GGQ_BF16;
-        rc = hip_status(launch_mmq(wt, true, epi, ydt, p, s), "mul_mat_id mmq");
+        p.q8_round = !q8_out ? 0 : hdt == GGQ_BF16 ? 1 : hdt == GGQ_F16 ? 2 : 0;
+        p.y_f16 = ydt == GGQ_F16;
+        rc = hip_status(launch_mmq(wt, true, epi, kernel_dt(ydt), p, s), "mul_mat_id mmq");
     }
     if (rc) return rc;
     if (weighted) rc = hip_status(launch_route_sum(L.o32, ids, route_w, T, (int)top_k, E, Np, y, ydt, s), "mul_mat_id route sum");

@@ -8,7 +8,7 @@
 namespace ggq {
 
 enum : int { T_Q4_0 = 2, T_Q8_0 = 8, T_Q4_K = 12, T_Q5_K = 13, T_Q6_K = 14 };
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_Q8_1 = 2 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_Q8_1 = 2, DT_F16 = 3 };
 
 constexpr int QK8_1 = 32;
 constexpr int Q8_1_BYTES = 40;   // float d, float s, int8 qs[32]
@@ -52,6 +52,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
+// fp32 -> IEEE binary16 bits, round to nearest even (v_cvt_f16_f32 in the
+// default rounding mode, subnormal halves kept); past the largest finite half
+// the result is inf.
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+// 16-bit elements: fp16 when h, else bf16.
+__device__ __forceinline__ uint32_t f32_to_16(float f, bool h) { return h ? f32_to_f16_bits(f) : f32_to_bf16_bits(f); }
+__device__ __forceinline__ float from_16(uint32_t b, bool h) { return h ? fp16_bits_to_f32(b) : bf16_bits_to_f32(b & 0xffffu); }
 
 // q8_1 quant of one value of a block whose largest magnitude is amax, with
 // d = amax / 127: x / d (IEEE fp32 division) rounded half away from zero; an

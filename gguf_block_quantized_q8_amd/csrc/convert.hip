@@ -36,16 +36,17 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const void *__restri
             } else {
                 for (int i = 0; i < 4; i++) v[i] = xf[i];
             }
-        } else {
+        } else {                           // bf16 or fp16
+            const bool h = XDT == DT_F16;
             const uint16_t *xb = static_cast<const uint16_t *>(x) + e0;
             if (VEC) {
                 v2i t = *reinterpret_cast<const v2i *>(xb);
-                v[0] = bf16_bits_to_f32((uint32_t)t.x & 0xffffu);
-                v[1] = bf16_bits_to_f32((uint32_t)t.x >> 16);
-                v[2] = bf16_bits_to_f32((uint32_t)t.y & 0xffffu);
-                v[3] = bf16_bits_to_f32((uint32_t)t.y >> 16);
+                v[0] = from_16((uint32_t)t.x & 0xffffu, h);
+                v[1] = from_16((uint32_t)t.x >> 16, h);
+                v[2] = from_16((uint32_t)t.y & 0xffffu, h);
+                v[3] = from_16((uint32_t)t.y >> 16, h);
             } else {
-                for (int i = 0; i < 4; i++) v[i] = bf16_bits_to_f32(xb[i]);
+                for (int i = 0; i < 4; i++) v[i] = from_16(xb[i], h);
             }
         }
     }
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
         for (int i = 0; i < 2; i++) {
             v4i t;
             for (int k = 0; k < 4; k++)
-                t[k] = (int)(f32_to_bf16_bits(w[8 * i + 2 * k]) | (f32_to_bf16_bits(w[8 * i + 2 * k + 1]) << 16));
+                t[k] = (int)(f32_to_16(w[8 * i + 2 * k], YDT == DT_F16) | (f32_to_16(w[8 * i + 2 * k + 1], YDT == DT_F16) << 16));
             yo[i] = t;
         }
     }
@@ -242,13 +243,14 @@ __global__ __launch_bounds__(256) void route_sum_kernel(const float *__restrict_
             if (YDT == DT_F32) {
                 *reinterpret_cast<v4f *>(static_cast<float *>(y) + idx) = v4f{acc[0], acc[1], acc[2], acc[3]};
             } else {
-                const v2i b = {(int)(f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16)),
-                               (int)(f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16))};
+                const bool h = YDT == DT_F16;
+                const v2i b = {(int)(f32_to_16(acc[0], h) | (f32_to_16(acc[1], h) << 16)),
+                               (int)(f32_to_16(acc[2], h) | (f32_to_16(acc[3], h) << 16))};
                 *reinterpret_cast<v2i *>(static_cast<uint16_t *>(y) + idx) = b;
             }
         } else {
             if (YDT == DT_F32) static_cast<float *>(y)[idx] = acc[0];
-            else static_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_bf16_bits(acc[0]);
+            else static_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_16(acc[0], YDT == DT_F16);
         }
     }
 }
@@ -290,6 +292,9 @@ hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t
     if (xdt == DT_F32) {
         if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
         else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
+    } else if (xdt == DT_F16) {
+        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
+        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
     } else {
         if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
         else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
@@ -313,6 +318,7 @@ hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, cons
 #define GGQ_DQ(TT)                                                                                                    \
     if (t == TT) {                                                                                                    \
         if (ydt == DT_F32) hipLaunchKernelGGL((dequant_kernel<TT, DT_F32>), g, b, 0, s, W, rows, K, ids, n, y, ldy);   \
+        else if (ydt == DT_F16) hipLaunchKernelGGL((dequant_kernel<TT, DT_F16>), g, b, 0, s, W, rows, K, ids, n, y, ldy); \
         else hipLaunchKernelGGL((dequant_kernel<TT, DT_BF16>), g, b, 0, s, W, rows, K, ids, n, y, ldy);               \
     }
     GGQ_DQ(T_Q4_0) GGQ_DQ(T_Q8_0) GGQ_DQ(T_Q4_K) GGQ_DQ(T_Q5_K) GGQ_DQ(T_Q6_K)
@@ -336,6 +342,9 @@ hipError_t launch_route_sum(const float *o, const int32_t *ids, const float *w, 
     if (ydt == DT_F32) {
         if (vec) hipLaunchKernelGGL((route_sum_kernel<DT_F32, 4>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
         else hipLaunchKernelGGL((route_sum_kernel<DT_F32, 1>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
+    } else if (ydt == DT_F16) {
+        if (vec) hipLaunchKernelGGL((route_sum_kernel<DT_F16, 4>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
+        else hipLaunchKernelGGL((route_sum_kernel<DT_F16, 1>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
     } else {
         if (vec) hipLaunchKernelGGL((route_sum_kernel<DT_BF16, 4>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
         else hipLaunchKernelGGL((route_sum_kernel<DT_BF16, 1>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
@@ -347,7 +356,8 @@ hipError_t launch_zero_inactive(const int32_t *ids, int64_t R, int64_t E, int64_
                                 hipStream_t s) {
     if (R == 0) return hipSuccess;
     if (ydt == DT_F32) hipLaunchKernelGGL(zero_inactive_kernel<DT_F32>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
-    else if (ydt == DT_BF16) hipLaunchKernelGGL(zero_inactive_kernel<DT_BF16>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
+    else if (ydt == DT_BF16 || ydt == DT_F16)                                     // 16-bit zeros
+        hipLaunchKernelGGL(zero_inactive_kernel<DT_BF16>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
     else hipLaunchKernelGGL(zero_inactive_kernel<DT_Q8_1>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
     return hipGetLastError();
 }

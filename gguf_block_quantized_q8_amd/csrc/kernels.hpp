@@ -70,6 +70,7 @@ struct MmvqParams {
     int x_per_route;
     const float *route_w;
     float *o32;           // weighted: per-route fp32 outputs [R][Np]
+    int y_f16;            // 16-bit output is fp16 (else bf16)
     int64_t groups_expected;   // routed: expected active groups (min(E, routes))
     // set by the launcher
     int64_t w_bytes;        // readable weight bytes from W (N*row_bytes, or up to the last expert's last row)
@@ -115,7 +116,8 @@ struct MmqParams {
     int x_per_route;
     const float *route_w;
     float *o32;           // weighted: per-route fp32 outputs [R][Np]
-    int q8_bf16;          // q8_1 output: round the values to bf16 before quantizing
+    int q8_round;         // q8_1 output: round the values to bf16 (1) or fp16 (2) before quantizing
+    int y_f16;            // 16-bit output is fp16 (else bf16)
 };
 constexpr int MMQ_NT = 128;   // weight rows per workgroup tile
 constexpr int MMQ_MT = 128;   // activation rows (routes) per workgroup tile

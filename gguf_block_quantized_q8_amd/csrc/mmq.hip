@@ -274,8 +274,9 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
+// YDT: DT_F32, or a 16-bit output (fp16 when h, else bf16).
 template <int YDT>
-__device__ __forceinline__ void store4(void *y, int64_t idx, const float *v, int n_valid) {
+__device__ __forceinline__ void store4(void *y, int64_t idx, const float *v, int n_valid, bool h = false) {
     if (YDT == DT_F32) {
         float *o = static_cast<float *>(y) + idx;
         if (n_valid == 4 && (idx & 3) == 0) *reinterpret_cast<v4f *>(o) = v4f{v[0], v[1], v[2], v[3]};
@@ -283,11 +284,11 @@ __device__ __forceinline__ void store4(void *y, int64_t idx, const float *v, int
     } else {
         uint16_t *o = static_cast<uint16_t *>(y) + idx;
         if (n_valid == 4 && (idx & 3) == 0) {
-            v2i t = {(int)(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16)),
-                     (int)(f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16))};
+            v2i t = {(int)(f32_to_16(v[0], h) | (f32_to_16(v[1], h) << 16)),
+                     (int)(f32_to_16(v[2], h) | (f32_to_16(v[3], h) << 16))};
             *reinterpret_cast<v2i *>(o) = t;
         } else {
-            for (int i = 0; i < n_valid; i++) o[i] = (uint16_t)f32_to_bf16_bits(v[i]);
+            for (int i = 0; i < n_valid; i++) o[i] = (uint16_t)f32_to_16(v[i], h);
         }
     }
 }
@@ -313,8 +314,8 @@ __device__ __forceinline__ void tile_of(int64_t b, int64_t m_tiles, int64_t n_ti
 // 32 consecutive outputs of one route: one 32-row MFMA tile row group of one
 // column, held 16 + 16 by lanes l and l + 32 (rows 8g + 4h + i, h = lane / 32),
 // so its amax and quant sum take one lane exchange.  The values are those the
-// fp32 / bf16 epilogue would store (SwiGLU applied, rounded to bf16 first when
-// p.q8_bf16), quantized as the q8_1 kernel does.
+// plain epilogue would store (SwiGLU applied, rounded first to bf16 or fp16
+// per p.q8_round), quantized as the q8_1 kernel does.
 template <int EPI, int T>
 __device__ __forceinline__ void store_q8_1(const MmqParams &p, const MmqSmem<T> &sm, const v16f (&acc)[2][2],
                                            int64_t bn, int tile_count, int wn, int wm, int lane) {
@@ -339,7 +340,7 @@ __device__ __forceinline__ void store_q8_1(const MmqParams &p, const MmqSmem<T> 
                 } else {
                     o = acc[bi][mi][e];
                 }
-                if (p.q8_bf16) o = bf16_bits_to_f32(f32_to_bf16_bits(o));
+                if (p.q8_round) o = from_16(f32_to_16(o, p.q8_round == 2), p.q8_round == 2);
                 v[e] = o;
                 amax = fmaxf(amax, fabsf(o));
             }
@@ -561,7 +562,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
                     if (n0 >= p.N) continue;
                     const int nv = (int)min<int64_t>(4, p.N - n0);
                     float v[4] = {acc[ni][mi][4 * g], acc[ni][mi][4 * g + 1], acc[ni][mi][4 * g + 2], acc[ni][mi][4 * g + 3]};
-                    store4<YDT>(p.y, (int64_t)xr * p.ldy + n0, v, nv);
+                    store4<YDT>(p.y, (int64_t)xr * p.ldy + n0, v, nv, p.y_f16);
                 }
             } else {
                 // weighted: per-route fp32 outputs, summed per token afterwards
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
                         h[i] = gt / (1.0f + expf(-gt)) * up;
                     }
                     if (p.o32) store4<DT_F32>(p.o32, r * p.Np + n0, h, nv);
-                    else store4<YDT>(p.y, r * p.Np + n0, h, nv);
+                    else store4<YDT>(p.y, r * p.Np + n0, h, nv, p.y_f16);
                 } else {
 #pragma unroll
                     for (int ni = 0; ni < 2; ni++) {
@@ -586,7 +587,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
                         const int nv = (int)min<int64_t>(4, p.N - n0);
                         float v[4] = {acc[ni][mi][4 * g], acc[ni][mi][4 * g + 1], acc[ni][mi][4 * g + 2], acc[ni][mi][4 * g + 3]};
                         if (p.o32) store4<DT_F32>(p.o32, r * p.Np + n0, v, nv);
-                        else store4<YDT>(p.y, r * p.Np + n0, v, nv);
+                        else store4<YDT>(p.y, r * p.Np + n0, v, nv, p.y_f16);
                     }
                 }
             }

@@ -350,21 +350,22 @@ struct Unit<T_Q4_0, NC> {
     }
 };
 
+// YDT: DT_F32, or a 16-bit output (fp16 when h, else bf16).
 template <int YDT>
-__device__ __forceinline__ void store_out(void *y, int64_t idx, float v) {
+__device__ __forceinline__ void store_out(void *y, int64_t idx, float v, bool h) {
     if (YDT == DT_F32) static_cast<float *>(y)[idx] = v;
-    else static_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_bf16_bits(v);
+    else static_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_16(v, h);
 }
 
 // Outputs idx and idx + 1 (both valid): one store when they are aligned together.
 template <int YDT>
-__device__ __forceinline__ void store_out2(void *y, int64_t idx, float v0, float v1) {
+__device__ __forceinline__ void store_out2(void *y, int64_t idx, float v0, float v1, bool h) {
     if ((idx & 1) == 0) {
         if (YDT == DT_F32) *reinterpret_cast<v2i *>(static_cast<float *>(y) + idx) = v2i{__builtin_bit_cast(int, v0), __builtin_bit_cast(int, v1)};
-        else *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(y) + idx) = f32_to_bf16_bits(v0) | (f32_to_bf16_bits(v1) << 16);
+        else *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(y) + idx) = f32_to_16(v0, h) | (f32_to_16(v1, h) << 16);
     } else {
-        store_out<YDT>(y, idx, v0);
-        store_out<YDT>(y, idx + 1, v1);
+        store_out<YDT>(y, idx, v0, h);
+        store_out<YDT>(y, idx + 1, v1, h);
     }
 }
 
@@ -460,10 +461,11 @@ struct ActStage {
             if (p.xsrc == DT_F32) {
                 v[0] = as_float(lo.x); v[1] = as_float(lo.y); v[2] = as_float(hi.x); v[3] = as_float(hi.y);
             } else {
-                v[0] = bf16_bits_to_f32((uint32_t)lo.x & 0xffffu);
-                v[1] = bf16_bits_to_f32((uint32_t)lo.x >> 16);
-                v[2] = bf16_bits_to_f32((uint32_t)lo.y & 0xffffu);
-                v[3] = bf16_bits_to_f32((uint32_t)lo.y >> 16);
+                const bool h = p.xsrc == DT_F16;
+                v[0] = from_16((uint32_t)lo.x & 0xffffu, h);
+                v[1] = from_16((uint32_t)lo.x >> 16, h);
+                v[2] = from_16((uint32_t)lo.y & 0xffffu, h);
+                v[3] = from_16((uint32_t)lo.y >> 16, h);
             }
             const float amax = max8(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
             const float d = amax / 127.0f;
@@ -820,21 +822,21 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
                 if (c >= ncols) break;
                 if (!MOE) {
                     const int64_t col = xrow[c];
-                    if (v1) store_out2<YDT>(p.y, col * p.ldy + r0, acc[0][c], acc[1][c]);   // r1 = r0 + 1
-                    else store_out<YDT>(p.y, col * p.ldy + r0, acc[0][c]);
+                    if (v1) store_out2<YDT>(p.y, col * p.ldy + r0, acc[0][c], acc[1][c], p.y_f16);   // r1 = r0 + 1
+                    else store_out<YDT>(p.y, col * p.ldy + r0, acc[0][c], p.y_f16);
                 } else {
                     // weighted: per-route fp32 outputs, summed per token afterwards
                     const int64_t r = route_s[c];
                     if (EPI == EPI_SWIGLU) {
                         const float h = silu_mul(acc[0][c], acc[1][c]);
                         if (p.o32) p.o32[r * p.Np + r0] = h;
-                        else store_out<YDT>(p.y, r * p.Np + r0, h);
+                        else store_out<YDT>(p.y, r * p.Np + r0, h, p.y_f16);
                     } else if (p.o32) {
                         p.o32[r * p.Np + r0] = acc[0][c];
                         if (v1) p.o32[r * p.Np + r1] = acc[1][c];
                     } else {
-                        store_out<YDT>(p.y, r * p.Np + r0, acc[0][c]);
-                        if (v1) store_out<YDT>(p.y, r * p.Np + r1, acc[1][c]);
+                        store_out<YDT>(p.y, r * p.Np + r0, acc[0][c], p.y_f16);
+                        if (v1) store_out<YDT>(p.y, r * p.Np + r1, acc[1][c], p.y_f16);
                     }
                 }
             }

@@ -16,7 +16,8 @@ Distributions (one numpy PCG64 stream per seed):
   * Q4_0 blocks: fp16 d ~ U(1e-3, 2e-2), 16 uniform random quant bytes.
   * Q5_K super-blocks: as Q4_K, plus 32 uniform random bytes of fifth bits.
   * Activations: fp32 N(0, 1); bf16 activations are those fp32 values
-    rounded to bf16 by torch (returned as uint16 bit patterns).
+    rounded to bf16 by torch (returned as uint16 bit patterns); fp16
+    activations are them rounded to float16 by numpy.
   * Routing: router logits fp32 N(0, 1) [T, E] -> softmax in fp64 -> fp32
     probabilities; top-k by probability, ties to the lower expert id; the
     route weights are the top-k probabilities, not renormalized.
@@ -112,8 +113,11 @@ def to_bf16_bits(x):
 
 
 def gen_act(M, K, seed, dtype="f32"):
-    """Activations N(0,1): float32 [M, K] or bf16 bit patterns uint16 [M, K]."""
+    """Activations N(0,1): float32 [M, K], bf16 bit patterns uint16 [M, K], or float16 [M, K]
+    (numpy's round-to-nearest-even conversion)."""
     x = rng(seed).standard_normal((M, K), dtype=np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16)
     return x if dtype == "f32" else to_bf16_bits(x)
 
 

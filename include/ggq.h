@@ -21,8 +21,11 @@
  *   - Weights are row-major GGUF blocks: row n of an N x K matrix starts at
  *     byte n * ggq_row_bytes(type, K).  Kernels never read outside
  *     [W, W + N * row_bytes) (no tail padding needed); all offsets are 64-bit.
- *   - Element types: GGQ_F32 = IEEE fp32, GGQ_BF16 = bfloat16 (output rounded
- *     to nearest even), GGQ_Q8_1 = pre-quantized q8_1 blocks (input only).
+ *   - Element types: GGQ_F32 = IEEE fp32, GGQ_BF16 = bfloat16, GGQ_F16 = IEEE
+ *     binary16 (16-bit outputs rounded to nearest even from the fp32 result;
+ *     fp16 overflows to inf), GGQ_Q8_1 = q8_1 blocks (input; and the routed
+ *     output of ggq_mul_mat_id).  fp16 activations and outputs are among the
+ *     variants PR #690 serves ("What the ggml patch changes").
  *   - q8_1 block (40 bytes, 32 values): float d = amax/127 (fp32 division),
  *     float s = d * (sum of the quants), int8 qs[32] = x/d (fp32 division)
  *     rounded half away from zero; an all-zero block has d = s = 0.
@@ -43,7 +46,7 @@ extern "C" {
 
 /* GGUF tensor type ids (public GGUF numbering). */
 typedef enum { GGQ_Q4_0 = 2, GGQ_Q8_0 = 8, GGQ_Q4_K = 12, GGQ_Q5_K = 13, GGQ_Q6_K = 14 } ggq_type;
-typedef enum { GGQ_F32 = 0, GGQ_BF16 = 1, GGQ_Q8_1 = 2 } ggq_dtype;
+typedef enum { GGQ_F32 = 0, GGQ_BF16 = 1, GGQ_Q8_1 = 2, GGQ_F16 = 3 } ggq_dtype;
 /* Kernel choice: AUTO picks MMVQ for few activation rows, MMQ above. */
 typedef enum { GGQ_PATH_AUTO = 0, GGQ_PATH_MMVQ = 1, GGQ_PATH_MMQ = 2 } ggq_path;
 typedef enum { GGQ_EPI_NONE = 0, GGQ_EPI_SWIGLU = 1 } ggq_epilogue;
@@ -65,7 +68,7 @@ size_t ggq_q8_1_bytes(int64_t M, int64_t K);
 
 /* q8_1 quantization of activations (PR #690, "What the ggml patch changes":
  * activations quantized to q8_1 directly).
- *   x   : [M][ldx] elements of xdt (GGQ_F32 or GGQ_BF16); K % 32 == 0, ldx >= K.
+ *   x   : [M][ldx] elements of xdt (GGQ_F32, GGQ_BF16 or GGQ_F16); K % 32 == 0, ldx >= K.
  *   q8  : output, [M][K/32] blocks of 40 bytes (ggq_q8_1_bytes(M, K)).
  * Bit-exact: the same blocks as the definition above. */
 int ggq_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx,
@@ -73,10 +76,10 @@ int ggq_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx,
 
 /* Dense quantized matmul: y[m][n] = sum_k W[n][k] * x[m][k] for n < N.
  *   W   : N rows of K weights of type wt (Q4_0, Q8_0, Q4_K, Q5_K, Q6_K).
- *   x   : [M][ldx] of xdt (GGQ_F32 / GGQ_BF16), or, with xdt = GGQ_Q8_1,
+ *   x   : [M][ldx] of xdt (GGQ_F32 / GGQ_BF16 / GGQ_F16), or, with xdt = GGQ_Q8_1,
  *         M rows of K/32 q8_1 blocks (ldx ignored) -- one quantization can
  *         be reused for several weight matrices (PR #690, second item).
- *   y   : [M][ldy] of ydt (GGQ_F32 / GGQ_BF16), ldy >= N; columns >= N are
+ *   y   : [M][ldy] of ydt (GGQ_F32 / GGQ_BF16 / GGQ_F16), ldy >= N; columns >= N are
  *         not written.
  *   ws  : workspace of at least ggq_mul_mat_ws(...) bytes (may be NULL when
  *         that is 0).
@@ -98,7 +101,7 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
  *                  N * row_bytes and a multiple of 16.
  *   x            : x_per_route == 0: [T][K] (each route of token t uses x[t]);
  *                  x_per_route == 1: [T][top_k][K] (route (t,k) uses x[t][k]).
- *                  Element type xdt (GGQ_F32 / GGQ_BF16), rows contiguous; or
+ *                  Element type xdt (GGQ_F32 / GGQ_BF16 / GGQ_F16), rows contiguous; or
  *                  xdt = GGQ_Q8_1: the same rows as K/32 q8_1 blocks each.
  *   ids          : [T][top_k] int32 expert ids.  id < 0: inactive route
  *                  (contributes nothing).  id >= E: skipped and counted in
@@ -112,10 +115,11 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
  *                  in ascending k with fp32 accumulation (deterministic: the
  *                  per-route fp32 outputs go to the workspace, then one pass
  *                  sums them per token).
- *   y            : output of ydt (GGQ_F32 / GGQ_BF16), contiguous.  With
+ *   y            : output of ydt (GGQ_F32 / GGQ_BF16 / GGQ_F16), contiguous.  With
  *                  route_w == NULL, ydt may be GGQ_Q8_1 (N' % 32 == 0): y is
  *                  [T][top_k][N'/32] q8_1 blocks, the blocks ggq_quantize_q8_1
- *                  makes from the plain output (bf16 for bf16 x, else fp32),
+ *                  makes from the plain output (bf16 / fp16 for bf16 / fp16
+ *                  x, else fp32),
  *                  bit for bit -- the SwiGLU h in the down projection's own
  *                  input format (PR #690 keeps intermediates in the activation
  *                  dtype and quantizes activations straight to q8_1).  The MMQ
@@ -135,22 +139,22 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K,
                    void *ws, size_t ws_bytes, int path, void *stream);
 
 /* Dequantize (convert) rows of weights: y[r][k] = exact block value in fp32,
- * or its round-to-nearest-even bf16 (PR #690 lists dequantize among its ops).
- * y: [rows][K] of ydt (GGQ_F32 / GGQ_BF16).  Bit-exact. */
+ * or its round-to-nearest-even bf16 / fp16 (PR #690 lists dequantize among
+ * its ops).  y: [rows][K] of ydt (GGQ_F32 / GGQ_BF16 / GGQ_F16).  Bit-exact. */
 int ggq_dequantize(int wt, const void *W, int64_t rows, int64_t K,
                    void *y, int ydt, void *stream);
 
 /* Gather rows of a quantized table (embeddings, or a tied lm_head read as
  * rows), dequantized: y[i][k] = exact value of table row ids[i], weight k, in
- * fp32, or its round-to-nearest-even bf16 -- the same values as
+ * fp32, or its round-to-nearest-even bf16 / fp16 -- the same values as
  * ggq_dequantize (PR #690 lists get_rows among the ops its backend serves
  * next to the matmuls).
  *   W   : table of `rows` rows of ggq_row_bytes(wt, K) bytes, 16-byte aligned.
  *   ids : [n] int32 row ids, device memory.  An id outside [0, rows) gives a
  *         row of zeros (no fault, no error: ids are not read on the host).
- *   y   : [n][ldy] of ydt (GGQ_F32 / GGQ_BF16); writes K values per row;
- *         ldy >= K and ldy keeps rows 16-byte aligned (multiple of 4 for
- *         fp32, 8 for bf16).
+ *   y   : [n][ldy] of ydt (GGQ_F32 / GGQ_BF16 / GGQ_F16); writes K values
+ *         per row; ldy >= K and ldy keeps rows 16-byte aligned (multiple of 4
+ *         for fp32, 8 for the 16-bit types).
  * n = 0 is a no-op.  Bit-exact.  Returns GGQ_OK or an error code. */
 int ggq_get_rows(int wt, const void *W, int64_t rows, int64_t K, const int32_t *ids, int64_t n,
                  void *y, int ydt, int64_t ldy, void *stream);

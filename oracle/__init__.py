@@ -17,7 +17,7 @@ import numpy as np
 from . import build as _build
 
 Q4_0, Q8_0, Q4_K, Q5_K, Q6_K = 2, 8, 12, 13, 14
-F32, BF16, Q8_1 = 0, 1, 2
+F32, BF16, Q8_1, F16 = 0, 1, 2, 3
 EPI_NONE, EPI_SWIGLU = 0, 1
 Q8_1_BYTES = 40
 
@@ -38,6 +38,8 @@ def lib():
         L.ggqo_bf16_to_fp32.argtypes = [ctypes.c_uint16]
         L.ggqo_fp32_to_bf16.restype = ctypes.c_uint16
         L.ggqo_fp32_to_bf16.argtypes = [ctypes.c_float]
+        L.ggqo_fp32_to_fp16.restype = ctypes.c_uint16
+        L.ggqo_fp32_to_fp16.argtypes = [ctypes.c_float]
         for f in ("ggqo_block_len", "ggqo_block_bytes", "ggqo_group_len"):
             getattr(L, f).restype = i64
             getattr(L, f).argtypes = [i32]
@@ -78,7 +80,9 @@ def _dt(x):
         return F32
     if x.dtype == np.uint16:
         return BF16
-    raise TypeError("activations must be float32 or bf16 bits (uint16)")
+    if x.dtype == np.float16:
+        return F16
+    raise TypeError("activations must be float32, bf16 bits (uint16) or float16")
 
 
 def block_len(t):
@@ -107,6 +111,17 @@ def bf16_to_fp32(b):
 
 def fp32_to_bf16(f):
     return lib().ggqo_fp32_to_bf16(float(f))
+
+
+def fp32_to_fp16(f):
+    """IEEE binary16 bits (uint16) of float32 f, round to nearest even."""
+    return lib().ggqo_fp32_to_fp16(float(f))
+
+
+def fp32_to_fp16_array(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    f = lib().ggqo_fp32_to_fp16
+    return np.array([f(float(v)) for v in a.ravel()], dtype=np.uint16).reshape(a.shape)
 
 
 def fp32_to_bf16_array(a):
@@ -182,7 +197,7 @@ def mul_mat(t, W, N, K, x, rows=None, xdt=None):
 
 def dequantize(t, W, rows, K, ydt=F32):
     W = np.ascontiguousarray(W, dtype=np.uint8)
-    y = np.zeros((rows, K), dtype=np.float32 if ydt == F32 else np.uint16)
+    y = np.zeros((rows, K), dtype=np.float32 if ydt == F32 else np.uint16)   # 16-bit: bf16 / fp16 bits
     _check(lib().ggqo_dequantize(t, _p(W), rows, K, _p(y), ydt), "dequantize")
     return y
 

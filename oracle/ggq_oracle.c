@@ -47,6 +47,33 @@ float ggqo_bf16_to_fp32(uint16_t b) {
     return f;
 }
 
+/* binary32 -> IEEE binary16, round to nearest, ties to even.  The value is
+ * written as an integer count of the target's units in the last place and
+ * rounded with rint (the default rounding mode is to nearest even); counts
+ * are exact in double.  Normal range: a = n * 2^(e - 11) with n in
+ * [1024, 2048); subnormal range (a < 2^-14): a = n * 2^-24.  From 65520 (half
+ * a unit above the largest finite half, 65504) up the result is infinity;
+ * NaN gives a quiet NaN of the same sign. */
+uint16_t ggqo_fp32_to_fp16(float f) {
+    uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    float a = fabsf(f);
+    if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+    if (a >= 65520.0f) return (uint16_t)(sign | 0x7c00u);
+    if (a < ldexpf(1.0f, -14)) {
+        double n = rint((double)a * 16777216.0);   /* units of 2^-24; 1024 is the smallest normal */
+        return (uint16_t)(sign | (uint16_t)n);
+    }
+    int e;
+    frexp((double)a, &e);                             /* a = m * 2^e, m in [0.5, 1) */
+    double n = rint(ldexp((double)a, 11 - e));       /* in [1024, 2048] */
+    if (n == 2048.0) {
+        n = 1024.0;
+        e += 1;
+    }
+    unsigned field = (unsigned)(e - 1 + 15);          /* biased exponent, 1..30 here */
+    return (uint16_t)(sign | (field << 10) | ((unsigned)n - 1024u));
+}
+
 /* binary32 -> bfloat16, round to nearest, ties to even; NaN stays NaN. */
 uint16_t ggqo_fp32_to_bf16(float f) {
     uint32_t u;
@@ -140,12 +167,15 @@ void ggqo_quantize_block_q8_1(const float *x, uint8_t *blk) {
 
 static float load_act(const void *x, int xdt, int64_t idx) {
     if (xdt == GGQO_F32) return ((const float *)x)[idx];
+    if (xdt == GGQO_F16) return ggqo_fp16_to_fp32(((const uint16_t *)x)[idx]);
     return ggqo_bf16_to_fp32(((const uint16_t *)x)[idx]);
 }
 
+static int act_dt(int xdt) { return xdt == GGQO_F32 || xdt == GGQO_BF16 || xdt == GGQO_F16; }
+
 int ggqo_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, void *q8) {
     if (!x || !q8 || M < 0 || K < 0 || K % QK8_1 || ldx < K) return -1;
-    if (xdt != GGQO_F32 && xdt != GGQO_BF16) return -1;
+    if (!act_dt(xdt)) return -1;
     int64_t nb = K / QK8_1;
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; m++) {
@@ -409,7 +439,7 @@ int ggqo_mul_mat(int type, const void *W, int64_t N, int64_t K,
  * subtraction of the min. */
 int ggqo_dequantize(int type, const void *W, int64_t rows, int64_t K, void *y, int ydt) {
     if (!W || !y || !check_w(type, rows, K)) return -1;
-    if (ydt != GGQO_F32 && ydt != GGQO_BF16) return -1;
+    if (ydt != GGQO_F32 && ydt != GGQO_BF16 && ydt != GGQO_F16) return -1;
     int64_t qk = ggqo_block_len(type), bb = ggqo_block_bytes(type), g = ggqo_group_len(type);
     int64_t nblk = K / qk;
 #pragma omp parallel for schedule(static)
@@ -432,6 +462,7 @@ int ggqo_dequantize(int type, const void *W, int64_t rows, int64_t K, void *y, i
                 }
                 int64_t idx = r * K + b * qk + i;
                 if (ydt == GGQO_F32) ((float *)y)[idx] = w;
+                else if (ydt == GGQO_F16) ((uint16_t *)y)[idx] = ggqo_fp32_to_fp16(w);
                 else ((uint16_t *)y)[idx] = ggqo_fp32_to_bf16(w);
             }
         }
@@ -448,7 +479,7 @@ int ggqo_mul_mat_id(int type, const void *W, int64_t E, int64_t N, int64_t K, in
                     const int32_t *ids, int64_t top_k, const float *route_w, int epi,
                     const int64_t *tokens, int64_t ntok, float *y) {
     if (!W || !x || !ids || !y || E < 0 || T < 0 || top_k <= 0 || !check_w(type, N, K)) return -1;
-    if (xdt != GGQO_F32 && xdt != GGQO_BF16) return -1;
+    if (!act_dt(xdt)) return -1;
     if (epi != GGQO_EPI_NONE && epi != GGQO_EPI_SWIGLU) return -1;
     if (epi == GGQO_EPI_SWIGLU && N % 2) return -1;
     if (expert_stride < ggqo_row_bytes(type, K) * N) return -1;

@@ -44,7 +44,7 @@ extern "C" {
 /* GGUF tensor type ids (public GGUF numbering). */
 enum { GGQO_Q4_0 = 2, GGQO_Q8_0 = 8, GGQO_Q4_K = 12, GGQO_Q5_K = 13, GGQO_Q6_K = 14 };
 /* Activation / output element types.  GGQO_Q8_1 = pre-quantized blocks. */
-enum { GGQO_F32 = 0, GGQO_BF16 = 1, GGQO_Q8_1 = 2 };
+enum { GGQO_F32 = 0, GGQO_BF16 = 1, GGQO_Q8_1 = 2, GGQO_F16 = 3 };
 /* Epilogues of mul_mat_id. */
 enum { GGQO_EPI_NONE = 0, GGQO_EPI_SWIGLU = 1 };
 
@@ -52,6 +52,7 @@ enum { GGQO_EPI_NONE = 0, GGQO_EPI_SWIGLU = 1 };
 float    ggqo_fp16_to_fp32(uint16_t h);
 float    ggqo_bf16_to_fp32(uint16_t b);
 uint16_t ggqo_fp32_to_bf16(float f);
+uint16_t ggqo_fp32_to_fp16(float f);   /* round to nearest even, overflow to inf */
 
 /* ---- geometry ---- */
 int64_t ggqo_block_len(int type);    /* weights per block: 32 or 256, 0 if unknown */
@@ -62,7 +63,7 @@ int64_t ggqo_row_bytes(int type, int64_t K); /* 0 if K is not a multiple of the 
 /* ---- q8_1 ---- */
 /* One block: 32 fp32 values -> 40 bytes. */
 void ggqo_quantize_block_q8_1(const float *x32, uint8_t *blk40);
-/* x: [M][ldx] elements of type xdt (F32 or BF16 bits); q8: [M][K/32] blocks. */
+/* x: [M][ldx] elements of type xdt (F32, BF16 or F16 bits); q8: [M][K/32] blocks. */
 int ggqo_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, void *q8);
 
 /* ---- unpack ---- */
@@ -94,7 +95,7 @@ int ggqo_mul_mat_q8(int type, const void *W, int64_t N, int64_t K,
                     float *y, int64_t ldy);
 
 /* Full path from float activations: quantize each row to q8_1 then
- * ggqo_mul_mat_q8.  xdt: F32, BF16 or Q8_1 (then x is [M][K/32] blocks and
+ * ggqo_mul_mat_q8.  xdt: F32, BF16, F16 or Q8_1 (then x is [M][K/32] blocks and
  * ldx is ignored).  Output fp32 [M][ldy]. */
 int ggqo_mul_mat(int type, const void *W, int64_t N, int64_t K,
                  const void *x, int xdt, int64_t M, int64_t ldx,
@@ -102,13 +103,13 @@ int ggqo_mul_mat(int type, const void *W, int64_t N, int64_t K,
                  float *y, int64_t ldy);
 
 /* ---- dequantize ---- */
-/* y: [rows][K] of ydt (F32 or BF16 bits). */
+/* y: [rows][K] of ydt (F32, BF16 or F16 bits). */
 int ggqo_dequantize(int type, const void *W, int64_t rows, int64_t K, void *y, int ydt);
 
 /* ---- routed experts ---- */
 /* W: E experts, expert e at byte offset e*expert_stride, each N rows x K.
  * x: x_per_route == 0 -> [T][K] (broadcast), == 1 -> [T][top_k][K] (gather),
- *    elements of xdt (F32 or BF16).
+ *    elements of xdt (F32, BF16 or F16).
  * ids: [T][top_k]; a route with id < 0 or id >= E is inactive.
  * epi SWIGLU: o' = silu(o[:N/2]) * o[N/2:], computed in fp64 from the fp32
  *    route outputs and rounded to fp32; N' = N/2.  Otherwise N' = N.

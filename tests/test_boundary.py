@@ -114,8 +114,8 @@ def test_mul_mat_id_validation(L):
     assert call(ws_bytes=64) == g.ERR_WORKSPACE
     assert call(wt=g.Q8_0, K=64, path=g.PATH_MMQ) == g.ERR_UNSUPPORTED
     assert call(T=0) == g.OK
-    assert call(xdt=3) == g.ERR_UNSUPPORTED
-    assert call(ydt=3) == g.ERR_UNSUPPORTED
+    assert call(xdt=4) == g.ERR_UNSUPPORTED
+    assert call(ydt=4) == g.ERR_UNSUPPORTED
     assert call(ydt=g.Q8_1, route_w=FAKE) == g.ERR_UNSUPPORTED    # q8_1 output is per route
     assert call(ydt=g.Q8_1, N=48) == g.ERR_INVALID                  # N' % 32
     assert call(ydt=g.Q8_1, N=64, epi=g.EPI_SWIGLU, ws_bytes=64) == g.ERR_WORKSPACE   # N' = 32 passes

@@ -17,7 +17,7 @@ from gguf_block_quantized_q8_amd import inputs
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 8e-3}
+TOL = {"f32": 1e-5, "bf16": 8e-3, "f16": 1e-3}     # f16: two units of its 2^-10 relative spacing
 TYPES = [g.Q8_0, g.Q4_K, g.Q6_K, g.Q4_0, g.Q5_K]
 
 
@@ -48,6 +48,8 @@ def ref_out(y32, kind):
     """Oracle fp32 result as the output dtype would hold it."""
     if kind == "f32":
         return y32
+    if kind == "f16":
+        return oracle.fp32_to_fp16_array(y32).view(np.float16).astype(np.float32)
     return torch.from_numpy(y32).to(torch.bfloat16).float().numpy()
 
 
@@ -57,7 +59,7 @@ def log(*a):
 
 # ------------------------------------------------------------------ q8_1
 
-@pytest.mark.parametrize("xdt", ["f32", "bf16"])
+@pytest.mark.parametrize("xdt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("M,K,ldx", [(1, 32, 32), (7, 512, 512), (33, 2048, 2080), (300, 4096, 4096)])
 def test_quantize_bit_exact(dev, xdt, M, K, ldx):
     log("quantize", xdt, M, K, ldx)
@@ -82,7 +84,7 @@ def test_quantize_ties_and_scales(dev):
 # ------------------------------------------------------------------ dequantize
 
 @pytest.mark.parametrize("wt", TYPES)
-@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16, torch.float16])
 def test_dequantize_bit_exact(dev, wt, ydt):
     log("dequant", wt, ydt)
     K = 512 if wt == g.Q8_0 else 1024
@@ -91,7 +93,7 @@ def test_dequantize_bit_exact(dev, wt, ydt):
     if ydt == torch.float32:
         assert np.array_equal(host(y).view(np.uint32), oracle.dequantize(wt, W, 37, K).view(np.uint32))
     else:
-        ref = oracle.dequantize(wt, W, 37, K, oracle.BF16)
+        ref = oracle.dequantize(wt, W, 37, K, oracle.BF16 if ydt == torch.bfloat16 else oracle.F16)
         assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), ref)
 
 
@@ -105,7 +107,7 @@ def test_dequantize_q6_K_large_scales(dev):
 
 
 @pytest.mark.parametrize("wt", TYPES)
-@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16, torch.float16])
 def test_get_rows_bit_exact(dev, wt, ydt):
     """Gathered rows equal the oracle's dequantized table rows bit for bit; ids
     outside the table give zeros; repeated ids repeat the row."""
@@ -115,7 +117,7 @@ def test_get_rows_bit_exact(dev, wt, ydt):
     ids = inputs.rng(41).integers(-3, rows + 3, 97).astype(np.int32)
     ids[:4] = [0, rows - 1, 5, 5]
     y = g.get_rows(T(W, dev), wt, K, T(ids, dev), ydt)
-    kind = oracle.BF16 if ydt == torch.bfloat16 else oracle.F32
+    kind = {torch.bfloat16: oracle.BF16, torch.float16: oracle.F16, torch.float32: oracle.F32}[ydt]
     table = oracle.dequantize(wt, W, rows, K, kind)
     ok = (ids >= 0) & (ids < rows)
     ref = np.zeros((ids.size, K), table.dtype)
@@ -397,6 +399,51 @@ def test_moe_swiglu_and_weighted_gather(dev, path):
     r = rel(host(y), _moe_ref(g.Q6_K, Wd, I, h_in, ids, top_k, route_w=w, x_per_route=True))
     log("weighted down", path, r)
     assert r <= TOL["f32"]
+
+
+@pytest.mark.parametrize("path", ["mmvq", "mmq"])
+@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K, g.Q8_0])
+def test_fp16_activations_and_outputs(dev, path, wt):
+    """fp16 in, fp16 out (and fp16 in, fp32 out) on both paths."""
+    N, K, M = 200, 512, (5 if path == "mmvq" else 70)
+    W = inputs.gen_weights(wt, N, K, 600 + wt)
+    x = inputs.gen_act(M, K, 601, "f16")
+    ref = oracle.mul_mat(wt, W, N, K, x)
+    yh = g.mul_mat(T(W, dev), wt, T(x, dev), path=path)
+    assert yh.dtype == torch.float16
+    r16 = rel(host(yh), ref_out(ref, "f16"))
+    y32 = g.mul_mat(T(W, dev), wt, T(x, dev), out_dtype=torch.float32, path=path)
+    r32 = rel(host(y32), ref)
+    log("fp16", wt, path, r16, r32)
+    assert r16 <= TOL["f16"] and r32 <= TOL["f32"]
+
+
+@pytest.mark.parametrize("path", ["mmvq", "mmq"])
+def test_fp16_moe_layer(dev, path):
+    """The routed layer in fp16: SwiGLU gate_up with fp16 h (and its q8_1 form,
+    rounded to fp16 before quantizing), weighted down with fp16 output.  The
+    activations are scaled by 1/16 so that h (a product of two projections)
+    stays inside fp16's range (65504)."""
+    E, H, I, Tn, top_k = 16, 512, 256, 45, 4
+    Wgu = inputs.gen_experts(g.Q4_K, E, 2 * I, H, 610)
+    Wd = inputs.gen_experts(g.Q6_K, E, H, I, 611)
+    x = (inputs.gen_act(Tn, H, 612, "f32") * np.float32(1 / 16)).astype(np.float16)
+    ids, w = inputs.gen_routing(Tn, E, top_k, 613)
+    ids[2, 1] = -1
+    Wgu_t, Wd_t, ids_t, w_t = T(Wgu, dev), T(Wd, dev), T(ids, dev), T(w, dev)
+    h = g.mul_mat_id(Wgu_t, g.Q4_K, T(x, dev), ids_t, H, epi=g.EPI_SWIGLU, path=path)
+    assert h.dtype == torch.float16
+    h_ref = _moe_ref(g.Q4_K, Wgu, H, x, ids, top_k, epi=oracle.EPI_SWIGLU)
+    assert rel(host(h), ref_out(h_ref, "f16")) <= TOL["f16"]
+    hq = g.mul_mat_id(Wgu_t, g.Q4_K, T(x, dev), ids_t, H, epi=g.EPI_SWIGLU, out_dtype="q8_1", path=path)
+    h_gpu = h.cpu().numpy()
+    assert np.array_equal(hq.cpu().numpy().reshape(Tn * top_k, -1), oracle.quantize_q8_1(h_gpu.reshape(Tn * top_k, I)))
+    y = g.mul_mat_id(Wd_t, g.Q6_K, h, ids_t, I, route_w=w_t, x_per_route=True, path=path)
+    assert y.dtype == torch.float16
+    y_ref = _moe_ref(g.Q6_K, Wd, I, h_gpu, ids, top_k, route_w=w, x_per_route=True)
+    r = rel(host(y), ref_out(y_ref, "f16"))
+    log("fp16 moe", path, r)
+    assert r <= TOL["f16"]
 
 
 def _bits(y):

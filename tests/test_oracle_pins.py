@@ -77,6 +77,36 @@ def test_fp32_to_bf16_rne_vs_torch():
     assert np.isnan(oracle.bf16_to_fp32(oracle.fp32_to_bf16(float("nan"))))
 
 
+def test_fp32_to_fp16_rne_vs_numpy():
+    """The oracle's fp32 -> binary16 (normal, subnormal, overflow, ties) against
+    numpy's float32 -> float16 conversion (round to nearest even)."""
+    r = np.random.Generator(np.random.PCG64(8))
+    h = np.arange(0x7c00, dtype=np.uint32).astype(np.uint16)              # every finite positive half
+    lo = h[:-1].view(np.float16).astype(np.float32)
+    hi = h[1:].view(np.float16).astype(np.float32)
+    mid = ((lo.astype(np.float64) + hi.astype(np.float64)) / 2).astype(np.float32)   # exact ties
+    vals = np.concatenate([
+        r.standard_normal(20000).astype(np.float32) * np.float32(2.0) ** r.integers(-30, 18, 20000),
+        mid, -mid[::7],
+        np.array([0.0, -0.0, np.inf, -np.inf, 65504.0, 65519.996, 65520.0, -65520.0, 1e30, 2.0 ** -25,
+                  2.0 ** -26, 1e-40, -1e-42], np.float32),
+    ]).astype(np.float32)
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    got = oracle.fp32_to_fp16_array(vals)
+    assert np.array_equal(got, ref)
+    assert oracle.fp32_to_fp16(float("nan")) & 0x7c00 == 0x7c00 and oracle.fp32_to_fp16(float("nan")) & 0x3ff
+
+
+def test_q8_1_fp16_input_equals_its_fp32_values():
+    """fp16 activations enter q8_1 through the exact fp16 -> fp32 decode."""
+    xh = inputs.gen_act(8, 256, 12, "f16")
+    assert np.array_equal(oracle.quantize_q8_1(xh), oracle.quantize_q8_1(xh.astype(np.float32)))
+    W = inputs.gen_q4_K(16, 256, 13)
+    assert np.array_equal(oracle.mul_mat(oracle.Q4_K, W, 16, 256, xh),
+                          oracle.mul_mat(oracle.Q4_K, W, 16, 256, xh.astype(np.float32)))
+
+
 # ---------------------------------------------------------------- q8_1
 
 def _q8(x):
