@@ -243,6 +243,41 @@ def bench_prefill(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, path=g.P
     return res
 
 
+# ------------------------------------------------------------------ crossover with dequantize + GEMM
+
+def bench_crossover(ctx, Ms=(1, 8, 64, 512, 8192)):
+    """Three ways to multiply the Q4_K 8192x2048 weight by M bf16 rows: MMVQ, MMQ,
+    and the baseline the pages compare against -- dequantize the weight to bf16
+    (this library's kernel) and multiply with the vendor GEMM (torch.mm,
+    hipBLASLt).  The baseline skips the q8_1 activation quantization, so
+    its result is not the method's; it is timed, not tested.  Mean call times
+    from HIP events; the weights stay in cache (same buffers every call)."""
+    dev, L = ctx.dev, ctx.L
+    N, K, wt = 8192, 2048, g.Q4_K
+    W = torch.from_numpy(inputs.gen_weights(wt, N, K, 301)).to(dev)
+    Wd = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    out = []
+    for M in Ms:
+        x = bf16(inputs.gen_act(M, K, 302, "bf16"), dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        row = {"workload": "q4_K_8192x2048_crossover", "M": M}
+        for path, pn in ((g.PATH_MMVQ, "mmvq"), (g.PATH_MMQ, "mmq")):
+            if pn == "mmvq" and M > 512:
+                continue
+            wsb = L.ggq_mul_mat_ws(wt, N, K, g.BF16, M, path)
+            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+            t = time_launches(lambda i: check(L.ggq_mul_mat(wt, vp(W), N, K, vp(x), g.BF16, M, K, vp(y), g.BF16, N,
+                                                            vp(ws), wsb, path, ctx.s), pn), 20)
+            row[pn + "_us"] = round(t * 1e6, 2)
+        dq = lambda i: check(L.ggq_dequantize(wt, vp(W), N, K, vp(Wd), g.BF16, ctx.s), "dequantize")
+        gemm = lambda i: torch.mm(x, Wd.t(), out=y)          # 2-D GEMM, weight as the transposed operand
+        row["dequant_us"] = round(time_launches(dq, 20) * 1e6, 2)
+        row["gemm_us"] = round(time_launches(gemm, 20) * 1e6, 2)
+        row["dequant_gemm_us"] = round(row["dequant_us"] + row["gemm_us"], 2)
+        out.append(row)
+    return out
+
+
 # ------------------------------------------------------------------ MoE layer
 
 def bench_moe(ctx, Tn, steps, warmup):
@@ -344,7 +379,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--workloads", default="all",
-                    help="comma list of: decode, prefill, sweep, lmhead1, lmhead2048, getrows, types, moe16, moe8192 (default all)")
+                    help="comma list of: decode, prefill, sweep, lmhead1, lmhead2048, getrows, types, crossover, "
+                         "moe16, moe8192 (default all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calib-copy", action="store_true",
@@ -374,7 +410,7 @@ def main():
     head = bench_decode(ctx, g.Q4_K, 4096, 4096, 1, 201, 202, torch.bfloat16, K, W)
     also = []
     sel = set(args.workloads.split(",")) if args.workloads != "all" else {
-        "decode", "prefill", "sweep", "lmhead1", "lmhead2048", "getrows", "types", "moe16", "moe8192"}
+        "decode", "prefill", "sweep", "lmhead1", "lmhead2048", "getrows", "types", "crossover", "moe16", "moe8192"}
     if args.only_headline:
         sel = set()
     if "decode" in sel:
@@ -405,6 +441,9 @@ def main():
             log(f"{name} 8192x2048 prefill M=8192")
             r = bench_prefill(ctx, wt, 8192, 2048, 8192, 301, 302, torch.bfloat16, max(5, K // 20), max(2, W // 10))
             also.append({"workload": f"{name}_8192x2048_prefill", "M": 8192, **r})
+    if "crossover" in sel:
+        log("q4_K 8192x2048 crossover: MMVQ / MMQ / dequantize + GEMM")
+        also.extend(bench_crossover(ctx))
     if "getrows" in sel:
         log("q6_K 248320x2048 get_rows n=8192")
         r = bench_get_rows(ctx, g.Q6_K, 248320, 2048, 8192, 401, 404, torch.bfloat16, max(20, K // 4), W)

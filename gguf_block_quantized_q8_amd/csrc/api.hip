@@ -91,6 +91,20 @@ bool use_mmq_id(int wt, int64_t K, int64_t T, int path) {
     return has_mmq(wt, K) && T > MMVQ_ID_MAX_TOKENS;
 }
 
+// Dense MMQ split K: with fewer tiles than two workgroups per CU (512), split
+// K (in whole super-blocks, at most 8 ways) until the grid fills the chip.
+int mmq_ksplit(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + MMQ_MT - 1) / MMQ_MT) * ((N + MMQ_NT - 1) / MMQ_NT), nsb = K / 256;
+    int ks = 1;
+    while (ks < 8 && nsb % (2 * ks) == 0 && tiles * 2 * ks <= 512) ks *= 2;
+    return ks;
+}
+
+size_t splitk_bytes(int64_t M, int64_t N, int64_t K) {
+    const int ks = mmq_ksplit(M, N, K);
+    return ks > 1 ? align256((size_t)ks * M * N * 4) : 0;
+}
+
 int check_weights(int wt, int64_t N, int64_t K) {
     if (!known_type(wt))
         return fail(GGQ_ERR_UNSUPPORTED, "ggml type %d is not supported (Q4_0=2, Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14)", wt);
@@ -170,7 +184,8 @@ int ggq_get_rows(int wt, const void *W, int64_t rows, int64_t K, const int32_t *
 
 size_t ggq_mul_mat_ws(int wt, int64_t N, int64_t K, int xdt, int64_t M, int path) {
     if (!known_type(wt) || M <= 0 || N <= 0 || K <= 0 || K % block_len(wt)) return 0;
-    return act_bytes(use_mmq(wt, K, M, path), M, K);
+    const bool mmq = use_mmq(wt, K, M, path);
+    return act_bytes(mmq, M, K) + (mmq ? splitk_bytes(M, N, K) : 0);
 }
 
 int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int xdt, int64_t M, int64_t ldx, void *y,
@@ -238,7 +253,12 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
     p.y = y;
     p.ldy = ldy;
     p.y_f16 = ydt == GGQ_F16;
-    return hip_status(launch_mmq(wt, false, GGQ_EPI_NONE, kernel_dt(ydt), p, s), "mul_mat mmq");
+    p.ksplit = mmq_ksplit(M, N, K);
+    p.part = p.ksplit > 1 ? c.take<float>((size_t)p.ksplit * M * N * 4) : nullptr;
+    rc = hip_status(launch_mmq(wt, false, GGQ_EPI_NONE, kernel_dt(ydt), p, s), "mul_mat mmq");
+    if (!rc && p.ksplit > 1)
+        rc = hip_status(launch_splitk_reduce(p.part, p.ksplit, M, N, y, kernel_dt(ydt), p.y_f16, ldy, s), "mul_mat split-K sum");
+    return rc;
 }
 
 // ---------------------------------------------------------------------------

@@ -255,25 +255,47 @@ __global__ __launch_bounds__(256) void route_sum_kernel(const float *__restrict_
     }
 }
 
+// Split-K finish: y[m][n] = sum over slices k in order of part[k][m][n]
+// (fp32), stored in the output dtype.  One thread per output.
+template <int YDT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int ks, int64_t M,
+                                                            int64_t N, void *__restrict__ y, int y_f16, int64_t ldy) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= M * N) return;
+    const int64_t m = i / N, n = i - m * N;
+    float acc = part[i];
+    for (int k = 1; k < ks; k++) acc += part[(int64_t)k * M * N + i];
+    if (YDT == DT_F32) static_cast<float *>(y)[m * ldy + n] = acc;
+    else static_cast<uint16_t *>(y)[m * ldy + n] = (uint16_t)f32_to_16(acc, y_f16 != 0);
+}
+
 // Zero the output rows of inactive routes (id < 0 or id >= E) in the
-// unweighted mul_mat_id output y[T*top_k][Np].
+// unweighted mul_mat_id output y[T*top_k][Np].  One thread per route reads
+// its id; each wave then zeroes its inactive routes' rows one at a time with
+// all 64 lanes (inactive routes are rare, so most waves only read ids).
 template <int YDT>
 __global__ __launch_bounds__(256) void zero_inactive_kernel(const int32_t *__restrict__ ids, int64_t R, int64_t E,
                                                             int64_t Np, void *__restrict__ y) {
-    const int64_t r = blockIdx.x;
-    if (r >= R) return;
-    const int32_t e = ids[r];
-    if (e >= 0 && e < E) return;
-    if (YDT == DT_Q8_1) {
-        // Np / 32 all-zero q8_1 blocks (d = s = 0, q = 0): what an all-zero row quantizes to
-        const int64_t words = Np / QK8_1 * (Q8_1_BYTES / 4);
-        uint32_t *o = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(y) + r * (Np / QK8_1) * Q8_1_BYTES);
-        for (int64_t i = threadIdx.x; i < words; i += blockDim.x) o[i] = 0u;
-        return;
+    const int64_t r0 = (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63u);   // this wave's first route
+    const int lane = threadIdx.x & 63;
+    bool dead = false;
+    if (r0 + lane < R) {
+        const int32_t e = ids[r0 + lane];
+        dead = e < 0 || e >= E;
     }
-    for (int64_t n = threadIdx.x; n < Np; n += blockDim.x) {
-        if (YDT == DT_F32) static_cast<float *>(y)[r * Np + n] = 0.0f;
-        else static_cast<uint16_t *>(y)[r * Np + n] = 0;
+    for (uint64_t m = __ballot(dead); m; m &= m - 1) {
+        const int64_t r = r0 + __builtin_ctzll(m);
+        if (YDT == DT_Q8_1) {
+            // Np / 32 all-zero q8_1 blocks (d = s = 0, q = 0): what an all-zero row quantizes to
+            const int64_t words = Np / QK8_1 * (Q8_1_BYTES / 4);
+            uint32_t *o = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(y) + r * (Np / QK8_1) * Q8_1_BYTES);
+            for (int64_t i = lane; i < words; i += 64) o[i] = 0u;
+        } else {
+            for (int64_t n = lane; n < Np; n += 64) {
+                if (YDT == DT_F32) static_cast<float *>(y)[r * Np + n] = 0.0f;
+                else static_cast<uint16_t *>(y)[r * Np + n] = 0;
+            }
+        }
     }
 }
 
@@ -352,13 +374,23 @@ hipError_t launch_route_sum(const float *o, const int32_t *ids, const float *w, 
     return hipGetLastError();
 }
 
+hipError_t launch_splitk_reduce(const float *part, int ks, int64_t M, int64_t N, void *y, int ydt, int y_f16,
+                                int64_t ldy, hipStream_t s) {
+    if (M * N == 0) return hipSuccess;
+    const dim3 g(grid_for(M * N)), b(256);
+    if (ydt == DT_F32) hipLaunchKernelGGL(splitk_reduce_kernel<DT_F32>, g, b, 0, s, part, ks, M, N, y, y_f16, ldy);
+    else hipLaunchKernelGGL(splitk_reduce_kernel<DT_BF16>, g, b, 0, s, part, ks, M, N, y, y_f16, ldy);
+    return hipGetLastError();
+}
+
 hipError_t launch_zero_inactive(const int32_t *ids, int64_t R, int64_t E, int64_t Np, void *y, int ydt,
                                 hipStream_t s) {
     if (R == 0) return hipSuccess;
-    if (ydt == DT_F32) hipLaunchKernelGGL(zero_inactive_kernel<DT_F32>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
+    const dim3 g(grid_for(R)), b(256);
+    if (ydt == DT_F32) hipLaunchKernelGGL(zero_inactive_kernel<DT_F32>, g, b, 0, s, ids, R, E, Np, y);
     else if (ydt == DT_BF16 || ydt == DT_F16)                                     // 16-bit zeros
-        hipLaunchKernelGGL(zero_inactive_kernel<DT_BF16>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
-    else hipLaunchKernelGGL(zero_inactive_kernel<DT_Q8_1>, dim3((unsigned)R), dim3(256), 0, s, ids, R, E, Np, y);
+        hipLaunchKernelGGL(zero_inactive_kernel<DT_BF16>, g, b, 0, s, ids, R, E, Np, y);
+    else hipLaunchKernelGGL(zero_inactive_kernel<DT_Q8_1>, g, b, 0, s, ids, R, E, Np, y);
     return hipGetLastError();
 }
 

@@ -17,6 +17,9 @@ hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, cons
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s);
 hipError_t launch_route_sum(const float *o, const int32_t *ids, const float *w, int64_t T, int top_k, int64_t E,
                             int64_t Np, void *y, int ydt, hipStream_t s);
+// y[m][n] = sum over k < ks, in order, of part[k][m][n] (fp32), stored as ydt (fp16 when y_f16)
+hipError_t launch_splitk_reduce(const float *part, int ks, int64_t M, int64_t N, void *y, int ydt, int y_f16,
+                                int64_t ldy, hipStream_t s);
 hipError_t launch_zero_inactive(const int32_t *ids, int64_t R, int64_t E, int64_t Np, void *y, int ydt,
                                 hipStream_t s);
 
@@ -118,6 +121,10 @@ struct MmqParams {
     float *o32;           // weighted: per-route fp32 outputs [R][Np]
     int q8_round;         // q8_1 output: round the values to bf16 (1) or fp16 (2) before quantizing
     int y_f16;            // 16-bit output is fp16 (else bf16)
+    // dense split K: ksplit workgroups per tile, each over K / ksplit (whole super-blocks),
+    // writing fp32 partial sums part[ksplit][M][N] that splitk_reduce adds in slice order
+    int ksplit;
+    float *part;
 };
 constexpr int MMQ_NT = 128;   // weight rows per workgroup tile
 constexpr int MMQ_MT = 128;   // activation rows (routes) per workgroup tile

@@ -377,6 +377,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wn = wave & 1, wm = wave >> 1;
     int64_t bm, bn;
+    int slice = 0;
     if (MOE) {
         // Workgroup b runs on XCD b mod 8.  That XCD takes the route tiles
         // t = b mod 8 (mod 8), each with all its weight tiles back to back, so a
@@ -386,7 +387,10 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
         bm = 8 * (i / p.n_tiles) + x;
         bn = i % p.n_tiles;
     } else {
-        tile_of(blockIdx.x, p.m_tiles, p.n_tiles, bm, bn);
+        // split K: workgroups [k * tiles, (k + 1) * tiles) take the k-th of p.ksplit equal K ranges
+        const int64_t tiles = p.m_tiles * p.n_tiles;
+        slice = p.ksplit > 1 ? (int)(blockIdx.x / tiles) : 0;
+        tile_of(blockIdx.x - (int64_t)slice * tiles, p.m_tiles, p.n_tiles, bm, bn);
     }
 
     // ---- tile columns (activation rows / routes) ----
@@ -434,7 +438,9 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
 #pragma unroll
         for (int b = 0; b < 2; b++) acc[a][b] = v16f{};
 
-    const int nst = (int)(p.K / KS);
+    // stages [s0, nst) of this workgroup: whole super-blocks (the slice length is a multiple of 8)
+    const int nst_all = (int)(p.K / KS), per = nst_all / (!MOE && p.ksplit > 1 ? p.ksplit : 1);
+    const int s0 = slice * per, nst = s0 + per;
     const int lr = lane & 31, kh = 8 * (lane >> 5);
     Stager<T, false> S;
     {
@@ -443,12 +449,12 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
         const int32_t xr = sm.xrow[tid >> 1];
         S.init(wr ? wr : W, p.xq, p.xd, p.xs, p.K, xr >= 0 ? xr : 0);
     }
-    S.load(0);
-    S.store(sm, 0);
-    if (nst > 1) S.load(1);
+    S.load(s0);
+    S.store(sm, s0);
+    if (s0 + 1 < nst) S.load(s0 + 1);
     lds_sync();
 #pragma unroll 1
-    for (int s = 0; s < nst; s++) {
+    for (int s = s0; s < nst; s++) {
         const int buf = s & 1, j = s & 7;
         if (s + 1 < nst) S.store(sm, s + 1);                 // into the other buffer
         if (s + 2 < nst) S.load(s + 2);
@@ -562,7 +568,8 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
                     if (n0 >= p.N) continue;
                     const int nv = (int)min<int64_t>(4, p.N - n0);
                     float v[4] = {acc[ni][mi][4 * g], acc[ni][mi][4 * g + 1], acc[ni][mi][4 * g + 2], acc[ni][mi][4 * g + 3]};
-                    store4<YDT>(p.y, (int64_t)xr * p.ldy + n0, v, nv, p.y_f16);
+                    if (p.ksplit > 1) store4<DT_F32>(p.part, ((int64_t)slice * p.M + xr) * p.N + n0, v, nv);
+                    else store4<YDT>(p.y, (int64_t)xr * p.ldy + n0, v, nv, p.y_f16);
                 }
             } else {
                 // weighted: per-route fp32 outputs, summed per token afterwards
@@ -664,7 +671,8 @@ static void launch_t(bool moe, int epi, int ydt, const MmqParams &p, hipStream_t
     // routed: route tiles rounded up to a multiple of 8 (the XCD interleave); the
     // extra workgroups, like those past the device's tile count, exit at once
     const int64_t mt = moe ? (p.m_tiles + 7) / 8 * 8 : p.m_tiles;
-    const dim3 g((unsigned)(mt * p.n_tiles)), b(256);
+    const int64_t ks = !moe && p.ksplit > 1 ? p.ksplit : 1;
+    const dim3 g((unsigned)(mt * p.n_tiles * ks)), b(256);
 #define GGQ_L(MOE, EPI, YDT) hipLaunchKernelGGL((mmq_kernel<T, MOE, EPI, YDT>), g, b, 0, s, p)
     if (!moe) {
         if (ydt == DT_F32) GGQ_L(false, EPI_NONE_, DT_F32); else GGQ_L(false, EPI_NONE_, DT_BF16);

@@ -234,6 +234,23 @@ def test_mmq_q6_K_large_scales(dev):
     _check_mul_mat(dev, g.Q6_K, 200, 512, 3, "f32", "f32", "mmvq", 83, W=W)
 
 
+@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K, g.Q8_0])
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16, torch.float16])
+def test_mmq_split_k(dev, wt, ydt):
+    """Few tiles, long K: the K range is split over up to 8 workgroups per tile and the
+    fp32 partial sums are added in slice order; strided output rows (ldy > N)."""
+    N, K, M = 200, 2048, 70
+    W = inputs.gen_weights(wt, N, K, 620 + wt)
+    x = inputs.gen_act(M, K, 621, "bf16")
+    out = torch.full((M, 256), 3.0, dtype=ydt, device=dev)
+    g.mul_mat(T(W, dev), wt, T(x, dev), path="mmq", out=out[:, :N])
+    kind = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}[ydt]
+    r = rel(host(out[:, :N]), ref_out(oracle.mul_mat(wt, W, N, K, x), kind))
+    log("split-K", wt, kind, r)
+    assert r <= TOL[kind]
+    assert (out[:, N:] == 3.0).all()
+
+
 def test_q8_1_input_reuse(dev):
     """Pre-quantized q8_1 input gives the same result as float input, on both paths."""
     W = inputs.gen_q4_K(96, 512, 90)
