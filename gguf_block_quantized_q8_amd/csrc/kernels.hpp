@@ -81,6 +81,7 @@ struct MmvqParams {
     int stage_bpc;          // blocks per staged row chunk (set by the launcher)
     int stage_cps;          // 16-byte pieces per staged row chunk (set by the launcher)
     int stage_ninst;        // 1 KB copy instructions per work item (set by the launcher)
+    int deep;               // two work items in flight per wave (set by the launcher)
     int act_dma;            // activation rows copied to LDS by DMA in the prologue (set by the launcher)
     uint32_t nb_magic;      // ceil(2^32 / (K / 32)): block index -> column by one high multiply (set by the launcher)
     uint32_t cps_magic;     // ceil(2^32 / stage_cps): piece index -> row slot (set by the launcher)

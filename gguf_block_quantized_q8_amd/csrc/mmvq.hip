@@ -632,7 +632,8 @@ struct MaxWaves { static constexpr int value = 16; };
 // its columns' q8_1 activations in LDS, then each wave walks its work items
 // (spw row pairs x K-chunks), copying item i+1 into its second LDS buffer
 // while it computes item i from the first.
-template <int T, int NC, bool MOE, int EPI, int YDT>
+// DEEP (dense, one column, many items per wave): two work items in flight per wave.
+template <int T, int NC, bool MOE, int EPI, int YDT, bool DEEP = false>
 __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const MmvqParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ int64_t xrow[NC];
@@ -769,6 +770,99 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
         for (int c = 0; c < NC; c++) acc[i][c] = 0.0f;
 
     const bool patch = (reinterpret_cast<uintptr_t>(wend) & 2) != 0;
+    if constexpr (DEEP) {
+        // row pair complete: reduce across the segment, store, and clear
+        auto finish_pair = [&](bool pvalid, bool v1, int64_t r0, int64_t r1) {
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int c = 0; c < NC; c++) acc[i][c] = seg_sum(acc[i][c], seg);
+            if (pvalid && lane_in == seg - 1) {          // seg_sum leaves the total in the segment's last lane
+#pragma unroll
+                for (int c = 0; c < NC; c++) {
+                    if (c >= ncols) break;
+                    if (!MOE) {
+                        const int64_t col = xrow[c];
+                        if (v1) store_out2<YDT>(p.y, col * p.ldy + r0, acc[0][c], acc[1][c], p.y_f16);   // r1 = r0 + 1
+                        else store_out<YDT>(p.y, col * p.ldy + r0, acc[0][c], p.y_f16);
+                    } else {
+                        // weighted: per-route fp32 outputs, summed per token afterwards
+                        const int64_t r = route_s[c];
+                        if (EPI == EPI_SWIGLU) {
+                            const float h = silu_mul(acc[0][c], acc[1][c]);
+                            if (p.o32) p.o32[r * p.Np + r0] = h;
+                            else store_out<YDT>(p.y, r * p.Np + r0, h, p.y_f16);
+                        } else if (p.o32) {
+                            p.o32[r * p.Np + r0] = acc[0][c];
+                            if (v1) p.o32[r * p.Np + r1] = acc[1][c];
+                        } else {
+                            store_out<YDT>(p.y, r * p.Np + r0, acc[0][c], p.y_f16);
+                            if (v1) store_out<YDT>(p.y, r * p.Np + r1, acc[1][c], p.y_f16);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int c = 0; c < NC; c++) acc[i][c] = 0.0f;
+        };
+        // Two items in flight: item i is computed from buffer i & 1 while item
+        // i+1 lands in the other; right after item i is consumed, item i+2 goes
+        // into its buffer.  Item 1 goes out now that the second buffers no
+        // longer hold the raw activation rows; (ipw, ikc) is the next item to copy.
+        auto next_item = [&](int64_t &w, int &k) {
+            if (++k == nkc) { k = 0; w += wave_stride; }
+        };
+        int64_t ipw = pw0;
+        int ikc = 0;
+        next_item(ipw, ikc);
+        bool ahead = false;                                     // item i+1 issued
+        if (first && ipw < p.npairs) {
+            stage_issue(chunk_addr(ipw, ikc), wend, wbuf + bstride, S, ninst);
+            next_item(ipw, ikc);
+            ahead = true;
+        }
+        int64_t pw = pw0;
+        int kc = 0, cur = 0;
+        while (pw < p.npairs) {                                 // wave-uniform
+            const int64_t pair = pw + sid;
+            const bool pvalid = pair < p.npairs;
+            const int64_t r0 = 2 * pair, r1 = 2 * pair + 1;
+            const bool v1 = pvalid && r1 < p.N;
+            const uint8_t *Acur = chunk_addr(pw, kc);
+            // item (pw, kc) has landed; the ninst copy instructions of the next one
+            // (issued after it, and after any output stores) may still be in flight
+            if (ahead) wait_vm_n(ninst);
+            else wait_vm();
+            if (patch) stage_patch(Acur, wend, wbuf + cur * bstride, S, ninst, lane);
+            compiler_fence();
+            if (pvalid) {
+                const uint32_t phi = (uint32_t)(reinterpret_cast<uintptr_t>(Acur) & 15);
+                const uint8_t *b = wbuf + cur * bstride;
+                const int back = kc * bpc * BB;
+                const lds_bp row0 = (lds_bp)(b + 2 * sid * cps * 16 + ((phi + relrb0) & 15)) - back;
+                const lds_bp row1 = (lds_bp)(b + (2 * sid + 1) * cps * 16 + ((phi + relrb1) & 15)) - back;
+                const int ubase = kc * seg * upl + lane_in;
+                for (int j = 0; j < upl; j++) {
+                    const int u = ubase + j * seg;
+                    if (u < p.units) U::run(u, row0, row1, A, ncols, acc);
+                }
+            }
+            wait_lgkm();                                        // LDS reads done before this buffer is refilled
+            compiler_fence();
+            if (kc + 1 == nkc) finish_pair(pvalid, v1, r0, r1);
+            compiler_fence();
+            ahead = ipw < p.npairs;                             // the item after next into the buffer just consumed
+            if (ahead) {
+                stage_issue(chunk_addr(ipw, ikc), wend, wbuf + cur * bstride, S, ninst);
+                next_item(ipw, ikc);
+            }
+            cur ^= 1;
+            next_item(pw, kc);
+        }
+        return;
+    }
     int64_t pw = pw0;
     int kc = 0, cur = 0;
     while (pw < p.npairs) {                                     // wave-uniform
@@ -926,16 +1020,19 @@ static void raise_lds_limit(K kernel, size_t lds) {
                                   (int)lds);
 }
 
-template <int T, int NC, bool MOE, int EPI, int YDT>
+template <int T, int NC, bool MOE, int EPI, int YDT, bool DEEP = false>
 static void launch_one(const MmvqParams &p, dim3 g, int waves, size_t lds, hipStream_t s) {
-    auto k = mmvq_kernel<T, NC, MOE, EPI, YDT>;
+    auto k = mmvq_kernel<T, NC, MOE, EPI, YDT, DEEP>;
     raise_lds_limit(k, lds);
     hipLaunchKernelGGL(k, g, dim3(64 * waves), lds, s, p);
 }
 
 template <int T, int NC>
 static void launch_nc(bool moe, int epi, int ydt, const MmvqParams &p, dim3 g, int waves, size_t lds, hipStream_t s) {
-    if (!moe) {
+    if (!moe && NC == 1 && p.deep) {
+        if (ydt == DT_F32) launch_one<T, 1, false, EPI_NONE, DT_F32, true>(p, g, waves, lds, s);
+        else launch_one<T, 1, false, EPI_NONE, DT_BF16, true>(p, g, waves, lds, s);
+    } else if (!moe) {
         if (ydt == DT_F32) launch_one<T, NC, false, EPI_NONE, DT_F32>(p, g, waves, lds, s);
         else launch_one<T, NC, false, EPI_NONE, DT_BF16>(p, g, waves, lds, s);
     } else if (epi == EPI_SWIGLU) {
@@ -1058,6 +1155,12 @@ hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqPara
     const int64_t active = moe ? std::max<int64_t>(1, std::min<int64_t>(ngroups_bound, p.groups_expected)) : ngroups_bound;
     const int64_t cap = std::max<int64_t>(1, 256 * per_cu / active);
     const dim3 g((unsigned)std::min<int64_t>(need, cap), (unsigned)ngroups_bound);
+    // Dense single-column calls where a wave has several items (lm_head-sized
+    // matrices) keep two items in flight per wave (a separate instantiation:
+    // the extra code would slow the short launches, whose instruction cache
+    // starts cold).
+    const int64_t nkc = (G.units + G.seg * G.upl - 1) / (G.seg * G.upl);
+    p.deep = !moe && nc == 1 && groups * nkc >= 4 * (int64_t)g.x * waves;
     if (t == T_Q4_K) launch_t<T_Q4_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
     else if (t == T_Q6_K) launch_t<T_Q6_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
     else if (t == T_Q5_K) launch_t<T_Q5_K>(nc, moe, epi, ydt, p, g, waves, lds, s);

@@ -311,6 +311,28 @@ def test_c3_crossover_sweep_both_paths(dev, M):
         assert r <= TOL["bf16"]
 
 
+# Long single-column matrices: a wave walks many work items, so the kernel keeps
+# two of them in flight (the lm_head-sized case); odd N (last row pair half
+# empty), K split over two items per row, and a weight end that is 2-byte but
+# not 4-byte aligned (the tail patch) are all covered here.
+@pytest.mark.parametrize("wt,N,K,xdt,ydt", [
+    (g.Q4_K, 262147, 512, "bf16", "bf16"),
+    (g.Q4_K, 12289, 16384, "f32", "f32"),
+    (g.Q8_0, 2000001, 32, "bf16", "f32"),
+    (g.Q6_K, 400001, 256, "f32", "bf16"),
+    (g.Q5_K, 200001, 1024, "bf16", "bf16"),
+])
+def test_mmvq_long_matrix_m1(dev, wt, N, K, xdt, ydt):
+    log("long matrix M=1", wt, N, K, xdt, ydt)
+    W = inputs.gen_weights(wt, N, K, 700 + wt)
+    x = inputs.gen_act(1, K, 701, xdt)
+    out = torch.float32 if ydt == "f32" else torch.bfloat16
+    y = host(g.mul_mat(T(W, dev), wt, T(x, dev), out_dtype=out, path="mmvq"))
+    r = rel(y, ref_out(oracle.mul_mat(wt, W, N, K, x), ydt))
+    log("  rel", r)
+    assert r <= TOL[ydt]
+
+
 def test_c4_q6_K_lm_head_m1_all_rows(dev):
     W = inputs.gen_q6_K(248320, 2048, 401)
     x = inputs.gen_act(1, 2048, 402, "bf16")
