@@ -165,6 +165,48 @@ def roofline_ops(ops, sec, kernel):
             "kernel_us": round(sec * 1e6, 3), "ops_note": "int8 ops = 2*M*N*K, peak = dense int8 MFMA"}
 
 
+# ------------------------------------------------------------------ measured ceilings
+
+def bench_ceilings(ctx, steps, warmup):
+    """Measured ceilings next to the published peaks: a plain streaming read at
+    the headline's size (rotating through 1 GiB so every launch reads from HBM,
+    graph-timed like the headline) and at the lm_head's weight size, and
+    MFMA-only loops (fp16 32x32x16, int8 32x32x32)."""
+    dev, L = ctx.dev, ctx.L
+    sink = torch.zeros(4096, dtype=torch.uint8, device=dev)
+    out = {}
+    small = 9453568                                     # the headline step's bytes, a multiple of 16
+    buf = torch.empty(ROTATE_BYTES, dtype=torch.uint8, device=dev)
+    R = ROTATE_BYTES // small
+
+    def step(i):
+        check(L.ggq_bench_stream_read(ctypes.c_void_p(buf.data_ptr() + (i % R) * small), small, vp(sink), 4096,
+                                      ctx.s), "bench_stream_read")
+    dt, gpu = time_steps(step, steps, warmup, graph=True)
+    out["read_gbs_9MB"] = round(small * steps / gpu / 1e9, 1)
+    big = 417177600                                     # the lm_head's weight bytes
+    sec = time_launches(lambda i: check(L.ggq_bench_stream_read(vp(buf), big, vp(sink), 4096, ctx.s),
+                                        "bench_stream_read"), 20)
+    out["read_gbs_417MB"] = round(big / sec / 1e9, 1)
+    del buf
+    iters = 20000
+    waves = 1024 * 4
+    for kind, name, ops in ((0, "mfma_f16_tflops", 32 * 32 * 16 * 2), (1, "mfma_i8_tops", 32 * 32 * 32 * 2)):
+        sec = time_launches(lambda i: check(L.ggq_bench_mfma_loop(kind, iters, vp(sink), 4096, ctx.s),
+                                            "bench_mfma_loop"), 5)
+        out[name] = round(waves * iters * 4 * ops / sec / 1e12, 1)
+    return out
+
+
+def with_ceiling(roof, ceiling):
+    """Add the fraction of a measured ceiling to a roofline object."""
+    if roof and ceiling:
+        roof = dict(roof)
+        roof["measured_ceiling"] = ceiling
+        roof["frac_of_measured"] = round(roof["achieved"] / ceiling, 4)
+    return roof
+
+
 # ------------------------------------------------------------------ dense decode (MMVQ)
 
 def bench_decode(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, rotate=True):
@@ -406,6 +448,8 @@ def main():
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
 
+    log("measured ceilings: streaming read, MFMA loops")
+    ceil = bench_ceilings(ctx, K, W)
     log("headline: q4_K 4096x4096 decode M=1")
     head = bench_decode(ctx, g.Q4_K, 4096, 4096, 1, 201, 202, torch.bfloat16, K, W)
     also = []
@@ -458,6 +502,16 @@ def main():
             log(f"moe T={Tn}")
             r = bench_moe(ctx, Tn, max(5, K // (1 if Tn <= 64 else 20)), max(2, W // 4))
             also.append({"workload": "moe_e256_top8_h2048_i512", "T": Tn, **r})
+    # secondary column: each kernel against the measured ceiling of its bound
+    for a in also:
+        r = a.get("roofline")
+        if not r:
+            continue
+        if r["bound"] == "hbm":
+            big = a.get("step_bytes", 0) > 32e6 or a["workload"].startswith("moe")
+            a["roofline"] = with_ceiling(r, ceil["read_gbs_417MB"] if big else ceil["read_gbs_9MB"])
+        else:
+            a["roofline"] = with_ceiling(r, ceil["mfma_i8_tops"])
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
     line = {
         "metric": METRIC, "value": round(head["value"], 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
@@ -466,7 +520,8 @@ def main():
         "config": {"workload": "q4_K_4096x4096_decode", "M": 1, "N": 4096, "K": 4096, "weights": "Q4_K",
                    "activations": "bf16 -> q8_1", "output": "bf16", "rotating_weight_copies": head["rotating_copies"],
                    "step_bytes": head["step_bytes"]},
-        "roofline": head["roofline"], "cpu_baseline": cpu, "also": also,
+        "roofline": with_ceiling(head["roofline"], ceil["read_gbs_9MB"]), "cpu_baseline": cpu,
+        "ceilings": ceil, "also": also,
     }
     print(json.dumps(line), flush=True)
 

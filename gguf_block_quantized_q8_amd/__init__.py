@@ -26,7 +26,7 @@ _lib = None
 
 EXPORTS = ["ggq_row_bytes", "ggq_q8_1_bytes", "ggq_quantize_q8_1", "ggq_mul_mat_ws", "ggq_mul_mat",
            "ggq_mul_mat_id_ws", "ggq_mul_mat_id", "ggq_dequantize", "ggq_get_rows", "ggq_last_error",
-           "ggq_test_block_dots_ws", "ggq_test_block_dots"]
+           "ggq_test_block_dots_ws", "ggq_test_block_dots", "ggq_bench_stream_read", "ggq_bench_mfma_loop"]
 
 
 def lib():
@@ -64,6 +64,10 @@ def lib():
     L.ggq_test_block_dots_ws.argtypes = [i32, i64, i64, i32]
     L.ggq_test_block_dots.restype = i32
     L.ggq_test_block_dots.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp, sz, i32, vp]
+    L.ggq_bench_stream_read.restype = i32
+    L.ggq_bench_stream_read.argtypes = [vp, i64, vp, sz, vp]
+    L.ggq_bench_mfma_loop.restype = i32
+    L.ggq_bench_mfma_loop.argtypes = [i32, i64, vp, sz, vp]
     _lib = L
     return L
 

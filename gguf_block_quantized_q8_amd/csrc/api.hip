@@ -452,4 +452,27 @@ int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K, const void 
     return hip_status(launch_mmq_dots(wt, static_cast<const uint8_t *>(W), N, K, pl.xq, M, out, s), "test_block_dots mmq");
 }
 
+int ggq_bench_stream_read(const void *buf, int64_t bytes, void *sink, size_t sink_bytes, void *stream) {
+    g_err[0] = 0;
+    if (bytes < 0) return fail(GGQ_ERR_INVALID, "bench_stream_read: bytes < 0");
+    if (bytes == 0) return GGQ_OK;
+    if (!buf || !sink) return fail(GGQ_ERR_INVALID, "bench_stream_read: null pointer");
+    if (!aligned16(buf)) return fail(GGQ_ERR_INVALID, "bench_stream_read: buffer not 16-byte aligned");
+    if (sink_bytes < (size_t)CEIL_READ_BLOCKS * 4)
+        return fail(GGQ_ERR_WORKSPACE, "bench_stream_read: sink %zu bytes < %d required", sink_bytes, CEIL_READ_BLOCKS * 4);
+    return hip_status(launch_stream_read(buf, bytes, static_cast<int *>(sink), static_cast<hipStream_t>(stream)),
+                      "bench_stream_read");
+}
+
+int ggq_bench_mfma_loop(int kind, int64_t iters, void *sink, size_t sink_bytes, void *stream) {
+    g_err[0] = 0;
+    if (kind != 0 && kind != 1) return fail(GGQ_ERR_INVALID, "bench_mfma_loop: kind must be 0 (fp16) or 1 (int8)");
+    if (iters < 0) return fail(GGQ_ERR_INVALID, "bench_mfma_loop: iters < 0");
+    if (!sink) return fail(GGQ_ERR_INVALID, "bench_mfma_loop: null sink");
+    if (sink_bytes < (size_t)CEIL_MFMA_BLOCKS * 4)
+        return fail(GGQ_ERR_WORKSPACE, "bench_mfma_loop: sink %zu bytes < %d required", sink_bytes, CEIL_MFMA_BLOCKS * 4);
+    return hip_status(launch_mfma_loop(kind, iters, static_cast<int *>(sink), static_cast<hipStream_t>(stream)),
+                      "bench_mfma_loop");
+}
+
 }  // extern "C"

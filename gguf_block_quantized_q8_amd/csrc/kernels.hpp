@@ -133,4 +133,12 @@ hipError_t launch_mmq(int t, bool moe, int epi, int ydt, const MmqParams &p, hip
 hipError_t launch_mmq_dots(int t, const uint8_t *W, int64_t N, int64_t K, const _Float16 *xq, int64_t M,
                            int32_t *out, hipStream_t s);
 
+// ---- ceiling.hip (bench-only measured ceilings) ----
+constexpr int CEIL_READ_BLOCKS = 256;    // workgroups of the streaming read (256 threads each)
+constexpr int CEIL_MFMA_BLOCKS = 1024;   // workgroups of the MFMA loops (4 waves each)
+// reads bytes / 16 whole 16-byte pieces of buf (16-byte aligned); sink: CEIL_READ_BLOCKS ints
+hipError_t launch_stream_read(const void *buf, int64_t bytes, int *sink, hipStream_t s);
+// kind 0: fp16 32x32x16, 1: int8 32x32x32; each wave runs iters x 4 MFMAs; sink: CEIL_MFMA_BLOCKS ints
+hipError_t launch_mfma_loop(int kind, int64_t iters, int *sink, hipStream_t s);
+
 }  // namespace ggq

@@ -174,6 +174,23 @@ int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K,
                         const void *q8, int64_t M, int32_t *out,
                         void *ws, size_t ws_bytes, int path, void *stream);
 
+/* Bench hooks (not part of the product API): measured ceilings reported next
+ * to the published peaks.  Both are asynchronous on `stream`, write nothing
+ * to `sink` in practice (a device buffer the caller owns, at least 1 KB for
+ * the read and 4 KB for the MFMA loop, else GGQ_ERR_WORKSPACE), and return
+ * GGQ_ERR_INVALID for bad arguments.
+ *
+ * ggq_bench_stream_read: reads the bytes / 16 whole 16-byte pieces of the
+ * device buffer buf (16-byte aligned) once, grid-stride, 256 workgroups of
+ * 256 threads: the HBM read rate a kernel doing nothing else achieves.
+ *
+ * ggq_bench_mfma_loop: 1024 workgroups of 4 waves; each wave issues iters x 4
+ * independent MFMAs, kind 0 = v_mfma_f32_32x32x16_f16 (32768 flops each),
+ * kind 1 = v_mfma_i32_32x32x32_i8 (65536 int8 ops each), with no memory
+ * traffic: the matrix-core rate.  iters >= 0. */
+int ggq_bench_stream_read(const void *buf, int64_t bytes, void *sink, size_t sink_bytes, void *stream);
+int ggq_bench_mfma_loop(int kind, int64_t iters, void *sink, size_t sink_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -144,3 +144,18 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(g, "LIB_PATH", "/nonexistent/libggq.so")
     with pytest.raises(RuntimeError, match="no fallback"):
         g.lib()
+
+
+def test_bench_hooks_validate_before_launch(L):
+    # streaming read: negative size, null buffer, misaligned buffer, small sink
+    assert L.ggq_bench_stream_read(FAKE, -16, FAKE, 4096, None) == g.ERR_INVALID
+    assert L.ggq_bench_stream_read(None, 1024, FAKE, 4096, None) == g.ERR_INVALID
+    assert L.ggq_bench_stream_read(ctypes.c_void_p(0x10004), 1024, FAKE, 4096, None) == g.ERR_INVALID
+    assert "aligned" in err(L)
+    assert L.ggq_bench_stream_read(FAKE, 1024, FAKE, 1023, None) == g.ERR_WORKSPACE
+    assert L.ggq_bench_stream_read(FAKE, 0, None, 0, None) == g.OK              # empty: no launch
+    # MFMA loop: unknown kind, negative trips, null or small sink
+    assert L.ggq_bench_mfma_loop(2, 10, FAKE, 4096, None) == g.ERR_INVALID
+    assert L.ggq_bench_mfma_loop(0, -1, FAKE, 4096, None) == g.ERR_INVALID
+    assert L.ggq_bench_mfma_loop(1, 10, None, 4096, None) == g.ERR_INVALID
+    assert L.ggq_bench_mfma_loop(1, 10, FAKE, 4095, None) == g.ERR_WORKSPACE
