@@ -46,9 +46,9 @@ ROTATE_BYTES = 1 << 30
 # by kernel, with the hash of the kernel sources they were measured on: reported
 # as null once those sources change.
 PROFILE_TRAFFIC = {
-    "mmvq_kernel<Q4_K,NC=1>": (9715302, "67bc7d398f35ac9d"),
-    "mmvq_kernel<Q6_K,NC=1>": (419605300, "67bc7d398f35ac9d"),
-    "mmq_kernel": (506671002, "17c177108c9ab6f0"),
+    "mmvq_kernel<Q4_K,NC=1>": (9731326, "c6b032eb650ef7ae"),
+    "mmvq_kernel<Q6_K,NC=1>": (419631079, "c6b032eb650ef7ae"),
+    "mmq_kernel<Q4_K> 8192x2048 M=8192": (506669418, "7e87dc5e7738ffc6"),
 }
 KERNEL_SOURCES = {"mmvq": ("mmvq.hip", "common.hpp", "kernels.hpp"),
                   "mmq": ("mmq.hip", "common.hpp", "kernels.hpp")}
@@ -280,7 +280,7 @@ def bench_prefill(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, path=g.P
         q8 = torch.empty(M * (K // 32) * 40, dtype=torch.uint8, device=dev)
         tq = time_launches(lambda i: check(ctx.L.ggq_quantize_q8_1(vp(x), g.BF16, M, K, K, vp(q8), ctx.s), "q"), 20)
         tc = time_launches(step, 20)
-        res["roofline"] = roofline_ops(ops, max(tc - tq, 1e-9), "mmq_kernel")
+        res["roofline"] = roofline_ops(ops, max(tc - tq, 1e-9), f"mmq_kernel<{TNAME[wt]}> {N}x{K} M={M}")
         res["quantize_us"] = round(tq * 1e6, 2)
     return res
 
