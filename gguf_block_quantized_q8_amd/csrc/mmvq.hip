@@ -632,7 +632,7 @@ struct MaxWaves { static constexpr int value = 16; };
 // its columns' q8_1 activations in LDS, then each wave walks its work items
 // (spw row pairs x K-chunks), copying item i+1 into its second LDS buffer
 // while it computes item i from the first.
-// DEEP (dense, one column, many items per wave): two work items in flight per wave.
+// DEEP (one or two columns, many items per wave): two work items in flight per wave.
 template <int T, int NC, bool MOE, int EPI, int YDT, bool DEEP = false>
 __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const MmvqParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -828,7 +828,9 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
         while (pw < p.npairs) {                                 // wave-uniform
             const int64_t pair = pw + sid;
             const bool pvalid = pair < p.npairs;
-            const int64_t r0 = 2 * pair, r1 = 2 * pair + 1;
+            int64_t r0, r1;
+            if (EPI == EPI_SWIGLU) { r0 = pair; r1 = pair + p.Np; }
+            else { r0 = 2 * pair; r1 = 2 * pair + 1; }
             const bool v1 = pvalid && r1 < p.N;
             const uint8_t *Acur = chunk_addr(pw, kc);
             // item (pw, kc) has landed; the ninst copy instructions of the next one
@@ -1028,11 +1030,28 @@ static void launch_one(const MmvqParams &p, dim3 g, int waves, size_t lds, hipSt
 }
 
 template <int T, int NC>
+static void launch_deep(bool moe, int epi, int ydt, const MmvqParams &p, dim3 g, int waves, size_t lds, hipStream_t s) {
+    if (!moe) {
+        if (ydt == DT_F32) launch_one<T, NC, false, EPI_NONE, DT_F32, true>(p, g, waves, lds, s);
+        else launch_one<T, NC, false, EPI_NONE, DT_BF16, true>(p, g, waves, lds, s);
+    } else if (epi == EPI_SWIGLU) {
+        if (ydt == DT_F32) launch_one<T, NC, true, EPI_SWIGLU, DT_F32, true>(p, g, waves, lds, s);
+        else launch_one<T, NC, true, EPI_SWIGLU, DT_BF16, true>(p, g, waves, lds, s);
+    } else {
+        if (ydt == DT_F32) launch_one<T, NC, true, EPI_NONE, DT_F32, true>(p, g, waves, lds, s);
+        else launch_one<T, NC, true, EPI_NONE, DT_BF16, true>(p, g, waves, lds, s);
+    }
+}
+
+template <int T, int NC>
 static void launch_nc(bool moe, int epi, int ydt, const MmvqParams &p, dim3 g, int waves, size_t lds, hipStream_t s) {
-    if (!moe && NC == 1 && p.deep) {
-        if (ydt == DT_F32) launch_one<T, 1, false, EPI_NONE, DT_F32, true>(p, g, waves, lds, s);
-        else launch_one<T, 1, false, EPI_NONE, DT_BF16, true>(p, g, waves, lds, s);
-    } else if (!moe) {
+    if constexpr (NC <= 2) {
+        if (p.deep) {
+            launch_deep<T, NC>(moe, epi, ydt, p, g, waves, lds, s);
+            return;
+        }
+    }
+    if (!moe) {
         if (ydt == DT_F32) launch_one<T, NC, false, EPI_NONE, DT_F32>(p, g, waves, lds, s);
         else launch_one<T, NC, false, EPI_NONE, DT_BF16>(p, g, waves, lds, s);
     } else if (epi == EPI_SWIGLU) {
@@ -1155,12 +1174,12 @@ hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqPara
     const int64_t active = moe ? std::max<int64_t>(1, std::min<int64_t>(ngroups_bound, p.groups_expected)) : ngroups_bound;
     const int64_t cap = std::max<int64_t>(1, 256 * per_cu / active);
     const dim3 g((unsigned)std::min<int64_t>(need, cap), (unsigned)ngroups_bound);
-    // Dense single-column calls where a wave has several items (lm_head-sized
-    // matrices) keep two items in flight per wave (a separate instantiation:
-    // the extra code would slow the short launches, whose instruction cache
-    // starts cold).
+    // One- and two-column calls where a wave walks several items (lm_head-sized
+    // matrices; routed decode, per expert) keep two items in flight per wave
+    // (a separate instantiation: the extra code would slow the short launches,
+    // whose instruction cache starts cold).
     const int64_t nkc = (G.units + G.seg * G.upl - 1) / (G.seg * G.upl);
-    p.deep = !moe && nc == 1 && groups * nkc >= 4 * (int64_t)g.x * waves;
+    p.deep = nc <= 2 && groups * nkc >= 4 * (int64_t)g.x * waves;
     if (t == T_Q4_K) launch_t<T_Q4_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
     else if (t == T_Q6_K) launch_t<T_Q6_K>(nc, moe, epi, ydt, p, g, waves, lds, s);
     else if (t == T_Q5_K) launch_t<T_Q5_K>(nc, moe, epi, ydt, p, g, waves, lds, s);

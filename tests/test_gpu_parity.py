@@ -315,17 +315,18 @@ def test_c3_crossover_sweep_both_paths(dev, M):
 # two of them in flight (the lm_head-sized case); odd N (last row pair half
 # empty), K split over two items per row, and a weight end that is 2-byte but
 # not 4-byte aligned (the tail patch) are all covered here.
-@pytest.mark.parametrize("wt,N,K,xdt,ydt", [
-    (g.Q4_K, 262147, 512, "bf16", "bf16"),
-    (g.Q4_K, 12289, 16384, "f32", "f32"),
-    (g.Q8_0, 2000001, 32, "bf16", "f32"),
-    (g.Q6_K, 400001, 256, "f32", "bf16"),
-    (g.Q5_K, 200001, 1024, "bf16", "bf16"),
+@pytest.mark.parametrize("wt,N,K,xdt,ydt,M", [
+    (g.Q4_K, 262147, 512, "bf16", "bf16", 1),
+    (g.Q4_K, 262147, 512, "f32", "f32", 2),
+    (g.Q4_K, 12289, 16384, "f32", "f32", 1),
+    (g.Q8_0, 2000001, 32, "bf16", "f32", 1),
+    (g.Q6_K, 400001, 256, "f32", "bf16", 1),
+    (g.Q5_K, 200001, 1024, "bf16", "bf16", 1),
 ])
-def test_mmvq_long_matrix_m1(dev, wt, N, K, xdt, ydt):
-    log("long matrix M=1", wt, N, K, xdt, ydt)
+def test_mmvq_long_matrix(dev, wt, N, K, xdt, ydt, M):
+    log("long matrix", wt, N, K, xdt, ydt, "M", M)
     W = inputs.gen_weights(wt, N, K, 700 + wt)
-    x = inputs.gen_act(1, K, 701, xdt)
+    x = inputs.gen_act(M, K, 701, xdt)
     out = torch.float32 if ydt == "f32" else torch.bfloat16
     y = host(g.mul_mat(T(W, dev), wt, T(x, dev), out_dtype=out, path="mmvq"))
     r = rel(y, ref_out(oracle.mul_mat(wt, W, N, K, x), ydt))
@@ -383,6 +384,28 @@ def test_moe_edge_routes(dev, path, wt):
     log("moe edges", wt, path, r)
     assert r <= TOL["f32"]
     assert (host(y)[1, 2] == 0).all() and (host(y)[3] == 0).all() and (host(y)[2, 0] == 0).all()
+    assert int(ws[:4].view(torch.int32).item()) == 1
+
+
+@pytest.mark.parametrize("epi", [0, 1])
+def test_moe_decode_many_experts_edges(dev, epi):
+    """Routed decode with many active experts and long expert matrices, the
+    shape where each wave walks several items and keeps two in flight:
+    duplicate, inactive and out-of-range ids, plain and SwiGLU outputs."""
+    E, N, K, Tn, top_k = 128, 4096, 512, 16, 8                           # about one route per expert: 2-column groups
+    W = inputs.gen_experts(g.Q4_K, E, N, K, 530)
+    x = inputs.gen_act(Tn, K, 531, "bf16")
+    ids = inputs.rng(532).integers(0, E, (Tn, top_k)).astype(np.int32)
+    ids[0] = 5                                                           # one token, one expert, 8 times
+    ids[1, :3] = -1
+    ids[2, 7] = E + 3                                                    # skipped and counted
+    y, ws = g.mul_mat_id(T(W, dev), g.Q4_K, T(x, dev), T(ids, dev), K, epi=epi, out_dtype=torch.float32,
+                         path="mmvq", return_workspace=True)
+    ref = _moe_ref(g.Q4_K, W, K, x, ids, top_k, epi=oracle.EPI_SWIGLU if epi else oracle.EPI_NONE)
+    r = rel(host(y), ref)
+    log("moe decode, many experts", epi, r)
+    assert r <= TOL["f32"]
+    assert (host(y)[1, :3] == 0).all() and (host(y)[2, 7] == 0).all()
     assert int(ws[:4].view(torch.int32).item()) == 1
 
 
