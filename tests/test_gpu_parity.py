@@ -60,7 +60,9 @@ def log(*a):
 # ------------------------------------------------------------------ q8_1
 
 @pytest.mark.parametrize("xdt", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("M,K,ldx", [(1, 32, 32), (7, 512, 512), (33, 2048, 2080), (300, 4096, 4096)])
+@pytest.mark.parametrize("M,K,ldx", [(1, 32, 32), (7, 512, 512), (33, 2048, 2080), (300, 4096, 4096),
+                                     (4, 96, 104),                  # ldx % 16 == 8: 8 values per lane
+                                     (5, 32, 36), (9, 64, 66)])     # ldx % 8 != 0: the 8-lane kernel
 def test_quantize_bit_exact(dev, xdt, M, K, ldx):
     log("quantize", xdt, M, K, ldx)
     x = inputs.gen_act(M, ldx, 1000 + M, xdt)
