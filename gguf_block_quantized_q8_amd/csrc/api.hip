@@ -344,15 +344,19 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     const int64_t Np = epi == GGQ_EPI_SWIGLU ? N / 2 : N;
     const int64_t rows = x_per_route ? R : T;
     const int J = mmq ? MMQ_MT : mmvq_id_cols(wt, R, E, K);
-    rc = hip_status(launch_route_build(ids, R, E, J, L.rt, s), "mul_mat_id routes");
-    if (rc) return rc;
     // q8_1 output: MMQ quantizes in its epilogue; MMVQ writes the values (in the
     // 16-bit input's dtype, else fp32) to the workspace and the q8_1 kernel follows
     const bool q8_out = ydt == GGQ_Q8_1;
     const int hdt = xdt == GGQ_BF16 || xdt == GGQ_F16 ? xdt : GGQ_F32;
     void *yk = q8_out && !mmq ? L.hstage : y;               // what the matmul kernel writes
     const int ydt_k = q8_out && !mmq ? hdt : ydt;
-    if (!weighted) {
+    // unweighted output: the rows of inactive routes are zeros (by the one-workgroup
+    // route build when it runs, else by their own kernel)
+    bool zeroed = false;
+    rc = hip_status(launch_route_build(ids, R, E, J, L.rt, s, weighted ? nullptr : yk, Np, ydt_k, &zeroed),
+                    "mul_mat_id routes");
+    if (rc) return rc;
+    if (!weighted && !zeroed) {
         rc = hip_status(launch_zero_inactive(ids, R, E, Np, yk, ydt_k, s), "mul_mat_id zero");
         if (rc) return rc;
     }

@@ -362,33 +362,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 }
 
 // Zero the output rows of inactive routes (id < 0 or id >= E) in the
-// unweighted mul_mat_id output y[T*top_k][Np].  One thread per route reads
-// its id; each wave then zeroes its inactive routes' rows one at a time with
-// all 64 lanes (inactive routes are rare, so most waves only read ids).
+// unweighted mul_mat_id output y[T*top_k][Np]: one lane per route.
 template <int YDT>
 __global__ __launch_bounds__(256) void zero_inactive_kernel(const int32_t *__restrict__ ids, int64_t R, int64_t E,
                                                             int64_t Np, void *__restrict__ y) {
     const int64_t r0 = (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63u);   // this wave's first route
-    const int lane = threadIdx.x & 63;
-    bool dead = false;
-    if (r0 + lane < R) {
-        const int32_t e = ids[r0 + lane];
-        dead = e < 0 || e >= E;
-    }
-    for (uint64_t m = __ballot(dead); m; m &= m - 1) {
-        const int64_t r = r0 + __builtin_ctzll(m);
-        if (YDT == DT_Q8_1) {
-            // Np / 32 all-zero q8_1 blocks (d = s = 0, q = 0): what an all-zero row quantizes to
-            const int64_t words = Np / QK8_1 * (Q8_1_BYTES / 4);
-            uint32_t *o = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(y) + r * (Np / QK8_1) * Q8_1_BYTES);
-            for (int64_t i = lane; i < words; i += 64) o[i] = 0u;
-        } else {
-            for (int64_t n = lane; n < Np; n += 64) {
-                if (YDT == DT_F32) static_cast<float *>(y)[r * Np + n] = 0.0f;
-                else static_cast<uint16_t *>(y)[r * Np + n] = 0;
-            }
-        }
-    }
+    zero_dead_routes<YDT>(ids, R, E, Np, y, r0, threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------------------

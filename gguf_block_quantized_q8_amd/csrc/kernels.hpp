@@ -6,6 +6,35 @@
 
 namespace ggq {
 
+// Zero the output rows of the inactive routes (id < 0 or id >= E) among
+// routes [r0, r0 + 64) of the unweighted mul_mat_id output y[R][Np]: each lane
+// reads one id, and the wave zeroes each inactive route's row with all 64
+// lanes (inactive routes are rare, so most waves only read ids).  YDT: DT_F32,
+// DT_BF16 (any 16-bit output) or DT_Q8_1 (Np / 32 all-zero blocks, what an
+// all-zero row quantizes to).  Called by whole waves.
+template <int YDT>
+__device__ __forceinline__ void zero_dead_routes(const int32_t *__restrict__ ids, int64_t R, int64_t E, int64_t Np,
+                                                 void *__restrict__ y, int64_t r0, int lane) {
+    bool dead = false;
+    if (r0 + lane < R) {
+        const int32_t e = ids[r0 + lane];
+        dead = e < 0 || e >= E;
+    }
+    for (uint64_t m = __ballot(dead); m; m &= m - 1) {
+        const int64_t r = r0 + __builtin_ctzll(m);
+        if (YDT == DT_Q8_1) {
+            const int64_t words = Np / QK8_1 * (Q8_1_BYTES / 4);
+            uint32_t *o = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(y) + r * (Np / QK8_1) * Q8_1_BYTES);
+            for (int64_t i = lane; i < words; i += 64) o[i] = 0u;
+        } else {
+            for (int64_t n = lane; n < Np; n += 64) {
+                if (YDT == DT_F32) static_cast<float *>(y)[r * Np + n] = 0.0f;
+                else static_cast<uint16_t *>(y)[r * Np + n] = 0;
+            }
+        }
+    }
+}
+
 // ---- convert.hip ----
 hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, uint8_t *q8, _Float16 *xq,
                            float *xd, float *xs, hipStream_t s);
@@ -37,8 +66,10 @@ struct RouteTables {
     int4 *tiles;          // [max_tiles] {expert, start, count, 0}
 };
 int64_t route_max_tiles(int64_t R, int64_t E, int J);
+// zy != nullptr: also zero the rows of the inactive routes in zy[R][Np] (dtype zdt) when the
+// build runs as one workgroup (returns whether it did; else the caller zeroes them)
 hipError_t launch_route_build(const int32_t *ids, int64_t R, int64_t E, int J, const RouteTables &rt,
-                              hipStream_t s);
+                              hipStream_t s, void *zy = nullptr, int64_t Np = 0, int zdt = 0, bool *zeroed = nullptr);
 
 // ---- mmvq.hip ----
 struct MmvqParams {

@@ -121,13 +121,17 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t *__res
 constexpr int64_t ROUTE_SMALL_R = 16384;
 constexpr int64_t ROUTE_SMALL_E = 4096;
 
+// ZDT >= 0: also zero the inactive routes' rows of the unweighted output zy
+// (what zero_inactive_kernel does), saving that launch.
+template <int ZDT>
 __global__ __launch_bounds__(1024) void route_build_small_kernel(const int32_t *__restrict__ ids, int64_t R, int64_t E,
                                                                  int J, uint32_t *__restrict__ counts,
                                                                  uint32_t *__restrict__ offsets,
                                                                  uint32_t *__restrict__ tile_off,
                                                                  uint32_t *__restrict__ ntiles, int4 *__restrict__ tiles,
                                                                  int32_t *__restrict__ rank, int32_t *__restrict__ perm,
-                                                                 uint32_t *__restrict__ bad) {
+                                                                 uint32_t *__restrict__ bad, void *__restrict__ zy,
+                                                                 int64_t Np) {
     __shared__ uint32_t s_cnt[ROUTE_SMALL_E], s_off[ROUTE_SMALL_E];
     __shared__ uint32_t s_c[1024], s_t[1024];
     __shared__ uint32_t s_bad, carry_c, carry_t;
@@ -184,13 +188,22 @@ __global__ __launch_bounds__(1024) void route_build_small_kernel(const int32_t *
         *ntiles = carry_t;
         *bad = s_bad;
     }
+    if (ZDT >= 0)
+        for (int64_t r0 = (int64_t)(tid & ~63); r0 < R; r0 += 1024) zero_dead_routes<ZDT>(ids, R, E, Np, zy, r0, tid & 63);
 }
 
 hipError_t launch_route_build(const int32_t *ids, int64_t R, int64_t E, int J, const RouteTables &rt,
-                              hipStream_t s) {
+                              hipStream_t s, void *zy, int64_t Np, int zdt, bool *zeroed) {
+    if (zeroed) *zeroed = false;
     if (R <= ROUTE_SMALL_R && E <= ROUTE_SMALL_E) {
-        hipLaunchKernelGGL(route_build_small_kernel, dim3(1), dim3(1024), 0, s, ids, R, E, J, rt.counts, rt.offsets,
-                           rt.tile_off, rt.ntiles, rt.tiles, rt.rank, rt.perm, rt.bad);
+#define GGQ_RB(Z) hipLaunchKernelGGL(route_build_small_kernel<Z>, dim3(1), dim3(1024), 0, s, ids, R, E, J, rt.counts, \
+                                     rt.offsets, rt.tile_off, rt.ntiles, rt.tiles, rt.rank, rt.perm, rt.bad, zy, Np)
+        if (!zy) GGQ_RB(-1);
+        else if (zdt == DT_F32) GGQ_RB(DT_F32);
+        else if (zdt == DT_Q8_1) GGQ_RB(DT_Q8_1);
+        else GGQ_RB(DT_BF16);                                   // any 16-bit output: 16-bit zeros
+#undef GGQ_RB
+        if (zeroed) *zeroed = zy != nullptr;
         return hipGetLastError();
     }
     hipError_t err = launch_fill_u32(rt.counts, E, 0u, s);
