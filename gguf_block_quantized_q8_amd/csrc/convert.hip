@@ -306,11 +306,16 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
 //   y[t][n] = sum over k in ascending order of w[t][k] * o[t*top_k + k][n]
 // for the active routes of token t (0 <= id < E), accumulated in fp32, then
 // stored in the output dtype.  One thread per V consecutive n (V = 4 when Np
-// is a multiple of 4, else 1).
+// is a multiple of 4, else 1).  The routes go in chunks of 8 whose row loads
+// are all issued before the first fma (one memory latency per chunk, not per
+// route); an inactive route's row (never written) is replaced by zeros after
+// its load, so it cannot feed a NaN into the sum.
 template <int YDT, int V>
 __global__ __launch_bounds__(256) void route_sum_kernel(const float *__restrict__ o, const int32_t *__restrict__ ids,
                                                         const float *__restrict__ w, int64_t T, int top_k, int64_t E,
                                                         int64_t Np, void *__restrict__ y) {
+    constexpr int KC = 8;
+    typedef float vf __attribute__((ext_vector_type(V)));
     const int64_t q = Np / V;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t st = (int64_t)gridDim.x * blockDim.x;
@@ -318,16 +323,27 @@ __global__ __launch_bounds__(256) void route_sum_kernel(const float *__restrict_
         const int64_t t = i / q, n = V * (i - t * q);
         float acc[V];
         for (int c = 0; c < V; c++) acc[c] = 0.0f;
-        for (int k = 0; k < top_k; k++) {
-            const int64_t r = t * top_k + k;
-            const int32_t e = ids[r];
-            if (e < 0 || e >= E) continue;
-            const float wk = w[r];
-            if (V == 4) {
-                const v4f v = *reinterpret_cast<const v4f *>(o + r * Np + n);
-                for (int c = 0; c < V; c++) acc[c] = __builtin_fmaf(wk, v[c], acc[c]);
-            } else {
-                acc[0] = __builtin_fmaf(wk, o[r * Np + n], acc[0]);
+        for (int k0 = 0; k0 < top_k; k0 += KC) {
+            bool on[KC];
+            float wk[KC];
+            vf v[KC];
+#pragma unroll
+            for (int k = 0; k < KC; k++) {
+                const int64_t r = t * top_k + k0 + k;
+                on[k] = false;
+                wk[k] = 0.0f;
+                if (k0 + k < top_k) {
+                    const int32_t e = ids[r];
+                    on[k] = e >= 0 && e < E;
+                    wk[k] = w[r];
+                    v[k] = *reinterpret_cast<const vf *>(o + r * Np + n);
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < KC; k++) {
+                if (!on[k]) continue;
+#pragma unroll
+                for (int c = 0; c < V; c++) acc[c] = __builtin_fmaf(wk[k], v[k][c], acc[c]);
             }
         }
         const int64_t idx = t * Np + n;
