@@ -628,3 +628,88 @@ def test_c5_moe_t16_mmq(dev):
 def test_c5_moe_t8192_sampled(dev):
     toks = inputs.sample_rows(8192, 512, 505)
     _c5(dev, 8192, "auto", tokens=toks)
+
+
+# ------------------------------------------------------------------ streams and graphs
+
+def _graph_case(dev):
+    """Static inputs and a step that runs every kind of call once: quantize,
+    MMVQ and MMQ (split K) dense calls, and a routed layer twice (16 tokens:
+    the one-workgroup route build; 2100 tokens x 8: the multi-kernel build with
+    its counter fills), unweighted SwiGLU gate_up and a weighted down."""
+    E, H, I, top_k = 8, 1024, 256, 8
+    W = T(inputs.gen_q4_K(512, H, 810), dev)
+    Wgu = T(inputs.gen_experts(g.Q4_K, E, 2 * I, H, 811), dev)
+    Wd = T(inputs.gen_experts(g.Q6_K, E, H, I, 812), dev)
+    st = {"x1": torch.empty((1, H), dtype=torch.bfloat16, device=dev),
+          "x2": torch.empty((64, H), dtype=torch.bfloat16, device=dev)}
+    for Tn in (16, 2100):
+        st[f"xt{Tn}"] = torch.empty((Tn, H), dtype=torch.bfloat16, device=dev)
+        st[f"ids{Tn}"] = torch.empty((Tn, top_k), dtype=torch.int32, device=dev)
+        st[f"w{Tn}"] = torch.empty((Tn, top_k), dtype=torch.float32, device=dev)
+
+    def fill(seed):
+        st["x1"].copy_(T(inputs.gen_act(1, H, seed, "bf16"), dev))
+        st["x2"].copy_(T(inputs.gen_act(64, H, seed + 1, "bf16"), dev))
+        for Tn in (16, 2100):
+            st[f"xt{Tn}"].copy_(T(inputs.gen_act(Tn, H, seed + 2, "bf16"), dev))
+            ids, w = inputs.gen_routing(Tn, E, top_k, seed + 3)
+            ids[0, 1] = -1                                  # an inactive route
+            st[f"ids{Tn}"].copy_(T(ids, dev))
+            st[f"w{Tn}"].copy_(T(w, dev))
+
+    def step():
+        out = [g.quantize_q8_1(st["x2"]),
+               g.mul_mat(W, g.Q4_K, st["x1"], path="mmvq"),
+               g.mul_mat(W, g.Q4_K, st["x2"], path="mmq")]
+        for Tn in (16, 2100):
+            h = g.mul_mat_id(Wgu, g.Q4_K, st[f"xt{Tn}"], st[f"ids{Tn}"], H, epi=g.EPI_SWIGLU)
+            out += [h, g.mul_mat_id(Wd, g.Q6_K, h, st[f"ids{Tn}"], I, route_w=st[f"w{Tn}"], x_per_route=True)]
+        return out
+
+    return fill, step
+
+
+def test_side_stream_matches_default(dev):
+    fill, step = _graph_case(dev)
+    fill(820)
+    ref = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        got = step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_graph_replay_matches_eager(dev):
+    """Captured once, replayed three times on new inputs with eager work and
+    synchronizations between replays: every replay equals the eager call bit
+    for bit (all kernels are deterministic)."""
+    fill, step = _graph_case(dev)
+    fill(830)
+    step()                                                  # warm call before capture
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        outs = step()
+    for rep in range(3):
+        fill(840 + 10 * rep)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in outs]
+        ref = step()                                        # eager, same inputs
+        torch.cuda.synchronize()
+        log("graph replay", rep)
+        for a, b in zip(got, ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
