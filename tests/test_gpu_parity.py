@@ -253,6 +253,22 @@ def test_mmq_split_k(dev, wt, ydt):
     assert (out[:, N:] == 3.0).all()
 
 
+@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K, g.Q8_0])
+@pytest.mark.parametrize("path,M", [("mmvq", 1), ("mmvq", 5), ("mmq", 40)])
+@pytest.mark.parametrize("xdt,pad", [("bf16", 8), ("bf16", 3), ("f32", 1)])
+def test_input_row_stride(dev, wt, path, M, xdt, pad):
+    """Activation rows ldx = K + pad apart: 16-byte multiples (MMVQ copies the rows
+    by DMA, the wide quantizer runs) and odd strides (MMVQ's direct loads at 2-byte
+    alignment, the 8-lane quantizer)."""
+    N, K = 96, 512
+    W = inputs.gen_weights(wt, N, K, 900 + wt)
+    xf = inputs.gen_act(M, K + pad, 901 + pad, xdt)
+    y = g.mul_mat(T(W, dev), wt, T(xf, dev)[:, :K], out_dtype=torch.float32, path=path)
+    r = rel(host(y), oracle.mul_mat(wt, W, N, K, np.ascontiguousarray(xf[:, :K])))
+    log("input stride", wt, path, M, xdt, pad, r)
+    assert r <= TOL["f32"]
+
+
 def test_q8_1_input_reuse(dev):
     """Pre-quantized q8_1 input gives the same result as float input, on both paths."""
     W = inputs.gen_q4_K(96, 512, 90)
