@@ -120,18 +120,26 @@ struct Stager {
         xs = (UNIT || !HAS_MIN) ? nullptr : sx + xr * nb + 4 * hf;
     }
 
+    // Stages are loaded once each, in order (load(s + 1) after store(s)), so
+    // registers that the next stage would load again keep their bytes: a
+    // K-quant super-block's header (Q5_K: also its fifth bits; Q6_K: its
+    // scales and d) is loaded at its first stage only, Q4_K / Q5_K quant bytes
+    // once per pair of stages (low nibbles, then high), Q6_K high bits once
+    // per four.
     __device__ void load(int s) {
         const int hf = threadIdx.x & 1;
         const int sb = s >> 3, j = s & 7;
         if (T == T_Q4_K) {
             const uint8_t *blk = wrow + (int64_t)sb * 144;
-            hdr = gld16(blk);
-            q0 = gld16(blk + 16 + 32 * (j >> 1) + 16 * hf);
+            if (j == 0) hdr = gld16(blk);
+            if ((j & 1) == 0) q0 = gld16(blk + 16 + 32 * (j >> 1) + 16 * hf);
         } else if (T == T_Q5_K) {
             const uint8_t *blk = wrow + (int64_t)sb * 176;
-            hdr = gld16(blk);
-            q0 = gld16(blk + 48 + 32 * (j >> 1) + 16 * hf);
-            q1 = gld16(blk + 16 + 16 * hf);                         // fifth bits of positions 16 hf ..
+            if (j == 0) {
+                hdr = gld16(blk);
+                q1 = gld16(blk + 16 + 16 * hf);                     // fifth bits of positions 16 hf ..
+            }
+            if ((j & 1) == 0) q0 = gld16(blk + 48 + 32 * (j >> 1) + 16 * hf);
         } else if (T == T_Q8_0) {
             const uint8_t *blk = wrow + (int64_t)s * 34;           // one block per stage
             q0 = ld16_a2(blk + 2 + 16 * hf);
@@ -144,9 +152,11 @@ struct Stager {
             const uint8_t *blk = wrow + (int64_t)sb * 210;
             const int hh = j >> 2, g = j & 3;
             q0 = ld16_a2(blk + 64 * hh + 32 * (g & 1) + 16 * hf);
-            q1 = ld16_a2(blk + 128 + 32 * hh + 16 * hf);
-            hdr = ld16_a2(blk + 192);
-            d6 = ld_u16(blk + 208);
+            if (g == 0) q1 = ld16_a2(blk + 128 + 32 * hh + 16 * hf);
+            if (j == 0) {
+                hdr = ld16_a2(blk + 192);
+                d6 = ld_u16(blk + 208);
+            }
         }
         const _Float16 *src = xrow + (int64_t)s * KS;
         b0 = *reinterpret_cast<const v4i *>(src);
