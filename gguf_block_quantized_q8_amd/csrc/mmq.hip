@@ -104,6 +104,7 @@ struct Stager {
     const float *xd, *xs;     // d, s of this thread's activation row + 4 * half
     v4i hdr;        // Q4_K / Q5_K: block header (d, dmin, 12 scale bytes); Q6_K: the 16 int8 scales
     v4i q0, q1;     // Q4_K: 16 quant bytes (q0); Q5_K: also 16 fifth-bit bytes (q1);
+    v4i q0o;        // Q6_K: the 16 ql bytes of the odd groups (q0: even groups)
                     // Q6_K: 16 ql bytes (q0), 16 qh bytes (q1); Q8_0: this half's 16 int8 quants;
                     // Q4_0: the block's 16 nibble bytes (both halves)
     uint32_t d6;    // Q6_K, Q8_0, Q4_0: fp16 d
@@ -124,8 +125,8 @@ struct Stager {
     // registers that the next stage would load again keep their bytes: a
     // K-quant super-block's header (Q5_K: also its fifth bits; Q6_K: its
     // scales and d) is loaded at its first stage only, Q4_K / Q5_K quant bytes
-    // once per pair of stages (low nibbles, then high), Q6_K high bits once
-    // per four.
+    // once per pair of stages (low nibbles, then high), Q6_K low bits once per
+    // pair (groups g and g + 2) and high bits once per four.
     __device__ void load(int s) {
         const int hf = threadIdx.x & 1;
         const int sb = s >> 3, j = s & 7;
@@ -151,7 +152,9 @@ struct Stager {
         } else {
             const uint8_t *blk = wrow + (int64_t)sb * 210;
             const int hh = j >> 2, g = j & 3;
-            q0 = ld16_a2(blk + 64 * hh + 32 * (g & 1) + 16 * hf);
+            // groups g and g + 2 share their ql bytes (low, then high nibbles)
+            if (g == 0) q0 = ld16_a2(blk + 64 * hh + 16 * hf);
+            if (g == 1) q0o = ld16_a2(blk + 64 * hh + 32 + 16 * hf);
             if (g == 0) q1 = ld16_a2(blk + 128 + 32 * hh + 16 * hf);
             if (j == 0) {
                 hdr = ld16_a2(blk + 192);
@@ -219,7 +222,8 @@ struct Stager {
             uint32_t oh[8], ol[8];
 #pragma unroll
             for (int w = 0; w < 4; w++) {
-                const uint32_t lo = g < 2 ? ((uint32_t)q0[w] & 0x0f0f0f0fu) : (((uint32_t)q0[w] >> 4) & 0x0f0f0f0fu);
+                const uint32_t ql = (uint32_t)((g & 1) ? q0o[w] : q0[w]);
+                const uint32_t lo = g < 2 ? (ql & 0x0f0f0f0fu) : ((ql >> 4) & 0x0f0f0f0fu);
                 const uint32_t q6 = lo | ((((uint32_t)q1[w] >> (2 * g)) & 0x03030303u) << 4);   // 0..63 per byte
 #pragma unroll
                 for (int hlf = 0; hlf < 2; hlf++) {
