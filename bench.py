@@ -48,7 +48,7 @@ ROTATE_BYTES = 1 << 30
 PROFILE_TRAFFIC = {
     "mmvq_kernel<Q4_K,NC=1>": (9739530, "e3135b38c3555ade"),
     "mmvq_kernel<Q6_K,NC=1>": (419646577, "e3135b38c3555ade"),
-    "mmq_kernel<Q4_K> 8192x2048 M=8192": (506675845, "64d8bcca905857ca"),
+    "mmq_kernel<Q4_K> 8192x2048 M=8192": (511689042, "7b36954cd3bc59be"),
 }
 KERNEL_SOURCES = {"mmvq": ("mmvq.hip", "common.hpp", "kernels.hpp"),
                   "mmq": ("mmq.hip", "common.hpp", "kernels.hpp")}
