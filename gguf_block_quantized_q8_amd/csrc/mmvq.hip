@@ -771,7 +771,10 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
 
     const bool patch = (reinterpret_cast<uintptr_t>(wend) & 2) != 0;
     if constexpr (DEEP) {
-        // row pair complete: reduce across the segment, store, and clear
+        // row pair complete: reduce across the segment, store, and clear (the
+        // one-ahead loop below keeps its own inline copy of these stores:
+        // routing it through this lambda changes that loop's code, and the
+        // short launches it serves start with a cold instruction cache)
         auto finish_pair = [&](bool pvalid, bool v1, int64_t r0, int64_t r1) {
 #pragma unroll
             for (int i = 0; i < 2; i++)
