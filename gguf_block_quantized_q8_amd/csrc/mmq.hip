@@ -424,9 +424,12 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
             sm.xrow[tid] = xr;
             sm.route[tid] = r;
         }
-    } else if (tid < MT) {
-        const int64_t m = bm * MT + tid;
-        sm.xrow[tid] = m < p.M ? (int32_t)m : -1;
+    } else {
+        tile_count = (int)min<int64_t>(MT, p.M - bm * MT);     // activation rows present in this tile
+        if (tid < MT) {
+            const int64_t m = bm * MT + tid;
+            sm.xrow[tid] = m < p.M ? (int32_t)m : -1;
+        }
     }
     // ---- tile rows (weight rows) ----
     if (tid >= MT) {
@@ -456,6 +459,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
     const int nst_all = (int)(p.K / KS), per = nst_all / (!MOE && p.ksplit > 1 ? p.ksplit : 1);
     const int s0 = slice * per, nst = s0 + per;
     const int lr = lane & 31, kh = 8 * (lane >> 5);
+    const bool live = 64 * wm < tile_count;                   // this wave's columns are not all empty
     Stager<T, false> S;
     {
         // rows / columns past the matrix stage row 0 / activation row 0 (never stored)
@@ -473,8 +477,11 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
         if (s + 1 < nst) S.store(sm, s + 1);                 // into the other buffer
         if (s + 2 < nst) S.load(s + 2);
         // ---- this stage: one q8_1 block of every column ----
+        // (a wave whose 64 columns are all empty, in a routed tile's remainder or
+        // past the last activation row, skips the compute; it still stages and
+        // meets the barriers)
 #pragma unroll
-        for (int ni = 0; ni < 2; ni++) {
+        for (int ni = 0; ni < (live ? 2 : 0); ni++) {
             v16f C[2] = {v16f{}, v16f{}};
 #pragma unroll
             for (int kk = 0; kk < 2; kk++) {
@@ -517,7 +524,7 @@ __global__ __launch_bounds__(256, 2) void mmq_kernel(const MmqParams p) {
                 }
             }
         }
-        if (j == 7 && !kBlk32<T>) {
+        if (j == 7 && !kBlk32<T> && live) {
             // ---- end of super-block: P * d (- dmin * min term) into acc ----
             if (MmqSmem<T>::NMIN) {
                 // one weight half-tile (ni) at a time: 32 registers of min-term sums live, not 64
