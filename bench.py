@@ -48,7 +48,7 @@ ROTATE_BYTES = 1 << 30
 PROFILE_TRAFFIC = {
     "mmvq_kernel<Q4_K,NC=1>": (9739489, "37d83509590215cf"),
     "mmvq_kernel<Q6_K,NC=1>": (419708938, "37d83509590215cf"),
-    "mmq_kernel<Q4_K> 8192x2048 M=8192": (511689042, "7b36954cd3bc59be"),
+    "mmq_kernel<Q4_K> 8192x2048 M=8192": (511636112, "42618ed8d0f70088"),
 }
 KERNEL_SOURCES = {"mmvq": ("mmvq.hip", "common.hpp", "kernels.hpp"),
                   "mmq": ("mmq.hip", "common.hpp", "kernels.hpp")}
