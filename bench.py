@@ -2,10 +2,13 @@
 
 Default (the headline): Q4_K 4096 x 4096 decode at M = 1 (bf16 activations
 quantized to q8_1 on the fly, MMVQ, bf16 out).  One step = one full call
-(q8_1 quantization + MMVQ) against the next of 120 weight copies (1.13 GB),
-so every step streams its weights from HBM rather than the 256 MB MALL; the K
-timed steps are captured in one HIP graph so launch overhead is not timed.
-value = algorithmic bytes per step x K / time (GB/s).
+(q8_1 quantization + MMVQ) against the next of about 114 weight copies
+(1 GiB), captured in one HIP graph so launch overhead on the host is not
+timed.  Before each timed graph replay 1 GiB of an unrelated buffer is
+streamed through the caches, so the timed steps read their weights from HBM
+rather than the 256 MB last-level cache, whatever the step count.
+value = algorithmic bytes per step x K / time (GB/s) of the first timed
+region; step_us_median / p10 / p90 come from that region and the repeats.
 
 The same JSON line carries, under "also", the other workloads of the
 benchmark set, each timed the same way: Q4_K 4096x4096 at M = 2, 4, 8; the
@@ -15,10 +18,10 @@ both paths; the Q6_K 248320 x 2048 lm_head at M = 1 (GB/s) and M = 2048
 route-weighted sum) at T = 16 and T = 8192.
 
 roofline: the dominant kernel's algorithmic bytes (or int8 ops) per launch over
-its mean launch duration, measured with HIP events recorded on the launch
-stream around each launch, against MI355X peaks (HBM 8 TB/s; dense int8 MFMA
-5.0 POP/s).  cpu_baseline: the CPU oracle on a bounded sample of the headline
-workload, on this host's cores.
+its launch duration from HIP events recorded on the launch stream (the source
+is named in each object), against MI355X peaks (HBM 8 TB/s; dense int8 MFMA
+5.0 POP/s).  cpu_baseline: the CPU oracle on the whole headline workload, on
+all of this host's cores and on one thread.
 """
 import argparse
 import ctypes
@@ -89,21 +92,36 @@ class Ctx:
         self.dev = dev
         self.L = g.lib()
         self.stream = torch.cuda.current_stream(dev)
+        self._flush = None
+        self._sink = torch.zeros(4096, dtype=torch.uint8, device=dev)
+
+    def evict(self):
+        """Stream 1 GiB of an unrelated buffer through the caches (4x the
+        256 MB last-level cache), so the next timed region reads its inputs from HBM."""
+        if self._flush is None:
+            self._flush = torch.ones(ROTATE_BYTES, dtype=torch.uint8, device=self.dev)
+        check(self.L.ggq_bench_stream_read(vp(self._flush), ROTATE_BYTES, vp(self._sink), 4096, self.s), "evict")
 
     @property
     def s(self):
         return ctypes.c_void_p(torch.cuda.current_stream(self.dev).cuda_stream)
 
 
-def time_steps(step, K, W, graph):
+def time_steps(step, K, W, graph, evict=None, reps=5):
     """W untimed warmup steps, then exactly K timed steps (optionally as one HIP graph).
+
+    Before every timed region `evict` (if given) streams 1 GiB through the
+    caches, so the steps' inputs come from HBM, whatever K is: the untimed
+    replay just before has read the same buffers.  The first timed region is
+    the measurement; `reps` - 1 more (each after an eviction) give the spread.
 
     Returns (wall seconds from perf_counter between two synchronizations, GPU
     seconds between HIP events recorded on the launch stream around the timed
-    region)."""
+    region, list of per-step GPU seconds of every timed region)."""
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
+    gr = None
     if graph:
         gr = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
@@ -117,38 +135,59 @@ def time_steps(step, K, W, graph):
                 step(i)
         gr.replay()                        # untimed first replay (uploads the graph)
         torch.cuda.synchronize()
+
+    def run():
+        if gr is not None:
+            gr.replay()
+        else:
+            for i in range(K):
+                step(i)
+
+    per_step, first = [], None
+    for rep in range(max(1, reps)):
+        if evict is not None:
+            evict()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record()
-        gr.replay()
+        run()
         e1.record()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
-        del gr
-        return dt, e0.elapsed_time(e1) * 1e-3
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(K):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    return time.perf_counter() - t0, e0.elapsed_time(e1) * 1e-3
+        gpu = e0.elapsed_time(e1) * 1e-3
+        per_step.append(gpu / K)
+        if first is None:
+            first = (dt, gpu)
+    del gr
+    return first[0], first[1], per_step
 
 
-def time_launches(launch, n):
-    """Mean duration of one launch: HIP events recorded on the launch stream around each launch."""
+def spread(per_step_s):
+    """Median and 10th / 90th percentiles of per-step times, in microseconds."""
+    a = np.asarray(per_step_s) * 1e6
+    return {"step_us_median": round(float(np.median(a)), 3), "step_us_p10": round(float(np.percentile(a, 10)), 3),
+            "step_us_p90": round(float(np.percentile(a, 90)), 3), "timed_regions": int(a.size)}
+
+
+def time_launches(launch, n, evict=None, stats=False):
+    """Duration of one launch: HIP events recorded on the launch stream around
+    each launch (after an eviction of the caches when `evict` is given).
+    Returns the mean, or (mean, median, p10, p90) with stats."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     launch(0)
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(evs):
+        if evict is not None:
+            evict()
         a.record()
         launch(i)
         b.record()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    return float(np.mean(ms)) * 1e-3
+    ms = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    if stats:
+        return float(ms.mean()), float(np.median(ms)), float(np.percentile(ms, 10)), float(np.percentile(ms, 90))
+    return float(ms.mean())
 
 
 def roofline_bytes(nbytes, sec, kernel):
@@ -182,11 +221,11 @@ def bench_ceilings(ctx, steps, warmup):
     def step(i):
         check(L.ggq_bench_stream_read(ctypes.c_void_p(buf.data_ptr() + (i % R) * small), small, vp(sink), 4096,
                                       ctx.s), "bench_stream_read")
-    dt, gpu = time_steps(step, steps, warmup, graph=True)
+    dt, gpu, _ = time_steps(step, steps, warmup, graph=True, evict=ctx.evict, reps=1)
     out["read_gbs_9MB"] = round(small * steps / gpu / 1e9, 1)
     big = 417177600                                     # the lm_head's weight bytes
     sec = time_launches(lambda i: check(L.ggq_bench_stream_read(vp(buf), big, vp(sink), 4096, ctx.s),
-                                        "bench_stream_read"), 20)
+                                        "bench_stream_read"), 10, evict=ctx.evict)
     out["read_gbs_417MB"] = round(big / sec / 1e9, 1)
     del buf
     iters = 20000
@@ -228,13 +267,15 @@ def bench_decode(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, rotate=Tr
                                 g.PATH_MMVQ, ctx.s), "mul_mat")
 
     # one step is one launch of the MMVQ kernel (it quantizes the activations itself)
-    dt, gpu = time_steps(step, steps, warmup, graph=True)
+    dt, gpu, per = time_steps(step, steps, warmup, graph=True, evict=ctx.evict)
     ysz = 4 if ydt == torch.float32 else 2
     step_bytes = wbytes + M * K * 2 + M * N * ysz     # weights + bf16 activations + output
     del Wr
+    roof = roofline_bytes(step_bytes, gpu / steps, f"mmvq_kernel<{TNAME[wt]},NC={min(8, M)}>")
+    roof["kernel_us_source"] = "HIP events around the timed graph replay of K launches, divided by K"
     return {"value": step_bytes * steps / dt / 1e9, "unit": "GB/s", "ms_per_step": dt / steps * 1e3,
-            "step_bytes": step_bytes, "rotating_copies": R,
-            "roofline": roofline_bytes(step_bytes, gpu / steps, f"mmvq_kernel<{TNAME[wt]},NC={min(8, M)}>")}
+            "step_bytes": step_bytes, "rotating_copies": R, "rotating_bytes": R * wbytes, **spread(per),
+            "roofline": roof}
 
 
 def bench_get_rows(ctx, wt, rows, K, n, seed_w, seed_ids, ydt, steps, warmup):
@@ -248,10 +289,10 @@ def bench_get_rows(ctx, wt, rows, K, n, seed_w, seed_ids, ydt, steps, warmup):
     def step(i):
         check(ctx.L.ggq_get_rows(wt, vp(W), rows, K, vp(ids), n, vp(y), ydt_c, K, ctx.s), "get_rows")
 
-    dt, gpu = time_steps(step, steps, warmup, graph=True)
+    dt, gpu, per = time_steps(step, steps, warmup, graph=True, evict=ctx.evict)
     step_bytes = n * (g.row_bytes(wt, K) + 4 + K * (4 if ydt == torch.float32 else 2))
     return {"value": step_bytes * steps / dt / 1e9, "unit": "GB/s", "ms_per_step": dt / steps * 1e3,
-            "step_bytes": step_bytes,
+            "step_bytes": step_bytes, **spread(per),
             "roofline": roofline_bytes(step_bytes, gpu / steps, f"dequant_kernel<{TNAME[wt]}> (get_rows)")}
 
 
@@ -271,16 +312,19 @@ def bench_prefill(ctx, wt, N, K, M, seed_w, seed_x, ydt, steps, warmup, path=g.P
               "mul_mat")
 
     graph = M * N * K < 2e11
-    dt, _ = time_steps(step, steps, warmup, graph=graph)
+    dt, _, per = time_steps(step, steps, warmup, graph=graph, evict=ctx.evict, reps=3)
     ops = 2.0 * M * N * K
-    res = {"value": ops * steps / dt / 1e12, "unit": "TOPS", "ms_per_step": dt / steps * 1e3}
+    res = {"value": ops * steps / dt / 1e12, "unit": "TOPS", "ms_per_step": dt / steps * 1e3, **spread(per)}
     if path != g.PATH_MMVQ and M > 8:
         # kernel alone: pre-quantized planar operands are produced inside the call, so time the
         # whole call and subtract the quantize kernel measured on its own
         q8 = torch.empty(M * (K // 32) * 40, dtype=torch.uint8, device=dev)
         tq = time_launches(lambda i: check(ctx.L.ggq_quantize_q8_1(vp(x), g.BF16, M, K, K, vp(q8), ctx.s), "q"), 20)
-        tc = time_launches(step, 20)
+        tc, tc_med, tc10, tc90 = time_launches(step, 20, stats=True)
         res["roofline"] = roofline_ops(ops, max(tc - tq, 1e-9), f"mmq_kernel<{TNAME[wt]}> {N}x{K} M={M}")
+        res["roofline"]["kernel_us_source"] = "HIP events around each of 20 calls (mean) minus the quantize kernel's"
+        res["call_us_median"], res["call_us_p10"], res["call_us_p90"] = (round(tc_med * 1e6, 2), round(tc10 * 1e6, 2),
+                                                                         round(tc90 * 1e6, 2))
         res["quantize_us"] = round(tq * 1e6, 2)
     return res
 
@@ -368,11 +412,11 @@ def bench_moe(ctx, Tn, steps, warmup):
         gate_up(i)
         down(i)
 
-    dt, _ = time_steps(step, steps, warmup, graph=Tn <= 64)
+    dt, _, per = time_steps(step, steps, warmup, graph=Tn <= 64, evict=ctx.evict, reps=3)
     sq = max(steps // 2, 1)
-    dt_q, _ = time_steps(step_q8_h, sq, max(warmup // 2, 1), graph=Tn <= 64)
+    dt_q, _, _ = time_steps(step_q8_h, sq, max(warmup // 2, 1), graph=Tn <= 64, evict=ctx.evict, reps=1)
     R = Tn * top_k
-    res = {"ms_per_step": dt / steps * 1e3, "h_between": "bf16",
+    res = {"ms_per_step": dt / steps * 1e3, "h_between": "bf16", **spread(per),
            "ms_per_step_q8_1_h": round(dt_q / sq * 1e3, 4)}
     tg = time_launches(lambda i: gate_up(i, False), 20)
     td = time_launches(lambda i: down(i, False), 20)
@@ -394,24 +438,55 @@ def bench_moe(ctx, Tn, steps, warmup):
 
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(seconds=10.0):
+def cpu_oracle_c2(seconds):
+    """Child-process body of the CPU baseline: the oracle on the whole headline
+    workload (Q4_K 4096 x 4096, one bf16 row: q8_1 quantization + fp64
+    quantized dot of every weight row), repeated for about `seconds`, with
+    the OpenMP thread count the environment sets."""
     import oracle
     N, K = 4096, 4096
     W = inputs.gen_q4_K(N, K, 201)
     x = inputs.gen_act(1, K, 202, "bf16")
-    rows = N // 4                      # bounded sample: a quarter of the rows per call
-    sel = np.arange(rows, dtype=np.int64)
-    oracle.mul_mat(oracle.Q4_K, W, N, K, x, rows=sel)
+    oracle.mul_mat(oracle.Q4_K, W, N, K, x)
     n, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < seconds:
-        oracle.mul_mat(oracle.Q4_K, W, N, K, x, rows=sel)
+        oracle.mul_mat(oracle.Q4_K, W, N, K, x)
         n += 1
     dt = time.perf_counter() - t0
-    moved = rows * g.row_bytes(g.Q4_K, K) + K * 2 + 2 * (K // 32) * 40 + rows * 2
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(moved * n / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"q4_K 4096x4096 M=1: {rows} of 4096 weight rows per call (quantize + fp64 quantized dot), "
-                      f"{n} calls in {dt:.1f} s"}
+    moved = N * g.row_bytes(g.Q4_K, K) + K * 2 + 2 * (K // 32) * 40 + N * 2
+    return {"value": round(moved * n / dt / 1e9, 3), "unit": "GB/s", "calls": n, "seconds": round(dt, 2),
+            "ms_per_call": round(dt / n * 1e3, 3)}
+
+
+def cpu_baseline(seconds=10.0):
+    """The CPU oracle on the headline workload, on this host's cores (all of
+    them, then one thread), each run in a child process with OMP_NUM_THREADS
+    set (the oracle parallelizes over output rows with OpenMP)."""
+    import subprocess
+    allc = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    runs = {}
+    for name, threads, sec in (("all", allc, seconds), ("one", 1, max(2.0, seconds / 2))):
+        env = dict(os.environ, OMP_NUM_THREADS=str(threads))
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-oracle-child", str(sec)], env=env,
+                           capture_output=True, text=True, timeout=600)
+        if r.returncode != 0:
+            raise RuntimeError(f"cpu baseline child failed: {r.stderr[-2000:]}")
+        runs[name] = json.loads(r.stdout.strip().splitlines()[-1])
+    a = runs["all"]
+    quota = None
+    try:                                               # cgroup v2 CPU quota, if the host sets one
+        q, per = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        quota = None if q == "max" else round(int(q) / int(per), 2)
+    except (OSError, ValueError):
+        pass
+    return {"value": a["value"], "unit": "GB/s", "cores": allc, "kind": "oracle",
+            "cpus_allowed": len(os.sched_getaffinity(0)), "cgroup_cpu_quota": quota,
+            "speedup_all_vs_one": round(a["value"] / max(runs["one"]["value"], 1e-12), 2),
+            "sample": f"the whole q4_K 4096x4096 M=1 workload per call (bf16 row -> q8_1, fp64 quantized dot of all "
+                      f"4096 rows): {a['calls']} calls in {a['seconds']} s, {a['ms_per_call']} ms per call",
+            "host_cpus": os.cpu_count(),
+            "single_thread": {"value": runs["one"]["value"], "unit": "GB/s", "cores": 1,
+                              "ms_per_call": runs["one"]["ms_per_call"], "calls": runs["one"]["calls"]}}
 
 
 def main():
@@ -425,9 +500,13 @@ def main():
                          "moe16, moe8192 (default all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-oracle-child", type=float, default=None, help=argparse.SUPPRESS)
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.cpu_oracle_child is not None:              # CPU baseline child: no GPU use
+        print(json.dumps(cpu_oracle_c2(args.cpu_oracle_child)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
@@ -474,7 +553,7 @@ def main():
                 also.append({"workload": "q4_K_8192x2048_prefill_sweep", "M": M, "path": pn, **r})
     if "lmhead1" in sel:
         log("q6_K 248320x2048 lm_head M=1")
-        r = bench_decode(ctx, g.Q6_K, 248320, 2048, 1, 401, 402, torch.float32, max(20, K // 4), W, rotate=False)
+        r = bench_decode(ctx, g.Q6_K, 248320, 2048, 1, 401, 402, torch.float32, max(20, K // 4), W)
         also.append({"workload": "q6_K_248320x2048_lm_head", "M": 1, **r})
     if "types" in sel:
         for wt, name in ((g.Q4_0, "q4_0"), (g.Q5_K, "q5_K")):

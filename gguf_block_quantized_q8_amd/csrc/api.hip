@@ -79,16 +79,25 @@ constexpr int64_t MMVQ_MAX_ROWS = 8;
 // Routed dispatch: MMVQ-id up to this many tokens, MMQ-id above.
 constexpr int64_t MMVQ_ID_MAX_TOKENS = 32;
 
+// AUTO also takes MMQ when MMVQ cannot hold a row of K activations in LDS.
 bool use_mmq(int wt, int64_t K, int64_t M, int path) {
     if (path == GGQ_PATH_MMQ) return true;
     if (path == GGQ_PATH_MMVQ) return false;
-    return has_mmq(wt, K) && M > MMVQ_MAX_ROWS;
+    return has_mmq(wt, K) && (M > MMVQ_MAX_ROWS || !mmvq_supported(wt, K));
 }
 
 bool use_mmq_id(int wt, int64_t K, int64_t T, int path) {
     if (path == GGQ_PATH_MMQ) return true;
     if (path == GGQ_PATH_MMVQ) return false;
-    return has_mmq(wt, K) && T > MMVQ_ID_MAX_TOKENS;
+    return has_mmq(wt, K) && (T > MMVQ_ID_MAX_TOKENS || !mmvq_supported(wt, K));
+}
+
+int mmvq_too_long(const char *what, int wt, int64_t K) {
+    int64_t kmax = 65536 / block_len(wt) * block_len(wt);
+    while (kmax > 0 && !mmvq_supported(wt, kmax)) kmax -= block_len(wt);
+    return fail(GGQ_ERR_UNSUPPORTED, "%s: K=%lld is too long for the MMVQ path of %s (a row of K activations must fit "
+                "its 64 KB of LDS: K <= %lld)%s", what, (long long)K, tname(wt), (long long)kmax,
+                has_mmq(wt, K) ? "; use MMQ" : "");
 }
 
 // Dense MMQ split K: with fewer tiles than two workgroups per CU (512), split
@@ -209,6 +218,7 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
     if (need && !aligned16(ws)) return fail(GGQ_ERR_INVALID, "mul_mat: workspace must be 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool mmq = use_mmq(wt, K, M, path);
+    if (!mmq && !mmvq_supported(wt, K)) return mmvq_too_long("mul_mat", wt, K);
     const int64_t rb = (int64_t)ggq_row_bytes(wt, K);
     Carve c(ws);
     if (!mmq) {
@@ -334,6 +344,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     if (!W || !x || !ids || !y) return fail(GGQ_ERR_INVALID, "mul_mat_id: null pointer");
     if (!aligned16(W) || !aligned16(x) || !aligned16(y) || !aligned16(ids)) return fail(GGQ_ERR_INVALID, "mul_mat_id: pointers must be 16-byte aligned");
     const bool mmq = use_mmq_id(wt, K, T, path);
+    if (!mmq && !mmvq_supported(wt, K)) return mmvq_too_long("mul_mat_id", wt, K);
     const bool weighted = route_w != nullptr;
     IdLayout L = id_layout(ws, wt, E, N, K, T, x_per_route, top_k, epi, weighted, mmq);
     if (!ws || ws_bytes < L.total) return fail(GGQ_ERR_WORKSPACE, "mul_mat_id: workspace %zu bytes < %zu required", ws_bytes, L.total);

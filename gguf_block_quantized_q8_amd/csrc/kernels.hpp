@@ -122,6 +122,9 @@ struct MmvqParams {
 };
 constexpr size_t MMVQ_LDS_MAX = 64 * 1024;     // activation bytes staged per block
 int mmvq_max_cols(int t, int64_t K);          // largest column group (8, 4, 2, 1) whose activations fit in LDS
+// whether MMVQ takes this K: one activation row fits its LDS region (K up to about 52K for
+// Q4_K / Q5_K / Q8_0 / Q4_0, 43K for Q6_K) and a row chunk fits one work item
+bool mmvq_supported(int t, int64_t K);
 hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqParams &p, int64_t ngroups_bound,
                        hipStream_t s);
 hipError_t launch_mmvq_dots(int t, const uint8_t *W, int64_t N, int64_t K, const uint8_t *q8, int64_t M,

@@ -1119,6 +1119,10 @@ static ItemGeo item_geo(int t, int64_t K) {
     return G;
 }
 
+bool mmvq_supported(int t, int64_t K) {
+    return K > 0 && K <= INT32_MAX / 16 && act_lds(t, 1, K) <= MMVQ_LDS_MAX && item_geo(t, K).ninst <= MMVQ_MAXI;
+}
+
 hipError_t launch_mmvq(int t, int nc, bool moe, int epi, int ydt, const MmvqParams &p0, int64_t ngroups_bound,
                        hipStream_t s) {
     MmvqParams p = p0;

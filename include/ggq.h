@@ -16,8 +16,9 @@
  *   - All buffers are device memory owned by the caller (the library
  *     allocates nothing on the device and keeps no pointer after returning).
  *     Base pointers must be 16-byte aligned.
- *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
- *     asynchronous on it and never synchronize the host.
+ *   - `stream` is a hipStream_t passed as void * (so that this header needs
+ *     no HIP include; NULL = the default stream).  Calls are asynchronous on
+ *     it and never synchronize the host.
  *   - Weights are row-major GGUF blocks: row n of an N x K matrix starts at
  *     byte n * ggq_row_bytes(type, K).  Kernels never read outside
  *     [W, W + N * row_bytes) (no tail padding needed); all offsets are 64-bit.
@@ -84,7 +85,12 @@ int ggq_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx,
  *   ws  : workspace of at least ggq_mul_mat_ws(...) bytes (may be NULL when
  *         that is 0).
  *   path: AUTO, or force MMVQ / MMQ (MMQ: every type; for Q4_0 and Q8_0
- *         only when K % 256 == 0, else AUTO takes MMVQ at every M).
+ *         only when K % 256 == 0, else AUTO takes MMVQ at every M).  MMVQ
+ *         holds one row of K activations in 64 KB of LDS: it takes K up to
+ *         43520 for Q6_K and about 52K for the other types; AUTO goes to MMQ
+ *         above that, and a call that would need MMVQ for a longer K (forced
+ *         MMVQ, or Q4_0 / Q8_0 with K % 256 != 0) returns
+ *         GGQ_ERR_UNSUPPORTED before launching anything.
  * fp32 accumulation; per-block integer dots are exact. */
 size_t ggq_mul_mat_ws(int wt, int64_t N, int64_t K, int xdt, int64_t M, int path);
 int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
@@ -92,10 +98,11 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
                 void *y, int ydt, int64_t ldy,
                 void *ws, size_t ws_bytes, int path, void *stream);
 
-/* Routed-expert matmul (MoE mul_mat_id; PR #690: "MoE MMQ runs a flat grid
- * over only the (expert, column tile) pairs that hold routes, so it needs no
- * host sync"; fused GLU and MoE weighted sum are the ops PR #690 lists next
- * to mul_mat).
+/* Routed-expert matmul (MoE mul_mat_id).  FreeToken PR #690, "What the ggml
+ * patch changes": the routed MMQ grid covers only the (expert, column tile)
+ * pairs that actually receive routes, and the host never waits for the
+ * routing to be known.  Fused GLU and the MoE weighted sum are ops the same
+ * PR lists beside mul_mat ("Our own code next to it").
  *   W            : E experts; expert e starts at byte e * expert_stride and
  *                  holds N rows of K weights of type wt.  expert_stride >=
  *                  N * row_bytes and a multiple of 16.
@@ -127,6 +134,9 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
  *                  plain output in the workspace and quantizes after.
  *   ws           : at least ggq_mul_mat_id_ws(...) bytes (includes that
  *                  staging for MMVQ-path calls without route weights).
+ *                  ggq_mul_mat_id_ws takes the call's shape and `weighted`
+ *                  (nonzero when route_w will be non-NULL: the per-route
+ *                  fp32 outputs of the weighted sum live in the workspace).
  * Tokens, routes and tiles are grouped on the device; no host sync. */
 size_t ggq_mul_mat_id_ws(int wt, int64_t E, int64_t N, int64_t K, int xdt,
                          int64_t T, int x_per_route, int64_t top_k,
@@ -165,9 +175,13 @@ const char *ggq_last_error(void);
 /* Test hook (not part of the product API): per-group int32 dots of raw weight
  * quants with q8_1 quants, out[M][N][K/g] (g = 32 for Q8_0, Q4_0 (nibbles
  * minus 8), Q4_K / Q5_K (values without the min); g = 16 for Q6_K: values
- * minus 32), computed by the same device unpack and dot code as the named
- * path (GGQ_PATH_MMVQ: the v_dot4 units; GGQ_PATH_MMQ: the staged fp16 tiles
- * and the MFMA, Q4_0 / Q8_0 with K % 256 == 0).
+ * minus 32).  They come from separate test kernels that reuse the named
+ * path's unpack helpers and dot instructions (GGQ_PATH_MMVQ: the weight
+ * decode helpers and v_dot4, reading blocks straight from memory;
+ * GGQ_PATH_MMQ: the MMQ staging code with unit sub-scales and the same MFMA
+ * fragment layout, Q4_0 / Q8_0 with K % 256 == 0), not from the production
+ * kernels' pipelines.  The production kernels' per-block dots are checked
+ * bit for bit through their outputs on exact-arithmetic inputs instead.
  * q8 is M rows of K/32 q8_1 blocks; ws needs ggq_test_block_dots_ws() bytes. */
 size_t ggq_test_block_dots_ws(int wt, int64_t K, int64_t M, int path);
 int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K,

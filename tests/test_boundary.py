@@ -159,3 +159,25 @@ def test_bench_hooks_validate_before_launch(L):
     assert L.ggq_bench_mfma_loop(0, -1, FAKE, 4096, None) == g.ERR_INVALID
     assert L.ggq_bench_mfma_loop(1, 10, None, 4096, None) == g.ERR_INVALID
     assert L.ggq_bench_mfma_loop(1, 10, FAKE, 4095, None) == g.ERR_WORKSPACE
+
+
+def test_mmvq_k_limit(L):
+    """MMVQ keeps one row of K activations in 64 KB of LDS: longer rows are
+    refused on the host before any launch (forced MMVQ, or AUTO for types
+    without an MMQ kernel at that K), and AUTO takes MMQ when it has one."""
+    rc = L.ggq_mul_mat(g.Q4_K, FAKE, 16, 65536, FAKE, g.F32, 1, 65536, FAKE, g.F32, 16, None, 0, g.PATH_MMVQ, None)
+    assert rc == g.ERR_UNSUPPORTED and "too long" in err(L) and "use MMQ" in err(L)
+    # AUTO at M = 1 now needs MMQ's workspace (the planar activations)
+    assert L.ggq_mul_mat_ws(g.Q4_K, 16, 65536, g.F32, 1, g.PATH_AUTO) > 0
+    assert L.ggq_mul_mat_ws(g.Q4_K, 16, 4096, g.F32, 1, g.PATH_AUTO) == 0
+    rc = L.ggq_mul_mat(g.Q4_K, FAKE, 16, 65536, FAKE, g.F32, 1, 65536, FAKE, g.F32, 16, None, 0, g.PATH_AUTO, None)
+    assert rc == g.ERR_WORKSPACE
+    # Q8_0 with K % 256 != 0 has no MMQ kernel: refused under AUTO too
+    rc = L.ggq_mul_mat(g.Q8_0, FAKE, 16, 65568, FAKE, g.F32, 1, 65568, FAKE, g.F32, 16, None, 0, g.PATH_AUTO, None)
+    assert rc == g.ERR_UNSUPPORTED and "too long" in err(L) and "K <= 52416" in err(L)
+    # the largest K MMVQ takes (43520 for Q6_K) keeps AUTO on MMVQ at M = 1 (no workspace); one block more goes to MMQ
+    assert L.ggq_mul_mat_ws(g.Q6_K, 16, 43520, g.F32, 1, g.PATH_AUTO) == 0
+    assert L.ggq_mul_mat_ws(g.Q6_K, 16, 43776, g.F32, 1, g.PATH_AUTO) > 0
+    rc = L.ggq_mul_mat_id(g.Q6_K, FAKE, 4, 16, 43776, 16 * 171 * 210, FAKE, g.F32, 2, 0, FAKE, 2, None, 0,
+                          FAKE, g.F32, FAKE, 1 << 20, g.PATH_MMVQ, None)
+    assert rc == g.ERR_UNSUPPORTED and "too long" in err(L)
