@@ -209,8 +209,9 @@ def roofline_ops(ops, sec, kernel):
 def bench_ceilings(ctx, steps, warmup):
     """Measured ceilings next to the published peaks: a plain streaming read at
     the headline's size (rotating through 1 GiB so every launch reads from HBM,
-    graph-timed like the headline) and at the lm_head's weight size, and
-    MFMA-only loops (fp16 32x32x16, int8 32x32x32)."""
+    graph-timed like the headline) and at the lm_head's weight size,
+    MFMA-only loops (fp16 32x32x16, int8 32x32x32) and the MMQ inner loop with
+    its per-block rescale in both operand types."""
     dev, L = ctx.dev, ctx.L
     sink = torch.zeros(4096, dtype=torch.uint8, device=dev)
     out = {}
@@ -234,6 +235,21 @@ def bench_ceilings(ctx, steps, warmup):
         sec = time_launches(lambda i: check(L.ggq_bench_mfma_loop(kind, iters, vp(sink), 4096, ctx.s),
                                             "bench_mfma_loop"), 5)
         out[name] = round(waves * iters * 4 * ops / sec / 1e12, 1)
+    # the MMQ inner loop alone (fragments and d8 from LDS, exact rescale per
+    # q8_1 block), fp16 against int8 MFMA, plain and software-pipelined, at 1
+    # and 2 workgroups of 4 waves per CU; kind 2 is the LDS read rate alone
+    iters = 20000
+    inner = {}
+    for kind, name in ((0, "f16"), (1, "i8"), (3, "f16_pipelined"), (4, "i8_pipelined"), (2, "lds_read")):
+        for bpc in (1, 2):
+            sec = time_launches(lambda i: check(L.ggq_bench_inner_loop(kind, bpc, iters, vp(sink), 4096, ctx.s),
+                                                "bench_inner_loop"), 3)
+            nw = 256 * bpc * 4
+            if kind == 2:
+                inner[f"{name}_B_per_clk_cu_{bpc}wg"] = round(nw * iters * 8192 / sec / 256 / 2.4e9, 1)
+            else:
+                inner[f"{name}_tops_{bpc}wg"] = round(nw * iters * 2 * 64 * 64 * 32 / sec / 1e12, 1)
+    out["mmq_inner_loop"] = inner
     return out
 
 

@@ -25,9 +25,15 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+# Per-source flags: the MFMA kernels keep their accumulators in ordinary VGPRs
+# (no AGPR round trip before the fp32 rescale that follows each MFMA).
+SRC_FLAGS = {"mmq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+             "ceiling.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = ["hipcc", *FLAGS, "-c", src, "-o", obj]
+    cmd = ["hipcc", *FLAGS, *SRC_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -44,10 +44,11 @@ int kernel_dt(int dt) { return dt == GGQ_F16 ? GGQ_BF16 : dt; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// activation rows quantized on the fly (MMVQ: q8_1 blocks; MMQ: planar fp16 + d + s)
+// activation rows quantized on the fly (MMVQ: none, it stages them in LDS; MMQ: planar fp16
+// quants, d, and the bf16 min-term operand)
 size_t act_bytes(bool mmq, int64_t rows, int64_t K) {
-    if (mmq) return align256((size_t)rows * K * 2) + 2 * align256((size_t)rows * (K / 32) * 4);
-    return 0;   // MMVQ stages its activations in LDS
+    if (mmq) return align256((size_t)rows * K * 2) + align256((size_t)rows * (K / 32) * 4) + align256((size_t)rows * (K / 4));
+    return 0;
 }
 
 struct Carve {
@@ -63,14 +64,15 @@ struct Carve {
 
 struct Planar {
     _Float16 *xq;
-    float *xd, *xs;
+    float *xd;
+    uint16_t *xm;
 };
 
 Planar carve_planar(Carve &c, int64_t rows, int64_t K) {
     Planar p;
     p.xq = c.take<_Float16>((size_t)rows * K * 2);
     p.xd = c.take<float>((size_t)rows * (K / 32) * 4);
-    p.xs = c.take<float>((size_t)rows * (K / 32) * 4);
+    p.xm = c.take<uint16_t>((size_t)rows * (K / 4));
     return p;
 }
 
@@ -100,12 +102,12 @@ int mmvq_too_long(const char *what, int wt, int64_t K) {
                 has_mmq(wt, K) ? "; use MMQ" : "");
 }
 
-// Dense MMQ split K: with fewer tiles than two workgroups per CU (512), split
+// Dense MMQ split K: with fewer tiles than one workgroup per CU (256), split
 // K (in whole super-blocks, at most 8 ways) until the grid fills the chip.
 int mmq_ksplit(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles = ((M + MMQ_MT - 1) / MMQ_MT) * ((N + MMQ_NT - 1) / MMQ_NT), nsb = K / 256;
     int ks = 1;
-    while (ks < 8 && nsb % (2 * ks) == 0 && tiles * 2 * ks <= 512) ks *= 2;
+    while (ks < 8 && nsb % (2 * ks) == 0 && tiles * 2 * ks <= 256) ks *= 2;
     return ks;
 }
 
@@ -245,8 +247,8 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
         return hip_status(launch_mmvq(wt, nc, false, GGQ_EPI_NONE, kernel_dt(ydt), p, (M + nc - 1) / nc, s), "mul_mat mmvq");
     }
     Planar pl = carve_planar(c, M, K);
-    if (xdt == GGQ_Q8_1) rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), M, K, pl.xq, pl.xd, pl.xs, s), "mul_mat expand");
-    else rc = hip_status(launch_quantize(x, xdt, M, K, ldx, nullptr, pl.xq, pl.xd, pl.xs, s), "mul_mat quantize");
+    if (xdt == GGQ_Q8_1) rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), M, K, pl.xq, pl.xd, pl.xm, s), "mul_mat expand");
+    else rc = hip_status(launch_quantize(x, xdt, M, K, ldx, nullptr, pl.xq, pl.xd, pl.xm, s), "mul_mat quantize");
     if (rc) return rc;
     MmqParams p{};
     p.W = static_cast<const uint8_t *>(W);
@@ -256,7 +258,7 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
     p.K = K;
     p.xq = pl.xq;
     p.xd = pl.xd;
-    p.xs = pl.xs;
+    p.xm = pl.xm;
     p.M = M;
     p.m_tiles = (M + MMQ_MT - 1) / MMQ_MT;
     p.n_tiles = (N + MMQ_NT - 1) / MMQ_NT;
@@ -345,6 +347,12 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     if (!aligned16(W) || !aligned16(x) || !aligned16(y) || !aligned16(ids)) return fail(GGQ_ERR_INVALID, "mul_mat_id: pointers must be 16-byte aligned");
     const bool mmq = use_mmq_id(wt, K, T, path);
     if (!mmq && !mmvq_supported(wt, K)) return mmvq_too_long("mul_mat_id", wt, K);
+    // routed MMQ gathers activation rows and SwiGLU up rows with 32-bit offsets
+    if (mmq && (x_per_route ? T * top_k : T) * K * 2 >= (int64_t)0x7fffff00)
+        return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: MMQ path takes at most 2 GiB of fp16 activation rows (%lld rows of K=%lld); split the tokens",
+                    (long long)(x_per_route ? T * top_k : T), (long long)K);
+    if (mmq && epi == GGQ_EPI_SWIGLU && N * rb >= (int64_t)0x7fffff00)
+        return fail(GGQ_ERR_UNSUPPORTED, "mul_mat_id: SwiGLU on the MMQ path needs an expert matrix below 2 GiB");
     const bool weighted = route_w != nullptr;
     IdLayout L = id_layout(ws, wt, E, N, K, T, x_per_route, top_k, epi, weighted, mmq);
     if (!ws || ws_bytes < L.total) return fail(GGQ_ERR_WORKSPACE, "mul_mat_id: workspace %zu bytes < %zu required", ws_bytes, L.total);
@@ -404,10 +412,10 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
                             "mul_mat_id q8_1 output");
     } else {
         if (xdt == GGQ_Q8_1)
-            rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), rows, K, L.pl.xq, L.pl.xd, L.pl.xs, s),
+            rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), rows, K, L.pl.xq, L.pl.xd, L.pl.xm, s),
                             "mul_mat_id expand");
         else
-            rc = hip_status(launch_quantize(x, xdt, rows, K, K, nullptr, L.pl.xq, L.pl.xd, L.pl.xs, s), "mul_mat_id quantize");
+            rc = hip_status(launch_quantize(x, xdt, rows, K, K, nullptr, L.pl.xq, L.pl.xd, L.pl.xm, s), "mul_mat_id quantize");
         if (rc) return rc;
         MmqParams p{};
         p.W = static_cast<const uint8_t *>(W);
@@ -418,7 +426,8 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.K = K;
         p.xq = L.pl.xq;
         p.xd = L.pl.xd;
-        p.xs = L.pl.xs;
+        p.xm = L.pl.xm;
+        p.x_rows = rows;
         p.m_tiles = L.max_tiles;
         p.n_tiles = epi == GGQ_EPI_SWIGLU ? (Np + 63) / 64 : (N + MMQ_NT - 1) / MMQ_NT;
         p.y = y;
@@ -462,7 +471,7 @@ int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K, const void 
     if (!ws || ws_bytes < need) return fail(GGQ_ERR_WORKSPACE, "test_block_dots: workspace %zu bytes < %zu required", ws_bytes, need);
     Carve c(ws);
     Planar pl = carve_planar(c, M, K);
-    rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(q8), M, K, pl.xq, pl.xd, pl.xs, s), "test_block_dots expand");
+    rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(q8), M, K, pl.xq, pl.xd, pl.xm, s), "test_block_dots expand");
     if (rc) return rc;
     return hip_status(launch_mmq_dots(wt, static_cast<const uint8_t *>(W), N, K, pl.xq, M, out, s), "test_block_dots mmq");
 }
@@ -488,6 +497,18 @@ int ggq_bench_mfma_loop(int kind, int64_t iters, void *sink, size_t sink_bytes, 
         return fail(GGQ_ERR_WORKSPACE, "bench_mfma_loop: sink %zu bytes < %d required", sink_bytes, CEIL_MFMA_BLOCKS * 4);
     return hip_status(launch_mfma_loop(kind, iters, static_cast<int *>(sink), static_cast<hipStream_t>(stream)),
                       "bench_mfma_loop");
+}
+
+int ggq_bench_inner_loop(int kind, int blocks_per_cu, int64_t iters, void *sink, size_t sink_bytes, void *stream) {
+    g_err[0] = 0;
+    if (kind < 0 || kind > 4) return fail(GGQ_ERR_INVALID, "bench_inner_loop: kind must be 0..4");
+    if (blocks_per_cu < 1 || blocks_per_cu > 8) return fail(GGQ_ERR_INVALID, "bench_inner_loop: blocks_per_cu must be 1..8");
+    if (iters < 0) return fail(GGQ_ERR_INVALID, "bench_inner_loop: iters < 0");
+    if (!sink) return fail(GGQ_ERR_INVALID, "bench_inner_loop: null sink");
+    if (sink_bytes < (size_t)256 * blocks_per_cu * 4)
+        return fail(GGQ_ERR_WORKSPACE, "bench_inner_loop: sink %zu bytes < %d required", sink_bytes, 256 * blocks_per_cu * 4);
+    return hip_status(launch_inner_loop(kind, blocks_per_cu, iters, static_cast<int *>(sink), static_cast<hipStream_t>(stream)),
+                      "bench_inner_loop");
 }
 
 }  // extern "C"

@@ -62,6 +62,172 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int64_t iters, int *__re
     if (r == 0x5a17c0de) sink[blockIdx.x] = r;
 }
 
+// ---- the MMQ inner loop, two ways, and LDS read bandwidth ----
+//
+// One wave owns a 64 x 64 output tile (2 x 2 tiles of 32 x 32) and, per
+// 32-wide q8_1 block, reads its weight and activation fragments and the
+// block's activation scale d8 from LDS (addresses cycle over four blocks, so
+// nothing is loop-invariant), forms the block's exact integer dot and adds it,
+// rescaled, to fp32 partial sums P:
+//   KIND 0 (fp16 MFMA): the sub-scale is already folded into the fp16 weight
+//     operand; two v_mfma_f32_32x32x16_f16 per 32 x 32 tile give sc * dot
+//     exactly in fp32, then one fma per output: P += C * d8.
+//   KIND 1 (int8 MFMA): one v_mfma_i32_32x32x32_i8 per tile gives the int32
+//     dot; per output an integer multiply by the row's sub-scale (held in
+//     registers here, which favours this variant), a conversion to fp32 and
+//     an fma: P += float(C * sc) * d8.
+//   KIND 2: LDS reads only (ds_read_b128, 1 KB per instruction per wave,
+//     conflict-free), for the bytes per clock the fragment reads compete for.
+// Work counted as int8 ops: 2 * 64 * 64 * 32 per wave per block (KIND 2: bytes).
+// v_mul_i32_i24: the full-rate integer multiply (|int32 dot| < 2^23 here)
+__device__ __forceinline__ int mul_i24(int a, int b) {
+    int r;
+    asm("v_mul_i32_i24 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void inner_loop_kernel(int64_t iters, int *__restrict__ sink) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[4][8][1024];   // 4 blocks x 8 fragments of 1 KB
+    __shared__ float d8s[4][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    for (int i = tid; i < 4 * 8 * 1024 / 4; i += 256)
+        reinterpret_cast<uint32_t *>(&lds[0][0][0])[i] = (uint32_t)(i * 2654435761u) & 0x0f0f0f0fu;
+    for (int i = tid; i < 4 * 64; i += 256) d8s[i / 64][i % 64] = 1.0f + 1e-3f * (float)(i & 15);
+    __syncthreads();
+    int r = 0;
+    if (KIND == 2) {
+        v4i acc = {0, 0, 0, 0};
+        for (int64_t t = 0; t < iters; t++) {
+            const int b = (int)(t & 3);
+#pragma unroll
+            for (int f = 0; f < 8; f++) acc ^= *reinterpret_cast<const v4i *>(&lds[b][f][16 * lane]);
+        }
+        r = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    } else {
+        v16f P[2][2];
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+#pragma unroll
+            for (int c = 0; c < 2; c++) P[a][c] = v16f{};
+        int sc[2][16];
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) sc[a][e] = 1 + ((lane + 7 * e + a) & 31);
+        for (int64_t t = 0; t < iters; t++) {
+            const int b = (int)(t & 3);
+            const float d8[2] = {d8s[b][lane & 31], d8s[b][32 + (lane & 31)]};
+            if (KIND == 3 || KIND == 4) {
+                // software-pipelined: the rescale of tile t is issued under the MFMAs of tile t + 1
+                // (distinct result registers per tile; the order is pinned by scheduling groups)
+                constexpr int NM = KIND == 3 ? 2 : 1;             // MFMAs per 32 x 32 tile
+                constexpr int NV = KIND == 3 ? 16 : 48;           // VALU per tile
+                v16f C[4];
+                if (KIND == 3) {
+                    v8h af[2][2], bf[2][2];
+#pragma unroll
+                    for (int x = 0; x < 2; x++)
+#pragma unroll
+                        for (int kk = 0; kk < 2; kk++) {
+                            af[x][kk] = *reinterpret_cast<const v8h *>(&lds[b][2 * x + kk][16 * lane]);
+                            bf[x][kk] = *reinterpret_cast<const v8h *>(&lds[b][4 + 2 * x + kk][16 * lane]);
+                        }
+#pragma unroll
+                    for (int t = 0; t < 4; t++) {
+                        C[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[t >> 1][0], bf[t & 1][0], v16f{}, 0, 0, 0);
+                        C[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[t >> 1][1], bf[t & 1][1], C[t], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int t = 0; t < 4; t++)
+#pragma unroll
+                        for (int e = 0; e < 16; e++) P[t >> 1][t & 1][e] = __builtin_fmaf(C[t][e], d8[t & 1], P[t >> 1][t & 1][e]);
+                } else {
+                    v4i af[2], bf[2];
+#pragma unroll
+                    for (int x = 0; x < 2; x++) {
+                        af[x] = *reinterpret_cast<const v4i *>(&lds[b][x][16 * lane]);
+                        bf[x] = *reinterpret_cast<const v4i *>(&lds[b][4 + x][16 * lane]);
+                    }
+                    v16i Ci[4];
+#pragma unroll
+                    for (int t = 0; t < 4; t++) Ci[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[t >> 1], bf[t & 1], v16i{}, 0, 0, 0);
+#pragma unroll
+                    for (int t = 0; t < 4; t++)
+#pragma unroll
+                        for (int e = 0; e < 16; e++)
+                            P[t >> 1][t & 1][e] = __builtin_fmaf((float)mul_i24(Ci[t][e], sc[t >> 1][e]), d8[t & 1],
+                                                                 P[t >> 1][t & 1][e]);
+                    (void)C;
+                }
+                // order: MFMAs of tiles 0 and 1, then per later tile its MFMAs interleaved with the
+                // previous tile's rescale, then the last tile's rescale
+                __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);          // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * NM, 0);     // MFMA t0, t1
+#pragma unroll
+                for (int t = 2; t < 4; t++) {
+#pragma unroll
+                    for (int m = 0; m < NM; m++) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA of tile t
+                        __builtin_amdgcn_sched_group_barrier(0x002, NV / NM, 0);   // rescale of tile t - 2
+                    }
+                }
+                __builtin_amdgcn_sched_group_barrier(0x002, 2 * NV, 0);     // rescale of tiles 2, 3
+            } else if (KIND == 0) {
+                v8h af[2][2], bf[2][2];
+#pragma unroll
+                for (int x = 0; x < 2; x++)
+#pragma unroll
+                    for (int kk = 0; kk < 2; kk++) {
+                        af[x][kk] = *reinterpret_cast<const v8h *>(&lds[b][2 * x + kk][16 * lane]);
+                        bf[x][kk] = *reinterpret_cast<const v8h *>(&lds[b][4 + 2 * x + kk][16 * lane]);
+                    }
+#pragma unroll
+                for (int ni = 0; ni < 2; ni++)
+#pragma unroll
+                    for (int mi = 0; mi < 2; mi++) {
+                        v16f C = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ni][0], bf[mi][0], v16f{}, 0, 0, 0);
+                        C = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ni][1], bf[mi][1], C, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 16; e++) P[ni][mi][e] = __builtin_fmaf(C[e], d8[mi], P[ni][mi][e]);
+                    }
+            } else {
+                v4i af[2], bf[2];
+#pragma unroll
+                for (int x = 0; x < 2; x++) {
+                    af[x] = *reinterpret_cast<const v4i *>(&lds[b][x][16 * lane]);
+                    bf[x] = *reinterpret_cast<const v4i *>(&lds[b][4 + x][16 * lane]);
+                }
+#pragma unroll
+                for (int ni = 0; ni < 2; ni++)
+#pragma unroll
+                    for (int mi = 0; mi < 2; mi++) {
+                        const v16i C = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ni], bf[mi], v16i{}, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 16; e++)
+                            P[ni][mi][e] = __builtin_fmaf((float)mul_i24(C[e], sc[ni][e]), d8[mi],
+                                                          P[ni][mi][e]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+#pragma unroll
+            for (int c = 0; c < 2; c++) r += (int)P[a][c][0] + (int)P[a][c][15];
+    }
+    if (r == 0x5a17c0de) sink[blockIdx.x] = r;
+}
+
+hipError_t launch_inner_loop(int kind, int blocks_per_cu, int64_t iters, int *sink, hipStream_t s) {
+    const dim3 g((unsigned)(256 * blocks_per_cu)), b(256);
+    if (kind == 0) hipLaunchKernelGGL(inner_loop_kernel<0>, g, b, 0, s, iters, sink);
+    else if (kind == 1) hipLaunchKernelGGL(inner_loop_kernel<1>, g, b, 0, s, iters, sink);
+    else if (kind == 2) hipLaunchKernelGGL(inner_loop_kernel<2>, g, b, 0, s, iters, sink);
+    else if (kind == 3) hipLaunchKernelGGL(inner_loop_kernel<3>, g, b, 0, s, iters, sink);
+    else hipLaunchKernelGGL(inner_loop_kernel<4>, g, b, 0, s, iters, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_stream_read(const void *buf, int64_t bytes, int *sink, hipStream_t s) {
     if (bytes < 16) return hipSuccess;
     hipLaunchKernelGGL(stream_read_kernel, dim3(CEIL_READ_BLOCKS), dim3(256), 0, s, static_cast<const v4i *>(buf),

@@ -71,6 +71,34 @@ __device__ __forceinline__ int q8_1_quant(float x, float d, float amax) {
     return (int)fminf(fmaxf(roundf(x / d), -127.0f), 127.0f);
 }
 
+// ---- MMQ planar activation operand ----
+// The Q4_K / Q5_K min term of MMQ multiplies each weight row's integer mins
+// by the activations' q8_1 sums s through a bf16 MFMA: per row and
+// super-block (256 values, 8 q8_1 blocks) the operand is 32 bf16 entries,
+// entries 3g, 3g + 1, 3g + 2 the three parts of s_g (their exact sum is s_g)
+// and entries 24..31 zero.  Written by whoever writes the quantized row.
+__device__ __forceinline__ uint16_t bf16_trunc_bits(float v) { return (uint16_t)(__builtin_bit_cast(uint32_t, v) >> 16); }
+__device__ __forceinline__ void split3_bf16_bits(float v, uint16_t &p0, uint16_t &p1, uint16_t &p2) {
+    const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v) & 0xffff0000u);
+    const float r1 = v - h0;                                   // exact
+    const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, r1) & 0xffff0000u);
+    const float r2 = r1 - h1;                                  // exact, at most 8 significant bits
+    p0 = bf16_trunc_bits(h0);
+    p1 = bf16_trunc_bits(h1);
+    p2 = bf16_trunc_bits(r2);
+}
+// xm: [rows][K/256][32] bf16 bits; row m, q8_1 block blk (K % 256 == 0)
+__device__ __forceinline__ void planar_write_min(uint16_t *xm, int64_t m, int64_t K, int64_t blk, float s) {
+    const int64_t nsb = K / 256, g = blk & 7;
+    uint16_t *o = xm + (m * nsb + (blk >> 3)) * 32;
+    uint16_t p0, p1, p2;
+    split3_bf16_bits(s, p0, p1, p2);
+    o[3 * g] = p0;
+    o[3 * g + 1] = p1;
+    o[3 * g + 2] = p2;
+    if (g == 7) *reinterpret_cast<v4i *>(o + 24) = v4i{0, 0, 0, 0};
+}
+
 // ---- loads ----
 __device__ __forceinline__ uint32_t ld_u16(const uint8_t *p) {
     return *reinterpret_cast<const uint16_t *>(p);

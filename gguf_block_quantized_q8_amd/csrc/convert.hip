@@ -9,14 +9,15 @@ namespace ggq {
 //   d = amax / 127 (IEEE fp32 division), q = roundf(x / d) (half away from
 //   zero), all-zero block -> d = s = 0, s = d * (float)sum(q).
 // Output either 40-byte blocks (q8 != nullptr) and/or the planar operand
-// layout of the MMQ kernels: fp16 quants [rows][K], d [rows][K/32],
-// s [rows][K/32] (xq != nullptr).
+// layout of the MMQ kernels (xq != nullptr; K % 256 == 0): fp16 quants
+// [rows][K], d [rows][K/32], and the min-term operand xm [rows][K/256][32]
+// bf16 (each block's s split exactly into three parts, planar_write_min).
 // ---------------------------------------------------------------------------
 template <int XDT, bool VEC>
 __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const void *__restrict__ x, int64_t M, int64_t K,
                                                             int64_t ldx, uint8_t *__restrict__ q8,
                                                             _Float16 *__restrict__ xq, float *__restrict__ xd,
-                                                            float *__restrict__ xs) {
+                                                            uint16_t *__restrict__ xm) {
     const int64_t nb = K / QK8_1;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t b = gid >> 3;            // block index over M * nb
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const void *__restri
         *reinterpret_cast<h4 *>(xq + m * K + blk * QK8_1 + sub * 4) = hv;
         if (sub == 0) {
             xd[m * nb + blk] = d;
-            xs[m * nb + blk] = s;
+            planar_write_min(xm, m, K, blk, s);
         }
     }
 }
@@ -91,7 +92,7 @@ template <int XDT, int LPB>
 __global__ __launch_bounds__(256) void quantize_q8_1_wide_kernel(const void *__restrict__ x, int64_t M, int64_t K,
                                                                  int64_t ldx, uint8_t *__restrict__ q8,
                                                                  _Float16 *__restrict__ xq, float *__restrict__ xd,
-                                                                 float *__restrict__ xs) {
+                                                                 uint16_t *__restrict__ xm) {
     constexpr int VPL = QK8_1 / LPB;
     const int64_t nb = K / QK8_1;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256) void quantize_q8_1_wide_kernel(const void *__r
         }
         if (sub == 0) {
             xd[m * nb + blk] = d;
-            xs[m * nb + blk] = s;
+            planar_write_min(xm, m, K, blk, s);
         }
     }
 }
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(256) void quantize_q8_1_wide_kernel(const void *__r
 // q8_1 blocks -> planar MMQ operand layout (for pre-quantized input).
 __global__ __launch_bounds__(256) void q8_1_to_planar_kernel(const uint8_t *__restrict__ q8, int64_t M, int64_t K,
                                                              _Float16 *__restrict__ xq, float *__restrict__ xd,
-                                                             float *__restrict__ xs) {
+                                                             uint16_t *__restrict__ xm) {
     const int64_t nb = K / QK8_1;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t b = gid >> 3;
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void q8_1_to_planar_kernel(const uint8_t *__re
     if (sub == 0) {
         float2 ds = *reinterpret_cast<const float2 *>(in);
         xd[b] = ds.x;
-        xs[b] = ds.y;
+        planar_write_min(xm, b / nb, K, b % nb, ds.y);
     }
 }
 
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(256) void zero_inactive_kernel(const int32_t *__res
 static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
 hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, uint8_t *q8, _Float16 *xq,
-                           float *xd, float *xs, hipStream_t s) {
+                           float *xd, uint16_t *xm, hipStream_t s) {
     const int64_t threads = M * (K / QK8_1) * 8;
     if (threads == 0) return hipSuccess;
     const uintptr_t a = reinterpret_cast<uintptr_t>(x);
@@ -403,9 +404,9 @@ hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t
 #define GGQ_QW(LPB)                                                                                                   \
     {                                                                                                                 \
         dim3 g(grid_for(threads / 8 * LPB)), b(256);                                                                  \
-        if (xdt == DT_F32) hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_F32, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs); \
-        else if (xdt == DT_F16) hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_F16, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs); \
-        else hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_BF16, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs); \
+        if (xdt == DT_F32) hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_F32, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm); \
+        else if (xdt == DT_F16) hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_F16, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm); \
+        else hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_BF16, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm); \
     }
         if ((ldx % 16) == 0) GGQ_QW(2) else GGQ_QW(4)
 #undef GGQ_QW
@@ -414,23 +415,23 @@ hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t
     const bool vec = xdt == DT_F32 ? ((ldx % 4) == 0 && (a % 16) == 0) : ((ldx % 4) == 0 && (a % 8) == 0);
     dim3 g(grid_for(threads)), b(256);
     if (xdt == DT_F32) {
-        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
-        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
+        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
+        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
     } else if (xdt == DT_F16) {
-        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
-        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
+        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
+        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
     } else {
-        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
-        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xs);
+        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
+        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float16 *xq, float *xd, float *xs,
+hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float16 *xq, float *xd, uint16_t *xm,
                                  hipStream_t s) {
     const int64_t threads = M * (K / QK8_1) * 8;
     if (threads == 0) return hipSuccess;
-    hipLaunchKernelGGL(q8_1_to_planar_kernel, dim3(grid_for(threads)), dim3(256), 0, s, q8, M, K, xq, xd, xs);
+    hipLaunchKernelGGL(q8_1_to_planar_kernel, dim3(grid_for(threads)), dim3(256), 0, s, q8, M, K, xq, xd, xm);
     return hipGetLastError();
 }
 

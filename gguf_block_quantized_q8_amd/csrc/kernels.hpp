@@ -36,9 +36,11 @@ __device__ __forceinline__ void zero_dead_routes(const int32_t *__restrict__ ids
 }
 
 // ---- convert.hip ----
+// q8 != nullptr: 40-byte q8_1 blocks; xq != nullptr (K % 256 == 0): the MMQ planar operand
+// (fp16 quants xq, d xd, min-term operand xm)
 hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, uint8_t *q8, _Float16 *xq,
-                           float *xd, float *xs, hipStream_t s);
-hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float16 *xq, float *xd, float *xs,
+                           float *xd, uint16_t *xm, hipStream_t s);
+hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float16 *xq, float *xd, uint16_t *xm,
                                  hipStream_t s);
 // y row r (of n) = table row ids[r] (r without ids), zeros for ids outside [0, rows); rows ldy apart
 hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, const int32_t *ids, int64_t n, void *y,
@@ -140,7 +142,8 @@ struct MmqParams {
     int64_t K;
     const _Float16 *xq;   // planar activations: fp16 quants [rows][K]
     const float *xd;      // [rows][K/32] q8_1 d
-    const float *xs;      // [rows][K/32] q8_1 s
+    const uint16_t *xm;   // [rows][K/256][32] bf16: min-term operand (planar_write_min)
+    int64_t x_rows;       // routed: rows of the planar activations (T, or T * top_k)
     int64_t M;            // dense: activation rows
     int64_t m_tiles;      // dense: tiles along M; routed: tile-list bound
     int64_t n_tiles;      // tiles along the output rows
@@ -162,7 +165,7 @@ struct MmqParams {
     float *part;
 };
 constexpr int MMQ_NT = 128;   // weight rows per workgroup tile
-constexpr int MMQ_MT = 128;   // activation rows (routes) per workgroup tile
+constexpr int MMQ_MT = 256;   // activation rows (routes) per workgroup tile
 hipError_t launch_mmq(int t, bool moe, int epi, int ydt, const MmqParams &p, hipStream_t s);
 hipError_t launch_mmq_dots(int t, const uint8_t *W, int64_t N, int64_t K, const _Float16 *xq, int64_t M,
                            int32_t *out, hipStream_t s);
@@ -174,5 +177,9 @@ constexpr int CEIL_MFMA_BLOCKS = 1024;   // workgroups of the MFMA loops (4 wave
 hipError_t launch_stream_read(const void *buf, int64_t bytes, int *sink, hipStream_t s);
 // kind 0: fp16 32x32x16, 1: int8 32x32x32; each wave runs iters x 4 MFMAs; sink: CEIL_MFMA_BLOCKS ints
 hipError_t launch_mfma_loop(int kind, int64_t iters, int *sink, hipStream_t s);
+// the MMQ inner loop on a 64 x 64 wave tile: kind 0 fp16 MFMA + one fma per output per block,
+// kind 1 int8 MFMA + multiply, convert and fma per output per block, kind 2 LDS reads only;
+// 256 * blocks_per_cu workgroups of 4 waves; sink: 256 * blocks_per_cu ints
+hipError_t launch_inner_loop(int kind, int blocks_per_cu, int64_t iters, int *sink, hipStream_t s);
 
 }  // namespace ggq

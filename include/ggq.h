@@ -205,6 +205,23 @@ int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K,
 int ggq_bench_stream_read(const void *buf, int64_t bytes, void *sink, size_t sink_bytes, void *stream);
 int ggq_bench_mfma_loop(int kind, int64_t iters, void *sink, size_t sink_bytes, void *stream);
 
+/* Bench hook (not part of the product API): the MMQ inner loop measured on
+ * its own, to compare the two matrix-core choices for the per-block int dot
+ * with its exact q8_1 rescale.  256 * blocks_per_cu workgroups (1..8) of 4
+ * waves; each wave owns a 64 x 64 output tile and runs `iters` 32-wide q8_1
+ * blocks: fragment and scale reads from LDS, then
+ *   kind 0: two v_mfma_f32_32x32x16_f16 per 32 x 32 tile (sub-scale folded
+ *           into the fp16 weight operand) and one fp32 fma per output;
+ *   kind 1: one v_mfma_i32_32x32x32_i8 per 32 x 32 tile, then per output an
+ *           integer multiply by the sub-scale, a conversion and an fma;
+ *   kind 2: the fragment reads alone (8 x 1 KB of ds_read_b128 per block);
+ *   kinds 3 and 4: kinds 0 and 1 software-pipelined, the rescale of one
+ *           32 x 32 tile issued under the MFMAs of the next.
+ * Work per wave per block: 2 * 64 * 64 * 32 int8 ops (kind 2: 8 KB read).
+ * Returns GGQ_ERR_INVALID for a kind outside 0..4 or blocks_per_cu outside 1..8.
+ * sink: device buffer of at least 256 * blocks_per_cu * 4 bytes. */
+int ggq_bench_inner_loop(int kind, int blocks_per_cu, int64_t iters, void *sink, size_t sink_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
