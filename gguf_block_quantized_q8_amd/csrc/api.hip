@@ -51,6 +51,9 @@ size_t act_bytes(bool mmq, int64_t rows, int64_t K) {
     return 0;
 }
 
+// rows of the dense MMQ operand: a multiple of 64 (the tiled layout's d groups)
+int64_t mmq_rows(int64_t M) { return (M + 63) & ~(int64_t)63; }
+
 struct Carve {
     uint8_t *base;
     size_t off = 0;
@@ -158,7 +161,7 @@ int ggq_quantize_q8_1(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx,
     if (M == 0 || K == 0) return GGQ_OK;
     if (!x || !q8) return fail(GGQ_ERR_INVALID, "quantize_q8_1: null pointer");
     if (!aligned16(x) || !aligned16(q8)) return fail(GGQ_ERR_INVALID, "quantize_q8_1: pointers must be 16-byte aligned");
-    return hip_status(launch_quantize(x, xdt, M, K, ldx, static_cast<uint8_t *>(q8), nullptr, nullptr, nullptr,
+    return hip_status(launch_quantize(x, xdt, M, K, ldx, static_cast<uint8_t *>(q8), nullptr, nullptr, nullptr, false,
                                       static_cast<hipStream_t>(stream)), "quantize_q8_1");
 }
 
@@ -196,7 +199,7 @@ int ggq_get_rows(int wt, const void *W, int64_t rows, int64_t K, const int32_t *
 size_t ggq_mul_mat_ws(int wt, int64_t N, int64_t K, int xdt, int64_t M, int path) {
     if (!known_type(wt) || M <= 0 || N <= 0 || K <= 0 || K % block_len(wt)) return 0;
     const bool mmq = use_mmq(wt, K, M, path);
-    return act_bytes(mmq, M, K) + (mmq ? splitk_bytes(M, N, K) : 0);
+    return act_bytes(mmq, mmq ? mmq_rows(M) : M, K) + (mmq ? splitk_bytes(M, N, K) : 0);
 }
 
 int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int xdt, int64_t M, int64_t ldx, void *y,
@@ -246,9 +249,11 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
         const int nc = std::min(nc_for(M), mmvq_max_cols(wt, K));
         return hip_status(launch_mmvq(wt, nc, false, GGQ_EPI_NONE, kernel_dt(ydt), p, (M + nc - 1) / nc, s), "mul_mat mmvq");
     }
-    Planar pl = carve_planar(c, M, K);
-    if (xdt == GGQ_Q8_1) rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), M, K, pl.xq, pl.xd, pl.xm, s), "mul_mat expand");
-    else rc = hip_status(launch_quantize(x, xdt, M, K, ldx, nullptr, pl.xq, pl.xd, pl.xm, s), "mul_mat quantize");
+    // tiled operand, rows padded to a multiple of 64 (the padding rows are never written;
+    // they only feed output columns that are not stored)
+    Planar pl = carve_planar(c, mmq_rows(M), K);
+    if (xdt == GGQ_Q8_1) rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), M, K, pl.xq, pl.xd, pl.xm, true, s), "mul_mat expand");
+    else rc = hip_status(launch_quantize(x, xdt, M, K, ldx, nullptr, pl.xq, pl.xd, pl.xm, true, s), "mul_mat quantize");
     if (rc) return rc;
     MmqParams p{};
     p.W = static_cast<const uint8_t *>(W);
@@ -260,6 +265,7 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K, const void *x, int 
     p.xd = pl.xd;
     p.xm = pl.xm;
     p.M = M;
+    p.x_rows = mmq_rows(M);
     p.m_tiles = (M + MMQ_MT - 1) / MMQ_MT;
     p.n_tiles = (N + MMQ_NT - 1) / MMQ_NT;
     p.y = y;
@@ -408,14 +414,14 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.w_bytes = (E - 1) * expert_stride + N * rb;
         rc = hip_status(launch_mmvq(wt, J, true, epi, kernel_dt(ydt_k), p, L.max_tiles, s), "mul_mat_id mmvq");
         if (!rc && q8_out)
-            rc = hip_status(launch_quantize(L.hstage, hdt, R, Np, Np, static_cast<uint8_t *>(y), nullptr, nullptr, nullptr, s),
+            rc = hip_status(launch_quantize(L.hstage, hdt, R, Np, Np, static_cast<uint8_t *>(y), nullptr, nullptr, nullptr, false, s),
                             "mul_mat_id q8_1 output");
     } else {
         if (xdt == GGQ_Q8_1)
-            rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), rows, K, L.pl.xq, L.pl.xd, L.pl.xm, s),
+            rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(x), rows, K, L.pl.xq, L.pl.xd, L.pl.xm, false, s),
                             "mul_mat_id expand");
         else
-            rc = hip_status(launch_quantize(x, xdt, rows, K, K, nullptr, L.pl.xq, L.pl.xd, L.pl.xm, s), "mul_mat_id quantize");
+            rc = hip_status(launch_quantize(x, xdt, rows, K, K, nullptr, L.pl.xq, L.pl.xd, L.pl.xm, false, s), "mul_mat_id quantize");
         if (rc) return rc;
         MmqParams p{};
         p.W = static_cast<const uint8_t *>(W);
@@ -471,7 +477,7 @@ int ggq_test_block_dots(int wt, const void *W, int64_t N, int64_t K, const void 
     if (!ws || ws_bytes < need) return fail(GGQ_ERR_WORKSPACE, "test_block_dots: workspace %zu bytes < %zu required", ws_bytes, need);
     Carve c(ws);
     Planar pl = carve_planar(c, M, K);
-    rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(q8), M, K, pl.xq, pl.xd, pl.xm, s), "test_block_dots expand");
+    rc = hip_status(launch_q8_1_to_planar(static_cast<const uint8_t *>(q8), M, K, pl.xq, pl.xd, pl.xm, false, s), "test_block_dots expand");
     if (rc) return rc;
     return hip_status(launch_mmq_dots(wt, static_cast<const uint8_t *>(W), N, K, pl.xq, M, out, s), "test_block_dots mmq");
 }

@@ -87,16 +87,35 @@ __device__ __forceinline__ void split3_bf16_bits(float v, uint16_t &p0, uint16_t
     p1 = bf16_trunc_bits(h1);
     p2 = bf16_trunc_bits(r2);
 }
-// xm: [rows][K/256][32] bf16 bits; row m, q8_1 block blk (K % 256 == 0)
-__device__ __forceinline__ void planar_write_min(uint16_t *xm, int64_t m, int64_t K, int64_t blk, float s) {
-    const int64_t nsb = K / 256, g = blk & 7;
-    uint16_t *o = xm + (m * nsb + (blk >> 3)) * 32;
+// Operand layouts.  Row-major (routed MMQ gathers arbitrary rows): xq [rows][K],
+// xd [rows][K/32], xm [rows][K/256][32].  Tiled (dense MMQ, rows padded to a multiple
+// of 64): every 32-row group and 32-value stage of xq is one contiguous 2 KB piece
+// holding the two 1 KB MFMA fragment images the kernel stages (half kk of 16 K values;
+// lane r + 32 h of a half holds row r, K values 16 kk + 8 h .. + 8); xd is
+// [rows / 64][K/32][64]; xm is [rows / 32][K/256][2][64][8] with the same fragment
+// order over its 32 entries.  So each copy the kernel issues reads whole cache lines.
+__device__ __forceinline__ int64_t xq_index(bool tiled, int64_t m, int64_t K, int64_t k) {
+    if (!tiled) return m * K + k;
+    const int kin = (int)(k & 31);
+    return ((((m >> 5) * (K >> 5) + (k >> 5)) * 2 + (kin >> 4)) * 64 + (m & 31) + 32 * ((kin >> 3) & 1)) * 8 + (kin & 7);
+}
+__device__ __forceinline__ int64_t xd_index(bool tiled, int64_t m, int64_t nb, int64_t blk) {
+    return tiled ? ((m >> 6) * nb + blk) * 64 + (m & 63) : m * nb + blk;
+}
+__device__ __forceinline__ int64_t xm_index(bool tiled, int64_t m, int64_t nsb, int64_t sb, int ent) {
+    if (!tiled) return (m * nsb + sb) * 32 + ent;
+    return ((((m >> 5) * nsb + sb) * 2 + (ent >> 4)) * 64 + (m & 31) + 32 * ((ent >> 3) & 1)) * 8 + (ent & 7);
+}
+// row m, q8_1 block blk (K % 256 == 0)
+__device__ __forceinline__ void planar_write_min(uint16_t *xm, bool tiled, int64_t m, int64_t K, int64_t blk, float s) {
+    const int64_t nsb = K / 256, sb = blk >> 3;
+    const int g = (int)(blk & 7);
     uint16_t p0, p1, p2;
     split3_bf16_bits(s, p0, p1, p2);
-    o[3 * g] = p0;
-    o[3 * g + 1] = p1;
-    o[3 * g + 2] = p2;
-    if (g == 7) *reinterpret_cast<v4i *>(o + 24) = v4i{0, 0, 0, 0};
+    xm[xm_index(tiled, m, nsb, sb, 3 * g)] = p0;
+    xm[xm_index(tiled, m, nsb, sb, 3 * g + 1)] = p1;
+    xm[xm_index(tiled, m, nsb, sb, 3 * g + 2)] = p2;
+    if (g == 7) *reinterpret_cast<v4i *>(xm + xm_index(tiled, m, nsb, sb, 24)) = v4i{0, 0, 0, 0};   // entries 24..31
 }
 
 // ---- loads ----

@@ -8,16 +8,16 @@ namespace ggq {
 // q8_1: 8 lanes per 32-value block, 4 values per lane.
 //   d = amax / 127 (IEEE fp32 division), q = roundf(x / d) (half away from
 //   zero), all-zero block -> d = s = 0, s = d * (float)sum(q).
-// Output either 40-byte blocks (q8 != nullptr) and/or the planar operand
-// layout of the MMQ kernels (xq != nullptr; K % 256 == 0): fp16 quants
-// [rows][K], d [rows][K/32], and the min-term operand xm [rows][K/256][32]
-// bf16 (each block's s split exactly into three parts, planar_write_min).
+// Output either 40-byte blocks (q8 != nullptr) and/or the MMQ operand
+// (xq != nullptr; K % 256 == 0): fp16 quants xq, d xd, and the min-term operand
+// xm (each block's s split exactly into three parts, planar_write_min), row-major
+// or tiled (xq_index).
 // ---------------------------------------------------------------------------
 template <int XDT, bool VEC>
 __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const void *__restrict__ x, int64_t M, int64_t K,
                                                             int64_t ldx, uint8_t *__restrict__ q8,
                                                             _Float16 *__restrict__ xq, float *__restrict__ xd,
-                                                            uint16_t *__restrict__ xm) {
+                                                            uint16_t *__restrict__ xm, bool tiled) {
     const int64_t nb = K / QK8_1;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t b = gid >> 3;            // block index over M * nb
@@ -74,10 +74,10 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const void *__restri
     if (xq) {
         typedef _Float16 h4 __attribute__((ext_vector_type(4)));
         h4 hv = {(_Float16)q[0], (_Float16)q[1], (_Float16)q[2], (_Float16)q[3]};
-        *reinterpret_cast<h4 *>(xq + m * K + blk * QK8_1 + sub * 4) = hv;
+        *reinterpret_cast<h4 *>(xq + xq_index(tiled, m, K, blk * QK8_1 + sub * 4)) = hv;
         if (sub == 0) {
-            xd[m * nb + blk] = d;
-            planar_write_min(xm, m, K, blk, s);
+            xd[xd_index(tiled, m, nb, blk)] = d;
+            planar_write_min(xm, tiled, m, K, blk, s);
         }
     }
 }
@@ -92,7 +92,7 @@ template <int XDT, int LPB>
 __global__ __launch_bounds__(256) void quantize_q8_1_wide_kernel(const void *__restrict__ x, int64_t M, int64_t K,
                                                                  int64_t ldx, uint8_t *__restrict__ q8,
                                                                  _Float16 *__restrict__ xq, float *__restrict__ xd,
-                                                                 uint16_t *__restrict__ xm) {
+                                                                 uint16_t *__restrict__ xm, bool tiled) {
     constexpr int VPL = QK8_1 / LPB;
     const int64_t nb = K / QK8_1;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -165,19 +165,19 @@ __global__ __launch_bounds__(256) void quantize_q8_1_wide_kernel(const void *__r
             v8h hv;
 #pragma unroll
             for (int i = 0; i < 8; i++) hv[i] = (_Float16)q[8 * c + i];
-            *reinterpret_cast<v8h *>(xq + m * K + blk * QK8_1 + sub * VPL + 8 * c) = hv;
+            *reinterpret_cast<v8h *>(xq + xq_index(tiled, m, K, blk * QK8_1 + sub * VPL + 8 * c)) = hv;
         }
         if (sub == 0) {
-            xd[m * nb + blk] = d;
-            planar_write_min(xm, m, K, blk, s);
+            xd[xd_index(tiled, m, nb, blk)] = d;
+            planar_write_min(xm, tiled, m, K, blk, s);
         }
     }
 }
 
-// q8_1 blocks -> planar MMQ operand layout (for pre-quantized input).
+// q8_1 blocks -> MMQ operand (for pre-quantized input).
 __global__ __launch_bounds__(256) void q8_1_to_planar_kernel(const uint8_t *__restrict__ q8, int64_t M, int64_t K,
                                                              _Float16 *__restrict__ xq, float *__restrict__ xd,
-                                                             uint16_t *__restrict__ xm) {
+                                                             uint16_t *__restrict__ xm, bool tiled) {
     const int64_t nb = K / QK8_1;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t b = gid >> 3;
@@ -188,11 +188,12 @@ __global__ __launch_bounds__(256) void q8_1_to_planar_kernel(const uint8_t *__re
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
     h4 hv = {(_Float16)(int8_t)(w & 0xff), (_Float16)(int8_t)((w >> 8) & 0xff),
              (_Float16)(int8_t)((w >> 16) & 0xff), (_Float16)(int8_t)(w >> 24)};
-    *reinterpret_cast<h4 *>(xq + b * QK8_1 + sub * 4) = hv;
+    const int64_t m = b / nb, blk = b - m * nb;
+    *reinterpret_cast<h4 *>(xq + xq_index(tiled, m, K, blk * QK8_1 + sub * 4)) = hv;
     if (sub == 0) {
         float2 ds = *reinterpret_cast<const float2 *>(in);
-        xd[b] = ds.x;
-        planar_write_min(xm, b / nb, K, b % nb, ds.y);
+        xd[xd_index(tiled, m, nb, blk)] = ds.x;
+        planar_write_min(xm, tiled, m, K, blk, ds.y);
     }
 }
 
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(256) void zero_inactive_kernel(const int32_t *__res
 static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
 hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, uint8_t *q8, _Float16 *xq,
-                           float *xd, uint16_t *xm, hipStream_t s) {
+                           float *xd, uint16_t *xm, bool tiled, hipStream_t s) {
     const int64_t threads = M * (K / QK8_1) * 8;
     if (threads == 0) return hipSuccess;
     const uintptr_t a = reinterpret_cast<uintptr_t>(x);
@@ -404,9 +405,9 @@ hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t
 #define GGQ_QW(LPB)                                                                                                   \
     {                                                                                                                 \
         dim3 g(grid_for(threads / 8 * LPB)), b(256);                                                                  \
-        if (xdt == DT_F32) hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_F32, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm); \
-        else if (xdt == DT_F16) hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_F16, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm); \
-        else hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_BF16, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm); \
+        if (xdt == DT_F32) hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_F32, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm, tiled); \
+        else if (xdt == DT_F16) hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_F16, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm, tiled); \
+        else hipLaunchKernelGGL((quantize_q8_1_wide_kernel<DT_BF16, LPB>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm, tiled); \
     }
         if ((ldx % 16) == 0) GGQ_QW(2) else GGQ_QW(4)
 #undef GGQ_QW
@@ -415,23 +416,23 @@ hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t
     const bool vec = xdt == DT_F32 ? ((ldx % 4) == 0 && (a % 16) == 0) : ((ldx % 4) == 0 && (a % 8) == 0);
     dim3 g(grid_for(threads)), b(256);
     if (xdt == DT_F32) {
-        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
-        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
+        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm, tiled);
+        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F32, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm, tiled);
     } else if (xdt == DT_F16) {
-        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
-        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
+        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm, tiled);
+        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_F16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm, tiled);
     } else {
-        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
-        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm);
+        if (vec) hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, true>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm, tiled);
+        else hipLaunchKernelGGL((quantize_q8_1_kernel<DT_BF16, false>), g, b, 0, s, x, M, K, ldx, q8, xq, xd, xm, tiled);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float16 *xq, float *xd, uint16_t *xm,
-                                 hipStream_t s) {
+                                 bool tiled, hipStream_t s) {
     const int64_t threads = M * (K / QK8_1) * 8;
     if (threads == 0) return hipSuccess;
-    hipLaunchKernelGGL(q8_1_to_planar_kernel, dim3(grid_for(threads)), dim3(256), 0, s, q8, M, K, xq, xd, xm);
+    hipLaunchKernelGGL(q8_1_to_planar_kernel, dim3(grid_for(threads)), dim3(256), 0, s, q8, M, K, xq, xd, xm, tiled);
     return hipGetLastError();
 }
 

@@ -36,12 +36,13 @@ __device__ __forceinline__ void zero_dead_routes(const int32_t *__restrict__ ids
 }
 
 // ---- convert.hip ----
-// q8 != nullptr: 40-byte q8_1 blocks; xq != nullptr (K % 256 == 0): the MMQ planar operand
-// (fp16 quants xq, d xd, min-term operand xm)
+// q8 != nullptr: 40-byte q8_1 blocks; xq != nullptr (K % 256 == 0): the MMQ operand
+// (fp16 quants xq, d xd, min-term operand xm), row-major or tiled (dense MMQ; rows a
+// multiple of 64 allocated, xq_index)
 hipError_t launch_quantize(const void *x, int xdt, int64_t M, int64_t K, int64_t ldx, uint8_t *q8, _Float16 *xq,
-                           float *xd, uint16_t *xm, hipStream_t s);
+                           float *xd, uint16_t *xm, bool tiled, hipStream_t s);
 hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float16 *xq, float *xd, uint16_t *xm,
-                                 hipStream_t s);
+                                 bool tiled, hipStream_t s);
 // y row r (of n) = table row ids[r] (r without ids), zeros for ids outside [0, rows); rows ldy apart
 hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, const int32_t *ids, int64_t n, void *y,
                           int ydt, int64_t ldy, hipStream_t s);
@@ -140,10 +141,10 @@ struct MmqParams {
     int64_t N;            // weight rows of one matrix
     int64_t Np;           // output rows (N, or N/2 with SwiGLU)
     int64_t K;
-    const _Float16 *xq;   // planar activations: fp16 quants [rows][K]
-    const float *xd;      // [rows][K/32] q8_1 d
-    const uint16_t *xm;   // [rows][K/256][32] bf16: min-term operand (planar_write_min)
-    int64_t x_rows;       // routed: rows of the planar activations (T, or T * top_k)
+    const _Float16 *xq;   // activations: fp16 quants (dense: tiled layout, routed: row-major; xq_index)
+    const float *xd;      // q8_1 d (xd_index)
+    const uint16_t *xm;   // bf16 min-term operand (xm_index, planar_write_min)
+    int64_t x_rows;       // rows of the operand (dense: M padded to 64; routed: T, or T * top_k)
     int64_t M;            // dense: activation rows
     int64_t m_tiles;      // dense: tiles along M; routed: tile-list bound
     int64_t n_tiles;      // tiles along the output rows

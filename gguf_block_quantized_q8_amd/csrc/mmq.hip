@@ -274,63 +274,67 @@ __device__ __forceinline__ void tile_of(int64_t b, int64_t m_tiles, int64_t n_ti
 }
 
 // Routed output as q8_1 blocks, y[route][Np / 32] (Np % 32 == 0).  A block is
-// 32 consecutive outputs of one route: one 32-row MFMA tile row group of one
-// column, held 16 + 16 by lanes l and l + 32 (rows 8g + 4h + i, h = lane / 32),
-// so its amax and quant sum take one lane exchange.  The values are those the
+// 32 consecutive outputs of one route: two 16-row MFMA tiles of one column,
+// rows 16 hh + 4 g + i held by lane c + 16 g (c: the column's lane, g = 0..3),
+// so its amax and quant sum take two lane exchanges.  The values are those the
 // plain epilogue would store (SwiGLU applied, rounded first to bf16 or fp16
 // per p.q8_round), quantized as the q8_1 kernel does.
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 template <int EPI>
 __device__ __forceinline__ void store_q8_1(const MmqParams &p, const lds_i32 *xrow, const lds_i32 *route,
-                                           const v16f (&acc)[2][2], int64_t bn, int tile_count, int wn, int wm,
+                                           const v4f (&acc)[4][4], int64_t bn, int tile_count, int wn, int wm,
                                            int lane) {
-    const int lr = lane & 31, h = lane >> 5;
+    const int g = lane >> 4;
     const int64_t bpr = p.Np / QK8_1;
 #pragma unroll
-    for (int mi = 0; mi < 2; mi++) {
-        const int col = 64 * wm + 32 * mi + lr;
+    for (int mt = 0; mt < 4; mt++) {
+        const int col = 64 * wm + 16 * mt + (lane & 15);
         const bool live = col < tile_count && xrow[col] >= 0;
         const int64_t r = live ? route[col] : 0;
 #pragma unroll
         for (int bi = 0; bi < (EPI == EPI_SWIGLU_ ? 1 : 2); bi++) {
             const int64_t n0 = EPI == EPI_SWIGLU_ ? bn * 64 + 32 * wn : bn * NT + 64 * wn + 32 * bi;
-            float v[16];
+            float v[8];
             float amax = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 16; e++) {
-                float o;
-                if (EPI == EPI_SWIGLU_) {
-                    const float gt = acc[0][mi][e], up = acc[1][mi][e];
-                    o = gt / (1.0f + expf(-gt)) * up;
-                } else {
-                    o = acc[bi][mi][e];
+            for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    float o;
+                    if (EPI == EPI_SWIGLU_) {
+                        const float gt = acc[hh][mt][i], up = acc[hh + 2][mt][i];
+                        o = gt / (1.0f + expf(-gt)) * up;
+                    } else {
+                        o = acc[2 * bi + hh][mt][i];
+                    }
+                    if (p.q8_round) o = from_16(f32_to_16(o, p.q8_round == 2), p.q8_round == 2);
+                    v[4 * hh + i] = o;
+                    amax = fmaxf(amax, fabsf(o));
                 }
-                if (p.q8_round) o = from_16(f32_to_16(o, p.q8_round == 2), p.q8_round == 2);
-                v[e] = o;
-                amax = fmaxf(amax, fabsf(o));
-            }
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
             amax = fmaxf(amax, __shfl_xor(amax, 32));
             float d = amax / 127.0f;
-            uint32_t qw[4];
+            uint32_t qw[2];
             int sum = 0;
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
+            for (int hh = 0; hh < 2; hh++) {
                 uint32_t w = 0;
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int q = q8_1_quant(v[4 * g + i], d, amax);
+                    const int q = q8_1_quant(v[4 * hh + i], d, amax);
                     sum += q;
                     w |= (uint32_t)(q & 0xff) << (8 * i);
                 }
-                qw[g] = w;
+                qw[hh] = w;
             }
+            sum += __shfl_xor(sum, 16);
             sum += __shfl_xor(sum, 32);
             if (amax == 0.0f) d = 0.0f;
             if (!live || n0 >= p.Np) continue;
             uint8_t *blk = static_cast<uint8_t *>(p.y) + (r * bpr + n0 / QK8_1) * Q8_1_BYTES;
 #pragma unroll
-            for (int g = 0; g < 4; g++) *reinterpret_cast<uint32_t *>(blk + 8 + 8 * g + 4 * h) = qw[g];
-            if (h == 0) *reinterpret_cast<float2 *>(blk) = make_float2(d, d * (float)sum);
+            for (int hh = 0; hh < 2; hh++) *reinterpret_cast<uint32_t *>(blk + 8 + 16 * hh + 4 * g) = qw[hh];
+            if (g == 0) *reinterpret_cast<float2 *>(blk) = make_float2(d, d * (float)sum);
         }
     }
 }
@@ -390,7 +394,7 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
         tile_count = (int)min<int64_t>(MT, p.M - bm * MT);
         if (tid < MT) xrow[tid] = tid < tile_count ? tid : -1;
         xbase_row = bm * MT;
-        xrows = tile_count;
+        xrows = min<int64_t>(MT, p.x_rows - xbase_row);      // tiled operand: whole 64-row groups
     }
     // ---- tile rows: weight rows, as byte offsets from the raw descriptor base ----
     // SwiGLU: tile row 64 w2 + 32 ni + rr is gate (ni = 0) or up (ni = 1) row
@@ -420,21 +424,32 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
     const v4i min_rsrc = kMin<T> ? make_rsrc(p.xm + xbase_row * (p.K / 8), xrows * (p.K / 256) * 64) : act_rsrc;
     const v4i raw_rsrc = make_rsrc(wbase, wend_off - wbase_off);
 
-    // this lane's activation fragments (2 per wave of the 16 per stage): column, K offset
+    // this lane's activation fragments (2 per wave of the 16 per stage).  Dense (tiled
+    // operand): fragment 2 gcol + kk of stage s is the 1 KB at ((gcol K/32 + s) 2 + kk) KB
+    // of the tile; routed (row-major): 16 bytes of the lane's gathered row
     uint32_t aoff[2];
+    const int64_t nblk = p.K / QK8_1;
 #pragma unroll
     for (int f = 0; f < 2; f++) {
         const int fr = 2 * wave + f, gcol = fr >> 1, kk = fr & 1;
-        const int col = 32 * gcol + (lane & 31);
-        const int32_t xr = xrow[col];
-        aoff[f] = (uint32_t)((int64_t)(xr < 0 ? 0 : xr) * p.K * 2) + (uint32_t)((16 * kk + 8 * (lane >> 5)) * 2);
+        if (MOE) {
+            const int32_t xr = xrow[32 * gcol + (lane & 31)];
+            aoff[f] = (uint32_t)((int64_t)(xr < 0 ? 0 : xr) * p.K * 2) + (uint32_t)((16 * kk + 8 * (lane >> 5)) * 2);
+        } else {
+            aoff[f] = (uint32_t)((gcol * nblk * 2 + kk) * 1024 + 16 * lane);
+        }
     }
+    constexpr uint32_t ASTEP = MOE ? KS * 2 : 2048;           // bytes from one stage to the next
 
-    v16f acc[2][2], P[2][2];
+    v4f acc[4][4], P[4][4];                                    // [16-row tile][16-column tile]
 #pragma unroll
-    for (int a = 0; a < 2; a++)
+    for (int a = 0; a < 4; a++)
 #pragma unroll
-        for (int b = 0; b < 2; b++) { acc[a][b] = v16f{}; P[a][b] = v16f{}; }
+        for (int b = 0; b < 4; b++) { acc[a][b] = v4f{}; P[a][b] = v4f{}; }
+    // 16 x 16 tiles: lane l holds column l & 15 and rows 4 fg .. + 4; its operand
+    // fragments start at foff in a 32-row fragment group (plus 256 for the upper 16 rows)
+    const int fg = lane >> 4;
+    const uint32_t foff = (fg >> 1) * 1024 + 16 * ((fg & 1) * 32 + (lane & 15));
 
     const int nst_all = (int)(p.K / KS), per = nst_all / (!MOE && p.ksplit > 1 ? p.ksplit : 1);
     const int s0 = slice * per, nst = s0 + per;
@@ -470,7 +485,7 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
         for (int f = 0; f < 2; f++) {
             const int fr = 2 * wave + f;
             llvm_amdgcn_raw_buffer_load_lds(act_rsrc, (lds_u32 *)(lds + L::ACT + (slot * 16 + fr) * 1024), 16,
-                                            (int)(aoff[f] + (uint32_t)s * (KS * 2)), 0, 0, 0);
+                                            (int)(aoff[f] + (uint32_t)s * ASTEP), 0, 0, 0);
         }
     };
     // raw super-block sb of this wave's 16 rows, instruction i: pieces P = 64 i + lane
@@ -489,17 +504,26 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
     };
     // block scales d8 of super-block sb: wave w copies block w of columns 64 i .. + 64
     auto issue_d8 = [&](int sb, int i) {
-        const int32_t xr = xrow[64 * i + lane];
-        const uint32_t off = (uint32_t)(((int64_t)(xr < 0 ? 0 : xr) * (p.K / QK8_1) + 8 * sb + wave) * 4);
+        uint32_t off;
+        if (MOE) {
+            const int32_t xr = xrow[64 * i + lane];
+            off = (uint32_t)(((int64_t)(xr < 0 ? 0 : xr) * nblk + 8 * sb + wave) * 4);
+        } else {
+            off = (uint32_t)(((i * nblk + 8 * sb + wave) * 64 + lane) * 4);
+        }
         llvm_amdgcn_raw_buffer_load_lds(d8_rsrc, (lds_u32 *)(lds + L::D8 + (((sb & 1) * 8 + wave) * MT + 64 * i) * 4),
                                         4, (int)off, 0, 0, 0);
     };
     // min-term operand of super-block sb, fragment 2 wave + f
     auto issue_min = [&](int sb, int f) {
         const int fr = 2 * wave + f, gcol = fr >> 1, kk = fr & 1;
-        const int32_t xr = xrow[32 * gcol + lr];
-        const uint32_t off = (uint32_t)(((int64_t)(xr < 0 ? 0 : xr) * (p.K / 256) + sb) * 64) +
-                             (uint32_t)((16 * kk + 8 * (lane >> 5)) * 2);
+        uint32_t off;
+        if (MOE) {
+            const int32_t xr = xrow[32 * gcol + lr];
+            off = (uint32_t)(((int64_t)(xr < 0 ? 0 : xr) * (p.K / 256) + sb) * 64) + (uint32_t)((16 * kk + 8 * (lane >> 5)) * 2);
+        } else {
+            off = (uint32_t)(((gcol * (p.K / 256) + sb) * 2 + kk) * 1024 + 16 * lane);
+        }
         llvm_amdgcn_raw_buffer_load_lds(min_rsrc, (lds_u32 *)(lds + L::BMIN + fr * 1024), 16, (int)off, 0, 0, 0);
     };
     // everything a super-block needs besides the activations, for the stages of super-block
@@ -579,18 +603,25 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
     };
 
     // stage s (activation slot aslot): MFMAs and rescale of this wave's 64 x 64
+    // Stage compute on 16 x 16 x 32 MFMAs: one instruction covers a whole q8_1 block of
+    // a 16 x 16 tile, so each tile's rescale is independent of the next tile's MFMA.  The
+    // staging buffers keep the 32-row fragment layout (a 32-row group of one stage is two
+    // 1 KB halves kk of 16 K values; lane l of half kk holds row l & 31, K values
+    // 16 kk + 8 (l >> 5) .. + 8); a 16 x 16 x 32 operand needs in lane l row 16 hh + (l & 15)
+    // and 8 consecutive K values, group l >> 4: found at foff + 256 hh.  Weight and
+    // activation operands use the same K order, so the dot is the block's.
     auto compute = [&](int s, int aslot) {
         const int j = s & 7, sb = s >> 3;
-        const lds_u8 *act = lds + L::ACT + aslot * 16 * 1024;
-        const lds_u8 *dec = lds + L::DEC + (s & 1) * NA * 8 * 1024;
-        const lds_u8 *d8t = lds + L::D8 + (((sb & 1) * 8 + j) * MT + 64 * wm + lr) * 4;
-        const float d8[2] = {ld_lds<float>(d8t), ld_lds<float>(d8t + 128)};
-        v8h bf[2][2];
+        const lds_u8 *act = lds + L::ACT + aslot * 16 * 1024 + 2 * wm * 2048 + foff;
+        const lds_u8 *dec = lds + L::DEC + (s & 1) * NA * 8 * 1024 + 2 * wn * 2048 + foff;
+        const lds_u8 *d8t = lds + L::D8 + (((sb & 1) * 8 + j) * MT + 64 * wm + (lane & 15)) * 4;
+        float d8[4];
+        v8h bf[4];
 #pragma unroll
-        for (int mi = 0; mi < 2; mi++)
-#pragma unroll
-            for (int kk = 0; kk < 2; kk++)
-                bf[mi][kk] = ld_lds<v8h>(act + ((2 * wm + mi) * 2 + kk) * 1024 + 16 * lane);
+        for (int mt = 0; mt < 4; mt++) {
+            d8[mt] = ld_lds<float>(d8t + 64 * mt);
+            bf[mt] = ld_lds<v8h>(act + (mt >> 1) * 2048 + (mt & 1) * 256);
+        }
         bool two[2] = {false, false};
         if (NA == 2) {
             const lds_u8 *fl = lds + L::FLAG + (sb & 1) * 32;
@@ -601,75 +632,62 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
             }
         }
 #pragma unroll
-        for (int ni = 0; ni < 2; ni++) {
-            const int rg = 2 * wn + ni;
-            v8h af[2], af2[2];
+        for (int nt = 0; nt < 4; nt++) {
+            const lds_u8 *a = dec + (nt >> 1) * 2048 + (nt & 1) * 256;
+            const v8h af = ld_lds<v8h>(a);
+            v4f C[4];
 #pragma unroll
-            for (int kk = 0; kk < 2; kk++) af[kk] = ld_lds<v8h>(dec + (rg * 2 + kk) * 1024 + 16 * lane);
-            if (NA == 2 && two[ni])
+            for (int mt = 0; mt < 4; mt++) C[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[mt], v4f{}, 0, 0, 0);
+            if (NA == 2 && two[nt >> 1]) {
+                const v8h af2 = ld_lds<v8h>(a + 8 * 1024);
 #pragma unroll
-                for (int kk = 0; kk < 2; kk++)
-                    af2[kk] = ld_lds<v8h>(dec + 8 * 1024 + (rg * 2 + kk) * 1024 + 16 * lane);
+                for (int mt = 0; mt < 4; mt++) C[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af2, bf[mt], C[mt], 0, 0, 0);
+            }
+            if (kBlk32<T>) {
+                // the block's weight scale per row: rows 16 nt + 4 (l >> 4) + i of the wave's 64
+                const v4f w4 = ld_lds<v4f>(lds + L::WD + ((s & 1) * NT + 64 * wn + 16 * nt + 4 * fg) * 4);
 #pragma unroll
-            for (int mi = 0; mi < 2; mi++) {
-                v16f C = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[0], bf[mi][0], v16f{}, 0, 0, 0);
-                C = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[1], bf[mi][1], C, 0, 0, 0);
-                if (NA == 2 && two[ni]) {
-                    C = __builtin_amdgcn_mfma_f32_32x32x16_f16(af2[0], bf[mi][0], C, 0, 0, 0);
-                    C = __builtin_amdgcn_mfma_f32_32x32x16_f16(af2[1], bf[mi][1], C, 0, 0, 0);
-                }
-                if (kBlk32<T>) {
-                    // the block's weight scale per row: rows 8 q + 4 h + i of the 32-row group
-                    const lds_u8 *dw = lds + L::WD + ((s & 1) * NT + 32 * rg + 4 * (lane >> 5)) * 4;
+                for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const v4f w4 = ld_lds<v4f>(dw + 32 * q);
+                    for (int i = 0; i < 4; i++)
+                        acc[nt][mt][i] = __builtin_fmaf(C[mt][i], d8[mt] * w4[i], acc[nt][mt][i]);
+            } else {
+                // P holds zeros at a super-block's first block
 #pragma unroll
-                        for (int i = 0; i < 4; i++)
-                            acc[ni][mi][4 * q + i] = __builtin_fmaf(C[4 * q + i], d8[mi] * w4[i], acc[ni][mi][4 * q + i]);
-                    }
-                } else {
-                    // P holds zeros at a super-block's first block
+                for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-                    for (int e = 0; e < 16; e++) P[ni][mi][e] = __builtin_fmaf(C[e], d8[mi], P[ni][mi][e]);
-                }
+                    for (int i = 0; i < 4; i++) P[nt][mt][i] = __builtin_fmaf(C[mt][i], d8[mt], P[nt][mt][i]);
             }
         }
         if (j == 7 && !kBlk32<T>) {
             // end of the super-block: acc += P * d (- dmin * min term), and P restarts at zero
-            const lds_u8 *wd = lds + L::WD + (sb & 1) * NT * 4;
-            const lds_u8 *wdm = lds + L::WDM + (sb & 1) * NT * 4;
+            const lds_u8 *wd = lds + L::WD + ((sb & 1) * NT + 64 * wn + 4 * fg) * 4;
+            const lds_u8 *wdm = lds + L::WDM + ((sb & 1) * NT + 64 * wn + 4 * fg) * 4;
+            v8bf bmv[4];
+            if (kMin<T>)
 #pragma unroll
-            for (int ni = 0; ni < 2; ni++) {
-                const int rg = 2 * wn + ni;
-                v16f Q[2] = {v16f{}, v16f{}};
+                for (int mt = 0; mt < 4; mt++)
+                    bmv[mt] = ld_lds<v8bf>(lds + L::BMIN + 2 * wm * 2048 + foff + (mt >> 1) * 2048 + (mt & 1) * 256);
+#pragma unroll
+            for (int nt = 0; nt < 4; nt++) {
+                v4f Q[4] = {v4f{}, v4f{}, v4f{}, v4f{}};
                 if (kMin<T>) {
+                    const v8bf am = ld_lds<v8bf>(lds + L::AMIN + 2 * wn * 2048 + foff + (nt >> 1) * 2048 + (nt & 1) * 256);
 #pragma unroll
-                    for (int kk = 0; kk < 2; kk++) {
-                        const v8bf am = ld_lds<v8bf>(lds + L::AMIN + (rg * 2 + kk) * 1024 + 16 * lane);
+                    for (int mt = 0; mt < 4; mt++) Q[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bmv[mt], v4f{}, 0, 0, 0);
+                }
+                const v4f d4 = ld_lds<v4f>(wd + 64 * nt);
+                v4f m4 = {0.f, 0.f, 0.f, 0.f};
+                if (kMin<T>) m4 = ld_lds<v4f>(wdm + 64 * nt);
 #pragma unroll
-                        for (int mi = 0; mi < 2; mi++) {
-                            const v8bf bmv = ld_lds<v8bf>(lds + L::BMIN + ((2 * wm + mi) * 2 + kk) * 1024 + 16 * lane);
-                            Q[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bmv, Q[mi], 0, 0, 0);
-                        }
+                for (int mt = 0; mt < 4; mt++) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        acc[nt][mt][i] = __builtin_fmaf(P[nt][mt][i], d4[i], acc[nt][mt][i]);
+                        if (kMin<T>) acc[nt][mt][i] = __builtin_fmaf(Q[mt][i], -m4[i], acc[nt][mt][i]);
                     }
+                    P[nt][mt] = v4f{};
                 }
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const v4f d4 = ld_lds<v4f>(wd + (32 * rg + 8 * q + 4 * (lane >> 5)) * 4);
-                    v4f m4 = {0.f, 0.f, 0.f, 0.f};
-                    if (kMin<T>) m4 = ld_lds<v4f>(wdm + (32 * rg + 8 * q + 4 * (lane >> 5)) * 4);
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-#pragma unroll
-                        for (int mi = 0; mi < 2; mi++) {
-                            const int e = 4 * q + i;
-                            acc[ni][mi][e] = __builtin_fmaf(P[ni][mi][e], d4[i], acc[ni][mi][e]);
-                            if (kMin<T>) acc[ni][mi][e] = __builtin_fmaf(Q[mi][e], -m4[i], acc[ni][mi][e]);
-                        }
-                }
-#pragma unroll
-                for (int mi = 0; mi < 2; mi++) P[ni][mi] = v16f{};
             }
         }
     };
@@ -726,48 +744,49 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
         return;
     }
 #pragma unroll
-    for (int mi = 0; mi < 2; mi++) {
-        const int col = 64 * wm + 32 * mi + lr;
+    for (int mt = 0; mt < 4; mt++) {
+        const int col = 64 * wm + 16 * mt + (lane & 15);
         if (col >= tile_count) continue;
         const int32_t xr = xrow[col];
         if (xr < 0) continue;
+        if (!MOE) {
+            const int64_t m = xbase_row + xr;
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-            if (!MOE) {
-                const int64_t m = xbase_row + xr;
+            for (int nt = 0; nt < 4; nt++) {
+                const int64_t n0 = bn * NT + 64 * wn + 16 * nt + 4 * fg;
+                if (n0 >= p.N) continue;
+                const int nv = (int)min<int64_t>(4, p.N - n0);
+                float v[4] = {acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]};
+                if (p.ksplit > 1) store4<DT_F32>(p.part, ((int64_t)slice * p.M + m) * p.N + n0, v, nv);
+                else store4<YDT>(p.y, m * p.ldy + n0, v, nv, p.y_f16);
+            }
+        } else {
+            const int64_t r = route[col];
+            if (EPI == EPI_SWIGLU_) {
+                // tiles 0, 1 hold gate rows, tiles 2, 3 the up rows of the same outputs
 #pragma unroll
-                for (int ni = 0; ni < 2; ni++) {
-                    const int64_t n0 = bn * NT + 64 * wn + 32 * ni + 8 * g + 4 * (lane >> 5);
-                    if (n0 >= p.N) continue;
-                    const int nv = (int)min<int64_t>(4, p.N - n0);
-                    float v[4] = {acc[ni][mi][4 * g], acc[ni][mi][4 * g + 1], acc[ni][mi][4 * g + 2], acc[ni][mi][4 * g + 3]};
-                    if (p.ksplit > 1) store4<DT_F32>(p.part, ((int64_t)slice * p.M + m) * p.N + n0, v, nv);
-                    else store4<YDT>(p.y, m * p.ldy + n0, v, nv, p.y_f16);
-                }
-            } else {
-                const int64_t r = route[col];
-                if (EPI == EPI_SWIGLU_) {
-                    const int64_t n0 = bn * 64 + 32 * wn + 8 * g + 4 * (lane >> 5);
+                for (int nt = 0; nt < 2; nt++) {
+                    const int64_t n0 = bn * 64 + 32 * wn + 16 * nt + 4 * fg;
                     if (n0 >= p.Np) continue;
                     const int nv = (int)min<int64_t>(4, p.Np - n0);
                     float h[4];
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
-                        const float gt = acc[0][mi][4 * g + i], up = acc[1][mi][4 * g + i];
+                        const float gt = acc[nt][mt][i], up = acc[nt + 2][mt][i];
                         h[i] = gt / (1.0f + expf(-gt)) * up;
                     }
                     if (p.o32) store4<DT_F32>(p.o32, r * p.Np + n0, h, nv);
                     else store4<YDT>(p.y, r * p.Np + n0, h, nv, p.y_f16);
-                } else {
+                }
+            } else {
 #pragma unroll
-                    for (int ni = 0; ni < 2; ni++) {
-                        const int64_t n0 = bn * NT + 64 * wn + 32 * ni + 8 * g + 4 * (lane >> 5);
-                        if (n0 >= p.N) continue;
-                        const int nv = (int)min<int64_t>(4, p.N - n0);
-                        float v[4] = {acc[ni][mi][4 * g], acc[ni][mi][4 * g + 1], acc[ni][mi][4 * g + 2], acc[ni][mi][4 * g + 3]};
-                        if (p.o32) store4<DT_F32>(p.o32, r * p.Np + n0, v, nv);
-                        else store4<YDT>(p.y, r * p.Np + n0, v, nv, p.y_f16);
-                    }
+                for (int nt = 0; nt < 4; nt++) {
+                    const int64_t n0 = bn * NT + 64 * wn + 16 * nt + 4 * fg;
+                    if (n0 >= p.N) continue;
+                    const int nv = (int)min<int64_t>(4, p.N - n0);
+                    float v[4] = {acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]};
+                    if (p.o32) store4<DT_F32>(p.o32, r * p.Np + n0, v, nv);
+                    else store4<YDT>(p.y, r * p.Np + n0, v, nv, p.y_f16);
                 }
             }
         }
