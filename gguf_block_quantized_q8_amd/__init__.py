@@ -25,7 +25,7 @@ _PATHS = {"auto": PATH_AUTO, "mmvq": PATH_MMVQ, "mmq": PATH_MMQ}
 _lib = None
 
 EXPORTS = ["ggq_row_bytes", "ggq_q8_1_bytes", "ggq_quantize_q8_1", "ggq_mul_mat_ws", "ggq_mul_mat",
-           "ggq_mul_mat_id_ws", "ggq_mul_mat_id", "ggq_dequantize", "ggq_get_rows", "ggq_last_error",
+           "ggq_mul_mat_id_ws", "ggq_mul_mat_id", "ggq_mul_mat_id_noalloc", "ggq_dequantize", "ggq_get_rows", "ggq_last_error",
            "ggq_test_block_dots_ws", "ggq_test_block_dots", "ggq_bench_stream_read", "ggq_bench_mfma_loop",
            "ggq_bench_inner_loop"]
 
@@ -55,6 +55,9 @@ def lib():
     L.ggq_mul_mat_id.restype = i32
     L.ggq_mul_mat_id.argtypes = [i32, vp, i64, i64, i64, i64, vp, i32, i64, i32, vp, i64, vp, i32,
                                  vp, i32, vp, sz, i32, vp]
+    L.ggq_mul_mat_id_noalloc.restype = i32
+    L.ggq_mul_mat_id_noalloc.argtypes = [i32, vp, i64, i64, i64, i64, vp, i32, i64, i32, vp, i64, vp, i32,
+                                         vp, i32, i32, vp]
     L.ggq_dequantize.restype = i32
     L.ggq_dequantize.argtypes = [i32, vp, i64, i64, vp, i32, vp]
     L.ggq_get_rows.restype = i32
@@ -215,6 +218,36 @@ def mul_mat_id(W, wt, x, ids, K, route_w=None, epi=EPI_NONE, x_per_route=False, 
                           _ptr(ws), ws.numel(), p, _stream(x.device))
     _raise(rc, "mul_mat_id")
     return (y, ws) if return_workspace else y
+
+
+def mul_mat_id_noalloc(W, wt, x, ids, K, route_w=None, epi=EPI_NONE, x_per_route=False, out_dtype=None,
+                       path="auto"):
+    """mul_mat_id through ggq_mul_mat_id_noalloc: the library's fixed per-GPU scratch
+    (NOALLOC_SCRATCH_BYTES) replaces the workspace; the output is allocated here."""
+    _check_gpu(W, x, ids, route_w)
+    E = W.shape[0]
+    rb = row_bytes(wt, K)
+    stride = W.stride(0)
+    N = W.shape[1] if W.dim() == 3 else stride // rb
+    T, top_k = ids.shape
+    Np = N // 2 if epi == EPI_SWIGLU else N
+    if out_dtype is None:
+        out_dtype = x.dtype if _xdt(x) != Q8_1 else torch.float32
+    if out_dtype == "q8_1":
+        y = torch.empty((T, top_k, Np // 32 * Q8_1_BYTES), dtype=torch.uint8, device=x.device)
+        ydt = Q8_1
+    else:
+        shape = (T, Np) if route_w is not None else (T, top_k, Np)
+        y = torch.empty(shape, dtype=out_dtype, device=x.device)
+        ydt = _ydt(out_dtype)
+    rc = lib().ggq_mul_mat_id_noalloc(wt, _ptr(W), E, N, K, stride, _ptr(x), _xdt(x), T, int(x_per_route),
+                                      _ptr(ids), top_k, _ptr(route_w), epi, _ptr(y), ydt, _PATHS[path],
+                                      _stream(x.device))
+    _raise(rc, "mul_mat_id_noalloc")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def dequantize(W, wt, K, out_dtype=torch.float32):

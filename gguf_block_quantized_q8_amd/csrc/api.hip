@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.hpp"
 #include "../../include/ggq.h"
@@ -515,6 +516,60 @@ int ggq_bench_inner_loop(int kind, int blocks_per_cu, int64_t iters, void *sink,
         return fail(GGQ_ERR_WORKSPACE, "bench_inner_loop: sink %zu bytes < %d required", sink_bytes, 256 * blocks_per_cu * 4);
     return hip_status(launch_inner_loop(kind, blocks_per_cu, iters, static_cast<int *>(sink), static_cast<hipStream_t>(stream)),
                       "bench_inner_loop");
+}
+
+// ---------------------------------------------------------------------------
+// routed experts without an allocation: the workspace is a fixed device array
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+// One copy per GPU, for the life of the process.  Host code never names it in a launch
+// or copy: its address on a device comes from hipGetSymbolAddress, taken once per device
+// with that device current.
+static __device__ __align__(256) uint8_t scratch[GGQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};
+
+int scratch_of_current_device(void **out) {
+    int dev = -1;
+    int rc = hip_status(hipGetDevice(&dev), "mul_mat_id_noalloc: current device");
+    if (rc) return rc;
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(GGQ_ERR_INVALID, "mul_mat_id_noalloc: device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        rc = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "mul_mat_id_noalloc: scratch address");
+        if (rc) return rc;
+        if (!ptr) return fail(GGQ_ERR_HIP, "mul_mat_id_noalloc: no scratch address on device %d", dev);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GGQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ggq_mul_mat_id_noalloc(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64_t expert_stride,
+                           const void *x, int xdt, int64_t T, int x_per_route, const int32_t *ids, int64_t top_k,
+                           const float *route_w, int epi, void *y, int ydt, int path, void *stream) {
+    g_err[0] = 0;
+    const size_t need = ggq_mul_mat_id_ws(wt, E, N, K, xdt, T, x_per_route, top_k, epi, route_w != nullptr, path);
+    if (need > GGQ_NOALLOC_SCRATCH_BYTES)
+        return fail(GGQ_ERR_WORKSPACE,
+                    "mul_mat_id_noalloc: this call needs %zu bytes of workspace, the fixed scratch holds %zu; "
+                    "call ggq_mul_mat_id with a workspace of ggq_mul_mat_id_ws() bytes",
+                    need, (size_t)GGQ_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    const int rc = scratch_of_current_device(&ws);
+    if (rc) return rc;
+    return ggq_mul_mat_id(wt, W, E, N, K, expert_stride, x, xdt, T, x_per_route, ids, top_k, route_w, epi, y, ydt, ws,
+                          GGQ_NOALLOC_SCRATCH_BYTES, path, stream);
 }
 
 }  // extern "C"

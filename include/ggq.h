@@ -148,6 +148,25 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K,
                    void *y, int ydt,
                    void *ws, size_t ws_bytes, int path, void *stream);
 
+/* ggq_mul_mat_id without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts that
+ * forbid allocation).  The workspace is a fixed device array of
+ * GGQ_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; the array of the current device (hipGetDevice) is used, so the
+ * stream must belong to that device.  Calls on one GPU share that array: calls
+ * that overlap in time on one GPU (on different streams, or from several
+ * threads without ordering) race, and must be serialized by the caller.  Each
+ * call clears the parts that must start at zero.  Arguments and results as
+ * ggq_mul_mat_id; a call whose ggq_mul_mat_id_ws() size exceeds the array
+ * returns GGQ_ERR_WORKSPACE and launches nothing.  Calls no allocating
+ * routine. */
+#define GGQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ggq_mul_mat_id_noalloc(int wt, const void *W, int64_t E, int64_t N, int64_t K,
+                           int64_t expert_stride,
+                           const void *x, int xdt, int64_t T, int x_per_route,
+                           const int32_t *ids, int64_t top_k, const float *route_w, int epi,
+                           void *y, int ydt, int path, void *stream);
+
 /* Dequantize (convert) rows of weights: y[r][k] = exact block value in fp32,
  * or its round-to-nearest-even bf16 / fp16 (PR #690 lists dequantize among
  * its ops).  y: [rows][K] of ydt (GGQ_F32 / GGQ_BF16 / GGQ_F16).  Bit-exact. */
