@@ -289,7 +289,7 @@ struct IdLayout {
     RouteTables rt;
     int64_t max_tiles;
     Planar pl;
-    float *o32;           // weighted: per-route fp32 outputs [R][Np]
+    void *oroute;         // weighted: per-route outputs [R][Np] (fp32 room; 16-bit when y is)
     void *hstage;         // MMVQ, unweighted: outputs [R][Np] (fp32 room) before a q8_1 output's quantization
     size_t total;
 };
@@ -312,7 +312,7 @@ IdLayout id_layout(void *ws, int wt, int64_t E, int64_t N, int64_t K, int64_t T,
     L.rt.perm = c.take<int32_t>((size_t)R * 4);
     L.rt.tiles = c.take<int4>((size_t)L.max_tiles * 16);
     if (mmq) L.pl = carve_planar(c, rows, K);
-    L.o32 = weighted ? c.take<float>((size_t)R * Np * 4) : nullptr;
+    L.oroute = weighted ? c.take<float>((size_t)R * Np * 4) : nullptr;
     L.hstage = !mmq && !weighted ? c.take<float>((size_t)R * Np * 4) : nullptr;
     L.total = c.off;
     (void)wt;
@@ -410,7 +410,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.top_k = (int)top_k;
         p.x_per_route = x_per_route;
         p.route_w = route_w;
-        p.o32 = L.o32;
+        p.oroute = L.oroute;
         p.groups_expected = std::min<int64_t>(E, R);
         p.w_bytes = (E - 1) * expert_stride + N * rb;
         rc = hip_status(launch_mmvq(wt, J, true, epi, kernel_dt(ydt_k), p, L.max_tiles, s), "mul_mat_id mmvq");
@@ -444,13 +444,13 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.top_k = (int)top_k;
         p.x_per_route = x_per_route;
         p.route_w = route_w;
-        p.o32 = L.o32;
+        p.oroute = L.oroute;
         p.q8_round = !q8_out ? 0 : hdt == GGQ_BF16 ? 1 : hdt == GGQ_F16 ? 2 : 0;
         p.y_f16 = ydt == GGQ_F16;
         rc = hip_status(launch_mmq(wt, true, epi, kernel_dt(ydt), p, s), "mul_mat_id mmq");
     }
     if (rc) return rc;
-    if (weighted) rc = hip_status(launch_route_sum(L.o32, ids, route_w, T, (int)top_k, E, Np, y, ydt, s), "mul_mat_id route sum");
+    if (weighted) rc = hip_status(launch_route_sum(L.oroute, ids, route_w, T, (int)top_k, E, Np, y, ydt, s), "mul_mat_id route sum");
     return rc;
 }
 

@@ -304,31 +304,57 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
     for (; i < n; i += st) p[i] = v;
 }
 
-// Route-weighted sum of per-route fp32 outputs:
+// Route-weighted sum of per-route outputs o (stored in the output dtype: fp32,
+// or the 16-bit type of y, as the activation-dtype intermediates of the pages):
 //   y[t][n] = sum over k in ascending order of w[t][k] * o[t*top_k + k][n]
 // for the active routes of token t (0 <= id < E), accumulated in fp32, then
-// stored in the output dtype.  One thread per V consecutive n (V = 4 when Np
-// is a multiple of 4, else 1).  The routes go in chunks of 8 whose row loads
-// are all issued before the first fma (one memory latency per chunk, not per
-// route); an inactive route's row (never written) is replaced by zeros after
-// its load, so it cannot feed a NaN into the sum.
+// stored in the output dtype.  One thread per V consecutive n (16 bytes of o
+// when Np allows it: V = 4 fp32 or 8 16-bit values, else V = 1).  The routes go
+// in chunks of 8 whose row loads are all issued before the first fma (one
+// memory latency per chunk, not per route); an inactive route's row (never
+// written) is skipped, so it cannot feed a NaN into the sum.
 template <int YDT, int V>
-__global__ __launch_bounds__(256) void route_sum_kernel(const float *__restrict__ o, const int32_t *__restrict__ ids,
+__device__ __forceinline__ void load_route(const void *o, int64_t idx, float (&v)[V]) {
+    if (YDT == DT_F32) {
+        const float *of = static_cast<const float *>(o) + idx;
+        if (V == 4) {
+            const v4f t = *reinterpret_cast<const v4f *>(of);
+#pragma unroll
+            for (int c = 0; c < V; c++) v[c] = t[c & 3];
+        } else {
+#pragma unroll
+            for (int c = 0; c < V; c++) v[c] = of[c];
+        }
+    } else {
+        const uint16_t *oh = static_cast<const uint16_t *>(o) + idx;
+        if (V == 8) {
+            const v4i t = *reinterpret_cast<const v4i *>(oh);
+#pragma unroll
+            for (int c = 0; c < V; c++) v[c] = from_16(((uint32_t)t[(c >> 1) & 3] >> (16 * (c & 1))) & 0xffffu, YDT == DT_F16);
+        } else {
+#pragma unroll
+            for (int c = 0; c < V; c++) v[c] = from_16(oh[c], YDT == DT_F16);
+        }
+    }
+}
+
+template <int YDT, int V>
+__global__ __launch_bounds__(256) void route_sum_kernel(const void *__restrict__ o, const int32_t *__restrict__ ids,
                                                         const float *__restrict__ w, int64_t T, int top_k, int64_t E,
                                                         int64_t Np, void *__restrict__ y) {
     constexpr int KC = 8;
-    typedef float vf __attribute__((ext_vector_type(V)));
     const int64_t q = Np / V;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t st = (int64_t)gridDim.x * blockDim.x;
     for (; i < T * q; i += st) {
         const int64_t t = i / q, n = V * (i - t * q);
         float acc[V];
+#pragma unroll
         for (int c = 0; c < V; c++) acc[c] = 0.0f;
         for (int k0 = 0; k0 < top_k; k0 += KC) {
             bool on[KC];
             float wk[KC];
-            vf v[KC];
+            float v[KC][V];
 #pragma unroll
             for (int k = 0; k < KC; k++) {
                 const int64_t r = t * top_k + k0 + k;
@@ -338,7 +364,7 @@ __global__ __launch_bounds__(256) void route_sum_kernel(const float *__restrict_
                     const int32_t e = ids[r];
                     on[k] = e >= 0 && e < E;
                     wk[k] = w[r];
-                    v[k] = *reinterpret_cast<const vf *>(o + r * Np + n);
+                    load_route<YDT, V>(o, r * Np + n, v[k]);
                 }
             }
 #pragma unroll
@@ -349,18 +375,20 @@ __global__ __launch_bounds__(256) void route_sum_kernel(const float *__restrict_
             }
         }
         const int64_t idx = t * Np + n;
-        if (V == 4) {
-            if (YDT == DT_F32) {
-                *reinterpret_cast<v4f *>(static_cast<float *>(y) + idx) = v4f{acc[0], acc[1], acc[2], acc[3]};
-            } else {
-                const bool h = YDT == DT_F16;
-                const v2i b = {(int)(f32_to_16(acc[0], h) | (f32_to_16(acc[1], h) << 16)),
-                               (int)(f32_to_16(acc[2], h) | (f32_to_16(acc[3], h) << 16))};
-                *reinterpret_cast<v2i *>(static_cast<uint16_t *>(y) + idx) = b;
-            }
+        if (YDT == DT_F32) {
+            if (V == 4) *reinterpret_cast<v4f *>(static_cast<float *>(y) + idx) = v4f{acc[0], acc[V > 1 ? 1 : 0], acc[V > 2 ? 2 : 0], acc[V > 3 ? 3 : 0]};
+            else for (int c = 0; c < V; c++) static_cast<float *>(y)[idx + c] = acc[c];
         } else {
-            if (YDT == DT_F32) static_cast<float *>(y)[idx] = acc[0];
-            else static_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_16(acc[0], YDT == DT_F16);
+            const bool h = YDT == DT_F16;
+            if (V == 8) {
+                v4i b;
+#pragma unroll
+                for (int c = 0; c < 4; c++)
+                    b[c] = (int)(f32_to_16(acc[(2 * c) % V], h) | (f32_to_16(acc[(2 * c + 1) % V], h) << 16));
+                *reinterpret_cast<v4i *>(static_cast<uint16_t *>(y) + idx) = b;
+            } else {
+                for (int c = 0; c < V; c++) static_cast<uint16_t *>(y)[idx + c] = (uint16_t)f32_to_16(acc[c], h);
+            }
         }
     }
 }
@@ -459,22 +487,25 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_route_sum(const float *o, const int32_t *ids, const float *w, int64_t T, int top_k, int64_t E,
+hipError_t launch_route_sum(const void *o, const int32_t *ids, const float *w, int64_t T, int top_k, int64_t E,
                             int64_t Np, void *y, int ydt, hipStream_t s) {
-    const bool vec = Np % 4 == 0;
-    const int64_t n = T * (vec ? Np / 4 : Np);
+    // 16-byte rows pieces when Np allows (o, y and the workspace are 16-byte aligned)
+    const int V = ydt == DT_F32 ? (Np % 4 == 0 ? 4 : 1) : (Np % 8 == 0 ? 8 : 1);
+    const int64_t n = T * (Np / V);
     if (n == 0) return hipSuccess;
     const dim3 g((unsigned)std::min<int64_t>((n + 255) / 256, 16384)), b(256);
+#define GGQ_RS(D, VV) hipLaunchKernelGGL((route_sum_kernel<D, VV>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y)
     if (ydt == DT_F32) {
-        if (vec) hipLaunchKernelGGL((route_sum_kernel<DT_F32, 4>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
-        else hipLaunchKernelGGL((route_sum_kernel<DT_F32, 1>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
+        if (V == 4) GGQ_RS(DT_F32, 4);
+        else GGQ_RS(DT_F32, 1);
     } else if (ydt == DT_F16) {
-        if (vec) hipLaunchKernelGGL((route_sum_kernel<DT_F16, 4>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
-        else hipLaunchKernelGGL((route_sum_kernel<DT_F16, 1>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
+        if (V == 8) GGQ_RS(DT_F16, 8);
+        else GGQ_RS(DT_F16, 1);
     } else {
-        if (vec) hipLaunchKernelGGL((route_sum_kernel<DT_BF16, 4>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
-        else hipLaunchKernelGGL((route_sum_kernel<DT_BF16, 1>), g, b, 0, s, o, ids, w, T, top_k, E, Np, y);
+        if (V == 8) GGQ_RS(DT_BF16, 8);
+        else GGQ_RS(DT_BF16, 1);
     }
+#undef GGQ_RS
     return hipGetLastError();
 }
 

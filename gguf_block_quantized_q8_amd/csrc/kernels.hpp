@@ -47,7 +47,7 @@ hipError_t launch_q8_1_to_planar(const uint8_t *q8, int64_t M, int64_t K, _Float
 hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, const int32_t *ids, int64_t n, void *y,
                           int ydt, int64_t ldy, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s);
-hipError_t launch_route_sum(const float *o, const int32_t *ids, const float *w, int64_t T, int top_k, int64_t E,
+hipError_t launch_route_sum(const void *o, const int32_t *ids, const float *w, int64_t T, int top_k, int64_t E,
                             int64_t Np, void *y, int ydt, hipStream_t s);
 // y[m][n] = sum over k < ks, in order, of part[k][m][n] (fp32), stored as ydt (fp16 when y_f16)
 hipError_t launch_splitk_reduce(const float *part, int ks, int64_t M, int64_t N, void *y, int ydt, int y_f16,
@@ -106,7 +106,8 @@ struct MmvqParams {
     int top_k;
     int x_per_route;
     const float *route_w;
-    float *o32;           // weighted: per-route fp32 outputs [R][Np]
+    void *oroute;         // weighted: per-route outputs [R][Np] in the output dtype (fp32, or the
+                          // 16-bit type of y), summed per token afterwards
     int y_f16;            // 16-bit output is fp16 (else bf16)
     int64_t groups_expected;   // routed: expected active groups (min(E, routes))
     // set by the launcher
@@ -157,7 +158,8 @@ struct MmqParams {
     int top_k;
     int x_per_route;
     const float *route_w;
-    float *o32;           // weighted: per-route fp32 outputs [R][Np]
+    void *oroute;         // weighted: per-route outputs [R][Np] in the output dtype (fp32, or the
+                          // 16-bit type of y), summed per token afterwards
     int q8_round;         // q8_1 output: round the values to bf16 (1) or fp16 (2) before quantizing
     int y_f16;            // 16-bit output is fp16 (else bf16)
     // dense split K: ksplit workgroups per tile, each over K / ksplit (whole super-blocks),

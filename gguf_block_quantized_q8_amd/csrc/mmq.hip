@@ -739,6 +739,61 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
     wait_vm_c<0>();                                            // no copy outlives the workgroup
 
     // ---- epilogue ----
+    // 16-bit outputs go through LDS: each column's rows of this tile (128, or 64 SwiGLU
+    // outputs) are staged contiguously, then written as whole 16-byte pieces, 256 (128)
+    // contiguous bytes per column, rather than 8-byte pieces from the MFMA layout
+    if (YDT == DT_BF16 && (MOE || p.ksplit == 1)) {
+        constexpr int RW = EPI == EPI_SWIGLU_ ? 64 : NT;        // output rows of one column here
+        constexpr int PITCH = RW * 2 + 16;                      // staged bytes per column (16-byte aligned)
+        static_assert(MT * PITCH <= L::WOFF, "staging overlaps the tile tables");
+        const bool hf = p.y_f16;
+        __syncthreads();                                        // every wave is past its last LDS read
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+            lds_u8 *cst = lds + (64 * wm + 16 * mt + (lane & 15)) * PITCH;
+#pragma unroll
+            for (int nt = 0; nt < (EPI == EPI_SWIGLU_ ? 2 : 4); nt++) {
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    if (EPI == EPI_SWIGLU_) {
+                        const float gt = acc[nt][mt][i], up = acc[nt + 2][mt][i];
+                        v[i] = gt / (1.0f + expf(-gt)) * up;
+                    } else {
+                        v[i] = acc[nt][mt][i];
+                    }
+                }
+                const int row = (EPI == EPI_SWIGLU_ ? 32 : 64) * wn + 16 * nt + 4 * fg;
+                st_lds<v2i>(cst + 2 * row, v2i{(int)(f32_to_16(v[0], hf) | (f32_to_16(v[1], hf) << 16)),
+                                                (int)(f32_to_16(v[2], hf) | (f32_to_16(v[3], hf) << 16))});
+            }
+        }
+        __syncthreads();
+        constexpr int LPC = RW / 8;                             // lanes per column, 8 values each
+        const int64_t row0 = EPI == EPI_SWIGLU_ ? bn * 64 : bn * NT;
+        const int64_t nrows = MOE ? p.Np : p.N;
+        const int nvalid = (int)min<int64_t>(RW, nrows - row0);
+        uint16_t *dst0 = static_cast<uint16_t *>(MOE && p.oroute ? p.oroute : p.y);
+        const int64_t ld = MOE ? p.Np : p.ldy;
+        const bool vec = (ld % 8) == 0;
+#pragma unroll 1
+        for (int c = tid / LPC; c < MT; c += NTHR / LPC) {
+            if (c >= tile_count) break;
+            const int32_t xr = xrow[c];
+            const int e0 = 8 * (tid % LPC);
+            if (xr < 0 || e0 >= nvalid) continue;
+            const int64_t orow = MOE ? (int64_t)route[c] : xbase_row + xr;
+            uint16_t *d = dst0 + orow * ld + row0 + e0;
+            const v4i v = ld_lds<v4i>(lds + c * PITCH + 2 * e0);
+            if (vec && e0 + 8 <= nvalid) {
+                *reinterpret_cast<v4i *>(d) = v;
+            } else {
+                const int n = min(8, nvalid - e0);
+                for (int i = 0; i < n; i++) d[i] = (uint16_t)((uint32_t)v[i >> 1] >> (16 * (i & 1)));
+            }
+        }
+        return;
+    }
     if (YDT == DT_Q8_1) {
         store_q8_1<EPI>(p, xrow, route, acc, bn, tile_count, wn, wm, lane);
         return;
@@ -775,7 +830,7 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
                         const float gt = acc[nt][mt][i], up = acc[nt + 2][mt][i];
                         h[i] = gt / (1.0f + expf(-gt)) * up;
                     }
-                    if (p.o32) store4<DT_F32>(p.o32, r * p.Np + n0, h, nv);
+                    if (p.oroute) store4<YDT>(p.oroute, r * p.Np + n0, h, nv, p.y_f16);
                     else store4<YDT>(p.y, r * p.Np + n0, h, nv, p.y_f16);
                 }
             } else {
@@ -785,7 +840,7 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
                     if (n0 >= p.N) continue;
                     const int nv = (int)min<int64_t>(4, p.N - n0);
                     float v[4] = {acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]};
-                    if (p.o32) store4<DT_F32>(p.o32, r * p.Np + n0, v, nv);
+                    if (p.oroute) store4<YDT>(p.oroute, r * p.Np + n0, v, nv, p.y_f16);
                     else store4<YDT>(p.y, r * p.Np + n0, v, nv, p.y_f16);
                 }
             }

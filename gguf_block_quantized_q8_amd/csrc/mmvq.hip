@@ -789,15 +789,15 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
                         if (v1) store_out2<YDT>(p.y, col * p.ldy + r0, acc[0][c], acc[1][c], p.y_f16);   // r1 = r0 + 1
                         else store_out<YDT>(p.y, col * p.ldy + r0, acc[0][c], p.y_f16);
                     } else {
-                        // weighted: per-route fp32 outputs, summed per token afterwards
+                        // weighted: per-route outputs (output dtype), summed per token afterwards
                         const int64_t r = route_s[c];
                         if (EPI == EPI_SWIGLU) {
                             const float h = silu_mul(acc[0][c], acc[1][c]);
-                            if (p.o32) p.o32[r * p.Np + r0] = h;
+                            if (p.oroute) store_out<YDT>(p.oroute, r * p.Np + r0, h, p.y_f16);
                             else store_out<YDT>(p.y, r * p.Np + r0, h, p.y_f16);
-                        } else if (p.o32) {
-                            p.o32[r * p.Np + r0] = acc[0][c];
-                            if (v1) p.o32[r * p.Np + r1] = acc[1][c];
+                        } else if (p.oroute) {
+                            store_out<YDT>(p.oroute, r * p.Np + r0, acc[0][c], p.y_f16);
+                            if (v1) store_out<YDT>(p.oroute, r * p.Np + r1, acc[1][c], p.y_f16);
                         } else {
                             store_out<YDT>(p.y, r * p.Np + r0, acc[0][c], p.y_f16);
                             if (v1) store_out<YDT>(p.y, r * p.Np + r1, acc[1][c], p.y_f16);
@@ -924,15 +924,15 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
                     if (v1) store_out2<YDT>(p.y, col * p.ldy + r0, acc[0][c], acc[1][c], p.y_f16);   // r1 = r0 + 1
                     else store_out<YDT>(p.y, col * p.ldy + r0, acc[0][c], p.y_f16);
                 } else {
-                    // weighted: per-route fp32 outputs, summed per token afterwards
+                    // weighted: per-route outputs (output dtype), summed per token afterwards
                     const int64_t r = route_s[c];
                     if (EPI == EPI_SWIGLU) {
                         const float h = silu_mul(acc[0][c], acc[1][c]);
-                        if (p.o32) p.o32[r * p.Np + r0] = h;
+                        if (p.oroute) store_out<YDT>(p.oroute, r * p.Np + r0, h, p.y_f16);
                         else store_out<YDT>(p.y, r * p.Np + r0, h, p.y_f16);
-                    } else if (p.o32) {
-                        p.o32[r * p.Np + r0] = acc[0][c];
-                        if (v1) p.o32[r * p.Np + r1] = acc[1][c];
+                    } else if (p.oroute) {
+                        store_out<YDT>(p.oroute, r * p.Np + r0, acc[0][c], p.y_f16);
+                        if (v1) store_out<YDT>(p.oroute, r * p.Np + r1, acc[1][c], p.y_f16);
                     } else {
                         store_out<YDT>(p.y, r * p.Np + r0, acc[0][c], p.y_f16);
                         if (v1) store_out<YDT>(p.y, r * p.Np + r1, acc[1][c], p.y_f16);

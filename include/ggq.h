@@ -120,8 +120,11 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
  *                  else [T][top_k] fp32 weights and y is [T][N'] =
  *                  sum_k route_w[t][k] * o'[t][k] over the active routes,
  *                  in ascending k with fp32 accumulation (deterministic: the
- *                  per-route fp32 outputs go to the workspace, then one pass
- *                  sums them per token).
+ *                  per-route outputs go to the workspace, then one pass sums
+ *                  them per token).  Each route output is held in the output
+ *                  dtype first: fp32 for GGQ_F32, else rounded to bf16 / fp16
+ *                  (an intermediate in the activation dtype, FreeToken PR #690,
+ *                  "Changes").
  *   y            : output of ydt (GGQ_F32 / GGQ_BF16 / GGQ_F16), contiguous.  With
  *                  route_w == NULL, ydt may be GGQ_Q8_1 (N' % 32 == 0): y is
  *                  [T][top_k][N'/32] q8_1 blocks, the blocks ggq_quantize_q8_1

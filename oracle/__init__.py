@@ -61,7 +61,7 @@ def lib():
         L.ggqo_dequantize.argtypes = [i32, vp, i64, i64, vp, i32]
         L.ggqo_mul_mat_id.restype = i32
         L.ggqo_mul_mat_id.argtypes = [i32, vp, i64, i64, i64, i64, vp, i32, i64, i32,
-                                      vp, i64, vp, i32, vp, i64, vp]
+                                      vp, i64, vp, i32, i32, vp, i64, vp]
         _lib = L
     return _lib
 
@@ -203,7 +203,10 @@ def dequantize(t, W, rows, K, ydt=F32):
 
 
 def mul_mat_id(t, W, E, N, K, expert_stride, x, T, x_per_route, ids, top_k,
-               route_w=None, epi=EPI_NONE, tokens=None):
+               route_w=None, epi=EPI_NONE, tokens=None, route_round=None):
+    """route_round (weighted only): None keeps each route's output in fp32 before the
+    weighted sum; "bf16" / "f16" rounds it to that 16-bit type first (the intermediate
+    held in a 16-bit activation dtype)."""
     W = np.ascontiguousarray(W, dtype=np.uint8)
     x = np.ascontiguousarray(x)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
@@ -214,5 +217,6 @@ def mul_mat_id(t, W, E, N, K, expert_stride, x, T, x_per_route, ids, top_k,
     shape = (nt, Np) if w is not None else (nt, top_k, Np)
     y = np.zeros(shape, dtype=np.float32)
     _check(lib().ggqo_mul_mat_id(t, _p(W), E, N, K, expert_stride, _p(x), _dt(x), T, int(x_per_route),
-                                 _p(ids), top_k, _p(w), epi, _p(tk), nt, _p(y)), "mul_mat_id")
+                                 _p(ids), top_k, _p(w), epi, {None: 0, "bf16": 1, "f16": 2}[route_round],
+                                 _p(tk), nt, _p(y)), "mul_mat_id")
     return y

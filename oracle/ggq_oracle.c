@@ -477,11 +477,12 @@ int ggqo_dequantize(int type, const void *W, int64_t rows, int64_t K, void *y, i
 int ggqo_mul_mat_id(int type, const void *W, int64_t E, int64_t N, int64_t K, int64_t expert_stride,
                     const void *x, int xdt, int64_t T, int x_per_route,
                     const int32_t *ids, int64_t top_k, const float *route_w, int epi,
-                    const int64_t *tokens, int64_t ntok, float *y) {
+                    int route_round, const int64_t *tokens, int64_t ntok, float *y) {
     if (!W || !x || !ids || !y || E < 0 || T < 0 || top_k <= 0 || !check_w(type, N, K)) return -1;
     if (!act_dt(xdt)) return -1;
     if (epi != GGQO_EPI_NONE && epi != GGQO_EPI_SWIGLU) return -1;
     if (epi == GGQO_EPI_SWIGLU && N % 2) return -1;
+    if (route_round < 0 || route_round > 2) return -1;
     if (expert_stride < ggqo_row_bytes(type, K) * N) return -1;
     int64_t nt = tokens ? ntok : T;
     for (int64_t i = 0; tokens && i < nt; i++)
@@ -520,6 +521,10 @@ int ggqo_mul_mat_id(int type, const void *W, int64_t E, int64_t N, int64_t K, in
                     v = (double)o[n];
                 }
                 float vf = (float)v;                          /* route output in fp32 */
+                /* weighted: the route output is an intermediate held in the 16-bit
+                 * activation dtype when route_round asks for it (1 bf16, 2 fp16) */
+                if (route_w && route_round == 1) vf = ggqo_bf16_to_fp32(ggqo_fp32_to_bf16(vf));
+                if (route_w && route_round == 2) vf = ggqo_fp16_to_fp32(ggqo_fp32_to_fp16(vf));
                 if (route_w) wsum[n] += (double)route_w[t * top_k + k] * (double)vf;
                 else yt[k * Np + n] = vf;
             }

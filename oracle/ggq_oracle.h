@@ -120,7 +120,7 @@ int ggqo_dequantize(int type, const void *W, int64_t rows, int64_t K, void *y, i
 int ggqo_mul_mat_id(int type, const void *W, int64_t E, int64_t N, int64_t K, int64_t expert_stride,
                     const void *x, int xdt, int64_t T, int x_per_route,
                     const int32_t *ids, int64_t top_k, const float *route_w, int epi,
-                    const int64_t *tokens, int64_t ntok, float *y);
+                    int route_round, const int64_t *tokens, int64_t ntok, float *y);
 
 #ifdef __cplusplus
 }

@@ -375,11 +375,12 @@ def test_c4_q6_K_lm_head_m2048_sampled(dev):
 
 # ------------------------------------------------------------------ routed experts
 
-def _moe_ref(wt, W, K, x, ids, top_k, route_w=None, epi=oracle.EPI_NONE, x_per_route=False, tokens=None):
+def _moe_ref(wt, W, K, x, ids, top_k, route_w=None, epi=oracle.EPI_NONE, x_per_route=False, tokens=None,
+             route_round=None):
     E, N = W.shape[0], W.shape[1]
     Tn = ids.shape[0]
     return oracle.mul_mat_id(wt, W, E, N, K, W.shape[1] * W.shape[2], x, Tn, int(x_per_route), ids, top_k,
-                             route_w=route_w, epi=epi, tokens=tokens)
+                             route_w=route_w, epi=epi, tokens=tokens, route_round=route_round)
 
 
 @pytest.mark.parametrize("path,wt", [("mmvq", g.Q4_K), ("mmq", g.Q4_K), ("mmvq", g.Q6_K), ("mmq", g.Q6_K),
@@ -520,7 +521,7 @@ def test_fp16_moe_layer(dev, path):
     assert np.array_equal(hq.cpu().numpy().reshape(Tn * top_k, -1), oracle.quantize_q8_1(h_gpu.reshape(Tn * top_k, I)))
     y = g.mul_mat_id(Wd_t, g.Q6_K, h, ids_t, I, route_w=w_t, x_per_route=True, path=path)
     assert y.dtype == torch.float16
-    y_ref = _moe_ref(g.Q6_K, Wd, I, h_gpu, ids, top_k, route_w=w, x_per_route=True)
+    y_ref = _moe_ref(g.Q6_K, Wd, I, h_gpu, ids, top_k, route_w=w, x_per_route=True, route_round="f16")
     r = rel(host(y), ref_out(y_ref, "f16"))
     log("fp16 moe", path, r)
     assert r <= TOL["f16"]
@@ -622,7 +623,8 @@ def _c5(dev, Tn, path, tokens=None):
     r_h = rel(hh[sel], ref_out(h_ref32, "bf16"))
     # down on the GPU's own h (identical inputs for the oracle)
     h_gpu = h.view(torch.int16).cpu().numpy().view(np.uint16)
-    y_ref32 = _moe_ref(g.Q6_K, Wd, I, h_gpu, ids, top_k, route_w=w, x_per_route=True, tokens=tokens)
+    y_ref32 = _moe_ref(g.Q6_K, Wd, I, h_gpu, ids, top_k, route_w=w, x_per_route=True, tokens=tokens,
+                       route_round="bf16")
     r_y = rel(yh[sel], ref_out(y_ref32, "bf16"))
     log(f"C5 T={Tn} path={path} gate_up rel={r_h:.3g} down rel={r_y:.3g}")
     assert r_h <= TOL["bf16"] and r_y <= TOL["bf16"]

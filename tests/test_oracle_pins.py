@@ -481,6 +481,30 @@ def test_mul_mat_id_swiglu_and_weighted_sum():
     assert np.array_equal(ys, ref.astype(np.float32))
 
 
+def test_weighted_sum_with_16_bit_route_outputs():
+    """route_round: each active route's fp32 output is rounded to bf16 / fp16 (round
+    to nearest even, as numpy's float16 cast and the bf16 rule do) before the
+    ascending-k fp64 weighted sum; the result differs from the fp32-intermediate sum."""
+    E, N, K, T, top_k, W, stride, x, ids, w = _moe_small(39)
+    o = oracle.mul_mat_id(oracle.Q4_K, W, E, N, K, stride, x, T, 0, ids, top_k)
+    active = ((ids >= 0) & (ids < E)).astype(np.float64)
+    plain = oracle.mul_mat_id(oracle.Q4_K, W, E, N, K, stride, x, T, 0, ids, top_k, route_w=w)
+    for kind in ("bf16", "f16"):
+        if kind == "f16":
+            o16 = o.astype(np.float16).astype(np.float64)
+        else:
+            bits = o.view(np.uint32).astype(np.uint64)
+            keep = (bits + 0x7fff + ((bits >> 16) & 1)) >> 16          # round to nearest even
+            o16 = (keep << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+        ref = np.zeros((T, N))
+        for t in range(T):
+            for k in range(top_k):
+                ref[t] += active[t, k] * float(w[t, k]) * o16[t, k]
+        ys = oracle.mul_mat_id(oracle.Q4_K, W, E, N, K, stride, x, T, 0, ids, top_k, route_w=w, route_round=kind)
+        assert np.array_equal(ys, ref.astype(np.float32)), kind
+        assert not np.array_equal(ys, plain), kind
+
+
 def test_routing_generator():
     ids, w = inputs.gen_routing(64, 256, 8, 504)
     assert ids.shape == (64, 8) and ids.min() >= 0 and ids.max() < 256
