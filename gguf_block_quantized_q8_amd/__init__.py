@@ -20,7 +20,8 @@ OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 Q8_1_BYTES = 40
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libggq.so")
+# GGQ_LIB: another build of the same library (the tests load a host-sanitized build this way)
+LIB_PATH = os.environ.get("GGQ_LIB") or os.path.join(_HERE, "libggq.so")
 _PATHS = {"auto": PATH_AUTO, "mmvq": PATH_MMVQ, "mmq": PATH_MMQ}
 _lib = None
 

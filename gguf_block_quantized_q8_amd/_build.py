@@ -57,5 +57,28 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+def build_host_sanitized(out: str) -> str:
+    """libggq with the C ABI's host code (api.hip: validation, workspace carving,
+    dispatch) under clang's AddressSanitizer and UndefinedBehaviorSanitizer; the
+    kernel sources are linked from the regular build's objects (build() first).
+    Device code is never instrumented.  Load it into a process that preloads the
+    clang ASan runtime."""
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in sources() if not s.endswith("api.hip")]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"build() first: missing {missing}")
+    api_o = out + ".api.o"
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g"]
+    src = os.path.join(CSRC, "api.hip")
+    r = subprocess.run(["hipcc", *flags, *san, "-c", src, "-o", api_o], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    subprocess.run(["hipcc", "-shared", f"--offload-arch={ARCH}", "-o", out, api_o, *objs], check=True)
+    os.remove(api_o)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

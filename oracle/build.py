@@ -22,5 +22,16 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_sanitized(out: str) -> str:
+    """The same source with gcc's AddressSanitizer and UndefinedBehaviorSanitizer
+    (host code only: the oracle is plain C).  Load it into a process that
+    preloads gcc's libasan and libubsan."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra", "-o", out, SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
