@@ -380,6 +380,78 @@ def bench_crossover(ctx, Ms=(1, 8, 64, 512, 8192)):
     return out
 
 
+# ------------------------------------------------------------------ dispatch thresholds
+
+def bench_thresholds(ctx):
+    """Call times that set the dispatch rules, caches evicted before every launch
+    (decode-sized calls read their weights from HBM in a real model):
+    dense Q4_K 4096x4096 at M = 1..16 on both paths; the MoE projections of
+    E=256 top-8 H=2048 I=512 at T = 8..1024 on both paths; the routes per MMVQ-id
+    group (1, 2, 4, 8) at T = 16..128 for uniform and skewed routing; and
+    MMQ-id at T = 8192 for both routings."""
+    dev, L = ctx.dev, ctx.L
+    out = []
+    N, K, wt = 4096, 4096, g.Q4_K
+    W = torch.from_numpy(inputs.gen_weights(wt, N, K, 201)).to(dev)
+    for M in range(1, 17):
+        x = bf16(inputs.gen_act(M, K, 202, "bf16"), dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        row = {"workload": "thresholds_dense_q4_K_4096x4096", "M": M}
+        for path, pn in ((g.PATH_MMVQ, "mmvq"), (g.PATH_MMQ, "mmq")):
+            wsb = L.ggq_mul_mat_ws(wt, N, K, g.BF16, M, path)
+            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+            t = time_launches(lambda i: check(L.ggq_mul_mat(wt, vp(W), N, K, vp(x), g.BF16, M, K, vp(y), g.BF16, N,
+                                                            vp(ws), wsb, path, ctx.s), pn), 10, evict=ctx.evict)
+            row[pn + "_us"] = round(t * 1e6, 2)
+        out.append(row)
+    del W
+    E, H, I, top_k = 256, 2048, 512, 8
+    Wgu = torch.from_numpy(inputs.gen_experts(g.Q4_K, E, 2 * I, H, 501)).to(dev)
+    Wd = torch.from_numpy(inputs.gen_experts(g.Q6_K, E, H, I, 502)).to(dev)
+
+    def moe_calls(Tn, routing, paths, reps):
+        ids_np, w_np = routing
+        x = bf16(inputs.gen_act(Tn, H, 503, "bf16"), dev)
+        h = bf16(inputs.gen_act(Tn * top_k, I, 505, "bf16"), dev)
+        ids, w = torch.from_numpy(ids_np).to(dev), torch.from_numpy(w_np).to(dev)
+        yg = torch.empty((Tn, top_k, I), dtype=torch.bfloat16, device=dev)
+        yd = torch.empty((Tn, H), dtype=torch.bfloat16, device=dev)
+        res = {}
+        for path, pn in paths:
+            w1 = L.ggq_mul_mat_id_ws(g.Q4_K, E, 2 * I, H, g.BF16, Tn, 0, top_k, g.EPI_SWIGLU, 0, path)
+            w2 = L.ggq_mul_mat_id_ws(g.Q6_K, E, H, I, g.BF16, Tn, 1, top_k, g.EPI_NONE, 1, path)
+            ws = torch.empty(max(w1, w2, 256), dtype=torch.uint8, device=dev)
+            gu = lambda i: check(L.ggq_mul_mat_id(g.Q4_K, vp(Wgu), E, 2 * I, H, Wgu.stride(0), vp(x), g.BF16, Tn, 0,
+                                                  vp(ids), top_k, None, g.EPI_SWIGLU, vp(yg), g.BF16, vp(ws), w1,
+                                                  path, ctx.s), "gate_up")
+            dn = lambda i: check(L.ggq_mul_mat_id(g.Q6_K, vp(Wd), E, H, I, Wd.stride(0), vp(h), g.BF16, Tn, 1,
+                                                  vp(ids), top_k, vp(w), g.EPI_NONE, vp(yd), g.BF16, vp(ws), w2,
+                                                  path, ctx.s), "down")
+            res[pn + "_gate_up_us"] = round(time_launches(gu, reps, evict=ctx.evict) * 1e6, 2)
+            res[pn + "_down_us"] = round(time_launches(dn, reps, evict=ctx.evict) * 1e6, 2)
+        return res
+
+    both = ((g.PATH_MMVQ, "mmvq"), (g.PATH_MMQ, "mmq"))
+    for Tn in (8, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512, 1024):
+        r = moe_calls(Tn, inputs.gen_routing(Tn, E, top_k, 504), both, 8 if Tn <= 256 else 4)
+        out.append({"workload": "thresholds_moe_e256_top8_h2048_i512", "T": Tn, **r})
+    for kind, gen in (("uniform", inputs.gen_routing), ("skewed", inputs.gen_routing_skewed)):
+        for Tn in (16, 32, 64, 128):
+            routing = gen(Tn, E, top_k, 504)
+            row = {"workload": "thresholds_mmvq_id_cols", "T": Tn, "routing": kind}
+            for J in (1, 2, 4, 8):
+                check(L.ggq_bench_set_mmvq_id_cols(J), "set cols")
+                r = moe_calls(Tn, routing, ((g.PATH_MMVQ, "mmvq"),), 8)
+                row[f"J{J}_gate_up_us"], row[f"J{J}_down_us"] = r["mmvq_gate_up_us"], r["mmvq_down_us"]
+            check(L.ggq_bench_set_mmvq_id_cols(0), "set cols")
+            r = moe_calls(Tn, routing, ((g.PATH_MMVQ, "mmvq"),), 8)
+            row["auto_gate_up_us"], row["auto_down_us"] = r["mmvq_gate_up_us"], r["mmvq_down_us"]
+            out.append(row)
+        r = moe_calls(8192, gen(8192, E, top_k, 504), ((g.PATH_MMQ, "mmq"),), 3)
+        out.append({"workload": "thresholds_mmq_id_t8192", "T": 8192, "routing": kind, **r})
+    return out
+
+
 # ------------------------------------------------------------------ MoE layer
 
 def bench_moe(ctx, Tn, steps, warmup):
@@ -513,7 +585,7 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--workloads", default="all",
                     help="comma list of: decode, prefill, sweep, lmhead1, lmhead2048, getrows, types, crossover, "
-                         "moe16, moe8192 (default all)")
+                         "moe16, moe8192 (default all), and thresholds (only when named)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-oracle-child", type=float, default=None, help=argparse.SUPPRESS)
@@ -580,6 +652,9 @@ def main():
             log(f"{name} 8192x2048 prefill M=8192")
             r = bench_prefill(ctx, wt, 8192, 2048, 8192, 301, 302, torch.bfloat16, max(5, K // 20), max(2, W // 10))
             also.append({"workload": f"{name}_8192x2048_prefill", "M": 8192, **r})
+    if "thresholds" in sel:
+        log("dispatch thresholds: dense M=1..16, routed T=8..128, MMVQ-id group widths, MMQ-id routings")
+        also.extend(bench_thresholds(ctx))
     if "crossover" in sel:
         log("q4_K 8192x2048 crossover: MMVQ / MMQ / dequantize + GEMM")
         also.extend(bench_crossover(ctx))

@@ -28,7 +28,7 @@ _lib = None
 EXPORTS = ["ggq_row_bytes", "ggq_q8_1_bytes", "ggq_quantize_q8_1", "ggq_mul_mat_ws", "ggq_mul_mat",
            "ggq_mul_mat_id_ws", "ggq_mul_mat_id", "ggq_mul_mat_id_noalloc", "ggq_dequantize", "ggq_get_rows", "ggq_last_error",
            "ggq_test_block_dots_ws", "ggq_test_block_dots", "ggq_bench_stream_read", "ggq_bench_mfma_loop",
-           "ggq_bench_inner_loop"]
+           "ggq_bench_inner_loop", "ggq_bench_set_mmvq_id_cols"]
 
 
 def lib():
@@ -75,6 +75,8 @@ def lib():
     L.ggq_bench_mfma_loop.argtypes = [i32, i64, vp, sz, vp]
     L.ggq_bench_inner_loop.restype = i32
     L.ggq_bench_inner_loop.argtypes = [i32, i32, i64, vp, sz, vp]
+    L.ggq_bench_set_mmvq_id_cols.restype = i32
+    L.ggq_bench_set_mmvq_id_cols.argtypes = [i32]
     _lib = L
     return L
 

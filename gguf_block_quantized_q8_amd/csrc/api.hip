@@ -82,8 +82,11 @@ Planar carve_planar(Carve &c, int64_t rows, int64_t K) {
 
 // Dense dispatch: MMVQ for up to 8 activation rows, MMQ above (when it has a kernel for the type and K).
 constexpr int64_t MMVQ_MAX_ROWS = 8;
-// Routed dispatch: MMVQ-id up to this many tokens, MMQ-id above.
-constexpr int64_t MMVQ_ID_MAX_TOKENS = 32;
+// Routed dispatch: MMVQ-id while the routes per expert stay at or below this mean,
+// MMQ-id above.  Measured on the E=256 top-8 H=2048 I=512 projections (caches
+// evicted): gate_up crosses over between 256 and 384 tokens (8 and 12 routes per
+// expert), the down projection between 384 and 512 (12 and 16).
+constexpr int64_t MMVQ_ID_MAX_ROUTES_PER_EXPERT = 12;
 
 // AUTO also takes MMQ when MMVQ cannot hold a row of K activations in LDS.
 bool use_mmq(int wt, int64_t K, int64_t M, int path) {
@@ -92,10 +95,10 @@ bool use_mmq(int wt, int64_t K, int64_t M, int path) {
     return has_mmq(wt, K) && (M > MMVQ_MAX_ROWS || !mmvq_supported(wt, K));
 }
 
-bool use_mmq_id(int wt, int64_t K, int64_t T, int path) {
+bool use_mmq_id(int wt, int64_t K, int64_t R, int64_t E, int path) {
     if (path == GGQ_PATH_MMQ) return true;
     if (path == GGQ_PATH_MMVQ) return false;
-    return has_mmq(wt, K) && (T > MMVQ_ID_MAX_TOKENS || !mmvq_supported(wt, K));
+    return has_mmq(wt, K) && (R > MMVQ_ID_MAX_ROUTES_PER_EXPERT * E || !mmvq_supported(wt, K));
 }
 
 int mmvq_too_long(const char *what, int wt, int64_t K) {
@@ -132,10 +135,16 @@ int check_weights(int wt, int64_t N, int64_t K) {
 
 int nc_for(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
-// Routes per MMVQ-id group: a little above the mean routes per expert, so an
-// expert's weights are rarely read twice and few columns sit idle.
+// Routes per MMVQ-id group, from the mean routes per expert m = R / E.  Measured
+// on the E=256 top-8 projections (uniform and skewed routing alike): one route
+// per group is fastest up to m = 1 (T <= 32: the single-column kernel streams the
+// weights best and experts with a second route are few), four from m = 2 to
+// m = 4 (T = 64, 128), eight above.
+int g_id_cols_override = 0;                                // bench hook: 0 = the rule below
 int mmvq_id_cols(int wt, int64_t R, int64_t E, int64_t K) {
-    return std::min(nc_for((R + E - 1) / E + 1), mmvq_max_cols(wt, K));
+    if (g_id_cols_override) return std::min(g_id_cols_override, mmvq_max_cols(wt, K));
+    const int j = R <= E ? 1 : R <= 4 * E ? 4 : 8;
+    return std::min(j, mmvq_max_cols(wt, K));
 }
 
 }  // namespace
@@ -325,7 +334,7 @@ size_t ggq_mul_mat_id_ws(int wt, int64_t E, int64_t N, int64_t K, int xdt, int64
                          int epi, int weighted, int path) {
     (void)xdt;
     if (!known_type(wt) || E <= 0 || N <= 0 || K <= 0 || K % block_len(wt) || T < 0 || top_k <= 0) return 0;
-    return id_layout(nullptr, wt, E, N, K, T, x_per_route, top_k, epi, weighted != 0, use_mmq_id(wt, K, T, path)).total;
+    return id_layout(nullptr, wt, E, N, K, T, x_per_route, top_k, epi, weighted != 0, use_mmq_id(wt, K, T * top_k, E, path)).total;
 }
 
 int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64_t expert_stride, const void *x, int xdt,
@@ -352,7 +361,7 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     if (T == 0 || N == 0) return GGQ_OK;
     if (!W || !x || !ids || !y) return fail(GGQ_ERR_INVALID, "mul_mat_id: null pointer");
     if (!aligned16(W) || !aligned16(x) || !aligned16(y) || !aligned16(ids)) return fail(GGQ_ERR_INVALID, "mul_mat_id: pointers must be 16-byte aligned");
-    const bool mmq = use_mmq_id(wt, K, T, path);
+    const bool mmq = use_mmq_id(wt, K, T * top_k, E, path);
     if (!mmq && !mmvq_supported(wt, K)) return mmvq_too_long("mul_mat_id", wt, K);
     // routed MMQ gathers activation rows and SwiGLU up rows with 32-bit offsets
     if (mmq && (x_per_route ? T * top_k : T) * K * 2 >= (int64_t)0x7fffff00)
@@ -504,6 +513,14 @@ int ggq_bench_mfma_loop(int kind, int64_t iters, void *sink, size_t sink_bytes, 
         return fail(GGQ_ERR_WORKSPACE, "bench_mfma_loop: sink %zu bytes < %d required", sink_bytes, CEIL_MFMA_BLOCKS * 4);
     return hip_status(launch_mfma_loop(kind, iters, static_cast<int *>(sink), static_cast<hipStream_t>(stream)),
                       "bench_mfma_loop");
+}
+
+int ggq_bench_set_mmvq_id_cols(int cols) {
+    g_err[0] = 0;
+    if (cols != 0 && cols != 1 && cols != 2 && cols != 4 && cols != 8)
+        return fail(GGQ_ERR_INVALID, "bench_set_mmvq_id_cols: cols must be 0 (automatic), 1, 2, 4 or 8");
+    g_id_cols_override = cols;
+    return GGQ_OK;
 }
 
 int ggq_bench_inner_loop(int kind, int blocks_per_cu, int64_t iters, void *sink, size_t sink_bytes, void *stream) {

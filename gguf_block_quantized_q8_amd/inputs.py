@@ -134,6 +134,20 @@ def gen_routing(T, E, top_k, seed):
     return ids, w
 
 
+def gen_routing_skewed(T, E, top_k, seed, hot=8, boost=2.5):
+    """As gen_routing, with `boost` added to the logits of experts 0..hot-1 (a few
+    experts draw most routes: about 60 % of them for hot=8, boost=2.5, E=256,
+    top_k=8)."""
+    logits = rng(seed).standard_normal((T, E), dtype=np.float32).astype(np.float64)
+    logits[:, :hot] += boost
+    logits -= logits.max(axis=1, keepdims=True)
+    p = np.exp(logits)
+    p /= p.sum(axis=1, keepdims=True)
+    p32 = p.astype(np.float32)
+    order = np.argsort(-p32, axis=1, kind="stable")[:, :top_k]
+    return order.astype(np.int32), np.take_along_axis(p32, order, axis=1).astype(np.float32)
+
+
 def sample_rows(N, count, seed):
     """Sorted distinct row indices: `count` seeded picks plus the first and last row."""
     picks = rng(seed).choice(N, size=min(count, N), replace=False)

@@ -139,7 +139,11 @@ int ggq_mul_mat(int wt, const void *W, int64_t N, int64_t K,
  *                  staging for MMVQ-path calls without route weights).
  *                  ggq_mul_mat_id_ws takes the call's shape and `weighted`
  *                  (nonzero when route_w will be non-NULL: the per-route
- *                  fp32 outputs of the weighted sum live in the workspace).
+ *                  outputs of the weighted sum live in the workspace).
+ *   path         : AUTO takes the MMVQ kernel while the routes per expert
+ *                  (T * top_k / E) stay at or below 12 and MMQ above (MMVQ
+ *                  alone where MMQ has no kernel, as for ggq_mul_mat), or
+ *                  force MMVQ / MMQ.
  * Tokens, routes and tiles are grouped on the device; no host sync. */
 size_t ggq_mul_mat_id_ws(int wt, int64_t E, int64_t N, int64_t K, int xdt,
                          int64_t T, int x_per_route, int64_t top_k,
@@ -243,6 +247,13 @@ int ggq_bench_mfma_loop(int kind, int64_t iters, void *sink, size_t sink_bytes, 
  * Returns GGQ_ERR_INVALID for a kind outside 0..4 or blocks_per_cu outside 1..8.
  * sink: device buffer of at least 256 * blocks_per_cu * 4 bytes. */
 int ggq_bench_inner_loop(int kind, int blocks_per_cu, int64_t iters, void *sink, size_t sink_bytes, void *stream);
+
+/* Bench hook (not part of the product API): the routes per MMVQ-id group
+ * (1, 2, 4 or 8; capped by what the type and K allow) for every later routed
+ * MMVQ call in this process, or 0 to restore the automatic choice (a little
+ * above the mean routes per expert).  Not thread-safe; for tuning sweeps.
+ * Returns GGQ_ERR_INVALID for any other value. */
+int ggq_bench_set_mmvq_id_cols(int cols);
 
 #ifdef __cplusplus
 }
