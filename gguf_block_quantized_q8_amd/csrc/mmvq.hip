@@ -391,13 +391,15 @@ __device__ __forceinline__ int quant_exact(float x, float d) {
     return (int)__builtin_amdgcn_fmed3f(q, -127.0f, 127.0f);
 }
 
-// Activation rows of this block's columns -> planar q8_1 in LDS, 8 lanes per
-// 32-value block (lane sub of a group holds values 4 sub .. 4 sub + 3), one
-// block per lane group per loop trip.  The loops stay rolled: every launch
-// starts with a cold instruction cache, so the prologue's cost follows its
-// code size more than its instruction count.  put() is the arithmetic of the
-// standalone quantizer (amax / 127 with IEEE division, round half away from
-// zero, s = d * sum(q)), or takes a given q8_1 block as is.
+// Activation rows of this block's columns -> planar q8_1 in LDS, 4 lanes per
+// 32-value block (lane sub of a group holds values 8 sub .. 8 sub + 7), one
+// block per lane group per loop trip: 512 lanes take a 4096-value row in one
+// trip.  The loops stay rolled: every launch starts with a cold instruction
+// cache, so the prologue's cost follows its code size more than its instruction
+// count.  put() is the arithmetic of the standalone quantizer (amax / 127 with
+// IEEE division, round half away from zero, s = d * sum(q)), or takes a given
+// q8_1 block as is.
+constexpr int ACT_LPB = 4;                                       // lanes per 32-value block
 template <int NC, bool H16>
 struct ActStage {
     uint32_t nb_magic;            // b / nb == umulhi(b, nb_magic) for every block index b used here
@@ -405,81 +407,91 @@ struct ActStage {
     __device__ void init(uint32_t magic) { nb_magic = magic; }
     __device__ int col_of(int b) const { return (int)__umulhi((uint32_t)b, nb_magic); }
 
-    // Raw bytes of block b for this lane, the same two 8-byte loads for every
-    // source type: f32 values at lo.x lo.y hi.x hi.y; bf16 values in lo (hi
-    // repeats lo); q8_1: d, s at lo, the lane's 4 quants at hi.y.
-    __device__ void fetch(const MmvqParams &p, const int64_t *xrow, int nb, int b, v2i &lo, v2i &hi) const {
-        const int sub = threadIdx.x & 7, c = col_of(b), blk = b - c * nb;
-        const uint8_t *a0, *a1;
+    // Raw bytes of block b for this lane, two 16-byte values for every source
+    // type: f32 values 8 sub .. + 8 in lo, hi; bf16 / fp16 values in lo; q8_1:
+    // d, s in lo.x, lo.y and the lane's 8 quants in hi.x, hi.y.
+    __device__ void fetch(const MmvqParams &p, const int64_t *xrow, int nb, int b, v4i &lo, v4i &hi) const {
+        const int sub = threadIdx.x & (ACT_LPB - 1), c = col_of(b), blk = b - c * nb;
         if (p.xsrc == DT_Q8_1) {
-            a0 = p.q8 + xrow[c] * p.q8_row + (int64_t)blk * Q8_1_BYTES;
-            a1 = a0 + 4 + 4 * sub;                                    // [4 + 4 sub, 12 + 4 sub) of the block
+            const uint8_t *a0 = p.q8 + xrow[c] * p.q8_row + (int64_t)blk * Q8_1_BYTES;
+            const v2i h = *reinterpret_cast<const v2i *>(a0), q = *reinterpret_cast<const v2i *>(a0 + 8 + 8 * sub);
+            lo = v4i{h.x, h.y, 0, 0};
+            hi = v4i{q.x, q.y, 0, 0};
         } else {
-            const int64_t e0 = xrow[c] * p.ldx + blk * QK8_1 + sub * 4;
+            const int64_t e0 = xrow[c] * p.ldx + blk * QK8_1 + sub * 8;
             const int esz = p.xsrc == DT_F32 ? 4 : 2;
-            a0 = static_cast<const uint8_t *>(p.x) + e0 * esz;
-            a1 = p.xsrc == DT_F32 ? a0 + 8 : a0;
+            const uint8_t *a0 = static_cast<const uint8_t *>(p.x) + e0 * esz;
+            lo = *reinterpret_cast<const v4i *>(a0);
+            hi = p.xsrc == DT_F32 ? *reinterpret_cast<const v4i *>(a0 + 16) : lo;
         }
-        lo = *reinterpret_cast<const v2i *>(a0);
-        hi = *reinterpret_cast<const v2i *>(a1);
     }
 
     // Same as fetch(), from raw activation rows already copied into LDS at
     // `raw` (column c at c * K * esz, or c * nb * 40 for q8_1 blocks).
-    __device__ void fetch_lds(const MmvqParams &p, const uint8_t *raw, int K, int nb, int b, v2i &lo, v2i &hi) const {
-        const int sub = threadIdx.x & 7, c = col_of(b), blk = b - c * nb;
-        lds_bp a0, a1;
+    __device__ void fetch_lds(const MmvqParams &p, const uint8_t *raw, int K, int nb, int b, v4i &lo, v4i &hi) const {
+        const int sub = threadIdx.x & (ACT_LPB - 1), c = col_of(b), blk = b - c * nb;
         if (p.xsrc == DT_Q8_1) {
-            a0 = (lds_bp)raw + (c * nb + blk) * Q8_1_BYTES;
-            a1 = a0 + 4 + 4 * sub;
+            const lds_bp a0 = (lds_bp)raw + (c * nb + blk) * Q8_1_BYTES;
+            const v2i h = l64(a0), q = l64(a0 + 8 + 8 * sub);
+            lo = v4i{h.x, h.y, 0, 0};
+            hi = v4i{q.x, q.y, 0, 0};
         } else {
             const int esz = p.xsrc == DT_F32 ? 4 : 2;
-            a0 = (lds_bp)raw + (c * K + blk * QK8_1 + sub * 4) * esz;
-            a1 = p.xsrc == DT_F32 ? a0 + 8 : a0;
+            const lds_bp a0 = (lds_bp)raw + (c * K + blk * QK8_1 + sub * 8) * esz;
+            lo = l128(a0);
+            hi = p.xsrc == DT_F32 ? l128(a0 + 16) : lo;
         }
-        lo = l64(a0);
-        hi = l64(a1);
     }
 
-    // Quantize (or take) block b and write it to the planar layout.  All 8
+    // Quantize (or take) block b and write it to the planar layout.  All 4
     // lanes of the group take part (cross-lane reductions within the group).
-    __device__ void put(uint8_t *lds, const MmvqParams &p, int K, int nb, int b, v2i lo, v2i hi) const {
+    __device__ void put(uint8_t *lds, const MmvqParams &p, int K, int nb, int b, v4i lo, v4i hi) const {
         uint8_t *qa = lds;
         float *d8 = reinterpret_cast<float *>(lds + NC * K);
         float *s8 = d8 + NC * nb;
         int *h16 = reinterpret_cast<int *>(s8 + NC * nb);
-        const int sub = threadIdx.x & 7;
-        int q, qsum;
+        const int sub = threadIdx.x & (ACT_LPB - 1);
+        int q0, q1, qsum;
         float dq, sq;
         if (p.xsrc == DT_Q8_1) {
-            q = hi.y;
+            q0 = hi.x;
+            q1 = hi.y;
             dq = as_float(lo.x);
             sq = as_float(lo.y);
-            qsum = dot4(q, 0x01010101, 0);
+            qsum = dot4(q0, 0x01010101, dot4(q1, 0x01010101, 0));
         } else {
-            float v[4];
+            float v[8];
             if (p.xsrc == DT_F32) {
-                v[0] = as_float(lo.x); v[1] = as_float(lo.y); v[2] = as_float(hi.x); v[3] = as_float(hi.y);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    v[i] = as_float(lo[i]);
+                    v[4 + i] = as_float(hi[i]);
+                }
             } else {
                 const bool h = p.xsrc == DT_F16;
-                v[0] = from_16((uint32_t)lo.x & 0xffffu, h);
-                v[1] = from_16((uint32_t)lo.x >> 16, h);
-                v[2] = from_16((uint32_t)lo.y & 0xffffu, h);
-                v[3] = from_16((uint32_t)lo.y >> 16, h);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    v[2 * i] = from_16((uint32_t)lo[i] & 0xffffu, h);
+                    v[2 * i + 1] = from_16((uint32_t)lo[i] >> 16, h);
+                }
             }
-            const float amax = max8(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
+            m = fmaxf(m, dpp_f<DPP_XOR1>(m));
+            const float amax = fmaxf(m, dpp_f<DPP_XOR2>(m));
             const float d = amax / 127.0f;
-            q = 0;
+            q0 = q1 = 0;
             qsum = 0;
             if (amax != 0.0f) {
                 // Adding 1.5 * 2^23 rounds |z| <= 128 to the nearest integer and
                 // leaves it, two's complement, in the low byte of the sum's bits.
                 constexpr float RM = 12582912.0f;
                 const float inv = __builtin_amdgcn_rcpf(d);
-                int qb[4];
+                int qb[8];
                 bool bad = false;
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
+                for (int i = 0; i < 8; i++) {
                     const float z = v[i] * inv;
                     const float r = z + RM;
                     bad |= !(fabsf(z - (r - RM)) < 0.5f - fabsf(z) * 0x1p-20f - 0x1p-30f);
@@ -487,23 +499,26 @@ struct ActStage {
                 }
                 if (bad) {
 #pragma unroll
-                    for (int i = 0; i < 4; i++) qb[i] = quant_exact(v[i], d);
+                    for (int i = 0; i < 8; i++) qb[i] = quant_exact(v[i], d);
                 }
-                q = (int)(__builtin_amdgcn_perm((uint32_t)qb[1], (uint32_t)qb[0], 0x0c0c0400u) |
-                          __builtin_amdgcn_perm((uint32_t)qb[3], (uint32_t)qb[2], 0x04000c0cu));
-                qsum = dot4(q, 0x01010101, 0);
+                q0 = (int)(__builtin_amdgcn_perm((uint32_t)qb[1], (uint32_t)qb[0], 0x0c0c0400u) |
+                           __builtin_amdgcn_perm((uint32_t)qb[3], (uint32_t)qb[2], 0x04000c0cu));
+                q1 = (int)(__builtin_amdgcn_perm((uint32_t)qb[5], (uint32_t)qb[4], 0x0c0c0400u) |
+                           __builtin_amdgcn_perm((uint32_t)qb[7], (uint32_t)qb[6], 0x04000c0cu));
+                qsum = dot4(q0, 0x01010101, dot4(q1, 0x01010101, 0));
             }
             dq = amax != 0.0f ? d : 0.0f;
-            sq = dq * (float)sum8(qsum);
+            sq = dq * (float)sum4(qsum);
         }
-        const int half = H16 ? sum4(qsum) : 0;                      // lanes 0..3: quants 0..15, 4..7: 16..31
+        // lanes 0, 1: quants 0..15; lanes 2, 3: 16..31
+        const int half = H16 ? qsum + dpp_i<DPP_XOR1>(qsum) : 0;
         const int c = col_of(b), blk = b - c * nb;
-        reinterpret_cast<int *>(qa + c * K + blk * QK8_1)[sub] = q;
+        *reinterpret_cast<v2i *>(qa + c * K + blk * QK8_1 + 8 * sub) = v2i{q0, q1};
         if (sub == 0) {
             d8[c * nb + blk] = dq;
             s8[c * nb + blk] = sq;
         }
-        if (H16 && (sub & 3) == 0) h16[(c * 2 + (sub >> 2)) * nb + blk] = -32 * half;
+        if (H16 && (sub & 1) == 0) h16[(c * 2 + (sub >> 1)) * nb + blk] = -32 * half;
     }
 };
 
@@ -590,6 +605,13 @@ __device__ __forceinline__ void stage_issue(const uint8_t *A, const uint8_t *wen
     }
 }
 
+// The first item of a wave, issued at the top of the kernel before the per-lane
+// table exists: the same offsets as stage_issue's, computed per instruction.
+template <int EPI>
+__device__ __forceinline__ void stage_issue_first(const uint8_t *A, const uint8_t *wend, uint8_t *buf, int ninst,
+                                                  int lane, uint32_t cps, uint32_t cps_magic, uint32_t spw,
+                                                  uint32_t rb32, uint32_t np_rb);
+
 // wend is 2-byte aligned; when it is not 4-byte aligned the dword holding its
 // last two bytes is outside the range and landed as zero: patch those two
 // bytes from a 16-bit load (after the copy has landed).
@@ -623,6 +645,27 @@ __device__ __forceinline__ uint32_t slot_off(uint32_t s, uint32_t rb, uint32_t n
     return EPI == EPI_SWIGLU ? __umul24(s >> 1, rb) + ((s & 1) ? np_rb : 0u) : __umul24(s, rb);
 }
 
+template <int EPI>
+__device__ __forceinline__ void stage_issue_first(const uint8_t *A, const uint8_t *wend, uint8_t *buf, int ninst,
+                                                  int lane, uint32_t cps, uint32_t cps_magic, uint32_t spw,
+                                                  uint32_t rb32, uint32_t np_rb) {
+    const uint32_t phi = (uint32_t)(reinterpret_cast<uintptr_t>(A) & 15);
+    const uint8_t *base = A - phi;
+    const int64_t avail = wend - base;
+    struct { const void *p; uint32_t range; uint32_t cfg; } r = {
+        base, (uint32_t)(avail < 0x7fffff00LL ? avail : 0x7fffff00LL), 0x00020000u};
+    v4i rsrc = __builtin_bit_cast(v4i, r);
+#pragma unroll
+    for (int i = 0; i < 4; i++) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+#pragma unroll 1
+    for (int k = 0; k < ninst; k++) {
+        const uint32_t P = (uint32_t)(lane + 64 * k), slot = __umulhi(P, cps_magic);
+        const uint32_t c16 = 16u * P - __umul24(slot, 16u * cps);
+        const uint32_t off = slot < 2u * spw ? slot_off<EPI>(slot, rb32, np_rb) + c16 : STAGE_UNUSED;
+        llvm_amdgcn_raw_buffer_load_lds(rsrc, (AS3 uint32_t *)(buf + 1024 * k), 16, (int)((phi + off) & ~15u), 0, 0, 0);
+    }
+}
+
 // Largest workgroup: 16 waves (one workgroup per CU quantizes the activations
 // once for all of them); every column count fits 128 registers.
 template <int NC>
@@ -654,6 +697,36 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
     uint8_t *raw = lds + p.act_lds_bytes + bstride;
     uint8_t *sink = raw + p.raw_region;
 
+    // ---- early copies (dense, activation rows through LDS): the activation rows, then
+    // the first weight item, go out before any table is built or barrier passed.  A
+    // short launch starts with a cold instruction cache, so every instruction ahead of
+    // these copies delays the first bytes; the activations stay older than the
+    // weights, so waiting for all but the weight instructions still covers them.
+    const bool early = !MOE && p.act_dma;
+    if (early) {
+        const int64_t c0 = grp * NC;
+        const int nce = (int)min<int64_t>(NC, p.M - c0);
+        const int nbe = (int)(p.K / QK8_1);
+        const uint32_t rowb = p.xsrc == DT_Q8_1 ? nbe * Q8_1_BYTES : (uint32_t)p.K * (p.xsrc == DT_F32 ? 4 : 2);
+        const uint32_t ppc = rowb / 16, pieces = nce * ppc;
+        const uint8_t *xb = p.xsrc == DT_Q8_1 ? p.q8 : static_cast<const uint8_t *>(p.x);
+        struct { const void *q; uint32_t range; uint32_t cfg; } r = {xb, (uint32_t)p.x_bytes, 0x00020000u};
+        v4i rsrc = __builtin_bit_cast(v4i, r);
+#pragma unroll
+        for (int i = 0; i < 4; i++) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+        for (uint32_t j0 = (uint32_t)wave * 64; j0 < pieces; j0 += (uint32_t)wpb * 64) {
+            const uint32_t j = j0 + lane, c = __umulhi(j, p.ppc_magic);
+            const uint32_t xo = (uint32_t)((c0 + ((int)c < nce ? (int)c : 0)) * p.x_stride);
+            const uint32_t voff = j < pieces ? xo + 16u * (j - __umul24(c, ppc)) : STAGE_UNUSED;
+            llvm_amdgcn_raw_buffer_load_lds(rsrc, (AS3 uint32_t *)(raw + j0 * 16), 16, (int)voff, 0, 0, 0);
+        }
+        const int64_t pwe = ((int64_t)blockIdx.x * wpb + wave) * spw;
+        if (pwe < p.npairs)
+            stage_issue_first<EPI>(p.W + (EPI == EPI_SWIGLU ? pwe : 2 * pwe) * p.row_bytes, p.W + p.w_bytes, wbuf,
+                                   ninst, lane, (uint32_t)cps, p.cps_magic, (uint32_t)spw, (uint32_t)p.row_bytes,
+                                   (uint32_t)(p.Np * p.row_bytes));
+    }
+
     // ---- columns of this group ----
     const uint8_t *W = p.W;
     int ncols;
@@ -681,7 +754,9 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
     }
     const uint8_t *wend = p.W + p.w_bytes;
     const int64_t rb = p.row_bytes;
-    __syncthreads();                                            // xrow / route_s visible
+    // xrow / route_s visible.  An LDS-only barrier: a full __syncthreads would also wait
+    // for the early copies (vmcnt), putting their whole latency ahead of the prologue.
+    lds_barrier();
 
     // ---- per-lane staging tables ----
     Stage S;
@@ -714,7 +789,7 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
     ActStage<NC, T == T_Q6_K> AS;
     const int K = (int)p.K, nb = K / QK8_1, total = ncols * nb;
     AS.init(p.nb_magic);
-    const int gstep = (int)(blockDim.x >> 3);                   // lane groups of the block
+    const int gstep = (int)(blockDim.x / ACT_LPB);              // lane groups of the block
     const bool first = pw0 < p.npairs;
     if (p.act_dma) {
         // raw activation rows -> LDS by the same DMA path (older than the weight
@@ -726,24 +801,26 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
         v4i rsrc = __builtin_bit_cast(v4i, r);
 #pragma unroll
         for (int i = 0; i < 4; i++) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
-        for (uint32_t j0 = (uint32_t)wave * 64; j0 < pieces; j0 += (uint32_t)wpb * 64) {
-            const uint32_t j = j0 + lane, c = __umulhi(j, p.ppc_magic);
-            const uint32_t voff = j < pieces ? xoff[c] + 16u * (j - __umul24(c, ppc)) : STAGE_UNUSED;
-            llvm_amdgcn_raw_buffer_load_lds(rsrc, (AS3 uint32_t *)(raw + j0 * 16), 16, (int)voff, 0, 0, 0);
+        if (!early) {
+            for (uint32_t j0 = (uint32_t)wave * 64; j0 < pieces; j0 += (uint32_t)wpb * 64) {
+                const uint32_t j = j0 + lane, c = __umulhi(j, p.ppc_magic);
+                const uint32_t voff = j < pieces ? xoff[c] + 16u * (j - __umul24(c, ppc)) : STAGE_UNUSED;
+                llvm_amdgcn_raw_buffer_load_lds(rsrc, (AS3 uint32_t *)(raw + j0 * 16), 16, (int)voff, 0, 0, 0);
+            }
+            if (first) stage_issue(chunk_addr(pw0, 0), wend, wbuf, S, ninst);
         }
-        if (first) stage_issue(chunk_addr(pw0, 0), wend, wbuf, S, ninst);
         wait_vm_n(first ? ninst : 0);
         lds_barrier();                                          // every wave's share has landed
 #pragma unroll 1
-        for (int b = (int)(threadIdx.x >> 3); b < total; b += gstep) {
-            v2i lo, hi;
+        for (int b = (int)(threadIdx.x / ACT_LPB); b < total; b += gstep) {
+            v4i lo, hi;
             AS.fetch_lds(p, raw, K, nb, b, lo, hi);
             AS.put(lds, p, K, nb, b, lo, hi);
         }
     } else {
         // the first block of every lane group is loaded ahead of the weight copy
-        const int b0 = (int)(threadIdx.x >> 3);
-        v2i lo, hi;
+        const int b0 = (int)(threadIdx.x / ACT_LPB);
+        v4i lo, hi;
         AS.fetch(p, xrow, nb, min(b0, total - 1), lo, hi);
         if (first) stage_issue<true>(chunk_addr(pw0, 0), wend, wbuf, S, ninst, sink);
         else stage_issue<true>(chunk_addr(0, 0), wend, wbuf, S, 0, sink);
