@@ -48,9 +48,9 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
 }
 // fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16, nan = (u >> 16) | 0x40u;
+    return (u & 0x7fffffffu) > 0x7f800000u ? nan : r;                  // a select, not a branch
 }
 // fp32 -> IEEE binary16 bits, round to nearest even (v_cvt_f16_f32 in the
 // default rounding mode, subnormal halves kept); past the largest finite half
@@ -185,19 +185,32 @@ __device__ __forceinline__ int sum8(int v) {
 }
 
 // Sum over aligned segments of `width` lanes (a power of two <= 64), with the
-// segment total in the LAST lane of each segment (width <= 16: in every lane).
-// Within a 16-lane row: DPP butterflies; across rows: DPP row broadcasts
-// (lane 15 of a row into the next row, lane 31 into rows 2 and 3).
-__device__ __forceinline__ float seg_sum(float v, int width) {
-    if (width >= 2) v += dpp_f<DPP_XOR1>(v);
-    if (width >= 4) v += dpp_f<DPP_XOR2>(v);
-    if (width >= 8) v += dpp_f<DPP_HALF_MIRROR>(v);
-    if (width >= 16) v += dpp_f<DPP_MIRROR>(v);
+// segment total in the LAST lane of each segment (width <= 16: in every lane),
+// for every value of a [2][N] array.  Within a 16-lane row: DPP butterflies;
+// across rows: DPP row broadcasts (lane 15 of a row into the next row, lane 31
+// into rows 2 and 3).  One step at a time for all values: `width` is a runtime
+// value, so a branch per step rather than per value and step, and the values'
+// independent DPP moves overlap.
+template <int N>
+__device__ __forceinline__ void seg_sum(float (&a)[2][N], int width) {
+    auto step = [&](auto f) {
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int c = 0; c < N; c++) a[i][c] += f(a[i][c]);
+    };
+    if (width >= 2) step([](float v) { return dpp_f<DPP_XOR1>(v); });
+    if (width >= 4) step([](float v) { return dpp_f<DPP_XOR2>(v); });
+    if (width >= 8) step([](float v) { return dpp_f<DPP_HALF_MIRROR>(v); });
+    if (width >= 16) step([](float v) { return dpp_f<DPP_MIRROR>(v); });
     if (width >= 32)                        // rows 1, 3 += lane 15 of rows 0, 2
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), DPP_ROW_BCAST15, 0xA, 0xF, false));
+        step([](float v) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), DPP_ROW_BCAST15, 0xA, 0xF, false));
+        });
     if (width >= 64)                        // rows 2, 3 += lane 31
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), DPP_ROW_BCAST31, 0xC, 0xF, false));
-    return v;
+        step([](float v) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), DPP_ROW_BCAST31, 0xC, 0xF, false));
+        });
 }
 
 }  // namespace ggq

@@ -357,19 +357,64 @@ __device__ __forceinline__ void store_out(void *y, int64_t idx, float v, bool h)
     else static_cast<uint16_t *>(y)[idx] = (uint16_t)f32_to_16(v, h);
 }
 
-// Outputs idx and idx + 1 (both valid): one store when they are aligned together.
-template <int YDT>
-__device__ __forceinline__ void store_out2(void *y, int64_t idx, float v0, float v1, bool h) {
-    if ((idx & 1) == 0) {
-        if (YDT == DT_F32) *reinterpret_cast<v2i *>(static_cast<float *>(y) + idx) = v2i{__builtin_bit_cast(int, v0), __builtin_bit_cast(int, v1)};
-        else *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(y) + idx) = f32_to_16(v0, h) | (f32_to_16(v1, h) << 16);
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Stores of a finished row pair (rows r0 and, when v1, r1) for the group's
+// columns, by the lane holding the segment totals.  The per-launch choices (fp16
+// or bf16 elements, whether a row pair's two outputs share one aligned store)
+// are taken once, outside the column loop, so that the loop is straight-line.
+// cix: the columns' activation rows (dense) or route indices (routed).
+template <int NC, bool MOE, int EPI, int YDT, bool H>
+__device__ __forceinline__ void store_cols(const MmvqParams &p, const float (&acc)[2][NC], const int64_t (&cix)[NC],
+                                           int ncols, bool v1, int64_t r0, int64_t r1) {
+    if (!MOE) {
+        if (v1 && (p.ldy & 1) == 0) {                      // r0 even, r1 = r0 + 1: one store per column
+#pragma unroll
+            for (int c = 0; c < NC; c++) {
+                if (c < ncols) {
+                    const int64_t idx = cix[c] * p.ldy + r0;
+                    if (YDT == DT_F32) {
+                        float *yp = static_cast<float *>(p.y) + idx;
+                        yp[0] = acc[0][c];
+                        yp[1] = acc[1][c];
+                    } else
+                        *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(p.y) + idx) =
+                            f32_to_16(acc[0][c], H) | (f32_to_16(acc[1][c], H) << 16);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NC; c++) {
+                if (c < ncols) {
+                    const int64_t idx = cix[c] * p.ldy + r0;
+                    store_out<YDT>(p.y, idx, acc[0][c], H);
+                    if (v1) store_out<YDT>(p.y, idx + 1, acc[1][c], H);
+                }
+            }
+        }
     } else {
-        store_out<YDT>(y, idx, v0, h);
-        store_out<YDT>(y, idx + 1, v1, h);
+        // weighted: per-route outputs (output dtype), summed per token afterwards
+        void *o = p.oroute ? p.oroute : p.y;
+#pragma unroll
+        for (int c = 0; c < NC; c++) {
+            if (c < ncols) {
+                const int64_t r = cix[c];
+                if (EPI == EPI_SWIGLU) {
+                    store_out<YDT>(o, r * p.Np + r0, silu_mul(acc[0][c], acc[1][c]), H);
+                } else {
+                    store_out<YDT>(o, r * p.Np + r0, acc[0][c], H);
+                    if (v1) store_out<YDT>(o, r * p.Np + r1, acc[1][c], H);
+                }
+            }
+        }
     }
 }
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+template <int NC, bool MOE, int EPI, int YDT>
+__device__ __forceinline__ void store_pair(const MmvqParams &p, const float (&acc)[2][NC], const int64_t (&cix)[NC],
+                                           int ncols, bool v1, int64_t r0, int64_t r1) {
+    if (YDT != DT_F32 && p.y_f16) store_cols<NC, MOE, EPI, YDT, true>(p, acc, cix, ncols, v1, r0, r1);
+    else store_cols<NC, MOE, EPI, YDT, false>(p, acc, cix, ncols, v1, r0, r1);
+}
 
 // Sum over aligned quads of lanes, result in every lane of the quad.
 __device__ __forceinline__ int sum4(int v) {
@@ -378,12 +423,9 @@ __device__ __forceinline__ int sum4(int v) {
 }
 
 // q = round-half-away(x / d) in fp32 with d = amax / 127 and the IEEE
-// quotient, as the quantizer defines it.  put() avoids this division per
-// value: with inv an approximate reciprocal (v_rcp, about 1 ulp), z = x * inv
-// is within about 4 ulp of the correctly rounded quotient, so both round to
-// the same integer unless z lies within a few ulp of a half-integer (then any
-// nearest rounding of z is that integer).  Lanes holding such a value, or a
-// non-finite one, take this exact path for their four values.
+// quotient, as the quantizer defines it, by the compiler's division: the
+// fallback of put() for blocks outside the range quant_div() covers, and for
+// f32 lanes whose fast rounding is ambiguous.
 __device__ __forceinline__ int quant_exact(float x, float d) {
     const float z = x / d;
     const float t = __builtin_truncf(z);
@@ -391,134 +433,218 @@ __device__ __forceinline__ int quant_exact(float x, float d) {
     return (int)__builtin_amdgcn_fmed3f(q, -127.0f, 127.0f);
 }
 
-// Activation rows of this block's columns -> planar q8_1 in LDS, 4 lanes per
-// 32-value block (lane sub of a group holds values 8 sub .. 8 sub + 7), one
-// block per lane group per loop trip: 512 lanes take a 4096-value row in one
-// trip.  The loops stay rolled: every launch starts with a cold instruction
-// cache, so the prologue's cost follows its code size more than its instruction
-// count.  put() is the arithmetic of the standalone quantizer (amax / 127 with
-// IEEE division, round half away from zero, s = d * sum(q)), or takes a given
-// q8_1 block as is.
-constexpr int ACT_LPB = 4;                                       // lanes per 32-value block
+// The same q without a division instruction per value, for a block scale
+// d = amax / 127 with 2^-60 <= amax <= 2^96 and |x| <= amax: z = fl(x / d)
+// from q0 = x y (y: v_rcp of d refined by one Newton step) and two
+// corrections q + (x - d q) y, each residual exact by the fma (Markstein's
+// correction steps); in that range no product, quotient or residual leaves the
+// normal range, so no operand scaling is needed.  Then round half away from
+// zero.
+__device__ __forceinline__ int quant_div(float x, float d, float y) {
+    const float q0 = x * y;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-d, q0, x), y, q0);
+    const float z = __builtin_fmaf(__builtin_fmaf(-d, q1, x), y, q1);
+    // for |z| <= 128, z + copysign(0.5 - 2^-25, z) truncated is z rounded half
+    // away from zero (checked for every float in that range)
+    return (int)(z + __builtin_copysignf(0x1.fffffep-2f, z));
+}
+
+// Activation rows of this block's columns -> planar q8_1 in LDS.  A 32-value
+// block is spread over LPB lanes (lane sub of a group holds values VPL sub ..
+// VPL sub + VPL - 1): 4 lanes for one column, so that 512 lanes take a
+// 4096-value row in one pass; 2 for two columns and 1 for more, so that the
+// per-block work (the block maximum and its cross-lane steps, the scale, the
+// stores) is shared by fewer lanes when every lane has several blocks to do.
+// put() is the arithmetic of the standalone quantizer (amax / 127 with IEEE
+// division, round half away from zero, s = d * sum(q)), or takes a given q8_1
+// block as is.
+// x / 127 correctly rounded, by one multiplication and two fmas: q = x * c
+// with c = fl(1/127), then q + (x - 127 q) c.  For 2^-96 <= x <= 2^126 every
+// intermediate is a normal number and the result equals IEEE division for all
+// such x (checked over every mantissa of a binade; scaling by powers of two
+// is exact there).  Other x (tiny, huge, inf) take the division.
+__device__ __forceinline__ float div127(float x) {
+    if (!(x >= 0x1p-96f && x <= 0x1p126f)) return x / 127.0f;
+    constexpr float c = 1.0f / 127.0f;
+    const float q = x * c;
+    return __builtin_fmaf(__builtin_fmaf(-q, 127.0f, x), c, q);
+}
+
+template <int NC>
+constexpr int act_lpb() { return NC == 1 ? 4 : NC == 2 ? 2 : 1; }
+
 template <int NC, bool H16>
 struct ActStage {
+    static constexpr int LPB = act_lpb<NC>(), VPL = QK8_1 / LPB;      // lanes per block, values per lane
+    static constexpr int NW = VPL / 4;                                  // 16-byte words of a lane's raw f32 values
+    // A lane's raw bytes of a block: f32 values in w[0 .. NW); bf16 / fp16 values
+    // in w[0 .. NW / 2); q8_1: d, s in w[0].x, w[0].y, the lane's VPL quants in
+    // the ints from w[1] on.
+    struct Raw {
+        v4i w[NW];
+        __device__ int word(int i) const { return w[i >> 2][i & 3]; }
+        __device__ void set_word(int i, int v) { w[i >> 2][i & 3] = v; }
+    };
     uint32_t nb_magic;            // b / nb == umulhi(b, nb_magic) for every block index b used here
 
     __device__ void init(uint32_t magic) { nb_magic = magic; }
     __device__ int col_of(int b) const { return (int)__umulhi((uint32_t)b, nb_magic); }
+    __device__ static int sub() { return (int)(threadIdx.x & (LPB - 1)); }
 
-    // Raw bytes of block b for this lane, two 16-byte values for every source
-    // type: f32 values 8 sub .. + 8 in lo, hi; bf16 / fp16 values in lo; q8_1:
-    // d, s in lo.x, lo.y and the lane's 8 quants in hi.x, hi.y.
-    __device__ void fetch(const MmvqParams &p, const int64_t *xrow, int nb, int b, v4i &lo, v4i &hi) const {
-        const int sub = threadIdx.x & (ACT_LPB - 1), c = col_of(b), blk = b - c * nb;
-        if (p.xsrc == DT_Q8_1) {
+    // Raw bytes of block b for this lane from global memory.  XS (the source
+    // type) is a template argument so that put() compiles to straight-line code.
+    template <int XS>
+    __device__ void fetch(const MmvqParams &p, const int64_t *xrow, int nb, int b, Raw &r) const {
+        const int c = col_of(b), blk = b - c * nb;
+        if (XS == DT_Q8_1) {
             const uint8_t *a0 = p.q8 + xrow[c] * p.q8_row + (int64_t)blk * Q8_1_BYTES;
-            const v2i h = *reinterpret_cast<const v2i *>(a0), q = *reinterpret_cast<const v2i *>(a0 + 8 + 8 * sub);
-            lo = v4i{h.x, h.y, 0, 0};
-            hi = v4i{q.x, q.y, 0, 0};
+            const v2i h = *reinterpret_cast<const v2i *>(a0);
+            r.w[0] = v4i{h.x, h.y, 0, 0};
+#pragma unroll
+            for (int i = 0; i < VPL / 8; i++) {
+                const v2i q = *reinterpret_cast<const v2i *>(a0 + 8 + VPL * sub() + 8 * i);
+                r.set_word(4 + 2 * i, q.x);
+                r.set_word(5 + 2 * i, q.y);
+            }
         } else {
-            const int64_t e0 = xrow[c] * p.ldx + blk * QK8_1 + sub * 8;
-            const int esz = p.xsrc == DT_F32 ? 4 : 2;
-            const uint8_t *a0 = static_cast<const uint8_t *>(p.x) + e0 * esz;
-            lo = *reinterpret_cast<const v4i *>(a0);
-            hi = p.xsrc == DT_F32 ? *reinterpret_cast<const v4i *>(a0 + 16) : lo;
+            constexpr int esz = XS == DT_F32 ? 4 : 2;
+            const uint8_t *a0 = static_cast<const uint8_t *>(p.x) + (xrow[c] * p.ldx + blk * QK8_1 + sub() * VPL) * esz;
+#pragma unroll
+            for (int i = 0; i < VPL * esz / 16; i++) r.w[i] = *reinterpret_cast<const v4i *>(a0 + 16 * i);
         }
     }
 
     // Same as fetch(), from raw activation rows already copied into LDS at
     // `raw` (column c at c * K * esz, or c * nb * 40 for q8_1 blocks).
-    __device__ void fetch_lds(const MmvqParams &p, const uint8_t *raw, int K, int nb, int b, v4i &lo, v4i &hi) const {
-        const int sub = threadIdx.x & (ACT_LPB - 1), c = col_of(b), blk = b - c * nb;
-        if (p.xsrc == DT_Q8_1) {
+    template <int XS>
+    __device__ void fetch_lds(const uint8_t *raw, int K, int nb, int b, Raw &r) const {
+        const int c = col_of(b), blk = b - c * nb;
+        if (XS == DT_Q8_1) {
             const lds_bp a0 = (lds_bp)raw + (c * nb + blk) * Q8_1_BYTES;
-            const v2i h = l64(a0), q = l64(a0 + 8 + 8 * sub);
-            lo = v4i{h.x, h.y, 0, 0};
-            hi = v4i{q.x, q.y, 0, 0};
+            const v2i h = l64(a0);
+            r.w[0] = v4i{h.x, h.y, 0, 0};
+#pragma unroll
+            for (int i = 0; i < VPL / 8; i++) {
+                const v2i q = l64(a0 + 8 + VPL * sub() + 8 * i);
+                r.set_word(4 + 2 * i, q.x);
+                r.set_word(5 + 2 * i, q.y);
+            }
         } else {
-            const int esz = p.xsrc == DT_F32 ? 4 : 2;
-            const lds_bp a0 = (lds_bp)raw + (c * K + blk * QK8_1 + sub * 8) * esz;
-            lo = l128(a0);
-            hi = p.xsrc == DT_F32 ? l128(a0 + 16) : lo;
+            constexpr int esz = XS == DT_F32 ? 4 : 2;
+            const lds_bp a0 = (lds_bp)raw + (c * K + blk * QK8_1 + sub() * VPL) * esz;
+#pragma unroll
+            for (int i = 0; i < VPL * esz / 16; i++) r.w[i] = l128(a0 + 16 * i);
         }
     }
 
-    // Quantize (or take) block b and write it to the planar layout.  All 4
-    // lanes of the group take part (cross-lane reductions within the group).
-    __device__ void put(uint8_t *lds, const MmvqParams &p, int K, int nb, int b, v4i lo, v4i hi) const {
+    // Quantize (or take) block b and write it to the planar layout.  All LPB
+    // lanes of the group take part (cross-lane steps within the group).
+    template <int XS>
+    __device__ void put(uint8_t *lds, int K, int nb, int b, const Raw &r) const {
         uint8_t *qa = lds;
         float *d8 = reinterpret_cast<float *>(lds + NC * K);
         float *s8 = d8 + NC * nb;
         int *h16 = reinterpret_cast<int *>(s8 + NC * nb);
-        const int sub = threadIdx.x & (ACT_LPB - 1);
-        int q0, q1, qsum;
+        int q[VPL / 4];                                   // the lane's quants, 4 per int
         float dq, sq;
-        if (p.xsrc == DT_Q8_1) {
-            q0 = hi.x;
-            q1 = hi.y;
-            dq = as_float(lo.x);
-            sq = as_float(lo.y);
-            qsum = dot4(q0, 0x01010101, dot4(q1, 0x01010101, 0));
+        if (XS == DT_Q8_1) {
+#pragma unroll
+            for (int i = 0; i < VPL / 4; i++) q[i] = r.word(4 + i);
+            dq = as_float(r.w[0].x);
+            sq = as_float(r.w[0].y);
         } else {
-            float v[8];
-            if (p.xsrc == DT_F32) {
+            float v[VPL];
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    v[i] = as_float(lo[i]);
-                    v[4 + i] = as_float(hi[i]);
-                }
-            } else {
-                const bool h = p.xsrc == DT_F16;
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    v[2 * i] = from_16((uint32_t)lo[i] & 0xffffu, h);
-                    v[2 * i + 1] = from_16((uint32_t)lo[i] >> 16, h);
-                }
+            for (int i = 0; i < VPL; i++) {
+                if (XS == DT_F32) v[i] = as_float(r.word(i));
+                else v[i] = from_16(((uint32_t)r.word(i >> 1) >> (16 * (i & 1))) & 0xffffu, XS == DT_F16);
             }
             float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(v[i]));
-            m = fmaxf(m, dpp_f<DPP_XOR1>(m));
-            const float amax = fmaxf(m, dpp_f<DPP_XOR2>(m));
-            const float d = amax / 127.0f;
-            q0 = q1 = 0;
-            qsum = 0;
+            for (int i = 0; i < VPL; i++) m = fmaxf(m, fabsf(v[i]));
+            if (LPB >= 2) m = fmaxf(m, dpp_f<DPP_XOR1>(m));
+            if (LPB >= 4) m = fmaxf(m, dpp_f<DPP_XOR2>(m));
+            const float amax = m;
+            float d = 0.0f;
+#pragma unroll
+            for (int i = 0; i < VPL / 4; i++) q[i] = 0;
             if (amax != 0.0f) {
-                // Adding 1.5 * 2^23 rounds |z| <= 128 to the nearest integer and
-                // leaves it, two's complement, in the low byte of the sum's bits.
-                constexpr float RM = 12582912.0f;
+                d = div127(amax);
                 const float inv = __builtin_amdgcn_rcpf(d);
-                int qb[8];
-                bool bad = false;
+                int qb[VPL];
+                const bool ranged = amax >= 0x1p-60f && amax <= 0x1p96f;
+                if (XS != DT_F32 && ranged) {
+                    // 16-bit values: short significands put about 1 value in 200
+                    // within 2^-14 of a half-integer quotient (many exactly on one),
+                    // so nearly every wave would take a fallback; the exact
+                    // quotient for every value costs less.
+                    const float y = __builtin_fmaf(__builtin_fmaf(-d, inv, 1.0f), inv, inv);
 #pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    const float z = v[i] * inv;
-                    const float r = z + RM;
-                    bad |= !(fabsf(z - (r - RM)) < 0.5f - fabsf(z) * 0x1p-20f - 0x1p-30f);
-                    qb[i] = __builtin_bit_cast(int, r);
-                }
-                if (bad) {
+                    for (int i = 0; i < VPL; i++) qb[i] = quant_div(v[i], d, y);
+                } else {
+                    // fma(v, inv, 1.5 * 2^23) rounds v * inv (|v * inv| <= 128) to
+                    // the nearest integer and leaves it, two's complement, in the low
+                    // byte of the result's bits.  e is the largest distance of a
+                    // product from its integer: below 0.5 - 2^-14 the quotient v / d,
+                    // within 128 * 2^-23 of v * inv (v_rcp_f32 is good to 1 ulp),
+                    // rounds to the same integer and is no tie; otherwise the lane's
+                    // values take the exact division.
+                    constexpr float RM = 12582912.0f;
+                    float e = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 8; i++) qb[i] = quant_exact(v[i], d);
+                    for (int i = 0; i < VPL; i++) {
+                        const float rv = __builtin_fmaf(v[i], inv, RM);
+                        e = fmaxf(e, fabsf(__builtin_fmaf(v[i], inv, RM - rv)));
+                        qb[i] = __builtin_bit_cast(int, rv);
+                    }
+                    if (!(e < 0.5f - 0x1p-14f)) {
+#pragma unroll
+                        for (int i = 0; i < VPL; i++) qb[i] = quant_exact(v[i], d);
+                    }
                 }
-                q0 = (int)(__builtin_amdgcn_perm((uint32_t)qb[1], (uint32_t)qb[0], 0x0c0c0400u) |
-                           __builtin_amdgcn_perm((uint32_t)qb[3], (uint32_t)qb[2], 0x04000c0cu));
-                q1 = (int)(__builtin_amdgcn_perm((uint32_t)qb[5], (uint32_t)qb[4], 0x0c0c0400u) |
-                           __builtin_amdgcn_perm((uint32_t)qb[7], (uint32_t)qb[6], 0x04000c0cu));
-                qsum = dot4(q0, 0x01010101, dot4(q1, 0x01010101, 0));
+#pragma unroll
+                for (int i = 0; i < VPL / 4; i++)
+                    q[i] = (int)(__builtin_amdgcn_perm((uint32_t)qb[4 * i + 1], (uint32_t)qb[4 * i], 0x0c0c0400u) |
+                                 __builtin_amdgcn_perm((uint32_t)qb[4 * i + 3], (uint32_t)qb[4 * i + 2], 0x04000c0cu));
             }
-            dq = amax != 0.0f ? d : 0.0f;
-            sq = dq * (float)sum4(qsum);
+            dq = d;
         }
-        // lanes 0, 1: quants 0..15; lanes 2, 3: 16..31
-        const int half = H16 ? qsum + dpp_i<DPP_XOR1>(qsum) : 0;
+        // sums of the lane's quants: by halves of the block when LPB == 1
+        int qs0 = 0, qs1 = 0;
+#pragma unroll
+        for (int i = 0; i < VPL / 4; i++) {
+            if (LPB == 1 && i >= VPL / 8) qs1 = dot4(q[i], 0x01010101, qs1);
+            else qs0 = dot4(q[i], 0x01010101, qs0);
+        }
+        if (XS != DT_Q8_1) {
+            int qsum = qs0 + qs1;
+            if (LPB >= 2) qsum += dpp_i<DPP_XOR1>(qsum);
+            if (LPB >= 4) qsum += dpp_i<DPP_XOR2>(qsum);
+            sq = dq * (float)qsum;
+        }
         const int c = col_of(b), blk = b - c * nb;
-        *reinterpret_cast<v2i *>(qa + c * K + blk * QK8_1 + 8 * sub) = v2i{q0, q1};
-        if (sub == 0) {
+        uint8_t *qdst = qa + c * K + blk * QK8_1 + VPL * sub();
+        if (VPL == 8) *reinterpret_cast<v2i *>(qdst) = v2i{q[0], q[1]};
+#pragma unroll
+        for (int i = 0; VPL >= 16 && i < VPL / 16; i++)
+            *reinterpret_cast<v4i *>(qdst + 16 * i) = v4i{q[4 * i], q[4 * i + 1], q[4 * i + 2], q[4 * i + 3]};
+        if (sub() == 0) {
             d8[c * nb + blk] = dq;
             s8[c * nb + blk] = sq;
         }
-        if (H16 && (sub & 1) == 0) h16[(c * 2 + (sub >> 1)) * nb + blk] = -32 * half;
+        if (H16) {
+            // sums of the quants 0..15 and 16..31 of the block
+            int *hd = h16 + c * 2 * nb + blk;
+            if (LPB == 4) {                                  // lanes 0, 1: quants 0..15; lanes 2, 3: 16..31
+                const int half = qs0 + dpp_i<DPP_XOR1>(qs0);
+                if ((sub() & 1) == 0) hd[(sub() >> 1) * nb] = -32 * half;
+            } else if (LPB == 2) {
+                hd[sub() * nb] = -32 * qs0;
+            } else {
+                hd[0] = -32 * qs0;
+                hd[nb] = -32 * qs1;
+            }
+        }
     }
 };
 
@@ -786,10 +912,11 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
     // Prologue: the activation loads of the first batch go out first, then the
     // first weight item, so the quantization below runs while the weights are
     // in flight (waiting only for the activation loads, which are older).
-    ActStage<NC, T == T_Q6_K> AS;
+    using ActS = ActStage<NC, T == T_Q6_K>;
+    ActS AS;
     const int K = (int)p.K, nb = K / QK8_1, total = ncols * nb;
     AS.init(p.nb_magic);
-    const int gstep = (int)(blockDim.x / ACT_LPB);              // lane groups of the block
+    const int gstep = (int)(blockDim.x / ActS::LPB);            // lane groups of the block
     const bool first = pw0 < p.npairs;
     if (p.act_dma) {
         // raw activation rows -> LDS by the same DMA path (older than the weight
@@ -811,25 +938,59 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
         }
         wait_vm_n(first ? ninst : 0);
         lds_barrier();                                          // every wave's share has landed
+    }
+    // The quantization, compiled once per source type (a branch per element
+    // otherwise): from the LDS copies, or from global memory.
+    auto quantize = [&](auto xs) {
+        constexpr int XS = decltype(xs)::value;
+        const int b0 = (int)(threadIdx.x / ActS::LPB);
+        if (p.act_dma) {
+            if (ActS::LPB > 1 && total > gstep) {
+                // several blocks per lane group of 2 or 4 lanes (long rows): two per
+                // trip, so that the two blocks' dependency chains overlap (a lane with a
+                // whole block has 32 independent values already).  The second index is
+                // clamped to the last block: a duplicate writes the same values as its
+                // owner.
 #pragma unroll 1
-        for (int b = (int)(threadIdx.x / ACT_LPB); b < total; b += gstep) {
-            v4i lo, hi;
-            AS.fetch_lds(p, raw, K, nb, b, lo, hi);
-            AS.put(lds, p, K, nb, b, lo, hi);
-        }
-    } else {
-        // the first block of every lane group is loaded ahead of the weight copy
-        const int b0 = (int)(threadIdx.x / ACT_LPB);
-        v4i lo, hi;
-        AS.fetch(p, xrow, nb, min(b0, total - 1), lo, hi);
-        if (first) stage_issue<true>(chunk_addr(pw0, 0), wend, wbuf, S, ninst, sink);
-        else stage_issue<true>(chunk_addr(0, 0), wend, wbuf, S, 0, sink);
-        if (b0 < total) AS.put(lds, p, K, nb, b0, lo, hi);
+                for (int b = b0; b < total; b += 2 * gstep) {
+                    const int b2 = min(b + gstep, total - 1);
+                    typename ActS::Raw r1, r2;
+                    AS.template fetch_lds<XS>(raw, K, nb, b, r1);
+                    AS.template fetch_lds<XS>(raw, K, nb, b2, r2);
+                    AS.template put<XS>(lds, K, nb, b, r1);
+                    AS.template put<XS>(lds, K, nb, b2, r2);
+                }
+            } else if (total > gstep) {
 #pragma unroll 1
-        for (int b = b0 + gstep; b < total; b += gstep) {          // larger column groups: further blocks
-            AS.fetch(p, xrow, nb, b, lo, hi);
-            AS.put(lds, p, K, nb, b, lo, hi);
+                for (int b = b0; b < total; b += gstep) {
+                    typename ActS::Raw r1;
+                    AS.template fetch_lds<XS>(raw, K, nb, b, r1);
+                    AS.template put<XS>(lds, K, nb, b, r1);
+                }
+            } else if (b0 < total) {
+                typename ActS::Raw r1;
+                AS.template fetch_lds<XS>(raw, K, nb, b0, r1);
+                AS.template put<XS>(lds, K, nb, b0, r1);
+            }
+        } else {
+            // the first block of every lane group is loaded ahead of the weight copy
+            typename ActS::Raw r1;
+            AS.template fetch<XS>(p, xrow, nb, min(b0, total - 1), r1);
+            if (first) stage_issue<true>(chunk_addr(pw0, 0), wend, wbuf, S, ninst, sink);
+            else stage_issue<true>(chunk_addr(0, 0), wend, wbuf, S, 0, sink);
+            if (b0 < total) AS.template put<XS>(lds, K, nb, b0, r1);
+#pragma unroll 1
+            for (int b = b0 + gstep; b < total; b += gstep) {      // larger column groups: further blocks
+                AS.template fetch<XS>(p, xrow, nb, b, r1);
+                AS.template put<XS>(lds, K, nb, b, r1);
+            }
         }
+    };
+    switch (p.xsrc) {
+    case DT_F32: quantize(std::integral_constant<int, DT_F32>{}); break;
+    case DT_F16: quantize(std::integral_constant<int, DT_F16>{}); break;
+    case DT_Q8_1: quantize(std::integral_constant<int, DT_Q8_1>{}); break;
+    default: quantize(std::integral_constant<int, DT_BF16>{}); break;
     }
     lds_barrier();                                              // planar activations complete
     ActL A;
@@ -853,34 +1014,12 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
         // routing it through this lambda changes that loop's code, and the
         // short launches it serves start with a cold instruction cache)
         auto finish_pair = [&](bool pvalid, bool v1, int64_t r0, int64_t r1) {
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int c = 0; c < NC; c++) acc[i][c] = seg_sum(acc[i][c], seg);
+            seg_sum(acc, seg);
             if (pvalid && lane_in == seg - 1) {          // seg_sum leaves the total in the segment's last lane
+                int64_t cix[NC];                              // all column / route indices in one LDS round trip
 #pragma unroll
-                for (int c = 0; c < NC; c++) {
-                    if (c >= ncols) break;
-                    if (!MOE) {
-                        const int64_t col = xrow[c];
-                        if (v1) store_out2<YDT>(p.y, col * p.ldy + r0, acc[0][c], acc[1][c], p.y_f16);   // r1 = r0 + 1
-                        else store_out<YDT>(p.y, col * p.ldy + r0, acc[0][c], p.y_f16);
-                    } else {
-                        // weighted: per-route outputs (output dtype), summed per token afterwards
-                        const int64_t r = route_s[c];
-                        if (EPI == EPI_SWIGLU) {
-                            const float h = silu_mul(acc[0][c], acc[1][c]);
-                            if (p.oroute) store_out<YDT>(p.oroute, r * p.Np + r0, h, p.y_f16);
-                            else store_out<YDT>(p.y, r * p.Np + r0, h, p.y_f16);
-                        } else if (p.oroute) {
-                            store_out<YDT>(p.oroute, r * p.Np + r0, acc[0][c], p.y_f16);
-                            if (v1) store_out<YDT>(p.oroute, r * p.Np + r1, acc[1][c], p.y_f16);
-                        } else {
-                            store_out<YDT>(p.y, r * p.Np + r0, acc[0][c], p.y_f16);
-                            if (v1) store_out<YDT>(p.y, r * p.Np + r1, acc[1][c], p.y_f16);
-                        }
-                    }
-                }
+                for (int c = 0; c < NC; c++) cix[c] = MOE ? (int64_t)route_s[c] : xrow[c];
+                store_pair<NC, MOE, EPI, YDT>(p, acc, cix, ncols, v1, r0, r1);
             }
 #pragma unroll
             for (int i = 0; i < 2; i++)
@@ -988,34 +1127,12 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
         // ---- row pair complete: reduce across the segment and store ----
         kc = 0;
         pw += wave_stride;
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int c = 0; c < NC; c++) acc[i][c] = seg_sum(acc[i][c], seg);
+        seg_sum(acc, seg);
         if (pvalid && lane_in == seg - 1) {          // seg_sum leaves the total in the segment's last lane
+            int64_t cix[NC];                              // all column / route indices in one LDS round trip
 #pragma unroll
-            for (int c = 0; c < NC; c++) {
-                if (c >= ncols) break;
-                if (!MOE) {
-                    const int64_t col = xrow[c];
-                    if (v1) store_out2<YDT>(p.y, col * p.ldy + r0, acc[0][c], acc[1][c], p.y_f16);   // r1 = r0 + 1
-                    else store_out<YDT>(p.y, col * p.ldy + r0, acc[0][c], p.y_f16);
-                } else {
-                    // weighted: per-route outputs (output dtype), summed per token afterwards
-                    const int64_t r = route_s[c];
-                    if (EPI == EPI_SWIGLU) {
-                        const float h = silu_mul(acc[0][c], acc[1][c]);
-                        if (p.oroute) store_out<YDT>(p.oroute, r * p.Np + r0, h, p.y_f16);
-                        else store_out<YDT>(p.y, r * p.Np + r0, h, p.y_f16);
-                    } else if (p.oroute) {
-                        store_out<YDT>(p.oroute, r * p.Np + r0, acc[0][c], p.y_f16);
-                        if (v1) store_out<YDT>(p.oroute, r * p.Np + r1, acc[1][c], p.y_f16);
-                    } else {
-                        store_out<YDT>(p.y, r * p.Np + r0, acc[0][c], p.y_f16);
-                        if (v1) store_out<YDT>(p.y, r * p.Np + r1, acc[1][c], p.y_f16);
-                    }
-                }
-            }
+            for (int c = 0; c < NC; c++) cix[c] = MOE ? (int64_t)route_s[c] : xrow[c];
+            store_pair<NC, MOE, EPI, YDT>(p, acc, cix, ncols, v1, r0, r1);
         }
 #pragma unroll
         for (int i = 0; i < 2; i++)
