@@ -385,15 +385,21 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
     const int hdt = xdt == GGQ_BF16 || xdt == GGQ_F16 ? xdt : GGQ_F32;
     void *yk = q8_out && !mmq ? L.hstage : y;               // what the matmul kernel writes
     const int ydt_k = q8_out && !mmq ? hdt : ydt;
-    // unweighted output: the rows of inactive routes are zeros (by the one-workgroup
-    // route build when it runs, else by their own kernel)
-    bool zeroed = false;
-    rc = hip_status(launch_route_build(ids, R, E, J, L.rt, s, weighted ? nullptr : yk, Np, ydt_k, &zeroed),
-                    "mul_mat_id routes");
-    if (rc) return rc;
-    if (!weighted && !zeroed) {
-        rc = hip_status(launch_zero_inactive(ids, R, E, Np, yk, ydt_k, s), "mul_mat_id zero");
+    // One route per MMVQ group: the kernel takes group g as route g straight from
+    // ids, zeroes an inactive route's unweighted row and counts the ids >= E; no
+    // route tables (one launch fewer).  Otherwise the route build groups routes by
+    // expert, and the rows of inactive routes of an unweighted output are zeros (by
+    // the one-workgroup route build when it runs, else by their own kernel).
+    const bool direct = !mmq && J == 1 && R > 0 && Np > 0;
+    if (!direct) {
+        bool zeroed = false;
+        rc = hip_status(launch_route_build(ids, R, E, J, L.rt, s, weighted ? nullptr : yk, Np, ydt_k, &zeroed),
+                        "mul_mat_id routes");
         if (rc) return rc;
+        if (!weighted && !zeroed) {
+            rc = hip_status(launch_zero_inactive(ids, R, E, Np, yk, ydt_k, s), "mul_mat_id zero");
+            if (rc) return rc;
+        }
     }
 
     if (!mmq) {
@@ -422,7 +428,13 @@ int ggq_mul_mat_id(int wt, const void *W, int64_t E, int64_t N, int64_t K, int64
         p.oroute = L.oroute;
         p.groups_expected = std::min<int64_t>(E, R);
         p.w_bytes = (E - 1) * expert_stride + N * rb;
-        rc = hip_status(launch_mmvq(wt, J, true, epi, kernel_dt(ydt_k), p, L.max_tiles, s), "mul_mat_id mmvq");
+        if (direct) {
+            p.ids = ids;
+            p.R = R;
+            p.E = E;
+            p.bad = L.rt.bad;
+        }
+        rc = hip_status(launch_mmvq(wt, J, true, epi, kernel_dt(ydt_k), p, direct ? R : L.max_tiles, s), "mul_mat_id mmvq");
         if (!rc && q8_out)
             rc = hip_status(launch_quantize(L.hstage, hdt, R, Np, Np, static_cast<uint8_t *>(y), nullptr, nullptr, nullptr, false, s),
                             "mul_mat_id q8_1 output");

@@ -110,6 +110,11 @@ struct MmvqParams {
                           // 16-bit type of y), summed per token afterwards
     int y_f16;            // 16-bit output is fp16 (else bf16)
     int64_t groups_expected;   // routed: expected active groups (min(E, routes))
+    // routed, one route per group without route tables: group g is route g (ids[g]
+    // its expert); perm / groups / ngroups unused.  Null otherwise.
+    const int32_t *ids;
+    int64_t R, E;         // direct: routes and experts
+    uint32_t *bad;        // direct: receives the count of ids >= E (group 0 writes it)
     // set by the launcher
     int64_t w_bytes;        // readable weight bytes from W (N*row_bytes, or up to the last expert's last row)
     int64_t act_lds_bytes;  // LDS bytes of the activation region (set by the launcher)

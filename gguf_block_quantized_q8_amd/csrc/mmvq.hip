@@ -864,6 +864,36 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
             xrow[threadIdx.x] = r;
             xoff[threadIdx.x] = (uint32_t)(r * p.x_stride);
         }
+    } else if (p.ids) {
+        // one route per group, no route tables: group grp is route grp.  Group 0
+        // also counts the ids >= E (block-uniform branches throughout)
+        if (grp >= p.R) return;
+        if (grp == 0 && blockIdx.x == 0) {
+            __shared__ uint32_t s_bad;
+            if (threadIdx.x == 0) s_bad = 0;
+            __syncthreads();
+            uint32_t nbad = 0;
+            for (int64_t r = threadIdx.x; r < p.R; r += blockDim.x) nbad += p.ids[r] >= p.E;
+            if (nbad) atomicAdd(&s_bad, nbad);
+            __syncthreads();
+            if (threadIdx.x == 0) *p.bad = s_bad;
+        }
+        const int32_t e = p.ids[grp];
+        if (e < 0 || e >= p.E) {
+            // inactive route: an unweighted output row is zeros (a weighted sum skips it)
+            if (!p.route_w && blockIdx.x == 0)
+                for (int64_t i = threadIdx.x; i < p.Np; i += blockDim.x) store_out<YDT>(p.y, grp * p.Np + i, 0.0f, p.y_f16);
+            return;
+        }
+        W += (int64_t)e * p.expert_stride;
+        ncols = 1;
+        if (threadIdx.x < NC) {
+            const int32_t r = (int32_t)grp;
+            route_s[threadIdx.x] = r;
+            const int64_t xr = p.x_per_route ? r : r / p.top_k;
+            xrow[threadIdx.x] = xr;
+            xoff[threadIdx.x] = (uint32_t)(xr * p.x_stride);
+        }
     } else {
         if (grp >= (int64_t)*p.ngroups) return;                 // block-uniform
         const int4 g = p.groups[grp];

@@ -411,7 +411,7 @@ def test_moe_decode_many_experts_edges(dev, epi):
     """Routed decode with many active experts and long expert matrices, the
     shape where each wave walks several items and keeps two in flight:
     duplicate, inactive and out-of-range ids, plain and SwiGLU outputs."""
-    E, N, K, Tn, top_k = 128, 4096, 512, 16, 8                           # about one route per expert: 2-column groups
+    E, N, K, Tn, top_k = 128, 4096, 512, 16, 8                           # one route per expert on average: one-route groups
     W = inputs.gen_experts(g.Q4_K, E, N, K, 530)
     x = inputs.gen_act(Tn, K, 531, "bf16")
     ids = inputs.rng(532).integers(0, E, (Tn, top_k)).astype(np.int32)
@@ -426,6 +426,48 @@ def test_moe_decode_many_experts_edges(dev, epi):
     assert r <= TOL["f32"]
     assert (host(y)[1, :3] == 0).all() and (host(y)[2, 7] == 0).all()
     assert int(ws[:4].view(torch.int32).item()) == 1
+
+
+@pytest.mark.parametrize("case", ["weighted_bf16", "plain_f32", "swiglu_bf16", "swiglu_q8_1"])
+def test_moe_direct_routes(dev, case):
+    """Routes <= experts: every MMVQ group is one route, taken straight from ids
+    (no route tables).  Duplicate, inactive and out-of-range ids; the out-of-range
+    count at workspace offset 0; zero rows for inactive routes of a plain output;
+    a q8_1 output equal to ggq_quantize_q8_1 of the bf16 output."""
+    E, H, I, Tn, top_k = 64, 512, 256, 6, 8
+    swiglu = case.startswith("swiglu")
+    N, K = (2 * I, H) if swiglu else (H, I)
+    W = inputs.gen_experts(g.Q4_K if swiglu else g.Q6_K, E, N, K, 540)
+    wt = g.Q4_K if swiglu else g.Q6_K
+    x = inputs.gen_act(Tn, K, 541, "bf16" if case != "plain_f32" else "f32")
+    ids, w = inputs.gen_routing(Tn, E, top_k, 542)
+    ids[0, :3] = 7                                                       # one expert, three routes of a token
+    ids[1, 1] = -1
+    ids[4] = -1                                                          # a token with no active route
+    ids[2, 5] = E + 1                                                    # skipped and counted
+    ids[5, 0] = E + 40
+    epi = g.EPI_SWIGLU if swiglu else g.EPI_NONE
+    oepi = oracle.EPI_SWIGLU if swiglu else oracle.EPI_NONE
+    xt, idt = T(x, dev), T(ids, dev)
+    weighted = case == "weighted_bf16"
+    odt = torch.float32 if case == "plain_f32" else torch.bfloat16
+    rw = T(w, dev) if weighted else None
+    y, ws = g.mul_mat_id(T(W, dev), wt, xt, idt, K, route_w=rw, epi=epi, out_dtype=odt, path="mmvq",
+                         return_workspace=True)
+    ref = _moe_ref(wt, W, K, x, ids, top_k, route_w=w if weighted else None, epi=oepi,
+                   route_round="bf16" if weighted else None)
+    r = rel(host(y), ref)
+    log("moe direct routes", case, r)
+    assert r <= TOL["f32" if odt == torch.float32 else "bf16"]
+    assert int(ws[:4].view(torch.int32).item()) == 2
+    if not weighted:
+        yh = host(y)
+        assert (yh[ids < 0] == 0).all() and (yh[ids >= E] == 0).all()
+    if case == "swiglu_q8_1":
+        yq = g.mul_mat_id(T(W, dev), wt, xt, idt, K, epi=epi, out_dtype="q8_1", path="mmvq")
+        Np = N // 2
+        want = g.quantize_q8_1(y.reshape(Tn * top_k, Np)).reshape(yq.shape)
+        assert torch.equal(yq, want)
 
 
 @pytest.mark.parametrize("path", ["mmvq", "mmq"])
