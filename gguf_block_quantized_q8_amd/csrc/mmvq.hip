@@ -823,15 +823,42 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
     uint8_t *raw = lds + p.act_lds_bytes + bstride;
     uint8_t *sink = raw + p.raw_region;
 
-    // ---- early copies (dense, activation rows through LDS): the activation rows, then
-    // the first weight item, go out before any table is built or barrier passed.  A
-    // short launch starts with a cold instruction cache, so every instruction ahead of
-    // these copies delays the first bytes; the activations stay older than the
-    // weights, so waiting for all but the weight instructions still covers them.
-    const bool early = !MOE && p.act_dma;
+    // ---- routed, one route per group, no route tables: group grp is route grp,
+    // ids[grp] its expert.  Group 0 also counts the ids >= E.  (Block-uniform
+    // branches; no copy is in flight yet, so an inactive route can just leave.)
+    int32_t de = 0;
+    if (MOE && p.ids) {
+        if (grp >= p.R) return;
+        if (grp == 0 && blockIdx.x == 0) {
+            __shared__ uint32_t s_bad;
+            if (threadIdx.x == 0) s_bad = 0;
+            __syncthreads();
+            uint32_t nbad = 0;
+            for (int64_t r = threadIdx.x; r < p.R; r += blockDim.x) nbad += p.ids[r] >= p.E;
+            if (nbad) atomicAdd(&s_bad, nbad);
+            __syncthreads();
+            if (threadIdx.x == 0) *p.bad = s_bad;
+        }
+        de = p.ids[grp];
+        if (de < 0 || de >= p.E) {
+            // inactive route: an unweighted output row is zeros (a weighted sum skips it)
+            if (!p.route_w && blockIdx.x == 0)
+                for (int64_t i = threadIdx.x; i < p.Np; i += blockDim.x) store_out<YDT>(p.y, grp * p.Np + i, 0.0f, p.y_f16);
+            return;
+        }
+    }
+
+    // ---- early copies (activation rows through LDS; dense, or routed with one route per
+    // group): the activation rows, then the first weight item, go out before any table
+    // is built or barrier passed.  A short launch starts with a cold instruction cache,
+    // so every instruction ahead of these copies delays the first bytes; the
+    // activations stay older than the weights, so waiting for all but the weight
+    // instructions still covers them.
+    const bool early = p.act_dma && (!MOE || p.ids);
     if (early) {
-        const int64_t c0 = grp * NC;
-        const int nce = (int)min<int64_t>(NC, p.M - c0);
+        // dense: columns grp * NC ..; direct routed: the route's activation row
+        const int64_t c0 = !MOE ? grp * NC : (p.x_per_route ? grp : grp / p.top_k);
+        const int nce = !MOE ? (int)min<int64_t>(NC, p.M - c0) : 1;
         const int nbe = (int)(p.K / QK8_1);
         const uint32_t rowb = p.xsrc == DT_Q8_1 ? nbe * Q8_1_BYTES : (uint32_t)p.K * (p.xsrc == DT_F32 ? 4 : 2);
         const uint32_t ppc = rowb / 16, pieces = nce * ppc;
@@ -847,8 +874,9 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
             llvm_amdgcn_raw_buffer_load_lds(rsrc, (AS3 uint32_t *)(raw + j0 * 16), 16, (int)voff, 0, 0, 0);
         }
         const int64_t pwe = ((int64_t)blockIdx.x * wpb + wave) * spw;
+        const uint8_t *We = p.W + (int64_t)de * p.expert_stride;
         if (pwe < p.npairs)
-            stage_issue_first<EPI>(p.W + (EPI == EPI_SWIGLU ? pwe : 2 * pwe) * p.row_bytes, p.W + p.w_bytes, wbuf,
+            stage_issue_first<EPI>(We + (EPI == EPI_SWIGLU ? pwe : 2 * pwe) * p.row_bytes, p.W + p.w_bytes, wbuf,
                                    ninst, lane, (uint32_t)cps, p.cps_magic, (uint32_t)spw, (uint32_t)p.row_bytes,
                                    (uint32_t)(p.Np * p.row_bytes));
     }
@@ -865,27 +893,7 @@ __global__ __launch_bounds__(64 * MaxWaves<NC>::value) void mmvq_kernel(const Mm
             xoff[threadIdx.x] = (uint32_t)(r * p.x_stride);
         }
     } else if (p.ids) {
-        // one route per group, no route tables: group grp is route grp.  Group 0
-        // also counts the ids >= E (block-uniform branches throughout)
-        if (grp >= p.R) return;
-        if (grp == 0 && blockIdx.x == 0) {
-            __shared__ uint32_t s_bad;
-            if (threadIdx.x == 0) s_bad = 0;
-            __syncthreads();
-            uint32_t nbad = 0;
-            for (int64_t r = threadIdx.x; r < p.R; r += blockDim.x) nbad += p.ids[r] >= p.E;
-            if (nbad) atomicAdd(&s_bad, nbad);
-            __syncthreads();
-            if (threadIdx.x == 0) *p.bad = s_bad;
-        }
-        const int32_t e = p.ids[grp];
-        if (e < 0 || e >= p.E) {
-            // inactive route: an unweighted output row is zeros (a weighted sum skips it)
-            if (!p.route_w && blockIdx.x == 0)
-                for (int64_t i = threadIdx.x; i < p.Np; i += blockDim.x) store_out<YDT>(p.y, grp * p.Np + i, 0.0f, p.y_f16);
-            return;
-        }
-        W += (int64_t)e * p.expert_stride;
+        W += (int64_t)de * p.expert_stride;                     // the route checked above
         ncols = 1;
         if (threadIdx.x < NC) {
             const int32_t r = (int32_t)grp;
