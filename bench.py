@@ -385,7 +385,7 @@ def bench_crossover(ctx, Ms=(1, 8, 64, 512, 8192)):
 def bench_thresholds(ctx):
     """Call times that set the dispatch rules, caches evicted before every launch
     (decode-sized calls read their weights from HBM in a real model):
-    dense Q4_K 4096x4096 at M = 1..16 on both paths; the MoE projections of
+    dense Q4_K 4096x4096 at M = 1..16, 24 .. 192 on both paths; the MoE projections of
     E=256 top-8 H=2048 I=512 at T = 8..1024 on both paths; the routes per MMVQ-id
     group (1, 2, 4, 8) at T = 16..128 for uniform and skewed routing; and
     MMQ-id at T = 8192 for both routings."""
@@ -393,7 +393,7 @@ def bench_thresholds(ctx):
     out = []
     N, K, wt = 4096, 4096, g.Q4_K
     W = torch.from_numpy(inputs.gen_weights(wt, N, K, 201)).to(dev)
-    for M in range(1, 17):
+    for M in list(range(1, 17)) + [24, 32, 48, 64, 96, 128, 192]:
         x = bf16(inputs.gen_act(M, K, 202, "bf16"), dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         row = {"workload": "thresholds_dense_q4_K_4096x4096", "M": M}

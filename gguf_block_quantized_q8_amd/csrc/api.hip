@@ -80,8 +80,10 @@ Planar carve_planar(Carve &c, int64_t rows, int64_t K) {
     return p;
 }
 
-// Dense dispatch: MMVQ for up to 8 activation rows, MMQ above (when it has a kernel for the type and K).
-constexpr int64_t MMVQ_MAX_ROWS = 8;
+// Dense dispatch: MMVQ for up to 16 activation rows, MMQ above (when it has a kernel for the type and K).
+// Measured on Q4_K 4096 x 4096 (caches evicted) and 8192 x 2048: MMVQ is ahead through
+// M = 16 (two 8-column groups), MMQ from M = 24.
+constexpr int64_t MMVQ_MAX_ROWS = 16;
 // Routed dispatch: MMVQ-id while the routes per expert stay at or below this mean,
 // MMQ-id above.  Measured on the E=256 top-8 H=2048 I=512 projections (caches
 // evicted): gate_up crosses over between 256 and 384 tokens (8 and 12 routes per
