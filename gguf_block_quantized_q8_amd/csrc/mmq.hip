@@ -54,15 +54,19 @@ template <int T> constexpr bool kMin = T == T_Q4_K || T == T_Q5_K;     // d * sc
 // pieces copied to cover it from the 16-byte boundary at or below its start
 // (Q6_K super-blocks start at any even phase; the others at phase 0 when K %
 // 256 == 0).
+// PP: the row pitch of the LDS copy in pieces, P or more: 16 rows at a pitch of 4 PP
+// dwords fall in 16 distinct LDS banks when 4 PP mod 64 is 4 times an odd number
+// (Q6_K's 14 pieces give 56 dwords, 8 distinct banks and two-way conflicts in the
+// decode's reads; 15 give 60: conflicts 35 % -> 15 % of LDS-active cycles).
 template <int T> struct SbGeo;
-template <> struct SbGeo<T_Q4_K> { static constexpr int B = 144, P = 9; };
-template <> struct SbGeo<T_Q5_K> { static constexpr int B = 176, P = 11; };
-template <> struct SbGeo<T_Q6_K> { static constexpr int B = 210, P = 14; };
-template <> struct SbGeo<T_Q8_0> { static constexpr int B = 272, P = 17; };   // 8 blocks of 34
-template <> struct SbGeo<T_Q4_0> { static constexpr int B = 144, P = 9; };    // 8 blocks of 18
+template <> struct SbGeo<T_Q4_K> { static constexpr int B = 144, P = 9, PP = 9; };
+template <> struct SbGeo<T_Q5_K> { static constexpr int B = 176, P = 11, PP = 11; };
+template <> struct SbGeo<T_Q6_K> { static constexpr int B = 210, P = 14, PP = 15; };
+template <> struct SbGeo<T_Q8_0> { static constexpr int B = 272, P = 17, PP = 17; };   // 8 blocks of 34
+template <> struct SbGeo<T_Q4_0> { static constexpr int B = 144, P = 9, PP = 9; };     // 8 blocks of 18
 
 // LDS-DMA instructions per wave for a super-block of its 16 rows.
-template <int T> constexpr int NIRAW = (16 * SbGeo<T>::P + 63) / 64;
+template <int T> constexpr int NIRAW = (16 * SbGeo<T>::PP + 63) / 64;
 
 // Dynamic LDS layout (bytes).  Fragment-ordered buffers hold 1 KB per MFMA
 // operand fragment: lane l's 16 bytes at 16 * l (row or column l & 31, K
@@ -71,8 +75,8 @@ template <int T> struct Lds {
     static constexpr int NA = T == T_Q6_K ? 2 : 1;                 // weight operand parts
     static constexpr int ACT = 0;                                  // [3][8 col groups][2 halves][1 KB]
     static constexpr int DEC = ACT + 3 * 16 * 1024;                // [2][NA][4 row groups][2 halves][1 KB]
-    static constexpr int RAWSLOT = NT * SbGeo<T>::P * 16;
-    static constexpr int RAW = DEC + 2 * NA * 8 * 1024;            // [2][NT rows][P pieces][16]
+    static constexpr int RAWSLOT = NT * SbGeo<T>::PP * 16;
+    static constexpr int RAW = DEC + 2 * NA * 8 * 1024;            // [2][NT rows][PP pieces][16]
     static constexpr int D8 = RAW + 2 * RAWSLOT;                   // float [2 sb][8 blocks][MT]
     static constexpr int BMIN = D8 + 2 * 8 * MT * 4;               // [8][2][1 KB] bf16 min operand (min types)
     static constexpr int AMIN = BMIN + (kMin<T> ? 16 * 1024 : 0);  // [4][2][1 KB]
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
     // activations); the first stage of a super-block also issues that super-block's min
     // operand and the next one's raw bytes and d8.  Wait counts are immediates. ----
     const uint32_t my_woff = woff[drow];
-    const lds_u8 *my_raw = lds + L::RAW + (16 * wave + (lane & 15)) * G::P * 16;
+    const lds_u8 *my_raw = lds + L::RAW + (16 * wave + (lane & 15)) * G::PP * 16;
 
     auto issue_act = [&](int s, int slot) {
 #pragma unroll
@@ -488,15 +492,15 @@ __global__ __launch_bounds__(NTHR, 1) void mmq_kernel(const MmqParams p) {
                                             (int)(aoff[f] + (uint32_t)s * ASTEP), 0, 0, 0);
         }
     };
-    // raw super-block sb of this wave's 16 rows, instruction i: pieces P = 64 i + lane
-    // (row P / G::P, piece P % G::P); lanes past the wave's pieces copy nothing (an
-    // exec-masked lane writes no LDS: the rest of that kilobyte belongs to the next
-    // wave's rows); lane 0 is always active
+    // raw super-block sb of this wave's 16 rows, instruction i: slots P = 64 i + lane
+    // (row P / G::PP, piece P % G::PP); lanes past the wave's pieces, and the pitch's
+    // spare pieces, copy nothing (an exec-masked lane writes no LDS: the rest of that
+    // kilobyte belongs to the next wave's rows); lane 0 is always active
     auto issue_raw = [&](int sb, int i) {
-        lds_u8 *slot = lds + L::RAW + (sb & 1) * L::RAWSLOT + 16 * wave * G::P * 16;
+        lds_u8 *slot = lds + L::RAW + (sb & 1) * L::RAWSLOT + 16 * wave * G::PP * 16;
         const int P_ = 64 * i + lane;
-        const int rl = P_ / G::P, q = P_ - rl * G::P;
-        if (P_ < 16 * G::P) {
+        const int rl = P_ / G::PP, q = P_ - rl * G::PP;
+        if (P_ < 16 * G::PP && q < G::P) {
             const uint32_t start = woff[16 * wave + rl] + (uint32_t)sb * G::B;
             const uint32_t off = (start & ~15u) + 16u * (uint32_t)q;
             llvm_amdgcn_raw_buffer_load_lds(raw_rsrc, (lds_u32 *)(slot + 1024 * i), 16, (int)off, 0, 0, 0);
