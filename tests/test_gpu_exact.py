@@ -167,9 +167,10 @@ def _dense(dev, wt, N, K, M, path, seed, ydt="f32", xdt="f32", rows=None, smax=6
 # ------------------------------------------------------------------ MMVQ
 
 @pytest.mark.parametrize("wt", TYPES)
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 13, 16])
 def test_exact_mmvq(dev, wt, M):
-    """Every column-group width (1, 2, 4, 8 and ragged groups), ragged row count."""
+    """Every column-group width (1, 2, 4, 8 and ragged groups), ragged row count;
+    13 and 16 rows: two column groups, as AUTO runs them up to 16 rows."""
     K = 512 if wt in (g.Q8_0, g.Q4_0, g.Q6_K) else 1024
     _dense(dev, wt, 301, K, M, "mmvq", 1100 + 10 * wt + M)
 
