@@ -309,7 +309,7 @@ def bench_get_rows(ctx, wt, rows, K, n, seed_w, seed_ids, ydt, steps, warmup):
     step_bytes = n * (g.row_bytes(wt, K) + 4 + K * (4 if ydt == torch.float32 else 2))
     return {"value": step_bytes * steps / dt / 1e9, "unit": "GB/s", "ms_per_step": dt / steps * 1e3,
             "step_bytes": step_bytes, **spread(per),
-            "roofline": roofline_bytes(step_bytes, gpu / steps, f"dequant_kernel<{TNAME[wt]}> (get_rows)")}
+            "roofline": roofline_bytes(step_bytes, gpu / steps, f"dequant_rows_kernel<{TNAME[wt]}> (get_rows)")}
 
 
 # ------------------------------------------------------------------ dense prefill (MMQ)

@@ -54,8 +54,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 // fp32 -> IEEE binary16 bits, round to nearest even (v_cvt_f16_f32 in the
 // default rounding mode, subnormal halves kept); past the largest finite half
-// the result is inf.
+// the result is inf.  f is a final fp32 value: the empty asm keeps the
+// compiler from folding the product that made it into a mixed fma that rounds
+// once, straight to fp16.
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    __asm__("" : "+v"(f));
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 // 16-bit elements: fp16 when h, else bf16.

@@ -198,12 +198,151 @@ __global__ __launch_bounds__(256) void q8_1_to_planar_kernel(const uint8_t *__re
 }
 
 // ---------------------------------------------------------------------------
-// Dequantize: one thread per 16 consecutive weights of an output row.
+// Dequantize: 16 consecutive weights of an output row at a time.
 //   Q8_0: d*q; Q4_0: d*(nib-8); Q4_K / Q5_K: (d*sc)*q - dmin*m; Q6_K: (d*sc)*(q-32).
 // Every product is exact in fp32; the subtraction of the min rounds once.
 // Output row r (of n) holds table row ids[r] (r itself without ids); a row id
 // outside [0, rows) gives a row of zeros.  y rows are ldy elements apart.
 // ---------------------------------------------------------------------------
+
+#define AS3 __attribute__((address_space(3)))
+typedef const uint8_t AS3 *lds_bp;
+extern "C" __device__ v4i llvm_amdgcn_raw_buffer_load_v4i32(v4i rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+
+// Bytes of one block, from global memory or from a row staged in LDS.  Block
+// sizes and field offsets are even, so every 16-bit field and 16-byte run
+// starts 2-byte aligned in both.
+struct GlobalBytes {
+    const uint8_t *p;
+    __device__ uint32_t u8(int o) const { return p[o]; }
+    __device__ uint32_t u16(int o) const { return ld_u16(p + o); }
+    template <int N> __device__ v4i v(int o) const {
+        static_assert(N == 16, "global reads take 16-byte runs");
+        return ld16_a2(p + o);
+    }
+};
+struct LdsBytes {
+    lds_bp p;
+    __device__ uint32_t u8(int o) const { return p[o]; }
+    __device__ uint32_t u16(int o) const { return *(const uint16_t AS3 *)(p + o); }   // 2-byte aligned
+    // N bytes (4, 8 or 16) at a 2-byte aligned offset: N/4 + 1 aligned dwords
+    // shifted into place; words past N/4 are zero.
+    template <int N> __device__ v4i v(int o) const {
+        const lds_bp q = p + o;
+        const uint32_t sh = (uint32_t)(uintptr_t)q & 3u;
+        const uint32_t AS3 *w = (const uint32_t AS3 *)(q - sh);
+        uint32_t x[N / 4 + 1];
+#pragma unroll
+        for (int i = 0; i <= N / 4; i++) x[i] = w[i];
+        v4i r = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < N / 4; i++) r[i] = (int)__builtin_amdgcn_alignbyte(x[i + 1], x[i], sh);
+        return r;
+    }
+};
+
+// Weights ib .. ib + N - 1 of the block at B (N = 4, 8 or 16; ib a multiple of
+// N below the block length): byte i of a run read at offset o is field byte
+// o + i.  Each group of four codes is gathered into the four bytes of a dword,
+// then turned into floats byte by byte: Q4_K / Q5_K codes as unsigned values u
+// with w = fma(d*sc, u, -dmin*m) (the product is exact, the one rounding is
+// that of the min subtraction, as in the block formula); Q4_0 / Q6_K codes
+// with their offset (8, 32) taken off in two's complement (flipping the top
+// bit of the field) and Q8_0's int8 as they are, sign-extended, then
+// w = scale * code, the block formula itself (signed zeros included).
+template <int T, int N, class Bytes>
+__device__ __forceinline__ void decode(const Bytes &B, int ib, float (&w)[N]) {
+    uint32_t x[N / 4];
+    float a, b = 0.0f;
+    if (T == T_Q4_0) {
+        // weights 0..15: low nibbles of the 16 quant bytes, 16..31: high nibbles
+        const v4i q = B.template v<N>(2 + ib % 16);
+#pragma unroll
+        for (int k = 0; k < N / 4; k++)
+            x[k] = ((ib >= 16 ? (uint32_t)q[k] >> 4 : (uint32_t)q[k]) & 0x0f0f0f0fu) ^ 0x08080808u;
+        a = fp16_bits_to_f32(B.u16(0));
+    } else if (T == T_Q4_K || T == T_Q5_K) {
+        // Q5_K: the nibble | bit j of the fifth-bit byte << 4
+        const float d = fp16_bits_to_f32(B.u16(0)), dmin = fp16_bits_to_f32(B.u16(2));
+        const int j = ib / 32;
+        int sc, mn;
+        if (j < 4) { sc = B.u8(4 + j) & 63; mn = B.u8(8 + j) & 63; }
+        else {
+            sc = (B.u8(8 + j) & 0x0f) | ((B.u8(j) >> 6) << 4);
+            mn = (B.u8(8 + j) >> 4) | ((B.u8(4 + j) >> 6) << 4);
+        }
+        const int c = ib / 64, l0 = ib % 32;
+        const bool hi = (ib % 64) >= 32;
+        const v4i q = B.template v<N>((T == T_Q4_K ? 16 : 48) + 32 * c + l0);
+        v4i h = v4i{0, 0, 0, 0};
+        if (T == T_Q5_K) h = B.template v<N>(16 + l0);
+#pragma unroll
+        for (int k = 0; k < N / 4; k++) {
+            x[k] = (hi ? (uint32_t)q[k] >> 4 : (uint32_t)q[k]) & 0x0f0f0f0fu;
+            if (T == T_Q5_K) x[k] |= (((uint32_t)h[k] >> j) & 0x01010101u) << 4;
+        }
+        a = d * (float)sc; b = -(dmin * (float)mn);
+    } else if (T == T_Q8_0) {
+        const v4i q = B.template v<N>(2 + ib);
+#pragma unroll
+        for (int k = 0; k < N / 4; k++) x[k] = (uint32_t)q[k];
+        a = fp16_bits_to_f32(B.u16(0));
+    } else {
+        // 6-bit code = 4 bits of ql | 2 bits of qh << 4, scale d * sc
+        const int h = ib / 128, rr = ib % 128, g = rr / 32, l = rr % 32;
+        const v4i ql = B.template v<N>(64 * h + 32 * (g & 1) + l);
+        const v4i qh = B.template v<N>(128 + 32 * h + l);
+#pragma unroll
+        for (int k = 0; k < N / 4; k++)
+            x[k] = (((g < 2 ? (uint32_t)ql[k] : (uint32_t)ql[k] >> 4) & 0x0f0f0f0fu) |
+                    ((((uint32_t)qh[k] >> (2 * g)) & 0x03030303u) << 4)) ^ 0x20202020u;
+        a = fp16_bits_to_f32(B.u16(208)) * (float)(int8_t)B.u8(192 + ib / 16);
+    }
+    constexpr int BITS = T == T_Q8_0 ? 8 : T == T_Q4_0 ? 4 : 6;   // signed field width
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        if (T == T_Q4_K || T == T_Q5_K)
+            w[i] = fmaf(a, (float)((x[i / 4] >> (8 * (i % 4))) & 0xffu), b);
+        else
+            w[i] = a * (float)((int32_t)(x[i / 4] << (32 - BITS - 8 * (i % 4))) >> (32 - BITS));
+    }
+}
+
+// Two values as bf16 (v_cvt_pk_bf16_f32, round to nearest even) or fp16 bits.
+template <int YDT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    if (YDT == DT_BF16) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+    }
+    return f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+}
+
+// N converted values (N * size = 16 bytes) as one 16-byte store.
+template <int YDT, int N>
+__device__ __forceinline__ void store_run(void *y, int64_t o, const float *w) {
+    static_assert(N * (YDT == DT_F32 ? 4 : 2) == 16, "one 16-byte store");
+    if (YDT == DT_F32) {
+        *reinterpret_cast<v4f *>(static_cast<float *>(y) + o) = v4f{w[0], w[1], w[2], w[3]};
+    } else {
+        v4i t;
+#pragma unroll
+        for (int k = 0; k < 4; k++) t[k] = (int)pack2<YDT>(w[2 * k], w[2 * k + 1]);
+        *reinterpret_cast<v4i *>(static_cast<uint16_t *>(y) + o) = t;
+    }
+}
+
+template <int YDT>
+__device__ __forceinline__ void store16(void *y, int64_t o, const float (&w)[16]) {
+    constexpr int S = YDT == DT_F32 ? 4 : 8;
+#pragma unroll
+    for (int i = 0; i < 16; i += S) store_run<YDT, S>(y, o + i, w + i);
+}
+
+// One thread per 16 weights, read from global memory: rows longer than the
+// staged kernel's limit.
 template <int T, int YDT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ W, int64_t rows, int64_t K,
                                                       const int32_t *__restrict__ ids, int64_t n,
@@ -215,82 +354,112 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     const int64_t i0 = (gid - r * per_row) * 16;         // first weight index in the row
     const int64_t src = ids ? (int64_t)ids[r] : r;
     constexpr int QK = Geom<T>::QK, BB = Geom<T>::BYTES;
-    const uint8_t *blk = W + (src >= 0 && src < rows ? src : 0) * (K / QK) * BB + (i0 / QK) * BB;
-    const int ib = (int)(i0 % QK);                       // index inside the block
     float w[16];
     if (src < 0 || src >= rows) {
         for (int i = 0; i < 16; i++) w[i] = 0.0f;
-    } else if (T == T_Q4_0) {
-        // weights 0..15: low nibbles of the 16 quant bytes, 16..31: high nibbles
-        const float d = fp16_bits_to_f32(ld_u16(blk));
-        const v4i q = ld16_a2(blk + 2);
-        for (int i = 0; i < 16; i++) {
-            const int byte = (q[i / 4] >> (8 * (i % 4))) & 0xff;
-            w[i] = d * (float)((ib ? byte >> 4 : byte & 15) - 8);
-        }
-    } else if (T == T_Q5_K) {
-        // the Q4_K fields (nibbles at byte 48) plus bit j of byte l of the 32 fifth-bit bytes
-        const uint8_t *s = blk + 4;
-        const float d = fp16_bits_to_f32(ld_u16(blk)), dmin = fp16_bits_to_f32(ld_u16(blk + 2));
-        const int j = ib / 32;
-        int sc, mn;
-        if (j < 4) { sc = s[j] & 63; mn = s[j + 4] & 63; }
-        else { sc = (s[j + 4] & 0x0f) | ((s[j - 4] >> 6) << 4); mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4); }
-        const int c = ib / 64, l0 = ib % 32;
-        const bool hi = (ib % 64) >= 32;
-        const v4i q = *reinterpret_cast<const v4i *>(blk + 48 + 32 * c + l0);
-        const v4i h = *reinterpret_cast<const v4i *>(blk + 16 + l0);
-        const float a = d * (float)sc, m = dmin * (float)mn;
-        for (int i = 0; i < 16; i++) {
-            const int byte = (q[i / 4] >> (8 * (i % 4))) & 0xff;
-            const int bit = (h[i / 4] >> (8 * (i % 4) + j)) & 1;
-            w[i] = a * (float)((hi ? (byte >> 4) : (byte & 15)) | (bit << 4)) - m;
-        }
-    } else if (T == T_Q8_0) {
-        const float d = fp16_bits_to_f32(ld_u16(blk));
-        v4i q = ld16_a2(blk + 2 + ib);
-        for (int i = 0; i < 16; i++) w[i] = d * (float)(int8_t)((q[i / 4] >> (8 * (i % 4))) & 0xff);
-    } else if (T == T_Q4_K) {
-        const uint8_t *s = blk + 4;
-        const float d = fp16_bits_to_f32(ld_u16(blk)), dmin = fp16_bits_to_f32(ld_u16(blk + 2));
-        const int j = ib / 32;
-        int sc, mn;
-        if (j < 4) { sc = s[j] & 63; mn = s[j + 4] & 63; }
-        else { sc = (s[j + 4] & 0x0f) | ((s[j - 4] >> 6) << 4); mn = (s[j + 4] >> 4) | ((s[j] >> 6) << 4); }
-        const int c = ib / 64, r64 = ib % 64;
-        const bool hi = r64 >= 32;
-        v4i q = *reinterpret_cast<const v4i *>(blk + 16 + 32 * c + (r64 & 31));
-        const float a = d * (float)sc, m = dmin * (float)mn;
-        for (int i = 0; i < 16; i++) {
-            int byte = (q[i / 4] >> (8 * (i % 4))) & 0xff;
-            int nib = hi ? (byte >> 4) : (byte & 15);
-            w[i] = a * (float)nib - m;
-        }
     } else {
-        const float d = fp16_bits_to_f32(ld_u16(blk + 208));
-        const int h = ib / 128, rr = ib % 128, g = rr / 32, l = rr % 32;
-        v4i ql = ld16_a2(blk + 64 * h + 32 * (g & 1) + l);
-        v4i qh = ld16_a2(blk + 128 + 32 * h + l);
-        const int sc = (int8_t)blk[192 + ib / 16];
-        const float a = d * (float)sc;
-        for (int i = 0; i < 16; i++) {
-            int lo = (ql[i / 4] >> (8 * (i % 4))) & 0xff;
-            lo = g < 2 ? (lo & 15) : (lo >> 4);
-            int hb = ((qh[i / 4] >> (8 * (i % 4))) >> (2 * g)) & 3;
-            w[i] = a * (float)((lo | (hb << 4)) - 32);
+        decode<T, 16>(GlobalBytes{W + src * (K / QK) * BB + (i0 / QK) * BB}, (int)(i0 % QK), w);
+    }
+    store16<YDT>(y, r * ldy + i0, w);
+}
+
+// Rows of up to DQ_ROW_MAX bytes: each wave walks output rows r, r + waves, ...
+// A row's bytes go to LDS by 16-byte loads from the 16-byte boundary at or
+// below its start, NL a lane (a buffer resource over the matrix, so nothing
+// past its end is read); the next row's loads are issued before the current
+// row is decoded, so they land while the wave decodes and stores.  Each lane
+// then decodes 8 bf16 / fp16 or 4 fp32 outputs (16 bytes) a step from LDS:
+// every store instruction writes 1 KB of the row.  A wave's LDS slot is `slot`
+// bytes (the row rounded up to 16, plus 32 for the phase and the last dword
+// read).
+constexpr int DQ_ROW_MAX = 8192;
+constexpr int DQ_MAX_WG = 2048;          // workgroups (4 waves each) at most
+
+template <int NL> struct RowFetch {
+    v4i v[NL];
+    int ph;
+    bool valid;
+};
+
+// Table row src (wave-uniform) into f.
+template <int T, int NL>
+__device__ __forceinline__ void row_fetch(RowFetch<NL> &f, const uint8_t *W, int64_t wbytes, int64_t rows,
+                                          int64_t rb, int64_t src, int lane) {
+    f.valid = src >= 0 && src < rows;
+    f.ph = 0;
+    if (!f.valid) return;
+    const int64_t start = src * rb, a0 = start & ~(int64_t)15;
+    f.ph = (int)(start - a0);
+    const int npc = (int)((f.ph + rb + 15) / 16);
+    struct { const void *q; uint32_t range; uint32_t cfg; } rd = {W + a0, (uint32_t)(wbytes - a0), 0x00020000u};
+    v4i rsrc = __builtin_bit_cast(v4i, rd);
+#pragma unroll
+    for (int i = 0; i < 4; i++) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc[i]);
+    const int64_t lim = wbytes - a0;                      // readable bytes from W + a0 (even)
+#pragma unroll
+    for (int i = 0; i < NL; i++) {
+        const int pc = lane + 64 * i;
+        if (pc < npc) {                                   // (words past npc are never stored to LDS)
+            f.v[i] = llvm_amdgcn_raw_buffer_load_v4i32(rsrc, 16 * pc, 0, 0);
+            // The range check zeroes each dword not wholly inside the range: a
+            // table whose end is 2 bytes into a dword gets those 2 bytes here.
+            const int64_t rem = lim - 16 * pc;
+            if (rem < 16 && (rem & 2)) f.v[i][rem >> 2] = (int)ld_u16(W + a0 + 16 * pc + (rem & ~3));
         }
     }
-    const int64_t o = r * ldy + i0;
-    if (YDT == DT_F32) {
-        v4f *yo = reinterpret_cast<v4f *>(static_cast<float *>(y) + o);
-        for (int i = 0; i < 4; i++) yo[i] = v4f{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
-    } else {
-        v4i *yo = reinterpret_cast<v4i *>(static_cast<uint16_t *>(y) + o);
-        for (int i = 0; i < 2; i++) {
-            v4i t;
-            for (int k = 0; k < 4; k++)
-                t[k] = (int)(f32_to_16(w[8 * i + 2 * k], YDT == DT_F16) | (f32_to_16(w[8 * i + 2 * k + 1], YDT == DT_F16) << 16));
-            yo[i] = t;
+}
+
+template <int T, int YDT, int NL>
+__global__ __launch_bounds__(256) void dequant_rows_kernel(const uint8_t *__restrict__ W, int64_t wbytes,
+                                                           int64_t rows, int64_t K, const int32_t *__restrict__ ids,
+                                                           int64_t n, void *__restrict__ y, int64_t ldy, int slot) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dq_stage[];
+    // wave index made uniform so row ids come in by scalar loads
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = (int)(threadIdx.x & 63);
+    const int64_t waves = (int64_t)gridDim.x * 4;
+    int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    if (r >= n) return;                                   // wave-uniform; no workgroup barrier below
+    constexpr int QK = Geom<T>::QK, BB = Geom<T>::BYTES;
+    constexpr int N = YDT == DT_F32 ? 4 : 8;
+    const int64_t rb = K / QK * BB;
+    uint8_t AS3 *const srow = (uint8_t AS3 *)&dq_stage[wave * slot];
+    auto src_of = [&](int64_t rr) -> int64_t { return rr < n ? (ids ? (int64_t)ids[rr] : rr) : -1; };
+    RowFetch<NL> f;
+    row_fetch<T>(f, W, wbytes, rows, rb, src_of(r), lane);
+    int64_t src_next = src_of(r + waves);                 // one row ahead of the fetch
+    for (; r < n; r += waves) {
+        // Lanes read bytes other lanes wrote and the slot is reused row after
+        // row: keep the compiler from moving LDS accesses across these points
+        // (a wave's LDS operations complete in order).
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const bool valid = f.valid;
+        const lds_bp row = srow + f.ph;
+        if (valid) {
+#pragma unroll
+            for (int i = 0; i < NL; i++)
+                if (lane + 64 * i < (f.ph + rb + 15) / 16) *(v4i AS3 *)(srow + 16 * (lane + 64 * i)) = f.v[i];
+        }
+        if (r + waves < n) {
+            row_fetch<T>(f, W, wbytes, rows, rb, src_next, lane);
+            src_next = src_of(r + 2 * waves);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // a step covers N * 64 weights, whole blocks: the lane's place in its
+        // block is the same every step
+        if (valid) {
+            int bo = (N * lane) / QK * BB;
+            for (int64_t i0 = N * (int64_t)lane; i0 < K; i0 += N * 64, bo += N * 64 / QK * BB) {
+                float w[N];
+                decode<T, N>(LdsBytes{row + bo}, (N * lane) % QK, w);
+                store_run<YDT, N>(y, r * ldy + i0, w);
+            }
+        } else {
+            const float w[N] = {};
+            for (int64_t i0 = N * (int64_t)lane; i0 < K; i0 += N * 64) store_run<YDT, N>(y, r * ldy + i0, w);
         }
     }
 }
@@ -468,15 +637,32 @@ hipError_t launch_dequant(int t, const uint8_t *W, int64_t rows, int64_t K, cons
                           int ydt, int64_t ldy, hipStream_t s) {
     const int64_t threads = n * (K / 16);
     if (threads == 0) return hipSuccess;
-    dim3 g(grid_for(threads)), b(256);
+    const int64_t rb = K / (t == T_Q4_0 || t == T_Q8_0 ? 32 : 256) *
+                       (t == T_Q4_0 ? 18 : t == T_Q8_0 ? 34 : t == T_Q4_K ? 144 : t == T_Q5_K ? 176 : 210);
+    const int64_t wbytes = rows * rb;
+    // staged rows: up to DQ_ROW_MAX bytes, buffer offsets within 32 bits
+    const bool staged = rb <= DQ_ROW_MAX && wbytes < (int64_t(1) << 31);
+    const int slot = (int)((rb + 15) / 16 * 16 + 32);
+    const int64_t chunks = (rb + 30) / 16;                // 16-byte loads a row needs at most
+    const int nl = chunks <= 128 ? 2 : chunks <= 256 ? 4 : 9;
+    dim3 g(grid_for(threads)), b(256), gr((unsigned)std::min<int64_t>((n + 3) / 4, DQ_MAX_WG));
+#define GGQ_DQ2(TT, D, NLV)                                                                                            \
+    hipLaunchKernelGGL((dequant_rows_kernel<TT, D, NLV>), gr, b, 4 * slot, s, W, wbytes, rows, K, ids, n, y, ldy, slot);
+#define GGQ_DQ1(TT, D)                                                                                                 \
+    if (!staged) hipLaunchKernelGGL((dequant_kernel<TT, D>), g, b, 0, s, W, rows, K, ids, n, y, ldy);                 \
+    else if (nl == 2) { GGQ_DQ2(TT, D, 2) }                                                                           \
+    else if (nl == 4) { GGQ_DQ2(TT, D, 4) }                                                                           \
+    else { GGQ_DQ2(TT, D, 9) }
 #define GGQ_DQ(TT)                                                                                                    \
     if (t == TT) {                                                                                                    \
-        if (ydt == DT_F32) hipLaunchKernelGGL((dequant_kernel<TT, DT_F32>), g, b, 0, s, W, rows, K, ids, n, y, ldy);   \
-        else if (ydt == DT_F16) hipLaunchKernelGGL((dequant_kernel<TT, DT_F16>), g, b, 0, s, W, rows, K, ids, n, y, ldy); \
-        else hipLaunchKernelGGL((dequant_kernel<TT, DT_BF16>), g, b, 0, s, W, rows, K, ids, n, y, ldy);               \
+        if (ydt == DT_F32) { GGQ_DQ1(TT, DT_F32) }                                                                    \
+        else if (ydt == DT_F16) { GGQ_DQ1(TT, DT_F16) }                                                               \
+        else { GGQ_DQ1(TT, DT_BF16) }                                                                                 \
     }
     GGQ_DQ(T_Q4_0) GGQ_DQ(T_Q8_0) GGQ_DQ(T_Q4_K) GGQ_DQ(T_Q5_K) GGQ_DQ(T_Q6_K)
 #undef GGQ_DQ
+#undef GGQ_DQ1
+#undef GGQ_DQ2
     return hipGetLastError();
 }
 

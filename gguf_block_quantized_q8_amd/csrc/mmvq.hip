@@ -416,12 +416,6 @@ __device__ __forceinline__ void store_pair(const MmvqParams &p, const float (&ac
     else store_cols<NC, MOE, EPI, YDT, false>(p, acc, cix, ncols, v1, r0, r1);
 }
 
-// Sum over aligned quads of lanes, result in every lane of the quad.
-__device__ __forceinline__ int sum4(int v) {
-    v += dpp_i<DPP_XOR1>(v);
-    return v + dpp_i<DPP_XOR2>(v);
-}
-
 // q = round-half-away(x / d) in fp32 with d = amax / 127 and the IEEE
 // quotient, as the quantizer defines it, by the compiler's division: the
 // fallback of put() for blocks outside the range quant_div() covers, and for

@@ -129,6 +129,35 @@ def test_get_rows_bit_exact(dev, wt, ydt):
                           ref.view(np.uint32) if ydt == torch.float32 else ref)
 
 
+# Row lengths around the staged kernel's 8192-byte limit, and short rows whose
+# start phase within a 16-byte line takes every even value (18- and 34-byte
+# blocks, an odd number of them): K -> bytes per row for each type.
+RAGGED_K = {g.Q4_0: [96, 14560, 14592], g.Q8_0: [96, 7680, 7744], g.Q4_K: [256, 14336, 14592],
+            g.Q5_K: [768, 11776, 12032], g.Q6_K: [768, 9984, 10240]}
+
+
+@pytest.mark.parametrize("wt", TYPES)
+@pytest.mark.parametrize("ki", [0, 1, 2])
+def test_dequant_row_lengths(dev, wt, ki):
+    """dequantize and get_rows bit-exact for row lengths at and past the LDS
+    staging limit (8064..8400 bytes) and for short rows at every 16-byte phase,
+    including the last row of a table whose end is not 16-byte aligned."""
+    K = RAGGED_K[wt][ki]
+    rows = 11
+    log("dequant rows", wt, K)
+    W = inputs.gen_weights(wt, rows, K, 60 + wt + ki)
+    y = g.dequantize(T(W, dev), wt, K)
+    table = oracle.dequantize(wt, W, rows, K)
+    assert np.array_equal(host(y).view(np.uint32), table.view(np.uint32))
+    ids = np.array([rows - 1, 0, -1, rows, 3, 3, rows - 2, 7, 2**31 - 1, 1], np.int32)
+    yb = g.get_rows(T(W, dev), wt, K, T(ids, dev), torch.bfloat16)
+    tb = oracle.dequantize(wt, W, rows, K, oracle.BF16)
+    ok = (ids >= 0) & (ids < rows)
+    ref = np.zeros((ids.size, K), tb.dtype)
+    ref[ok] = tb[ids[ok]]
+    assert np.array_equal(yb.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
 def test_get_rows_empty_and_errors(dev):
     W = T(inputs.gen_q4_K(8, 256, 42), dev)
     assert g.get_rows(W, g.Q4_K, 256, torch.empty(0, dtype=torch.int32, device=dev)).shape == (0, 256)
