@@ -49,12 +49,14 @@ ROTATE_BYTES = 1 << 30
 # by kernel, with the hash of the kernel sources they were measured on: reported
 # as null once those sources change.
 PROFILE_TRAFFIC = {
-    "mmvq_kernel<Q4_K,NC=1>": (9813192, "e34e9232017e3f2d"),
-    "mmvq_kernel<Q6_K,NC=1>": (419647048, "e34e9232017e3f2d"),
-    "mmq_kernel<Q4_K> 8192x2048 M=8192": (539830813, "fd306f747ed1a819"),
+    "mmvq_kernel<Q4_K,NC=1>": (9799948, "91c2d6acffd71e4b"),
+    "mmvq_kernel<Q6_K,NC=1>": (419662083, "91c2d6acffd71e4b"),
+    "mmq_kernel<Q4_K> 8192x2048 M=8192": (539850193, "c853d2e2da691aaf"),
+    "dequant_rows_kernel<Q6_K> (get_rows)": (48517864, "00bc638143aba435"),
 }
 KERNEL_SOURCES = {"mmvq": ("mmvq.hip", "common.hpp", "kernels.hpp"),
-                  "mmq": ("mmq.hip", "common.hpp", "kernels.hpp")}
+                  "mmq": ("mmq.hip", "common.hpp", "kernels.hpp"),
+                  "dequant": ("convert.hip", "common.hpp", "kernels.hpp")}
 
 
 def source_hash(kind):
