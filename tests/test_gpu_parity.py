@@ -158,6 +158,37 @@ def test_dequant_row_lengths(dev, wt, ki):
     assert np.array_equal(yb.view(torch.int16).cpu().numpy().view(np.uint16), ref)
 
 
+@pytest.mark.parametrize("ydt", [torch.bfloat16, torch.float32])
+def test_get_rows_strided_output(dev, ydt):
+    """Output rows ldy > K apart (through the C ABI): each row's K values equal
+    the oracle's table row; the gap after each row keeps its canary; a row
+    table over 8 KB takes the unstaged kernel with the same result."""
+    import ctypes
+    L = g.lib()
+    for wt, K in [(g.Q6_K, 512), (g.Q8_0, 7744)]:
+        log("get_rows strided", wt, K, ydt)
+        rows, n = 9, 6
+        W = inputs.gen_weights(wt, rows, K, 70 + wt)
+        ids = np.array([8, 0, 3, -2, 3, 7], np.int32)
+        ldy = K + (8 if ydt == torch.bfloat16 else 4) * 3
+        canary = torch.full((n, ldy), -7.0, dtype=ydt, device=dev)
+        Wd, idd = T(W, dev), T(ids, dev)
+        ydt_c = g.BF16 if ydt == torch.bfloat16 else g.F32
+        rc = L.ggq_get_rows(wt, ctypes.c_void_p(Wd.data_ptr()), rows, K, ctypes.c_void_p(idd.data_ptr()), n,
+                            ctypes.c_void_p(canary.data_ptr()), ydt_c, ldy, None)
+        assert rc == 0
+        torch.cuda.synchronize()
+        got = canary.float().cpu().numpy()
+        table = oracle.dequantize(wt, W, rows, K)
+        if ydt == torch.bfloat16:
+            table = torch.from_numpy(table).to(torch.bfloat16).float().numpy()
+        ok = (ids >= 0) & (ids < rows)
+        ref = np.zeros((n, K), np.float32)
+        ref[ok] = table[ids[ok]]
+        assert np.array_equal(got[:, :K].view(np.uint32), ref.view(np.uint32))
+        assert (got[:, K:] == -7.0).all()
+
+
 def test_get_rows_empty_and_errors(dev):
     W = T(inputs.gen_q4_K(8, 256, 42), dev)
     assert g.get_rows(W, g.Q4_K, 256, torch.empty(0, dtype=torch.int32, device=dev)).shape == (0, 256)
