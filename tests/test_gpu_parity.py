@@ -158,6 +158,28 @@ def test_dequant_row_lengths(dev, wt, ki):
     assert np.array_equal(yb.view(torch.int16).cpu().numpy().view(np.uint16), ref)
 
 
+@pytest.mark.parametrize("wt", [g.Q4_K, g.Q6_K, g.Q8_0])
+def test_dequant_many_rows_per_wave(dev, wt):
+    """More output rows than the staged kernel's 8192 waves, so each wave walks
+    several rows with the next row's loads in flight: dequantize of a
+    20,000-row table and get_rows of 30,000 ids (a run of invalid ids in the
+    middle, so waves go from valid to invalid rows and back), bit-exact."""
+    rows, K = 20000, 256
+    log("dequant many rows", wt)
+    W = inputs.gen_weights(wt, rows, K, 80 + wt)
+    table = oracle.dequantize(wt, W, rows, K, oracle.BF16)
+    y = g.dequantize(T(W, dev), wt, K, torch.bfloat16)
+    assert np.array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), table)
+    ids = inputs.rng(81).integers(0, rows, 30000).astype(np.int32)
+    ids[12000:12500] = -1
+    ids[20000:20003] = [rows, rows + 7, -5]
+    yb = g.get_rows(T(W, dev), wt, K, T(ids, dev), torch.bfloat16)
+    ok = (ids >= 0) & (ids < rows)
+    ref = np.zeros((ids.size, K), np.uint16)
+    ref[ok] = table[ids[ok]]
+    assert np.array_equal(yb.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
 @pytest.mark.parametrize("ydt", [torch.bfloat16, torch.float32])
 def test_get_rows_strided_output(dev, ydt):
     """Output rows ldy > K apart (through the C ABI): each row's K values equal
