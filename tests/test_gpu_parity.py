@@ -129,19 +129,20 @@ def test_get_rows_bit_exact(dev, wt, ydt):
                           ref.view(np.uint32) if ydt == torch.float32 else ref)
 
 
-# Row lengths around the staged kernel's 8192-byte limit, and short rows whose
+# Row lengths around the staged kernel's 8192-byte limit, short rows whose
 # start phase within a 16-byte line takes every even value (18- and 34-byte
-# blocks, an odd number of them): K -> bytes per row for each type.
-RAGGED_K = {g.Q4_0: [96, 14560, 14592], g.Q8_0: [96, 7680, 7744], g.Q4_K: [256, 14336, 14592],
-            g.Q5_K: [768, 11776, 12032], g.Q6_K: [768, 9984, 10240]}
+# blocks, an odd number of them), and rows of 2..4 KB: K for each type.
+RAGGED_K = {g.Q4_0: [96, 14560, 14592, 4096], g.Q8_0: [96, 7680, 7744, 2048], g.Q4_K: [256, 14336, 14592, 4096],
+            g.Q5_K: [768, 11776, 12032, 4096], g.Q6_K: [768, 9984, 10240, 4096]}
 
 
 @pytest.mark.parametrize("wt", TYPES)
-@pytest.mark.parametrize("ki", [0, 1, 2])
+@pytest.mark.parametrize("ki", [0, 1, 2, 3])
 def test_dequant_row_lengths(dev, wt, ki):
     """dequantize and get_rows bit-exact for row lengths at and past the LDS
-    staging limit (8064..8400 bytes) and for short rows at every 16-byte phase,
-    including the last row of a table whose end is not 16-byte aligned."""
+    staging limit (8064..8400 bytes), rows of 2..4 KB (four loads a lane), and
+    short rows at every 16-byte phase, including the last row of a table whose
+    end is not 16-byte aligned."""
     K = RAGGED_K[wt][ki]
     rows = 11
     log("dequant rows", wt, K)
