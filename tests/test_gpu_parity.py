@@ -444,6 +444,27 @@ def test_c4_q6_K_lm_head_m1_all_rows(dev):
     assert r <= TOL["f32"]
 
 
+def test_get_rows_full_table_sampled(dev):
+    """The get_rows workload as timed: 8192 ids over the whole 248320 x 2048
+    Q6_K table, bf16 out; 96 sampled output rows bit-exact against the
+    oracle's dequantization of their table rows, plus every row's first and
+    last 16 values."""
+    rows, K, n = 248320, 2048, 8192
+    W = inputs.gen_q6_K(rows, K, 401)
+    ids = inputs.rng(404).integers(0, rows, n).astype(np.int32)
+    y = g.get_rows(T(W, dev), g.Q6_K, K, T(ids, dev), torch.bfloat16).view(torch.int16).cpu().numpy().view(np.uint16)
+    rb = W.size // rows
+    Wr = W.reshape(rows, rb)
+    pick = inputs.rng(405).choice(n, 96, replace=False)
+    ref = oracle.dequantize(g.Q6_K, np.ascontiguousarray(Wr[ids[pick]]).reshape(-1), 96, K, oracle.BF16)
+    assert np.array_equal(y[pick], ref)
+    # ends of every row: the first and the last block of each id
+    first = oracle.dequantize(g.Q6_K, np.ascontiguousarray(Wr[ids, :210]).reshape(-1), n, 256, oracle.BF16)
+    last = oracle.dequantize(g.Q6_K, np.ascontiguousarray(Wr[ids, rb - 210:]).reshape(-1), n, 256, oracle.BF16)
+    assert np.array_equal(y[:, :16], first[:, :16])
+    assert np.array_equal(y[:, -16:], last[:, -16:])
+
+
 def test_c4_q6_K_lm_head_m2048_sampled(dev):
     W = inputs.gen_q6_K(248320, 2048, 401)
     x = inputs.gen_act(2048, 2048, 402, "bf16")
